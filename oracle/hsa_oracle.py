@@ -1,0 +1,347 @@
+"""CPU oracle of the HSA decode step -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the package's smoke check and the benchmark's CPU-baseline leg
+may import this module.  It shares no code with the GPU path (the HIP
+library): it is a plain, slow, float64 NumPy restatement of what the method
+computes, written from these pages:
+
+  [WA]  "WorldAttention: An Efficient Attention Architecture for Interactive
+        Video World Models", paper full text (paperpeel.com/paper/2609.34606)
+  [SUM] the structured Chinese summary of the same paper
+        (paper.rainbus.top/paper/2609.34606), method steps (1)-(6)
+
+Steps, in the pages' order:
+  S1 page scoring   [WA §3.2 "Stage 2: page-level retrieval", score equation;
+                     SUM step (3)]: alpha_j = mean_h( Qbar_h . Kbar_{j,h} ) / sqrt(d_k),
+                     top-K_p pages.
+  S2 active KV      [WA §3.2 "Active KV construction"; SUM step (4)]: the
+                     selected pages concatenated, ascending page id.
+  S3 linear branch  [WA §3.3 "Linear branch", output equation; SUM
+                     prerequisites, linear attention]: Ktil = E_K K,
+                     Vtil = E_V V (E given as [r][L]); O_lin = softmax(Q Ktil^T/sqrt d) Vtil.
+  S4 block selection[WA §3.3 "Head-level sparsity adaptation"; appendix A.1.2;
+                     SUM step (5)]: mean-pooled blocks, pooled softmax mass per
+                     (head, query block); the smallest set of key blocks whose
+                     mass reaches tau_h.
+  S5 sparse branch  [WA §3.3 "Sparse branch"; appendix A.1.3]: exact softmax
+                     attention restricted to the tokens of the selected blocks.
+  S6 fusion         [WA §3.3 "Gated fusion of two branches"; SUM step (6)]:
+                     G = X W, sigmoid gates per (token, head) and branch,
+                     O = O_lin * g_lin + O_sp * g_sp.
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes of the repository):
+  * head averaging of the page score (Qbar has one vector per head);
+  * ties in any top-k go to the lower index; selections are emitted in
+    ascending index order;
+  * blocks are contiguous B-token ranges of the tile-major sequence; pooling
+    is the mean; the mass is the softmax of pooled logits with the same
+    1/sqrt(d) scale; "exceeds" is read as >=, tau_h >= 1 keeps every block,
+    and at least one block is always kept;
+  * one E_K and one E_V per layer shared by all heads; two independent
+    sigmoid gates, W given as [2H][D] (row c -> gate column c), no bias.
+
+Selections at near-ties are flagged (gap < TIE_EPS); there several answers
+are valid and `valid_page_selection` / `valid_block_selection` decide
+validity instead of equality.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Sequence, Tuple
+
+import numpy as np
+
+TIE_EPS = 1e-5
+
+# --------------------------------------------------------------------------
+# O1 -- token order.  [WA appendix A.1.3]: each contiguous group of B tokens
+# of the flattened sequence is one (C_t, C_h, C_w) cube of the (T, H, W)
+# latent volume.  The cube order and the order inside a cube are not given
+# (the formula is missing from the page); reading: cubes in raster order of
+# the cube grid, tokens raster order inside the cube.
+# --------------------------------------------------------------------------
+
+
+def tile_major_index(f: int, y: int, x: int, frame_h: int, frame_w: int,
+                     tile: Tuple[int, int, int]) -> int:
+    ct, ch, cw = tile
+    gh, gw = frame_h // ch, frame_w // cw
+    b = ct * ch * cw
+    cube = ((f // ct) * gh + y // ch) * gw + x // cw
+    inner = ((f % ct) * ch + y % ch) * cw + x % cw
+    return cube * b + inner
+
+
+def raster_to_tile_major(n_frames: int, frame_h: int, frame_w: int,
+                         tile: Tuple[int, int, int]) -> np.ndarray:
+    """perm[raster_index] = tile-major index, for a volume of n_frames frames."""
+    out = np.empty(n_frames * frame_h * frame_w, dtype=np.int64)
+    i = 0
+    for f in range(n_frames):
+        for y in range(frame_h):
+            for x in range(frame_w):
+                out[i] = tile_major_index(f, y, x, frame_h, frame_w, tile)
+                i += 1
+    return out
+
+
+# --------------------------------------------------------------------------
+# S1 -- page scoring.  [WA §3.2 Stage 2, score equation; SUM step (3)]
+# --------------------------------------------------------------------------
+
+
+def mean_over_tokens(t: np.ndarray) -> np.ndarray:
+    """[N][H][d] -> [H][d]: the average over the N tokens (float64)."""
+    return np.asarray(t, dtype=np.float64).mean(axis=0)
+
+
+def page_scores(qbar: np.ndarray, kbars: np.ndarray) -> np.ndarray:
+    """qbar [H][d], kbars [P][H][d] -> alpha [P].
+
+    alpha_j = (1/H) sum_h qbar_h . kbar_{j,h} / sqrt(d)  (head-averaged reading).
+    """
+    H, d = qbar.shape
+    dots = np.einsum("hd,phd->ph", qbar.astype(np.float64), kbars.astype(np.float64))
+    return dots.mean(axis=1) / math.sqrt(d)
+
+
+def top_k_lower_index(vals: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Order by (value descending, index ascending); return (order, top-k ascending)."""
+    idx = np.arange(len(vals))
+    order = np.lexsort((idx, -np.asarray(vals, dtype=np.float64)))
+    return order, np.sort(order[:k])
+
+
+def select_pages(alpha: np.ndarray, k: int) -> Tuple[np.ndarray, bool]:
+    """Top-k pages (ascending ids) and whether the k-th/(k+1)-th gap is a near-tie."""
+    order, sel = top_k_lower_index(alpha, k)
+    tie = False
+    if k < len(alpha):
+        tie = bool(alpha[order[k - 1]] - alpha[order[k]] < TIE_EPS)
+    return sel, tie
+
+
+def valid_page_selection(alpha: np.ndarray, sel: Sequence[int], k: int) -> bool:
+    sel = np.asarray(sel)
+    if len(sel) != k or len(set(sel.tolist())) != k:
+        return False
+    if np.any(sel < 0) or np.any(sel >= len(alpha)):
+        return False
+    rest = np.setdiff1d(np.arange(len(alpha)), sel)
+    if len(rest) == 0:
+        return True
+    return bool(alpha[sel].min() >= alpha[rest].max() - TIE_EPS)
+
+
+def score_and_select(q: np.ndarray, pages_k: Sequence[np.ndarray], k: int):
+    qbar = mean_over_tokens(q)
+    kbars = np.stack([mean_over_tokens(p) for p in pages_k])
+    alpha = page_scores(qbar, kbars)
+    sel, tie = select_pages(alpha, k)
+    return dict(qbar=qbar, kbars=kbars, alpha=alpha, sel=sel, tie=tie)
+
+
+# --------------------------------------------------------------------------
+# S2 -- active KV.  [WA §3.2 "Active KV construction"; SUM step (4)]
+# --------------------------------------------------------------------------
+
+
+def gather_active(pages: Sequence[np.ndarray], sel: Sequence[int]) -> np.ndarray:
+    """Concatenate the selected pages ([Lp][H][d] each), ascending id -> [H][L][d]."""
+    cat = np.concatenate([np.asarray(pages[j]) for j in sel], axis=0)   # [L][H][d]
+    return np.ascontiguousarray(cat.transpose(1, 0, 2))
+
+
+# --------------------------------------------------------------------------
+# S3 -- linear branch.  [WA §3.3 "Linear branch", output equation;
+# SUM prerequisites, Linformer projection E_K^T K with r << L]
+# --------------------------------------------------------------------------
+
+
+def project(e: np.ndarray, act: np.ndarray) -> np.ndarray:
+    """e [r][L], act [H][L][d] -> [H][r][d]: the sequence-axis projection per head."""
+    return np.einsum("rl,hld->hrd", e.astype(np.float64), act.astype(np.float64))
+
+
+def softmax_rows(s: np.ndarray) -> np.ndarray:
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    return p / p.sum(axis=-1, keepdims=True)
+
+
+def linear_attention(q: np.ndarray, ktil: np.ndarray, vtil: np.ndarray) -> np.ndarray:
+    """q [Lq][H][d], ktil/vtil [H][r][d] -> O_lin [Lq][H][d]."""
+    Lq, H, d = q.shape
+    out = np.empty((Lq, H, d))
+    for h in range(H):
+        s = q[:, h, :].astype(np.float64) @ ktil[h].T / math.sqrt(d)
+        out[:, h, :] = softmax_rows(s) @ vtil[h]
+    return out
+
+
+def linear_branch(q, k_act, v_act, e_k, e_v):
+    ktil = project(e_k, k_act)
+    vtil = project(e_v, v_act)
+    return dict(ktil=ktil, vtil=vtil, o_lin=linear_attention(q, ktil, vtil))
+
+
+# --------------------------------------------------------------------------
+# S4 -- head-adaptive block selection.  [WA §3.3 "Head-level sparsity
+# adaptation"; appendix A.1.2 (cheap coarse estimate of where the mass is);
+# SUM step (5), pooled coarse selection]
+# --------------------------------------------------------------------------
+
+
+def block_means(t: np.ndarray, b: int) -> np.ndarray:
+    """[H][N][d] -> [H][N/b][d]: mean of each contiguous b-token block."""
+    H, N, d = t.shape
+    return np.asarray(t, dtype=np.float64).reshape(H, N // b, b, d).mean(axis=2)
+
+
+def pooled_mass(qbar_i: np.ndarray, kbar: np.ndarray) -> np.ndarray:
+    """qbar_i [d], kbar [nKB][d] -> softmax over key blocks of qbar_i.kbar_j/sqrt(d)."""
+    d = qbar_i.shape[0]
+    s = kbar.astype(np.float64) @ qbar_i.astype(np.float64) / math.sqrt(d)
+    return softmax_rows(s[None, :])[0]
+
+
+def select_blocks(m: np.ndarray, tau: float) -> Tuple[np.ndarray, bool]:
+    """Smallest mass-ordered prefix whose cumulative mass reaches tau (ascending ids), tie flag."""
+    n_all = len(m)
+    order, _ = top_k_lower_index(m, n_all)
+    c = np.cumsum(m[order])
+    tau = float(tau)
+    if tau >= 1.0:
+        n = n_all
+    else:
+        hit = np.nonzero(c >= tau)[0]
+        n = int(hit[0]) + 1 if len(hit) else n_all
+    sel = np.sort(order[:n])
+    flag = False
+    if tau < 1.0:
+        if n < n_all and m[order[n - 1]] - m[order[n]] < TIE_EPS:
+            flag = True
+        if abs(c[n - 1] - tau) < TIE_EPS:
+            flag = True
+        if n >= 2 and abs(c[n - 2] - tau) < TIE_EPS:
+            flag = True
+    return sel, flag
+
+
+def valid_block_selection(m: np.ndarray, sel: Sequence[int], tau: float) -> bool:
+    sel = np.asarray(sel)
+    n_all = len(m)
+    if len(sel) == 0 or len(set(sel.tolist())) != len(sel):
+        return False
+    if np.any(sel < 0) or np.any(sel >= n_all):
+        return False
+    if float(tau) >= 1.0:
+        return len(sel) == n_all
+    rest = np.setdiff1d(np.arange(n_all), sel)
+    if len(rest) and m[sel].min() < m[rest].max() - TIE_EPS:
+        return False
+    tot = m[sel].sum()
+    if tot < tau - TIE_EPS:
+        return False
+    return bool(tot - m[sel].min() < tau + TIE_EPS)
+
+
+def block_selection(q: np.ndarray, k_act: np.ndarray, tau: Sequence[float], b: int):
+    """q [Lq][H][d], k_act [H][L][d] -> per (h, i) selections, masses and tie flags."""
+    qb = block_means(np.asarray(q).transpose(1, 0, 2), b)     # [H][nQB][d]
+    kb = block_means(k_act, b)                                 # [H][nKB][d]
+    H, nqb, _ = qb.shape
+    nkb = kb.shape[1]
+    mass = np.empty((H, nqb, nkb))
+    sel: List[List[np.ndarray]] = []
+    flags = np.zeros((H, nqb), dtype=bool)
+    for h in range(H):
+        row = []
+        for i in range(nqb):
+            mass[h, i] = pooled_mass(qb[h, i], kb[h])
+            s, f = select_blocks(mass[h, i], tau[h])
+            row.append(s)
+            flags[h, i] = f
+        sel.append(row)
+    counts = np.array([[len(s) for s in r] for r in sel], dtype=np.int64)
+    return dict(qbar=qb, kbar=kb, mass=mass, sel=sel, counts=counts, flags=flags)
+
+
+# --------------------------------------------------------------------------
+# S5 -- block-sparse attention.  [WA §3.3 "Sparse branch"; appendix A.1.3]
+# Given the selection this has a plain definition: softmax attention over
+# exactly the tokens of the selected key blocks (computed two-pass here).
+# --------------------------------------------------------------------------
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Plain softmax attention: q [n][d], k/v [m][d] -> [n][d] (float64)."""
+    d = q.shape[-1]
+    s = q.astype(np.float64) @ k.astype(np.float64).T / math.sqrt(d)
+    mx = s.max(axis=1, keepdims=True)
+    p = np.exp(s - mx)
+    return (p @ v.astype(np.float64)) / p.sum(axis=1, keepdims=True)
+
+
+def sparse_row(q_i: np.ndarray, k_h: np.ndarray, v_h: np.ndarray, blocks: Sequence[int], b: int) -> np.ndarray:
+    idx = np.concatenate([np.arange(j * b, (j + 1) * b) for j in blocks])
+    return attention(q_i, k_h[idx], v_h[idx])
+
+
+def sparse_attention(q, k_act, v_act, sel, b):
+    """q [Lq][H][d]; sel[h][i] block ids -> O_sp [Lq][H][d]."""
+    Lq, H, d = q.shape
+    out = np.empty((Lq, H, d))
+    for h in range(H):
+        for i in range(Lq // b):
+            out[i * b:(i + 1) * b, h, :] = sparse_row(q[i * b:(i + 1) * b, h, :], k_act[h], v_act[h], sel[h][i], b)
+    return out
+
+
+# --------------------------------------------------------------------------
+# S6 -- gated fusion.  [WA §3.3 "Gated fusion of two branches"; SUM step (6)]
+# --------------------------------------------------------------------------
+
+
+def sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def gates(x: np.ndarray, w_g: np.ndarray, n_heads: int) -> Tuple[np.ndarray, np.ndarray]:
+    """x [Lq][D], w_g [2H][D] -> (g_lin, g_sp), each [Lq][H]."""
+    g = x.astype(np.float64) @ w_g.astype(np.float64).T
+    s = sigmoid(g)
+    return s[:, :n_heads], s[:, n_heads:]
+
+
+def fuse_with(g_lin, g_sp, o_lin, o_sp):
+    return o_lin * g_lin[:, :, None] + o_sp * g_sp[:, :, None]
+
+
+def fuse(x, w_g, o_lin, o_sp):
+    gl, gs = gates(x, w_g, o_lin.shape[1])
+    return fuse_with(gl, gs, o_lin, o_sp)
+
+
+# --------------------------------------------------------------------------
+# Whole step (one layer, one denoising step)
+# --------------------------------------------------------------------------
+
+
+def hsa_step(q, pages_k, pages_v, e_k, e_v, w_g, x, tau, n_sel_pages, block,
+             sel_pages=None, block_sel=None) -> Dict[str, object]:
+    """Run S1..S6.  `sel_pages` / `block_sel` override the selections (used to
+    re-run the downstream stages with another valid selection at a tie)."""
+    q = np.asarray(q, dtype=np.float64)
+    sc = score_and_select(q, pages_k, n_sel_pages)
+    sp = np.asarray(sc["sel"] if sel_pages is None else sel_pages)
+    k_act = gather_active([np.asarray(p, np.float64) for p in pages_k], sp)
+    v_act = gather_active([np.asarray(p, np.float64) for p in pages_v], sp)
+    lin = linear_branch(q, k_act, v_act, e_k, e_v)
+    bs = block_selection(q, k_act, tau, block)
+    bsel = bs["sel"] if block_sel is None else block_sel
+    o_sp = sparse_attention(q, k_act, v_act, bsel, block)
+    out = fuse(x, w_g, lin["o_lin"], o_sp)
+    return dict(score=sc, sel_pages=sp, k_act=k_act, v_act=v_act, lin=lin,
+                blocks=bs, block_sel=bsel, o_sp=o_sp, out=out)
