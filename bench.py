@@ -1,0 +1,219 @@
+"""Benchmark of the HSA decode step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--config c1_full] [--no-cpu-baseline]
+
+One step = the whole hot path over one chunk of one layer: page scoring ->
+gather -> linear branch -> block selection -> sparse branch -> fusion (six
+C-ABI calls on one stream), on seeded synthetic inputs already resident in
+HBM.  Prints ONE JSON line.  The metric is ms per chunk (lower is better);
+attended TFLOP/s of the sparse branch, per-stage times, the roofline of the
+dominant kernel and the CPU oracle's time (bounded sample) are reported in
+the same line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HSA ms/chunk at 49,920 retrieved tokens; attended TFLOP/s & % MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 matrix peak
+PEAK_F32_TFLOPS = 157.3      # MI355X dense fp32 matrix peak
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+STAGES = ("score", "gather", "linear", "select", "sparse", "fuse")
+
+
+def stage_model(cfg, n_sel_total: int):
+    """Algorithmic work of one call of each stage (bytes moved or flops)."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    H, d, Lp, Lq, L, B, r, P = (cfg.n_heads, cfg.head_dim, cfg.page_tokens, cfg.query_tokens,
+                                cfg.active_tokens, cfg.block, cfg.rank, cfg.n_pages)
+    D = H * d
+    return {
+        "score": dict(bound="hbm", bytes=P * Lp * D * es + Lq * D * es),
+        "gather": dict(bound="hbm", bytes=2 * (2 * L * D * es)),
+        "linear": dict(bound="mfma", flops=2 * 2 * H * r * L * d + 2 * 2 * H * Lq * r * d,
+                       bytes=2 * L * D * es + 2 * r * L * es + Lq * D * es + Lq * D * 4),
+        "select": dict(bound="hbm", bytes=Lq * D * es + H * (L // B) * d * 4),
+        "sparse": dict(bound="mfma", flops=4 * B * B * d * n_sel_total),
+        "fuse": dict(bound="hbm", bytes=Lq * D * es + 2 * Lq * D * 4 + Lq * D * es),
+    }
+
+
+def cpu_baseline(cfg, w, arrays):
+    """Time the float64 oracle on a bounded sample of the same workload and
+    scale it to one chunk: scoring and fusion run whole; gather, linear
+    branch and block selection run for head 0 (x H); the sparse branch for
+    head 0 on the first 8 query blocks (x H x nQB/8)."""
+    from oracle import hsa_oracle as orc
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    s, pk, pv = arrays
+    H, B = cfg.n_heads, cfg.block
+    nq = min(8, cfg.n_qblocks)
+    t = {}
+    t0 = time.perf_counter()
+    sc = orc.score_and_select(s["q"], pk, cfg.n_sel_pages)
+    t["score"] = time.perf_counter() - t0
+    sel = sc["sel"]
+    t0 = time.perf_counter()
+    cat_k = np.concatenate([pk[j][:, :1, :] for j in sel], axis=0).astype(np.float64).transpose(1, 0, 2)
+    cat_v = np.concatenate([pv[j][:, :1, :] for j in sel], axis=0).astype(np.float64).transpose(1, 0, 2)
+    t["gather"] = (time.perf_counter() - t0) * H
+    q0 = s["q"][:, :1, :].astype(np.float64)
+    t0 = time.perf_counter()
+    orc.linear_branch(q0, cat_k, cat_v, s["e_k"], s["e_v"])
+    t["linear"] = (time.perf_counter() - t0) * H
+    t0 = time.perf_counter()
+    bs = orc.block_selection(q0, cat_k, s["tau"][:1], B)
+    t["select"] = (time.perf_counter() - t0) * H
+    t0 = time.perf_counter()
+    orc.sparse_attention(q0[:nq * B], cat_k, cat_v, [bs["sel"][0][:nq]], B)
+    t["sparse"] = (time.perf_counter() - t0) * H * cfg.n_qblocks / nq
+    o = np.zeros((cfg.query_tokens, H, cfg.head_dim))
+    t0 = time.perf_counter()
+    orc.fuse(s["x"], s["w_g"], o, o)
+    t["fuse"] = time.perf_counter() - t0
+    total_ms = 1e3 * sum(t.values())
+    return {"value": round(total_ms, 1), "unit": "ms/chunk", "cores": int(cores), "kind": "oracle",
+            "sample": f"float64 NumPy oracle; scoring and fusion whole; gather, linear branch and block selection "
+                      f"on head 0 of {H} (x{H}); sparse branch on head 0, query blocks 0..{nq - 1} of "
+                      f"{cfg.n_qblocks} (x{H}x{cfg.n_qblocks}/{nq})",
+            "stages_ms": {k: round(1e3 * v, 1) for k, v in t.items()}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c1_full")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay the step as one HIP graph")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py: this build measures one GPU; --gpus > 1 is not supported "
+              "(the HSA step shards by head, see the design notes, but no multi-GPU path is built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synth import CONFIGS, Workload
+    from sparse_linear_attention_hsa_amd.ops import make_geom
+    from sparse_linear_attention_hsa_amd.step import HsaStep
+
+    cfg = CONFIGS[args.config]
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    w = Workload(cfg)
+    s = w.small_inputs()
+    pk_np = [w.page_k(j) for j in range(cfg.n_pages)]
+    pv_np = [w.page_v(j) for j in range(cfg.n_pages)]
+    up = lambda a: torch.from_numpy(a).to(tdt).cuda()
+    q, x, e_k, e_v, w_g = (up(s[k]) for k in ("q", "x", "e_k", "e_v", "w_g"))
+    tau = torch.from_numpy(s["tau"]).cuda()
+    pk = [up(a) for a in pk_np]
+    pv = [up(a) for a in pv_np]
+    geom = make_geom(cfg.n_heads, cfg.head_dim, cfg.frame_h, cfg.frame_w, cfg.frames_per_page,
+                     cfg.query_frames, cfg.tile, cfg.n_sel_pages, cfg.rank, cfg.dtype)
+    st = HsaStep(geom, cfg.n_pages)
+    stream = torch.cuda.current_stream()
+
+    def one_step(ev=None):
+        calls = (lambda: st.score(q, pk), lambda: st.gather(pk, pv), lambda: st.linear(q, e_k, e_v),
+                 lambda: st.select(q, tau), lambda: st.sparse(q), lambda: st.fuse(x, w_g))
+        for i, fn in enumerate(calls):
+            if ev is not None:
+                ev[i][0].record(stream)
+            fn()
+            if ev is not None:
+                ev[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_step()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    # timed region: K whole steps
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            one_step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+
+    # per-stage HIP events over a second timed pass (same launches, events between calls)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in STAGES]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        one_step(evs[k])
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(args.steps)]))
+                for i, name in enumerate(STAGES)}
+
+    counts = st.blk_count.cpu().numpy()
+    n_sel_total = int(counts.sum())
+    model = stage_model(cfg, n_sel_total)
+    sparse_tf = model["sparse"]["flops"] / (stage_ms["sparse"] * 1e-3) / 1e12
+    lin_tf = model["linear"]["flops"] / (stage_ms["linear"] * 1e-3) / 1e12
+    peak_tf = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    dom = max(STAGES, key=lambda k: stage_ms[k])
+    dm = model[dom]
+    if dm["bound"] == "mfma":
+        ach = dm["flops"] / (stage_ms[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(ach / peak_tf, 4), "traffic": None, "stage": dom}
+    else:
+        ach = dm["bytes"] / (stage_ms[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "stage": dom}
+
+    out = {
+        "metric": METRIC, "value": round(ms, 4), "unit": "ms/chunk", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "heads": cfg.n_heads, "head_dim": cfg.head_dim,
+                   "retrieved_tokens": cfg.active_tokens, "query_tokens": cfg.query_tokens,
+                   "history_pages": cfg.n_pages, "block": cfg.block, "rank": cfg.rank,
+                   "graph": bool(args.graph)},
+        "attended_tflops": round(sparse_tf, 1), "mfma_frac_sparse": round(sparse_tf / peak_tf, 4),
+        "selected_block_frac": round(n_sel_total / (cfg.n_heads * cfg.n_qblocks * cfg.n_kblocks), 4),
+        "linear_tflops": round(lin_tf, 1),
+        "score_gbs": round(model["score"]["bytes"] / (stage_ms["score"] * 1e-3) / 1e9, 1),
+        "gather_gbs": round(model["gather"]["bytes"] / (stage_ms["gather"] * 1e-3) / 1e9, 1),
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, w, (s, pk_np, pv_np))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

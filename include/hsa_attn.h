@@ -1,0 +1,230 @@
+/*
+ * hsa_attn.h -- C ABI of the Hybrid Sparse Attention (HSA) decode step over
+ * a paged KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The method is WorldAttention's (paper "WorldAttention: An Efficient
+ * Attention Architecture for Interactive Video World Models"): page-level
+ * retrieval of history KV pages by mean-query / mean-key score, a contiguous
+ * active KV buffer, a low-rank linear branch, a head-adaptive block-sparse
+ * branch, and a sigmoid-gated fusion of the two branches.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor argument is a DEVICE pointer owned by the caller, except
+ *    the page pointer tables (`page_k`, `page_v`), which are HOST arrays of
+ *    device pointers.  The library never allocates or frees memory and keeps
+ *    no mutable global state; scratch memory is the caller's workspace
+ *    (size from hsa_workspace_bytes).  Calls are re-entrant on different
+ *    streams as long as they do not share a workspace.
+ *  - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
+ *    default stream) and returns; results are valid once the stream has
+ *    reached that point.  No call synchronises with the host, so a sequence
+ *    of calls can be captured into a HIP graph.
+ *  - All arguments are validated on the host before anything is launched;
+ *    on any error nothing is launched and nothing is written, and the error
+ *    code says why.  HSA_ERR_HIP reports a failed launch (hipGetLastError);
+ *    faults inside a kernel surface at the caller's next synchronisation.
+ *  - Element type: Q, page K/V, the active KV, X, E_K, E_V, W_g and the
+ *    fused output all have the element type
+ *    geom->dtype (HSA_F32 or HSA_BF16).  Scores, means, masses, thresholds,
+ *    the projected K/V, the two branch outputs and gate overrides are float32.  Every reduction
+ *    and every selection decision is computed in float32 (never rounded to
+ *    bfloat16); the matrix products of the bf16 path take bf16 operands with
+ *    float32 accumulation.
+ *  - Token order: every token buffer is in tile-major order -- the sequence
+ *    is cut into contiguous groups of B = tile_t*tile_h*tile_w tokens, one
+ *    per (C_t, C_h, C_w) cube of the latent volume (paper, appendix A.1.3).
+ *    The library itself needs no raster knowledge.
+ *  - Sizes used below: H = n_heads, d = head_dim (64 or 128), D = H*d,
+ *    Lp = frames_per_page*frame_h*frame_w (tokens per page),
+ *    Lq = query_frames*frame_h*frame_w (query tokens of the chunk),
+ *    B = tile_t*tile_h*tile_w, L = n_sel_pages*Lp (active keys),
+ *    nKB = L/B, nQB = Lq/B, r = rank, P = n_pages.
+ */
+#ifndef HSA_ATTN_H
+#define HSA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HSA_ATTN_ABI_VERSION 1
+#define HSA_MAX_PAGES 128      /* pages per call (pointer tables travel as launch arguments) */
+#define HSA_MAX_KBLOCKS 2048   /* nKB limit of the block selection (one sort per row in LDS) */
+
+typedef enum {
+  HSA_OK = 0,
+  HSA_ERR_NULL_ARG = 1,    /* a required pointer is NULL                                */
+  HSA_ERR_BAD_SHAPE = 2,   /* geometry inconsistent (a tile does not divide, sizes <= 0) */
+  HSA_ERR_BAD_DTYPE = 3,   /* dtype not HSA_F32 / HSA_BF16                              */
+  HSA_ERR_BAD_PARAM = 4,   /* n_pages, K_p, head_dim, rank or flags out of range        */
+  HSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than hsa_workspace_bytes         */
+  HSA_ERR_HIP = 6          /* a HIP launch failed                                        */
+} hsa_rc;
+
+typedef enum { HSA_F32 = 0, HSA_BF16 = 1 } hsa_dtype;
+
+typedef struct {
+  int32_t n_heads, head_dim;             /* H, d (d in {64, 128})                        */
+  int32_t frame_h, frame_w;              /* latent frame size; tokens/frame = frame_h*frame_w */
+  int32_t frames_per_page, query_frames; /* frames in one KV page, frames in the query chunk */
+  int32_t tile_t, tile_h, tile_w;        /* block cube (C_t, C_h, C_w); must divide the above;
+                                            B = product, a multiple of 16, at most 192    */
+  int32_t n_sel_pages, rank;             /* K_p (pages retrieved), r (linear-branch rank) */
+  int32_t dtype;                         /* hsa_dtype                                     */
+} hsa_geom;
+
+typedef struct ihipStream_t* hsa_stream;  /* a hipStream_t */
+
+/* Linear-branch flags. */
+#define HSA_LIN_REUSE_PROJ 1  /* skip the projection: k_proj / v_proj are inputs        */
+#define HSA_LIN_PROJ_ONLY 2   /* only the projection: o_lin (and q) are not touched     */
+
+/* ---------------------------------------------------------------------------
+ * S1 -- page-level retrieval.  Paper section 3.2, "Stage 2: page-level
+ * retrieval" (score equation): alpha_j = Qbar . Kbar_j / sqrt(d), Qbar the
+ * mean query of the chunk, Kbar_j the mean key of page j; the top-K_p pages
+ * are retrieved.  Reading for several heads: the per-head dot products are
+ * averaged, alpha_j = (1/H) sum_h Qbar_h . Kbar_{j,h} / sqrt(d).  Ties go to
+ * the lower page id.
+ *
+ *  q           [Lq][H][d] dtype.
+ *  page_k      HOST array of n_pages device pointers, page j's keys [Lp][H][d]
+ *              dtype.  An entry may be NULL only if page_kmean is given: that
+ *              page's mean is then read from page_kmean[j] (a page that is not
+ *              resident in device memory is scored from its cached mean).
+ *  page_kmean  [P][H][d] float32 or NULL.  For every non-NULL page the mean
+ *              key is written here (a reusable page index); for NULL pages it
+ *              is read.
+ *  n_pages     1 <= P <= HSA_MAX_PAGES, K_p <= P.
+ *  scores      [P] float32 out: alpha_j.
+ *  sel_pages   [K_p] int32 out: the retrieved page ids, ascending.
+ *  ws          workspace of ws_bytes >= hsa_workspace_bytes(geom, n_pages).
+ * ------------------------------------------------------------------------- */
+hsa_rc hsa_score_pages(const hsa_geom* geom, const void* q, const void* const* page_k,
+                       float* page_kmean, int32_t n_pages, float* scores, int32_t* sel_pages,
+                       void* ws, size_t ws_bytes, hsa_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * S2 -- active KV construction.  Paper section 3.2, "Active KV construction";
+ * structured summary, method step (4): the retrieved pages are concatenated
+ * (ascending page id) into one contiguous buffer in device memory.
+ *
+ *  page_k, page_v  HOST arrays of n_pages non-NULL device pointers, each page
+ *                  [Lp][H][d] dtype (token-major, as the model writes them).
+ *  sel_pages       [K_p] int32 device, ascending ids in [0, n_pages) (the
+ *                  output of hsa_score_pages).  Out-of-range ids are clamped.
+ *  k_act           [H][L][d] dtype out: active keys, head-major.
+ *  v_act           [H][L/16][d][16] dtype out: active values, head-major, in
+ *                  16-token granules stored d-major (the transposed layout the
+ *                  PV and projection products read).  Element (h, t, c) is at
+ *                  ((h*(L/16) + t/16)*d + c)*16 + t%16.
+ *  kblk_mean       [H][nKB][d] float32 out or NULL: mean key of every B-token
+ *                  block of the active buffer (input of hsa_block_select).
+ * ------------------------------------------------------------------------- */
+hsa_rc hsa_gather_pages(const hsa_geom* geom, const void* const* page_k, const void* const* page_v,
+                        int32_t n_pages, const int32_t* sel_pages, void* k_act, void* v_act,
+                        float* kblk_mean, hsa_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * S3 -- linear branch.  Paper section 3.3, "Linear branch" (output equation);
+ * structured summary, prerequisite "linear attention": the sequence axis of
+ * K and V is projected to rank r (Linformer), Ktil_h = E_K K_h, Vtil_h = E_V V_h,
+ * and O_lin_h = softmax(Q_h Ktil_h^T / sqrt(d)) Vtil_h.  One E_K and one E_V
+ * per layer, shared by all heads.
+ *
+ *  q            [Lq][H][d] dtype.
+ *  k_act/v_act  as written by hsa_gather_pages.
+ *  e_k, e_v     [r][L] dtype (the weight layout of a sequence-axis Linear).
+ *  k_proj       [H][r][d] float32: out, or in with HSA_LIN_REUSE_PROJ.
+ *  v_proj       [H][d][r] float32 (Vtil transposed): out, or in with REUSE.
+ *               The projections stay in float32: with peaked heads |Q| is
+ *               large and a bf16 copy of Ktil would move the logits by more
+ *               than the output tolerance; the bf16 product splits Ktil into
+ *               a bf16 high and low part instead.
+ *  o_lin        [Lq][H][d] float32 out (untouched with HSA_LIN_PROJ_ONLY).
+ *  flags        0, HSA_LIN_REUSE_PROJ or HSA_LIN_PROJ_ONLY.
+ *  With HSA_LIN_REUSE_PROJ, k_act, v_act, e_k and e_v may be NULL.
+ * ------------------------------------------------------------------------- */
+hsa_rc hsa_linear_branch(const hsa_geom* geom, const void* q, const void* k_act, const void* v_act,
+                         const void* e_k, const void* e_v, void* k_proj, void* v_proj, float* o_lin,
+                         int32_t flags, void* ws, size_t ws_bytes, hsa_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * S4 -- head-adaptive block selection.  Paper section 3.3, "Head-level
+ * sparsity adaptation" (per head, the smallest set of blocks whose cumulative
+ * attention mass passes tau_h) and appendix A.1.2 (a cheap coarse estimate of
+ * where the mass lies); structured summary, method step (5) (block pooling).
+ * Readings: blocks are mean-pooled; for query block i of head h the mass of
+ * key block j is m_j = softmax_j(qbar_i . kbar_j / sqrt(d)); blocks are taken
+ * in order of decreasing m (ties: lower j first) until the running sum is
+ * >= tau_h; tau_h >= 1 keeps every block; at least one block is kept.
+ *
+ *  q          [Lq][H][d] dtype.
+ *  k_act      [H][L][d] dtype; may be NULL when kblk_mean is given.
+ *  kblk_mean  [H][nKB][d] float32 or NULL (computed from k_act when NULL).
+ *  tau        [H] float32, each > 0.
+ *  blk_count  [H][nQB] int32 out: number of selected key blocks.
+ *  blk_idx    [H][nQB][nKB] int32 out: selected key-block ids, ascending;
+ *             entries past the count are -1.
+ *  blk_mass   [H][nQB][nKB] float32 out or NULL: the pooled masses m.
+ *  Requires nKB <= HSA_MAX_KBLOCKS.
+ * ------------------------------------------------------------------------- */
+hsa_rc hsa_block_select(const hsa_geom* geom, const void* q, const void* k_act, const float* kblk_mean,
+                        const float* tau, int32_t* blk_count, int32_t* blk_idx, float* blk_mass,
+                        void* ws, size_t ws_bytes, hsa_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * S5 -- block-sparse attention.  Paper section 3.3, "Sparse branch" and
+ * appendix A.1.3: attention at token resolution, computed only between a
+ * query block and its selected key blocks: for query block i of head h,
+ * O = softmax(Q_i K_S^T / sqrt(d)) V_S over exactly the tokens S of the
+ * selected blocks.
+ *
+ *  q, k_act, v_act        as above.
+ *  blk_count, blk_idx     as written by hsa_block_select.  Entries outside
+ *                         [0, nKB) are skipped; a count is clamped to [0, nKB];
+ *                         a row with no valid block gets zeros.
+ *  o_sp                   [Lq][H][d] float32 out.
+ * ------------------------------------------------------------------------- */
+hsa_rc hsa_sparse_attn(const hsa_geom* geom, const void* q, const void* k_act, const void* v_act,
+                       const int32_t* blk_count, const int32_t* blk_idx, float* o_sp,
+                       void* ws, size_t ws_bytes, hsa_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * S6 -- gated fusion.  Paper section 3.3, "Gated fusion of two branches";
+ * structured summary, method step (6): G = X W, sigmoid gates, and
+ * O = O_lin * G_lin + O_sp * G_sp per head and token.  Reading: W has 2H
+ * output columns (no bias); column h gates the linear branch of head h and
+ * column H+h its sparse branch.
+ *
+ *  x              [Lq][D] dtype, or NULL to use gate_override.
+ *  w_g            [2H][D] dtype (row c produces gate column c); unused when x is NULL.
+ *  gate_override  [Lq][2H] float32 gate VALUES (after the sigmoid), used iff x == NULL.
+ *  o_lin, o_sp    [Lq][H][d] float32.
+ *  out            [Lq][H][d] dtype out.
+ * ------------------------------------------------------------------------- */
+hsa_rc hsa_fuse(const hsa_geom* geom, const void* x, const void* w_g, const float* gate_override,
+                const float* o_lin, const float* o_sp, void* out, hsa_stream stream);
+
+/* Bytes of workspace every call above needs for this geometry (0 if the
+ * geometry is invalid).  One workspace serves all calls on one stream. */
+size_t hsa_workspace_bytes(const hsa_geom* geom, int32_t n_pages);
+
+/* Host-only validation of a geometry (HSA_OK or the reason it is invalid). */
+hsa_rc hsa_geom_check(const hsa_geom* geom);
+
+/* Static text of a return code. */
+const char* hsa_rc_string(hsa_rc rc);
+
+/* HSA_ATTN_ABI_VERSION of the built library. */
+int32_t hsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSA_ATTN_H */

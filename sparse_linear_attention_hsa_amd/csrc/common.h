@@ -1,0 +1,152 @@
+// Device-side helpers shared by the HSA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hsa_attn.h"
+
+namespace hsa {
+
+typedef uint16_t bf16_t;  // storage of a bfloat16 value
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int kMaxPages = HSA_MAX_PAGES;
+
+// Page pointer tables travel by value as launch arguments.
+struct PageTable {
+  const void* p[kMaxPages];
+};
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// float -> bfloat16, round to nearest even (inputs here are finite).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+
+// Elements of T in one 16-byte chunk.
+template <typename T> struct Vec { static constexpr int N = 16 / sizeof(T); };
+
+// Unpack a 16-byte chunk of T into floats.
+template <typename T> __device__ __forceinline__ void unpack16(const uint4& c, float* out);
+template <> __device__ __forceinline__ void unpack16<float>(const uint4& c, float* out) {
+  out[0] = __uint_as_float(c.x); out[1] = __uint_as_float(c.y);
+  out[2] = __uint_as_float(c.z); out[3] = __uint_as_float(c.w);
+}
+template <> __device__ __forceinline__ void unpack16<bf16_t>(const uint4& c, float* out) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+// Pack floats into a 16-byte chunk of T.
+template <typename T> __device__ __forceinline__ uint4 pack16(const float* in);
+template <> __device__ __forceinline__ uint4 pack16<float>(const float* in) {
+  return make_uint4(__float_as_uint(in[0]), __float_as_uint(in[1]), __float_as_uint(in[2]), __float_as_uint(in[3]));
+}
+template <> __device__ __forceinline__ uint4 pack16<bf16_t>(const float* in) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = static_cast<uint32_t>(f32_to_bf16(in[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(in[2 * i + 1])) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// ---------------------------------------------------------------------------
+// 16x16 matrix-core step.  Lane l = 16*g + c (g = l/16 in 0..3, c = l%16)
+// supplies one 16-byte chunk of A row c and one of B column c; both chunks
+// hold the contraction elements of "slot g".  Any assignment of contraction
+// indices to (g, element) works as long as A and B use the same one, because
+// the product sums over all of them.  The result is the standard 16x16 layout:
+// lane (g, c) holds C[4g + i][c] in acc[i].
+//   bf16: contraction 32 per step (8 per lane), v_mfma_f32_16x16x32_bf16.
+//   f32 : contraction 16 per step (4 per lane), four v_mfma_f32_16x16x4_f32,
+//         instruction j taking element j of every lane's chunk.
+// ---------------------------------------------------------------------------
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16_t> {
+  static constexpr int K = 32;
+  __device__ __forceinline__ static void run(f32x4& acc, const uint4& a, const uint4& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<float> {
+  static constexpr int K = 16;
+  __device__ __forceinline__ static void run(f32x4& acc, const uint4& a, const uint4& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+  }
+};
+
+// Row permutation inside one contraction group of a product whose result is
+// fed back as the B operand of a second product (S^T -> P^T).  For bf16 the
+// second product contracts 32 keys per step, covering two 16-row result
+// tiles kt = 0, 1.  Loading result-tile kt row c from source row
+// perm_row(kt, c) = 8*(c/4) + 4*kt + c%4 makes lane (g, q) end up holding
+// source rows 8g .. 8g+7, i.e. one contiguous chunk of the second product's
+// operand.  For f32 (one 16-row tile per step) the identity does the same.
+template <typename T> __device__ __forceinline__ int perm_row(int kt, int c);
+template <> __device__ __forceinline__ int perm_row<bf16_t>(int kt, int c) { return 8 * (c >> 2) + 4 * kt + (c & 3); }
+template <> __device__ __forceinline__ int perm_row<float>(int kt, int c) { return c; }
+
+// Pack the probabilities a lane holds for one contraction step into the B chunk.
+template <typename T> __device__ __forceinline__ uint4 pack_p(const f32x4* p);
+template <> __device__ __forceinline__ uint4 pack_p<bf16_t>(const f32x4* p) {
+  float t[8] = {p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]};
+  return pack16<bf16_t>(t);
+}
+template <> __device__ __forceinline__ uint4 pack_p<float>(const f32x4* p) {
+  return make_uint4(__float_as_uint(p[0][0]), __float_as_uint(p[0][1]), __float_as_uint(p[0][2]), __float_as_uint(p[0][3]));
+}
+
+// Cross-lane reductions over the four lanes (g = 0..3) that share c = l%16.
+__device__ __forceinline__ float max4g(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float sum4g(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// The 8 XCDs of an MI355X receive consecutive workgroup ids round-robin.
+// Remapping blockIdx so that each XCD walks one contiguous range of work
+// items keeps the items an XCD runs together (same head, same K/V) in that
+// XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int per = ceil_div(n, 8);
+  const int x = bid & 7, k = bid >> 3;
+  const int item = x * per + k;
+  return (k < per && item < n) ? item : -1;
+}
+
+}  // namespace hsa

@@ -1,0 +1,148 @@
+// S2 -- active KV construction: the K_p retrieved pages, ascending id, copied
+// into one contiguous head-major buffer.  WorldAttention paper, section 3.2
+// "Active KV construction"; structured summary, method step (4).
+//
+// One workgroup moves one B-token block of one head of one selected page:
+//  * keys   [Lp][H][d] rows -> k_act [H][L][d]   (plain copy, 16-byte chunks),
+//    summing the block's keys on the way (the pooled block means of S4);
+//  * values [Lp][H][d] rows -> v_act [H][L/16][d][16] (16-token granules
+//    stored d-major), transposed through LDS, because the PV product and the
+//    low-rank projection contract over tokens and want tokens contiguous.
+// All loads of a block are issued before any store so each thread keeps
+// several 16-byte requests in flight (the kernel is HBM-bound).
+#include "common.h"
+#include "host.h"
+
+namespace hsa {
+namespace {
+
+constexpr int kGatherThreads = 256;
+constexpr int kBatch = 6;  // passes whose loads are in flight together
+
+template <typename T, int D>
+__global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
+    PageTable pk, PageTable pv, int n_pages, const int32_t* __restrict__ sel, int H, int Lp, int B,
+    int L, T* __restrict__ k_act, T* __restrict__ v_act, float* __restrict__ kblk_mean) {
+  constexpr int E = Vec<T>::N;
+  constexpr int CPR = D / E;                       // 16-byte chunks per (token, head) row
+  constexpr int RPP = kGatherThreads / CPR;        // rows per pass
+  constexpr int VPAD = E;                          // LDS row padding (elements)
+  constexpr int VS = D + VPAD;                     // LDS row stride (elements)
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* vs = reinterpret_cast<T*>(smem);                              // [B][VS]
+  float* red = reinterpret_cast<float*>(smem + (size_t)B * VS * sizeof(T));  // [256][E]
+
+  const int bpp = Lp / B;
+  const int p = blockIdx.x / bpp, blk = blockIdx.x % bpp, h = blockIdx.y;
+  int page = sel[p];
+  page = page < 0 ? 0 : (page >= n_pages ? n_pages - 1 : page);
+  const T* ksrc = reinterpret_cast<const T*>(pk.p[page]);
+  const T* vsrc = reinterpret_cast<const T*>(pv.p[page]);
+  const int t = threadIdx.x;
+  const int ch = t % CPR, r0 = t / CPR;
+  const size_t tok0 = (size_t)blk * B;           // first token of the block in the page
+  const size_t act0 = (size_t)p * Lp + tok0;     // first token of the block in the active buffer
+
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  const int npass = (B + RPP - 1) / RPP;
+  for (int base = 0; base < npass; base += kBatch) {
+    uint4 kv[kBatch], vv[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int row = (base + u) * RPP + r0;
+      if (base + u < npass && row < B) {
+        const size_t off = ((tok0 + row) * H + h) * D + ch * E;
+        kv[u] = ld16(ksrc + off);
+        vv[u] = ld16(vsrc + off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int row = (base + u) * RPP + r0;
+      if (base + u < npass && row < B) {
+        st16(k_act + ((size_t)h * L + act0 + row) * D + ch * E, kv[u]);
+        float f[E];
+        unpack16<T>(kv[u], f);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += f[e];
+        st16(vs + row * VS + ch * E, vv[u]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) red[t * E + e] = acc[e];
+  __syncthreads();
+
+  // values: [16 tokens][D] granules in LDS -> [D][16] granules in memory
+  constexpr int PARTS = 16 / E;  // 16-byte chunks per 16-token granule row
+  const int ngr = B / 16;
+  const size_t g0 = act0 / 16;
+  for (int c = t; c < ngr * D * PARTS; c += kGatherThreads) {
+    const int gr = c / (D * PARTS);
+    const int rem = c % (D * PARTS);
+    const int drow = rem / PARTS, part = rem % PARTS;
+    float f[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) f[e] = to_f32<T>(vs[(gr * 16 + part * E + e) * VS + drow]);
+    st16(v_act + (((size_t)h * (L / 16) + g0 + gr) * D + drow) * 16 + part * E, pack16<T>(f));
+  }
+
+  // block mean of the keys (fixed-order sum over the row phases)
+  if (kblk_mean != nullptr && t < CPR) {
+    float s[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[e] = 0.f;
+    for (int ph = 0; ph < RPP; ++ph) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[e] += red[(ph * CPR + t) * E + e];
+    }
+    const float inv = 1.f / (float)B;
+    const int j = (int)(act0 / B);
+    float* dst = kblk_mean + ((size_t)h * (L / B) + j) * D + t * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) dst[e] = s[e] * inv;
+  }
+}
+
+template <typename T, int D>
+void launch_gather(const Dims& s, const PageTable& pk, const PageTable& pv, int n_pages, const int32_t* sel,
+                   void* k_act, void* v_act, float* kblk_mean, hipStream_t st) {
+  constexpr int E = Vec<T>::N;
+  const size_t smem = (size_t)s.B * (D + E) * sizeof(T) + (size_t)kGatherThreads * E * sizeof(float);
+  dim3 grid(s.Kp * (s.Lp / s.B), s.H);
+  hipLaunchKernelGGL((gather_block_kernel<T, D>), grid, dim3(kGatherThreads), smem, st, pk, pv, n_pages,
+                     sel, s.H, s.Lp, s.B, s.L, reinterpret_cast<T*>(k_act), reinterpret_cast<T*>(v_act),
+                     kblk_mean);
+}
+
+}  // namespace
+}  // namespace hsa
+
+extern "C" hsa_rc hsa_gather_pages(const hsa_geom* geom, const void* const* page_k, const void* const* page_v,
+                                   int32_t n_pages, const int32_t* sel_pages, void* k_act, void* v_act,
+                                   float* kblk_mean, hsa_stream stream) {
+  using namespace hsa;
+  Dims s;
+  hsa_rc rc = derive(geom, &s);
+  if (rc != HSA_OK) return rc;
+  if (!page_k || !page_v || !sel_pages || !k_act || !v_act) return HSA_ERR_NULL_ARG;
+  if (n_pages < 1 || n_pages > HSA_MAX_PAGES || s.Kp > n_pages) return HSA_ERR_BAD_PARAM;
+  PageTable pk, pv;
+  for (int j = 0; j < kMaxPages; ++j) pk.p[j] = pv.p[j] = nullptr;
+  for (int j = 0; j < n_pages; ++j) {
+    if (!page_k[j] || !page_v[j]) return HSA_ERR_NULL_ARG;
+    pk.p[j] = page_k[j];
+    pv.p[j] = page_v[j];
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (s.bf16) {
+    if (s.d == 128) launch_gather<bf16_t, 128>(s, pk, pv, n_pages, sel_pages, k_act, v_act, kblk_mean, st);
+    else launch_gather<bf16_t, 64>(s, pk, pv, n_pages, sel_pages, k_act, v_act, kblk_mean, st);
+  } else {
+    if (s.d == 128) launch_gather<float, 128>(s, pk, pv, n_pages, sel_pages, k_act, v_act, kblk_mean, st);
+    else launch_gather<float, 64>(s, pk, pv, n_pages, sel_pages, k_act, v_act, kblk_mean, st);
+  }
+  return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
+}

@@ -1,0 +1,140 @@
+// Host-side geometry validation, work plans and workspace layout.
+#include "host.h"
+
+#include <algorithm>
+
+namespace hsa {
+
+namespace {
+inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+}  // namespace
+
+hsa_rc derive(const hsa_geom* g, Dims* o) {
+  if (!g) return HSA_ERR_NULL_ARG;
+  if (g->dtype != HSA_F32 && g->dtype != HSA_BF16) return HSA_ERR_BAD_DTYPE;
+  if (g->head_dim != 64 && g->head_dim != 128) return HSA_ERR_BAD_PARAM;
+  if (g->n_heads < 1 || g->n_heads > 32) return HSA_ERR_BAD_PARAM;
+  if (g->n_sel_pages < 1 || g->rank < 1 || g->rank > 256) return HSA_ERR_BAD_PARAM;
+  if (g->frame_h < 1 || g->frame_w < 1 || g->frames_per_page < 1 || g->query_frames < 1 ||
+      g->tile_t < 1 || g->tile_h < 1 || g->tile_w < 1)
+    return HSA_ERR_BAD_SHAPE;
+  if (g->frame_h % g->tile_h || g->frame_w % g->tile_w || g->frames_per_page % g->tile_t ||
+      g->query_frames % g->tile_t)
+    return HSA_ERR_BAD_SHAPE;
+  const long long B = 1LL * g->tile_t * g->tile_h * g->tile_w;
+  if (B % 16 || B > 192) return HSA_ERR_BAD_SHAPE;
+  const long long tpf = 1LL * g->frame_h * g->frame_w;
+  const long long Lp = tpf * g->frames_per_page, Lq = tpf * g->query_frames;
+  const long long L = Lp * g->n_sel_pages;
+  const long long D = 1LL * g->n_heads * g->head_dim;
+  // every buffer index must fit comfortably in 32-bit element offsets per head
+  if (Lp > (1LL << 24) || Lq > (1LL << 24) || L > (1LL << 24) || L * D > (1LL << 31) ||
+      Lq * D > (1LL << 31) || Lp * D > (1LL << 31))
+    return HSA_ERR_BAD_SHAPE;
+  if (L / B > HSA_MAX_KBLOCKS) return HSA_ERR_BAD_SHAPE;
+  Dims s;
+  s.H = g->n_heads; s.d = g->head_dim; s.D = (int)D;
+  s.Lp = (int)Lp; s.Lq = (int)Lq; s.B = (int)B; s.Kp = g->n_sel_pages; s.L = (int)L;
+  s.nKB = (int)(L / B); s.nQB = (int)(Lq / B); s.r = g->rank;
+  s.bf16 = g->dtype == HSA_BF16; s.esize = s.bf16 ? 2 : 4;
+  s.rows = s.H * s.nQB;
+  if (o) *o = s;
+  return HSA_OK;
+}
+
+ScorePlan score_plan(const Dims& s, int n_pages) {
+  ScorePlan p;
+  const int target = 2048;
+  int pc = std::max(1, std::min(cdiv(s.Lp, 16), cdiv(target, std::max(1, n_pages))));
+  p.page_rows = cdiv(s.Lp, pc);
+  p.page_chunks = cdiv(s.Lp, p.page_rows);
+  int qc = std::max(1, std::min(cdiv(s.Lq, 16), 128));
+  p.q_rows = cdiv(s.Lq, qc);
+  p.q_chunks = cdiv(s.Lq, p.q_rows);
+  p.units = n_pages * p.page_chunks + p.q_chunks;
+  return p;
+}
+
+ProjPlan proj_plan(const Dims& s) {
+  ProjPlan p;
+  const int K = s.bf16 ? 32 : 16;
+  p.steps = cdiv(s.L, K);
+  p.splits = std::max(1, std::min(p.steps, cdiv(512, 2 * s.H)));
+  p.rtiles = cdiv(s.r, 16);
+  p.rpad = cdiv(s.r, K) * K;
+  return p;
+}
+
+SparsePlan sparse_plan(const Dims& s) {
+  SparsePlan p;
+  p.granules_per_block = s.B / 16;
+  const int seg_blocks = 32;
+  int sg = seg_blocks * p.granules_per_block;
+  if (sg & 1) sg += 1;
+  p.seg_granules = sg;
+  p.max_segs = cdiv(s.nKB * p.granules_per_block, sg);
+  p.max_items = s.rows * p.max_segs;
+  p.grid = cdiv(p.max_items, 8) * 8;
+  return p;
+}
+
+WsLayout ws_layout(const Dims& s, int n_pages) {
+  WsLayout w;
+  const size_t hd = (size_t)s.H * s.d;
+  // score
+  ScorePlan sp = score_plan(s, n_pages);
+  w.score_partial = 0;
+  w.score_qbar = align256(w.score_partial + (size_t)sp.units * hd * 4);
+  w.score_kbar = align256(w.score_qbar + hd * 4);
+  w.score_end = align256(w.score_kbar + (size_t)n_pages * hd * 4);
+  // linear
+  ProjPlan pp = proj_plan(s);
+  w.lin_partial = 0;
+  w.lin_end = align256((size_t)pp.splits * 2 * s.H * pp.rtiles * 16 * s.d * 4);
+  // select
+  w.sel_qbar = 0;
+  w.sel_kbar = align256((size_t)s.H * s.nQB * s.d * 4);
+  w.sel_end = align256(w.sel_kbar + (size_t)s.H * s.nKB * s.d * 4);
+  // sparse
+  SparsePlan qp = sparse_plan(s);
+  w.sp_items = 0;
+  w.sp_rowinfo = align256((size_t)qp.max_items * 16);
+  w.sp_meta = align256(w.sp_rowinfo + (size_t)s.rows * 8);
+  w.sp_part_o = align256(w.sp_meta + 64);
+  w.sp_part_ml = align256(w.sp_part_o + (size_t)qp.max_items * s.B * s.d * 4);
+  w.sp_end = align256(w.sp_part_ml + (size_t)qp.max_items * s.B * 2 * 4);
+  w.total = std::max(std::max(w.score_end, w.lin_end), std::max(w.sel_end, w.sp_end));
+  return w;
+}
+
+}  // namespace hsa
+
+extern "C" {
+
+size_t hsa_workspace_bytes(const hsa_geom* geom, int32_t n_pages) {
+  hsa::Dims s;
+  if (hsa::derive(geom, &s) != HSA_OK) return 0;
+  if (n_pages < 1) n_pages = 1;
+  if (n_pages > HSA_MAX_PAGES) return 0;
+  return hsa::ws_layout(s, n_pages).total;
+}
+
+hsa_rc hsa_geom_check(const hsa_geom* geom) { return hsa::derive(geom, nullptr); }
+
+const char* hsa_rc_string(hsa_rc rc) {
+  switch (rc) {
+    case HSA_OK: return "HSA_OK";
+    case HSA_ERR_NULL_ARG: return "HSA_ERR_NULL_ARG: a required pointer is NULL";
+    case HSA_ERR_BAD_SHAPE: return "HSA_ERR_BAD_SHAPE: inconsistent geometry";
+    case HSA_ERR_BAD_DTYPE: return "HSA_ERR_BAD_DTYPE: dtype must be HSA_F32 or HSA_BF16";
+    case HSA_ERR_BAD_PARAM: return "HSA_ERR_BAD_PARAM: parameter out of range";
+    case HSA_ERR_WORKSPACE: return "HSA_ERR_WORKSPACE: workspace missing or too small";
+    case HSA_ERR_HIP: return "HSA_ERR_HIP: a HIP launch failed";
+  }
+  return "unknown hsa_rc";
+}
+
+int32_t hsa_abi_version(void) { return HSA_ATTN_ABI_VERSION; }
+
+}  // extern "C"

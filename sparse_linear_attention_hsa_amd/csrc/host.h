@@ -1,0 +1,66 @@
+// Host-side geometry, validation and workspace layout of the HSA library.
+// Plain C++ (no HIP), so the validation logic can be exercised without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "hsa_attn.h"
+
+namespace hsa {
+
+// Sizes derived from an hsa_geom.
+struct Dims {
+  int H, d, D, Lp, Lq, B, Kp, L, nKB, nQB, r;
+  int bf16;  // 1 if dtype == HSA_BF16
+  int esize; // bytes per element
+  int rows;  // H * nQB selection rows
+};
+
+hsa_rc derive(const hsa_geom* g, Dims* out);
+
+// Page scoring work split: units of `chunk_rows` tokens.
+struct ScorePlan {
+  int page_chunks;   // chunks per page
+  int page_rows;     // tokens per page chunk (last one ragged)
+  int q_chunks;      // chunks of the query buffer
+  int q_rows;
+  int units;         // n_pages * page_chunks + q_chunks
+};
+ScorePlan score_plan(const Dims& s, int n_pages);
+
+// Linear-branch projection split over the sequence axis.
+struct ProjPlan {
+  int splits;        // S: slices of the sequence axis per (head, K|V)
+  int steps;         // contraction steps of the whole sequence
+  int rtiles;        // ceil(r / 16)
+  int rpad;          // r padded to the product's contraction step
+};
+ProjPlan proj_plan(const Dims& s);
+
+// Sparse-branch segmentation of the selected-block rows.
+struct SparsePlan {
+  int granules_per_block;  // B / 16
+  int seg_granules;        // target granules per work item
+  int max_segs;            // per row
+  int max_items;           // rows * max_segs
+  int grid;                // launch size (multiple of 8)
+};
+SparsePlan sparse_plan(const Dims& s);
+
+// Byte offsets inside the caller's workspace; each call uses the regions it
+// needs, all starting at offset 0 of the same buffer.
+struct WsLayout {
+  // score
+  size_t score_partial, score_qbar, score_kbar, score_end;
+  // linear
+  size_t lin_partial, lin_end;
+  // select
+  size_t sel_qbar, sel_kbar, sel_end;
+  // sparse
+  size_t sp_items, sp_rowinfo, sp_meta, sp_part_o, sp_part_ml, sp_end;
+  size_t total;
+};
+WsLayout ws_layout(const Dims& s, int n_pages);
+
+}  // namespace hsa

@@ -1,0 +1,219 @@
+// S1 -- page-level retrieval: mean query, mean key of every page, head-averaged
+// score alpha_j = (1/H) sum_h Qbar_h . Kbar_{j,h} / sqrt(d), top-K_p pages.
+// WorldAttention paper, section 3.2 "Stage 2: page-level retrieval" (score
+// equation); structured summary, method step (3).
+//
+// HBM-bound streaming reduction.  Every page is read once, token row by token
+// row (each row is H*d contiguous elements); a workgroup reduces one chunk of
+// rows of one page into a float32 partial, then one workgroup per page sums
+// its partials in a fixed order (bitwise reproducible), and a last small
+// kernel scores and ranks the pages.
+#include "common.h"
+#include "host.h"
+
+namespace hsa {
+namespace {
+
+constexpr int kScoreThreads = 256;
+constexpr int kUnroll = 4;
+
+// Column layout of one workgroup: `cols` 16-byte chunks per row handled at
+// once, `par` rows in flight side by side.
+struct ColMap {
+  int cols, par;
+};
+inline ColMap col_map(int cpr) {
+  ColMap m;
+  m.cols = cpr < kScoreThreads ? cpr : kScoreThreads;
+  m.par = kScoreThreads / m.cols;
+  return m;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kScoreThreads) void score_partial_kernel(
+    const T* __restrict__ q, PageTable pages, int n_pages, int Lp, int Lq, int cpr,
+    int page_chunks, int page_rows, int q_rows, int mcols, int mpar, float* __restrict__ partial) {
+  constexpr int E = Vec<T>::N;
+  __shared__ float red[kScoreThreads * E];
+  const int unit = blockIdx.x;
+  const int t = threadIdx.x;
+  const int col = blockIdx.y * mcols + (t % mcols);
+  const int phase = t / mcols;
+  const bool active = phase < mpar && col < cpr;
+  const size_t row_elems = (size_t)cpr * E;
+
+  const T* base;
+  int r0, r1;
+  if (unit < n_pages * page_chunks) {
+    const int j = unit / page_chunks, c = unit % page_chunks;
+    base = reinterpret_cast<const T*>(pages.p[j]);
+    r0 = c * page_rows;
+    r1 = min(Lp, r0 + page_rows);
+  } else {
+    const int c = unit - n_pages * page_chunks;
+    base = q;
+    r0 = c * q_rows;
+    r1 = min(Lq, r0 + q_rows);
+  }
+  if (base == nullptr) return;  // non-resident page: its mean comes from the cache (whole block exits)
+
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  if (active) {
+    const T* p = base + (size_t)col * E;
+    int r = r0 + phase;
+    for (; r + (kUnroll - 1) * mpar < r1; r += kUnroll * mpar) {
+      uint4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) v[u] = ld16(p + (size_t)(r + u * mpar) * row_elems);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        float f[E];
+        unpack16<T>(v[u], f);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += f[e];
+      }
+    }
+    for (; r < r1; r += mpar) {
+      float f[E];
+      unpack16<T>(ld16(p + (size_t)r * row_elems), f);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += f[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) red[t * E + e] = acc[e];
+  __syncthreads();
+  if (active && phase == 0) {
+    float s[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[e] = acc[e];
+    for (int ph = 1; ph < mpar; ++ph) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[e] += red[(ph * mcols + (t % mcols)) * E + e];
+    }
+    float* out = partial + (size_t)unit * row_elems + (size_t)col * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) out[e] = s[e];
+  }
+}
+
+// One workgroup per page (and one more for the queries): fixed-order sum of
+// the chunk partials, divided by the token count.
+__global__ __launch_bounds__(kScoreThreads) void score_means_kernel(
+    const float* __restrict__ partial, PageTable pages, int n_pages, int page_chunks, int q_chunks,
+    int hd, int Lp, int Lq, float* __restrict__ page_kmean, float* __restrict__ kbar,
+    float* __restrict__ qbar) {
+  const int j = blockIdx.x;
+  if (j < n_pages) {
+    float* dst = kbar + (size_t)j * hd;
+    if (pages.p[j] == nullptr) {
+      for (int c = threadIdx.x; c < hd; c += kScoreThreads) dst[c] = page_kmean[(size_t)j * hd + c];
+      return;
+    }
+    const float inv = 1.f / (float)Lp;
+    for (int c = threadIdx.x; c < hd; c += kScoreThreads) {
+      float s = 0.f;
+      for (int u = 0; u < page_chunks; ++u) s += partial[((size_t)j * page_chunks + u) * hd + c];
+      const float m = s * inv;
+      dst[c] = m;
+      if (page_kmean) page_kmean[(size_t)j * hd + c] = m;
+    }
+  } else {
+    const float inv = 1.f / (float)Lq;
+    const size_t base = (size_t)n_pages * page_chunks;
+    for (int c = threadIdx.x; c < hd; c += kScoreThreads) {
+      float s = 0.f;
+      for (int u = 0; u < q_chunks; ++u) s += partial[(base + u) * hd + c];
+      qbar[c] = s * inv;
+    }
+  }
+}
+
+// Scores and the top-K_p set.  One wave per page computes the dot product in
+// a fixed order; page j is selected iff fewer than K_p pages rank above it
+// (higher score, or equal score and lower id); the selected ids are written
+// in ascending order.
+__global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar, int n_pages, int hd, float scale,
+    int kp, float* __restrict__ scores, int32_t* __restrict__ sel) {
+  __shared__ float alpha[kMaxPages];
+  __shared__ int chosen[kMaxPages];
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  for (int j = w; j < n_pages; j += kScoreThreads / kWave) {
+    float s = 0.f;
+    for (int c = lane; c < hd; c += kWave) s += qbar[c] * kbar[(size_t)j * hd + c];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+    if (lane == 0) alpha[j] = s * scale;
+  }
+  __syncthreads();
+  const int j = threadIdx.x;
+  if (j < n_pages) {
+    const float a = alpha[j];
+    int rank = 0;
+    for (int i = 0; i < n_pages; ++i) {
+      const float b = alpha[i];
+      rank += (b > a) || (b == a && i < j);
+    }
+    chosen[j] = rank < kp;
+    scores[j] = a;
+  }
+  __syncthreads();
+  if (j < n_pages && chosen[j]) {
+    int pos = 0;
+    for (int i = 0; i < j; ++i) pos += chosen[i];
+    if (pos < kp) sel[pos] = j;
+  }
+}
+
+template <typename T>
+void launch_score(const Dims& s, const void* q, const PageTable& tab, int n_pages, float* page_kmean,
+                  float* scores, int32_t* sel, char* ws, const WsLayout& w, hipStream_t st) {
+  const ScorePlan sp = score_plan(s, n_pages);
+  const int cpr = s.H * s.d * s.esize / 16;
+  const ColMap m = col_map(cpr);
+  dim3 grid(sp.units, (cpr + m.cols - 1) / m.cols);
+  float* partial = reinterpret_cast<float*>(ws + w.score_partial);
+  float* qbar = reinterpret_cast<float*>(ws + w.score_qbar);
+  float* kbar = reinterpret_cast<float*>(ws + w.score_kbar);
+  hipLaunchKernelGGL(score_partial_kernel<T>, grid, dim3(kScoreThreads), 0, st,
+                     reinterpret_cast<const T*>(q), tab, n_pages, s.Lp, s.Lq, cpr, sp.page_chunks,
+                     sp.page_rows, sp.q_rows, m.cols, m.par, partial);
+  const int hd = s.H * s.d;
+  hipLaunchKernelGGL(score_means_kernel, dim3(n_pages + 1), dim3(kScoreThreads), 0, st, partial, tab,
+                     n_pages, sp.page_chunks, sp.q_chunks, hd, s.Lp, s.Lq, page_kmean, kbar, qbar);
+  const float scale = 1.f / ((float)s.H * sqrtf((float)s.d));
+  hipLaunchKernelGGL(score_topk_kernel, dim3(1), dim3(kScoreThreads), 0, st, qbar, kbar, n_pages, hd,
+                     scale, s.Kp, scores, sel);
+}
+
+}  // namespace
+}  // namespace hsa
+
+extern "C" hsa_rc hsa_score_pages(const hsa_geom* geom, const void* q, const void* const* page_k,
+                                  float* page_kmean, int32_t n_pages, float* scores, int32_t* sel_pages,
+                                  void* ws, size_t ws_bytes, hsa_stream stream) {
+  using namespace hsa;
+  Dims s;
+  hsa_rc rc = derive(geom, &s);
+  if (rc != HSA_OK) return rc;
+  if (!q || !page_k || !scores || !sel_pages) return HSA_ERR_NULL_ARG;
+  if (n_pages < 1 || n_pages > HSA_MAX_PAGES || s.Kp > n_pages) return HSA_ERR_BAD_PARAM;
+  PageTable tab;
+  for (int j = 0; j < kMaxPages; ++j) tab.p[j] = nullptr;
+  for (int j = 0; j < n_pages; ++j) {
+    tab.p[j] = page_k[j];
+    if (!page_k[j] && !page_kmean) return HSA_ERR_NULL_ARG;
+  }
+  const WsLayout w = ws_layout(s, n_pages);
+  if (!ws || ws_bytes < w.total) return HSA_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(ws);
+  if (s.bf16)
+    launch_score<bf16_t>(s, q, tab, n_pages, page_kmean, scores, sel_pages, wsb, w, st);
+  else
+    launch_score<float>(s, q, tab, n_pages, page_kmean, scores, sel_pages, wsb, w, st);
+  return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
+}

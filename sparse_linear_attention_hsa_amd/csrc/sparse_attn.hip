@@ -1,0 +1,405 @@
+// S5 -- block-sparse attention.  WorldAttention paper, section 3.3 "Sparse
+// branch" and appendix A.1.3: attention at token resolution, restricted to
+// the (query block, key block) pairs that were selected; for query block i of
+// head h, O = softmax(Q_i K_S^T / sqrt(d)) V_S over exactly the tokens S of
+// its selected key blocks.
+//
+// Design (gfx950, wave64, 16x16 matrix cores):
+//  * Work is cut in 16-token key granules.  A row (head, query block) owns
+//    count*B/16 granules; rows longer than a segment are split into balanced
+//    segments so that every workgroup gets a similar amount of work even when
+//    heads keep very different numbers of blocks.  A tiny plan kernel lays the
+//    segments out; segments of a split row write un-normalised partial
+//    outputs with their running max and sum, merged exactly by a combine
+//    kernel (fixed order, no atomics).
+//  * Workgroup = NW waves; wave w owns QPW 16-row query tiles of the block.
+//    Per step it stages KS keys (32 for bf16, 16 for f32) of K (row-major)
+//    and of V (d-major, as the gather lays V out) in LDS, double buffered,
+//    and every wave computes S^T = K Q^T (keys on the rows, so each lane owns
+//    one query column), an online softmax per query, and O^T += V^T P^T.
+//    Keeping queries on the lane-column axis puts the softmax state and the
+//    output column of a query in the same lane: no cross-lane rescaling.
+//  * XCD-aware item order: each XCD runs a contiguous range of rows, i.e.
+//    mostly one head, so the K/V blocks its workgroups share stay in its L2.
+#include "common.h"
+#include "host.h"
+
+namespace hsa {
+namespace {
+
+constexpr int kPlanThreads = 1024;
+
+__device__ int scan_incl_1024(int v, int* buf) {
+  const int t = threadIdx.x;
+  buf[t] = v;
+  __syncthreads();
+  for (int o = 1; o < kPlanThreads; o <<= 1) {
+    const int a = t >= o ? buf[t - o] : 0;
+    __syncthreads();
+    buf[t] += a;
+    __syncthreads();
+  }
+  const int r = buf[t];
+  __syncthreads();
+  return r;
+}
+
+// items[k] = {row, first granule, granules, partial slot or -1};
+// rowinfo[row] = {segments, first slot}; meta = {items, slots}.
+__global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
+    const int32_t* __restrict__ blk_count, int rows, int nKB, int gpb, int gps, int seg_granules,
+    int4* __restrict__ items, int2* __restrict__ rowinfo, int* __restrict__ meta) {
+  __shared__ int buf[kPlanThreads];
+  __shared__ int carry_items, carry_slots;
+  const int t = threadIdx.x;
+  if (t == 0) carry_items = carry_slots = 0;
+  __syncthreads();
+  for (int base = 0; base < rows; base += kPlanThreads) {
+    const int row = base + t;
+    int nseg = 0, per = 0, G = 0;
+    if (row < rows) {
+      int n = blk_count[row];
+      n = n < 0 ? 0 : (n > nKB ? nKB : n);
+      G = n * gpb;
+      if (G > 0) {
+        nseg = (G + seg_granules - 1) / seg_granules;
+        per = (G + nseg - 1) / nseg;
+        per = (per + gps - 1) / gps * gps;
+        nseg = (G + per - 1) / per;
+      }
+    }
+    const int nslot = nseg > 1 ? nseg : 0;
+    const int ci = scan_incl_1024(nseg, buf) - nseg;
+    const int cs = scan_incl_1024(nslot, buf) - nslot;
+    const int i0 = carry_items + ci, s0 = carry_slots + cs;
+    if (row < rows) {
+      for (int s = 0; s < nseg; ++s)
+        items[i0 + s] = make_int4(row, s * per, min(per, G - s * per), nslot ? s0 + s : -1);
+      rowinfo[row] = make_int2(nseg, s0);
+    }
+    __syncthreads();
+    if (t == kPlanThreads - 1) {
+      carry_items += ci + nseg;
+      carry_slots += cs + nslot;
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    meta[0] = carry_items;
+    meta[1] = carry_slots;
+  }
+}
+
+template <typename T, int D, int NW, int QPW>
+__global__ __launch_bounds__(NW * kWave) void sparse_attn_kernel(
+    const T* __restrict__ q, const T* __restrict__ k_act, const T* __restrict__ v_act,
+    const int32_t* __restrict__ blk_idx, const int4* __restrict__ items, const int* __restrict__ meta,
+    int H, int B, int L, int nKB, int nQB, float scale_log2, float* __restrict__ o_sp,
+    float* __restrict__ part_o, float* __restrict__ part_ml) {
+  constexpr int E = Vec<T>::N;          // elements per 16-byte chunk
+  constexpr int KS = Mma<T>::K;         // keys per step
+  constexpr int GPS = KS / 16;          // granules per step
+  constexpr int DCH = D / E;            // chunks per key row
+  constexpr int DSTEPS = D / KS;        // contraction steps over d in S^T = K Q^T
+  constexpr int DT = D / 16;            // output d-tiles
+  constexpr int KSTR = D + E;           // LDS row stride of the K stage (padded)
+  constexpr int VSTR = KS + E;          // LDS row stride of the V^T stage (padded)
+  constexpr int KSTAGE = KS * KSTR;
+  constexpr int VSTAGE = D * VSTR;
+  constexpr int NT = NW * kWave;
+  constexpr int CK = GPS * 16 * DCH;    // K chunks per step
+  constexpr int CV = GPS * D * (16 / E);
+  constexpr int NLD = (CK + CV + NT - 1) / NT;
+  constexpr int PV = 16 / E;            // chunks per 16-token granule row of V
+
+  __shared__ __align__(16) T lds_k[2][KSTAGE];
+  __shared__ __align__(16) T lds_v[2][VSTAGE];
+
+  const int item = xcd_remap(blockIdx.x, meta[0]);
+  if (item < 0) return;
+  const int4 it = items[item];
+  const int row = it.x, g0 = it.y, gcount = it.z, slot = it.w;
+  const int h = row / nQB, qb = row % nQB;
+  const int gpb = B / 16;
+  const int32_t* list = blk_idx + (size_t)row * nKB;
+
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int g = lane >> 4, c = lane & 15;
+  const int QT = B / 16;
+  const int ntile = min(QPW, QT - w * QPW);
+
+  // Q^T operand: lane (g, c) holds Q[row c of tile][chunk 4s+g] for step s.
+  uint4 qreg[QPW][DSTEPS];
+#pragma unroll
+  for (int t = 0; t < QPW; ++t) {
+    if (t < ntile) {
+      const size_t qrow = (size_t)qb * B + (w * QPW + t) * 16 + c;
+      const T* qp = q + (qrow * H + h) * D;
+#pragma unroll
+      for (int s = 0; s < DSTEPS; ++s) qreg[t][s] = ld16(qp + (4 * s + g) * E);
+    }
+  }
+
+  f32x4 o[QPW][DT];
+  float m_run[QPW], l_run[QPW];
+#pragma unroll
+  for (int t = 0; t < QPW; ++t) {
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int nsub = (gcount + GPS - 1) / GPS;
+
+  // key offset of granule `j` of step `sub`, or -1 when it is past the end or its block id is invalid
+  auto granule_key = [&](int sub, int j) -> int {
+    const int gi = sub * GPS + j;
+    if (gi >= gcount) return -1;
+    const int ga = g0 + gi;
+    const int blk = list[ga / gpb];
+    if (blk < 0 || blk >= nKB) return -1;
+    return blk * B + (ga % gpb) * 16;
+  };
+
+  uint4 pre[NLD];
+  auto load_step = [&](int sub) {
+    int kofs[GPS];
+#pragma unroll
+    for (int j = 0; j < GPS; ++j) kofs[j] = granule_key(sub, j);
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int cidx = tid + u * NT;
+      pre[u] = make_uint4(0, 0, 0, 0);
+      if (cidx < CK) {
+        const int j = cidx / (16 * DCH), rr = (cidx / DCH) % 16, cc = cidx % DCH;
+        if (kofs[j] >= 0) pre[u] = ld16(k_act + ((size_t)h * L + kofs[j] + rr) * D + cc * E);
+      } else if (cidx < CK + CV) {
+        const int c2 = cidx - CK;
+        const int j = c2 / (D * PV), rem = c2 % (D * PV);
+        const int drow = rem / PV, part = rem % PV;
+        if (kofs[j] >= 0)
+          pre[u] = ld16(v_act + (((size_t)h * (L / 16) + kofs[j] / 16) * D + drow) * 16 + part * E);
+      }
+    }
+  };
+  auto store_step = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int cidx = tid + u * NT;
+      if (cidx < CK) {
+        const int j = cidx / (16 * DCH), rr = (cidx / DCH) % 16, cc = cidx % DCH;
+        st16(&lds_k[buf][(16 * j + rr) * KSTR + cc * E], pre[u]);
+      } else if (cidx < CK + CV) {
+        const int c2 = cidx - CK;
+        const int j = c2 / (D * PV), rem = c2 % (D * PV);
+        const int drow = rem / PV, part = rem % PV;
+        st16(&lds_v[buf][drow * VSTR + 16 * j + part * E], pre[u]);
+      }
+    }
+  };
+
+  load_step(0);
+  store_step(0);
+  __syncthreads();
+
+  for (int sub = 0; sub < nsub; ++sub) {
+    const int buf = sub & 1;
+    const bool more = sub + 1 < nsub;
+    if (more) load_step(sub + 1);
+
+    // validity of this lane's keys: for bf16 lane group g holds keys of granule g/2
+    bool valid = true;
+    if (GPS == 2) valid = (sub * GPS + (g >> 1)) < gcount && granule_key(sub, g >> 1) >= 0;
+    else valid = granule_key(sub, 0) >= 0;
+
+    if (w * QPW < QT) {
+      f32x4 sacc[QPW][GPS];
+#pragma unroll
+      for (int t = 0; t < QPW; ++t)
+#pragma unroll
+        for (int kt = 0; kt < GPS; ++kt) sacc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < GPS; ++kt) {
+        const T* krow = &lds_k[buf][perm_row<T>(kt, c) * KSTR];
+#pragma unroll
+        for (int s = 0; s < DSTEPS; ++s) {
+          const uint4 a = *reinterpret_cast<const uint4*>(krow + (4 * s + g) * E);
+#pragma unroll
+          for (int t = 0; t < QPW; ++t)
+            if (t < ntile) Mma<T>::run(sacc[t][kt], a, qreg[t][s]);
+        }
+      }
+      uint4 pk[QPW];
+#pragma unroll
+      for (int t = 0; t < QPW; ++t) {
+        if (t < ntile) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int kt = 0; kt < GPS; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (!valid) sacc[t][kt][i] = -INFINITY;
+              mx = fmaxf(mx, sacc[t][kt][i]);
+            }
+          mx = max4g(mx);
+          const float m_new = fmaxf(m_run[t], mx * scale_log2);
+          const float alpha = exp2f(m_run[t] - m_new);
+          float ls = 0.f;
+          f32x4 p[GPS];
+#pragma unroll
+          for (int kt = 0; kt < GPS; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float e = exp2f(sacc[t][kt][i] * scale_log2 - m_new);
+              p[kt][i] = e;
+              ls += e;
+            }
+          l_run[t] = l_run[t] * alpha + ls;
+          m_run[t] = m_new;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
+          pk[t] = pack_p<T>(p);
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint4 a = *reinterpret_cast<const uint4*>(&lds_v[buf][(16 * dt + c) * VSTR + g * E]);
+#pragma unroll
+        for (int t = 0; t < QPW; ++t)
+          if (t < ntile) Mma<T>::run(o[t][dt], a, pk[t]);
+      }
+    }
+    if (more) store_step(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue
+#pragma unroll
+  for (int t = 0; t < QPW; ++t) {
+    if (t < ntile) {
+      const float l_tot = sum4g(l_run[t]);
+      const int r = (w * QPW + t) * 16 + c;  // query row inside the block
+      if (slot < 0) {
+        const float inv = 1.f / l_tot;
+        float* dst = o_sp + (((size_t)qb * B + r) * H + h) * D + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const f32x4 v = o[t][dt] * inv;
+          *reinterpret_cast<float4*>(dst + 16 * dt) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      } else {
+        float* dst = part_o + ((size_t)slot * B + r) * D + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<float4*>(dst + 16 * dt) = make_float4(o[t][dt][0], o[t][dt][1], o[t][dt][2], o[t][dt][3]);
+        if (g == 0) {
+          part_ml[((size_t)slot * B + r) * 2 + 0] = m_run[t];
+          part_ml[((size_t)slot * B + r) * 2 + 1] = l_tot;
+        }
+      }
+    }
+  }
+}
+
+// Merge the partial outputs of split rows (fixed segment order); rows with
+// no selected block get zeros.
+template <int D>
+__global__ __launch_bounds__(256) void sparse_combine_kernel(
+    const int2* __restrict__ rowinfo, const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    int H, int B, int nQB, float* __restrict__ o_sp) {
+  const int row = blockIdx.x;
+  const int2 ri = rowinfo[row];
+  const int nseg = ri.x, s0 = ri.y;
+  if (nseg == 1) return;
+  const int h = row / nQB, qb = row % nQB;
+  for (int e = threadIdx.x; e < B * (D / 4); e += 256) {
+    const int r = e / (D / 4), c4 = e % (D / 4);
+    float4* dst = reinterpret_cast<float4*>(o_sp + (((size_t)qb * B + r) * H + h) * D) + c4;
+    if (nseg == 0) {
+      *dst = make_float4(0.f, 0.f, 0.f, 0.f);
+      continue;
+    }
+    float M = -INFINITY;
+    for (int s = 0; s < nseg; ++s) M = fmaxf(M, part_ml[((size_t)(s0 + s) * B + r) * 2]);
+    float den = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < nseg; ++s) {
+      const size_t sr = (size_t)(s0 + s) * B + r;
+      const float wgt = exp2f(part_ml[sr * 2] - M);
+      den += wgt * part_ml[sr * 2 + 1];
+      const float4 v = reinterpret_cast<const float4*>(part_o + sr * D)[c4];
+      acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
+    }
+    const float inv = 1.f / den;
+    *dst = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  }
+}
+
+template <typename T, int D, int NW, int QPW>
+void launch_attn(const Dims& s, const SparsePlan& pl, const void* q, const void* k_act, const void* v_act,
+                 const int32_t* idx, const int4* items, const int* meta, float* o_sp, float* po, float* pml,
+                 hipStream_t st) {
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
+  hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW>), dim3(pl.grid), dim3(NW * kWave), 0, st,
+                     reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act),
+                     reinterpret_cast<const T*>(v_act), idx, items, meta, s.H, s.B, s.L, s.nKB, s.nQB,
+                     scale_log2, o_sp, po, pml);
+}
+
+template <typename T, int D>
+void dispatch_attn(const Dims& s, const SparsePlan& pl, const void* q, const void* k_act, const void* v_act,
+                   const int32_t* idx, const int4* items, const int* meta, float* o_sp, float* po, float* pml,
+                   hipStream_t st) {
+  const int QT = s.B / 16;
+  const int nw = (QT + 2) / 3;
+  const int qpw = (QT + nw - 1) / nw;
+#define HSA_ATTN_CASE(NW_, QPW_) \
+  if (nw == NW_ && qpw == QPW_) return launch_attn<T, D, NW_, QPW_>(s, pl, q, k_act, v_act, idx, items, meta, o_sp, po, pml, st);
+  HSA_ATTN_CASE(1, 1)
+  HSA_ATTN_CASE(1, 2)
+  HSA_ATTN_CASE(1, 3)
+  HSA_ATTN_CASE(2, 2)
+  HSA_ATTN_CASE(2, 3)
+  HSA_ATTN_CASE(3, 3)
+  HSA_ATTN_CASE(4, 3)
+#undef HSA_ATTN_CASE
+}
+
+}  // namespace
+}  // namespace hsa
+
+extern "C" hsa_rc hsa_sparse_attn(const hsa_geom* geom, const void* q, const void* k_act, const void* v_act,
+                                  const int32_t* blk_count, const int32_t* blk_idx, float* o_sp, void* ws,
+                                  size_t ws_bytes, hsa_stream stream) {
+  using namespace hsa;
+  Dims s;
+  hsa_rc rc = derive(geom, &s);
+  if (rc != HSA_OK) return rc;
+  if (!q || !k_act || !v_act || !blk_count || !blk_idx || !o_sp) return HSA_ERR_NULL_ARG;
+  const WsLayout w = ws_layout(s, 1);
+  if (!ws || ws_bytes < w.sp_end) return HSA_ERR_WORKSPACE;
+  const SparsePlan pl = sparse_plan(s);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(ws);
+  int4* items = reinterpret_cast<int4*>(wsb + w.sp_items);
+  int2* rowinfo = reinterpret_cast<int2*>(wsb + w.sp_rowinfo);
+  int* meta = reinterpret_cast<int*>(wsb + w.sp_meta);
+  float* po = reinterpret_cast<float*>(wsb + w.sp_part_o);
+  float* pml = reinterpret_cast<float*>(wsb + w.sp_part_ml);
+  const int gps = s.bf16 ? 2 : 1;
+  hipLaunchKernelGGL(sparse_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, blk_count, s.rows, s.nKB,
+                     pl.granules_per_block, gps, pl.seg_granules, items, rowinfo, meta);
+  if (s.bf16) {
+    if (s.d == 128) dispatch_attn<bf16_t, 128>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
+    else dispatch_attn<bf16_t, 64>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
+  } else {
+    if (s.d == 128) dispatch_attn<float, 128>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
+    else dispatch_attn<float, 64>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
+  }
+  if (s.d == 128)
+    hipLaunchKernelGGL(sparse_combine_kernel<128>, dim3(s.rows), dim3(256), 0, st, rowinfo, po, pml, s.H, s.B, s.nQB, o_sp);
+  else
+    hipLaunchKernelGGL(sparse_combine_kernel<64>, dim3(s.rows), dim3(256), 0, st, rowinfo, po, pml, s.H, s.B, s.nQB, o_sp);
+  return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
+}

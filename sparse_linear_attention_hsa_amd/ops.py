@@ -1,0 +1,113 @@
+"""Python entry points of the HSA library, one per C-ABI call (same names).
+
+Tensors are torch tensors on the GPU (torch is used only for device memory
+and streams); each function forwards raw pointers and the current HIP stream
+to libhsa_attn.so and raises HsaError on a non-zero return code.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+from ._lib import HSA_BF16, HSA_F32, Geom, check, lib
+
+_DTYPES = {torch.float32: HSA_F32, torch.bfloat16: HSA_BF16}
+
+
+def make_geom(n_heads, head_dim, frame_h, frame_w, frames_per_page, query_frames, tile,
+              n_sel_pages, rank, dtype) -> Geom:
+    dt = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else {"f32": HSA_F32, "bf16": HSA_BF16}[dtype]
+    return Geom(n_heads, head_dim, frame_h, frame_w, frames_per_page, query_frames,
+                tile[0], tile[1], tile[2], n_sel_pages, rank, dt)
+
+
+@dataclass(frozen=True)
+class Dims:
+    """Buffer sizes implied by a geometry (mirrors the library's own derivation)."""
+    H: int
+    d: int
+    Lp: int
+    Lq: int
+    B: int
+    Kp: int
+    L: int
+    nKB: int
+    nQB: int
+    r: int
+    dtype: torch.dtype
+
+    @staticmethod
+    def of(g: Geom) -> "Dims":
+        tpf = g.frame_h * g.frame_w
+        B = g.tile_t * g.tile_h * g.tile_w
+        Lp, Lq = tpf * g.frames_per_page, tpf * g.query_frames
+        L = Lp * g.n_sel_pages
+        return Dims(g.n_heads, g.head_dim, Lp, Lq, B, g.n_sel_pages, L, L // B, Lq // B, g.rank,
+                    torch.bfloat16 if g.dtype == HSA_BF16 else torch.float32)
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("HSA buffers must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _s(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _table(pages: Sequence[Optional[torch.Tensor]]):
+    arr = (ctypes.c_void_p * len(pages))()
+    for i, t in enumerate(pages):
+        arr[i] = None if t is None else t.data_ptr()
+    return arr
+
+
+def hsa_workspace_bytes(geom: Geom, n_pages: int) -> int:
+    return int(lib().hsa_workspace_bytes(ctypes.byref(geom), n_pages))
+
+
+def hsa_geom_check(geom: Geom) -> int:
+    return int(lib().hsa_geom_check(ctypes.byref(geom)))
+
+
+def hsa_score_pages(geom, q, pages_k, page_kmean, scores, sel_pages, ws, stream=None):
+    check("hsa_score_pages", lib().hsa_score_pages(
+        ctypes.byref(geom), _p(q), _table(pages_k), _p(page_kmean), len(pages_k), _p(scores), _p(sel_pages),
+        _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+
+
+def hsa_gather_pages(geom, pages_k, pages_v, sel_pages, k_act, v_act, kblk_mean=None, stream=None):
+    check("hsa_gather_pages", lib().hsa_gather_pages(
+        ctypes.byref(geom), _table(pages_k), _table(pages_v), len(pages_k), _p(sel_pages), _p(k_act), _p(v_act),
+        _p(kblk_mean), _s(stream)))
+
+
+def hsa_linear_branch(geom, q, k_act, v_act, e_k, e_v, k_proj, v_proj, o_lin, flags, ws, stream=None):
+    check("hsa_linear_branch", lib().hsa_linear_branch(
+        ctypes.byref(geom), _p(q), _p(k_act), _p(v_act), _p(e_k), _p(e_v), _p(k_proj), _p(v_proj), _p(o_lin),
+        flags, _p(ws), 0 if ws is None else ws.numel() * ws.element_size(), _s(stream)))
+
+
+def hsa_block_select(geom, q, k_act, kblk_mean, tau, blk_count, blk_idx, blk_mass, ws, stream=None):
+    check("hsa_block_select", lib().hsa_block_select(
+        ctypes.byref(geom), _p(q), _p(k_act), _p(kblk_mean), _p(tau), _p(blk_count), _p(blk_idx), _p(blk_mass),
+        _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+
+
+def hsa_sparse_attn(geom, q, k_act, v_act, blk_count, blk_idx, o_sp, ws, stream=None):
+    check("hsa_sparse_attn", lib().hsa_sparse_attn(
+        ctypes.byref(geom), _p(q), _p(k_act), _p(v_act), _p(blk_count), _p(blk_idx), _p(o_sp),
+        _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+
+
+def hsa_fuse(geom, x, w_g, gate_override, o_lin, o_sp, out, stream=None):
+    check("hsa_fuse", lib().hsa_fuse(
+        ctypes.byref(geom), _p(x), _p(w_g), _p(gate_override), _p(o_lin), _p(o_sp), _p(out), _s(stream)))

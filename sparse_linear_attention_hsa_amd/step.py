@@ -1,0 +1,83 @@
+"""One HSA decode step (one layer, one denoising step) over device buffers.
+
+Holds the intermediate buffers of the six stages (allocated once with torch)
+and issues the six C-ABI calls in order on one stream:
+
+    score_pages -> gather_pages -> linear_branch -> block_select -> sparse_attn -> fuse
+
+Nothing here computes: every stage runs in the library's HIP kernels, and the
+selections never leave the device.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import torch
+
+from . import ops
+from ._lib import HSA_LIN_REUSE_PROJ
+from .ops import Dims, Geom
+
+
+class HsaStep:
+    def __init__(self, geom: Geom, n_pages: int, device: str = "cuda"):
+        self.geom = geom
+        self.n_pages = n_pages
+        self.s = s = Dims.of(geom)
+        dev = torch.device(device)
+        f32, i32, dt = torch.float32, torch.int32, s.dtype
+        self.page_kmean = torch.empty(n_pages, s.H, s.d, dtype=f32, device=dev)
+        self.scores = torch.empty(n_pages, dtype=f32, device=dev)
+        self.sel_pages = torch.empty(s.Kp, dtype=i32, device=dev)
+        self.k_act = torch.empty(s.H, s.L, s.d, dtype=dt, device=dev)
+        self.v_act = torch.empty(s.H, s.L // 16, s.d, 16, dtype=dt, device=dev)
+        self.kblk_mean = torch.empty(s.H, s.nKB, s.d, dtype=f32, device=dev)
+        self.k_proj = torch.empty(s.H, s.r, s.d, dtype=f32, device=dev)
+        self.v_proj = torch.empty(s.H, s.d, s.r, dtype=f32, device=dev)
+        self.o_lin = torch.empty(s.Lq, s.H, s.d, dtype=f32, device=dev)
+        self.blk_count = torch.empty(s.H, s.nQB, dtype=i32, device=dev)
+        self.blk_idx = torch.empty(s.H, s.nQB, s.nKB, dtype=i32, device=dev)
+        self.blk_mass = torch.empty(s.H, s.nQB, s.nKB, dtype=f32, device=dev)
+        self.o_sp = torch.empty(s.Lq, s.H, s.d, dtype=f32, device=dev)
+        self.out = torch.empty(s.Lq, s.H, s.d, dtype=dt, device=dev)
+        nbytes = ops.hsa_workspace_bytes(geom, n_pages)
+        if nbytes == 0:
+            raise ValueError("invalid geometry")
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    # individual stages --------------------------------------------------
+    def score(self, q, pages_k: Sequence[Optional[torch.Tensor]], stream=None, use_cache: bool = False):
+        ops.hsa_score_pages(self.geom, q, pages_k, self.page_kmean, self.scores, self.sel_pages, self.ws, stream)
+
+    def gather(self, pages_k, pages_v, stream=None):
+        ops.hsa_gather_pages(self.geom, pages_k, pages_v, self.sel_pages, self.k_act, self.v_act, self.kblk_mean,
+                             stream)
+
+    def linear(self, q, e_k, e_v, flags: int = 0, stream=None):
+        if flags & HSA_LIN_REUSE_PROJ:
+            ops.hsa_linear_branch(self.geom, q, None, None, None, None, self.k_proj, self.v_proj, self.o_lin,
+                                  flags, self.ws, stream)
+        else:
+            ops.hsa_linear_branch(self.geom, q, self.k_act, self.v_act, e_k, e_v, self.k_proj, self.v_proj,
+                                  self.o_lin, flags, self.ws, stream)
+
+    def select(self, q, tau, use_kblk_mean: bool = True, stream=None):
+        ops.hsa_block_select(self.geom, q, self.k_act, self.kblk_mean if use_kblk_mean else None, tau,
+                             self.blk_count, self.blk_idx, self.blk_mass, self.ws, stream)
+
+    def sparse(self, q, stream=None):
+        ops.hsa_sparse_attn(self.geom, q, self.k_act, self.v_act, self.blk_count, self.blk_idx, self.o_sp, self.ws,
+                            stream)
+
+    def fuse(self, x, w_g, stream=None):
+        ops.hsa_fuse(self.geom, x, w_g, None, self.o_lin, self.o_sp, self.out, stream)
+
+    # the whole step -----------------------------------------------------
+    def run(self, q, pages_k, pages_v, e_k, e_v, w_g, x, tau, stream=None):
+        self.score(q, pages_k, stream)
+        self.gather(pages_k, pages_v, stream)
+        self.linear(q, e_k, e_v, 0, stream)
+        self.select(q, tau, True, stream)
+        self.sparse(q, stream)
+        self.fuse(x, w_g, stream)
+        return self.out

@@ -1,0 +1,111 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and
+its host-side validation rejects bad arguments before launching anything.
+No kernel is launched here (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_linear_attention_hsa_amd import _lib
+from sparse_linear_attention_hsa_amd._lib import Geom
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "hsa_attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hsa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def c1_geom(**kw):
+    g = dict(n_heads=12, head_dim=128, frame_h=30, frame_w=52, frames_per_page=8, query_frames=4,
+             tile_t=4, tile_h=6, tile_w=4, n_sel_pages=4, rank=256, dtype=_lib.HSA_BF16)
+    g.update(kw)
+    return Geom(**g)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n)
+    assert lib.hsa_abi_version() == 1
+
+
+def test_geometry_validation(lib):
+    ok = c1_geom()
+    assert lib.hsa_geom_check(ctypes.byref(ok)) == 0
+    assert lib.hsa_geom_check(None) == 1
+    bad = {
+        "dtype": (dict(dtype=7), 3),
+        "head_dim": (dict(head_dim=96), 4),
+        "rank": (dict(rank=0), 4),
+        "rank_big": (dict(rank=512), 4),
+        "tile_not_dividing": (dict(tile_h=8), 2),         # 8 does not divide 30
+        "tile_t": (dict(tile_t=3), 2),
+        "block_not_16": (dict(tile_t=1, tile_h=6, tile_w=4), 2),   # B = 24
+        "block_too_big": (dict(tile_t=4, tile_h=6, tile_w=13, frame_w=52), 2),  # B = 312
+        "zero_frames": (dict(query_frames=0), 2),
+        "zero_pages": (dict(n_sel_pages=0), 4),
+        "too_many_heads": (dict(n_heads=33), 4),
+    }
+    for name, (kw, rc) in bad.items():
+        g = c1_geom(**kw)
+        assert lib.hsa_geom_check(ctypes.byref(g)) == rc, name
+        assert lib.hsa_workspace_bytes(ctypes.byref(g), 16) == 0, name
+
+
+def test_workspace_sizes(lib):
+    g = c1_geom()
+    a = lib.hsa_workspace_bytes(ctypes.byref(g), 16)
+    b = lib.hsa_workspace_bytes(ctypes.byref(g), 120)
+    assert 0 < a <= b
+    assert lib.hsa_workspace_bytes(ctypes.byref(g), _lib.HSA_MAX_PAGES + 1) == 0
+
+
+def test_entry_points_reject_bad_arguments_before_launch(lib):
+    g = c1_geom()
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+    pages = (ctypes.c_void_p * 16)(*([0x1000] * 16))
+    null_pages = (ctypes.c_void_p * 16)()
+    ws_small = ctypes.c_size_t(16)
+    # score: NULL q, NULL page without cache, bad page counts, short workspace
+    assert lib.hsa_score_pages(ctypes.byref(g), None, pages, None, 16, fake, fake, fake, 1 << 40, None) == 1
+    assert lib.hsa_score_pages(ctypes.byref(g), fake, null_pages, None, 16, fake, fake, fake, 1 << 40, None) == 1
+    assert lib.hsa_score_pages(ctypes.byref(g), fake, pages, None, 3, fake, fake, fake, 1 << 40, None) == 4
+    assert lib.hsa_score_pages(ctypes.byref(g), fake, pages, None, 0, fake, fake, fake, 1 << 40, None) == 4
+    assert lib.hsa_score_pages(ctypes.byref(g), fake, pages, None, 16, fake, fake, fake, ws_small, None) == 5
+    assert lib.hsa_score_pages(ctypes.byref(g), fake, pages, None, 16, fake, fake, None, 1 << 40, None) == 5
+    # gather: NULL page entry, NULL outputs
+    assert lib.hsa_gather_pages(ctypes.byref(g), null_pages, pages, 16, fake, fake, fake, None, None) == 1
+    assert lib.hsa_gather_pages(ctypes.byref(g), pages, pages, 16, fake, None, fake, None, None) == 1
+    assert lib.hsa_gather_pages(ctypes.byref(g), pages, pages, 200, fake, fake, fake, None, None) == 4
+    # linear: bad flags, missing projections, short workspace
+    assert lib.hsa_linear_branch(ctypes.byref(g), fake, fake, fake, fake, fake, fake, fake, fake, 3, fake, 1 << 40, None) == 4
+    assert lib.hsa_linear_branch(ctypes.byref(g), fake, fake, fake, fake, fake, fake, fake, fake, 8, fake, 1 << 40, None) == 4
+    assert lib.hsa_linear_branch(ctypes.byref(g), fake, fake, fake, None, fake, fake, fake, fake, 0, fake, 1 << 40, None) == 1
+    assert lib.hsa_linear_branch(ctypes.byref(g), fake, fake, fake, fake, fake, fake, fake, fake, 0, fake, ws_small, None) == 5
+    # select: neither k_act nor block means
+    assert lib.hsa_block_select(ctypes.byref(g), fake, None, None, fake, fake, fake, None, fake, 1 << 40, None) == 1
+    assert lib.hsa_block_select(ctypes.byref(g), fake, fake, None, fake, fake, fake, None, fake, ws_small, None) == 5
+    # sparse
+    assert lib.hsa_sparse_attn(ctypes.byref(g), fake, fake, None, fake, fake, fake, fake, 1 << 40, None) == 1
+    assert lib.hsa_sparse_attn(ctypes.byref(g), fake, fake, fake, fake, fake, fake, fake, ws_small, None) == 5
+    # fuse: x without weights, neither x nor override
+    assert lib.hsa_fuse(ctypes.byref(g), fake, None, None, fake, fake, fake, None) == 1
+    assert lib.hsa_fuse(ctypes.byref(g), None, None, None, fake, fake, fake, None) == 1
+    # geometry errors win before anything else
+    bad = c1_geom(dtype=9)
+    assert lib.hsa_fuse(ctypes.byref(bad), fake, fake, None, fake, fake, fake, None) == 3
+
+
+def test_status_strings(lib):
+    for rc, name in _lib.RC_NAMES.items():
+        assert lib.hsa_rc_string(rc).decode().startswith(name)
