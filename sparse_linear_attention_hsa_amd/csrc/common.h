@@ -24,11 +24,9 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
-// float -> bfloat16, round to nearest even (inputs here are finite).
+// float -> bfloat16, round to nearest even (gfx950 converts in hardware).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
 template <typename T> __device__ __forceinline__ float to_f32(T v);

@@ -4,74 +4,81 @@
 // W has 2H output columns: column h gates the linear branch of head h and
 // column H+h its sparse branch.
 //
-// One wave per 16 query tokens: the 16 x 2H gate logits come from the matrix
-// cores (X rows and W rows are both contiguous along D), the sigmoid values go
-// through LDS, then the wave streams O_lin / O_sp and writes O in the element
-// type.  HBM-bound: X, O_lin, O_sp are read once and O written once.
+// The 16 x 2H gate logits of a 16-token tile come from the matrix cores (X rows
+// and W rows are both contiguous along D), the sigmoid values go through LDS,
+// then the workgroup streams O_lin / O_sp and writes O in the element type.
+// HBM-bound: X, O_lin, O_sp are read once and O written once.
 #include "common.h"
 #include "host.h"
 
 namespace hsa {
 namespace {
 
-constexpr int kFuseThreads = 256;  // 4 waves, 16 tokens each
+constexpr int kFuseThreads = 256;  // 4 waves per 16-token tile
 constexpr int kMaxGateTiles = 4;   // 2H <= 64
 
+// One workgroup (4 waves) per 16 query tokens.  The gate contraction over the
+// model width is split across the waves (wave w takes every 4th step), the
+// partial logits meet in LDS, and then all four waves stream the blend.
 template <typename T, int D>
 __global__ __launch_bounds__(kFuseThreads) void fuse_kernel(
     const T* __restrict__ x, const T* __restrict__ w_g, const float* __restrict__ gate_override,
     const float* __restrict__ o_lin, const float* __restrict__ o_sp, int H, int Lq, T* __restrict__ out) {
   constexpr int E = Vec<T>::N;
   constexpr int KS = Mma<T>::K;
-  __shared__ float gate_s[4][16][2 * 32];
+  __shared__ float part_s[4][16][2 * 32 + 1];
+  __shared__ float gate_s[16][2 * 32];
   const int tid = threadIdx.x, wv = tid / kWave, lane = tid % kWave;
   const int g = lane >> 4, c = lane & 15;
-  const int tok0 = (blockIdx.x * 4 + wv) * 16;
+  const int tok0 = blockIdx.x * 16;
   const int G2 = 2 * H;
   const int Dm = H * D;  // model width
-  if (tok0 < Lq) {
-    if (x != nullptr) {
-      const int ntile = (G2 + 15) / 16;
-      f32x4 acc[kMaxGateTiles];
+  if (x != nullptr) {
+    const int ntile = (G2 + 15) / 16;
+    f32x4 acc[kMaxGateTiles];
 #pragma unroll
-      for (int n = 0; n < kMaxGateTiles; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // G^T[col][tok] = W[col][:] . X[tok][:] ; A = W rows (gate column), B = X^T (token)
-      const int tk = tok0 + c;
-      const T* xr = x + (size_t)min(tk, Lq - 1) * Dm;
-      for (int k0 = 0; k0 < Dm; k0 += KS) {
-        const uint4 b = ld16(xr + k0 + g * E);
-#pragma unroll
-        for (int n = 0; n < kMaxGateTiles; ++n) {
-          if (n < ntile) {
-            const int col = 16 * n + c;
-            const uint4 a = col < G2 ? ld16(w_g + (size_t)col * Dm + k0 + g * E) : make_uint4(0, 0, 0, 0);
-            Mma<T>::run(acc[n], a, b);
-          }
-        }
-      }
-      // lane (g, c) holds G^T[16n + 4g + i][token c]
+    for (int n = 0; n < kMaxGateTiles; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // G^T[col][tok] = W[col][:] . X[tok][:] ; A = W rows (gate column), B = X^T (token)
+    const int tk = tok0 + c;
+    const T* xr = x + (size_t)min(tk, Lq - 1) * Dm;
+    for (int k0 = wv * KS; k0 < Dm; k0 += 4 * KS) {
+      const uint4 b = ld16(xr + k0 + g * E);
 #pragma unroll
       for (int n = 0; n < kMaxGateTiles; ++n) {
         if (n < ntile) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int col = 16 * n + 4 * g + i;
-            if (col < G2) gate_s[wv][c][col] = 1.f / (1.f + expf(-acc[n][i]));
-          }
+          const int col = 16 * n + c;
+          const uint4 a = col < G2 ? ld16(w_g + (size_t)col * Dm + k0 + g * E) : make_uint4(0, 0, 0, 0);
+          Mma<T>::run(acc[n], a, b);
         }
       }
-    } else {
-      for (int e = lane; e < 16 * G2; e += kWave) {
-        const int tr = e / G2, col = e % G2;
-        gate_s[wv][tr][col] = tok0 + tr < Lq ? gate_override[(size_t)(tok0 + tr) * G2 + col] : 0.f;
+    }
+    // lane (g, c) holds partial G^T[16n + 4g + i][token c]
+#pragma unroll
+    for (int n = 0; n < kMaxGateTiles; ++n) {
+      if (n < ntile) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int col = 16 * n + 4 * g + i;
+          if (col < G2) part_s[wv][c][col] = acc[n][i];
+        }
       }
+    }
+    __syncthreads();
+    for (int e = tid; e < 16 * G2; e += kFuseThreads) {
+      const int tr = e / G2, col = e % G2;
+      const float z = (part_s[0][tr][col] + part_s[1][tr][col]) + (part_s[2][tr][col] + part_s[3][tr][col]);
+      gate_s[tr][col] = 1.f / (1.f + expf(-z));
+    }
+  } else {
+    for (int e = tid; e < 16 * G2; e += kFuseThreads) {
+      const int tr = e / G2, col = e % G2;
+      gate_s[tr][col] = tok0 + tr < Lq ? gate_override[(size_t)(tok0 + tr) * G2 + col] : 0.f;
     }
   }
   __syncthreads();
-  if (tok0 >= Lq) return;
-  // blend: 16 tokens x H heads x D, 4 floats per lane step
+  // blend: 16 tokens x H heads x D, 4 floats per thread step
   const int per_tok = H * D / 4;
-  for (int e = lane; e < 16 * per_tok; e += kWave) {
+  for (int e = tid; e < 16 * per_tok; e += kFuseThreads) {
     const int tr = e / per_tok, rem = e % per_tok;
     const int tk = tok0 + tr;
     if (tk >= Lq) break;
@@ -79,7 +86,7 @@ __global__ __launch_bounds__(kFuseThreads) void fuse_kernel(
     const size_t off = (size_t)tk * H * D + rem * 4;
     const float4 a = *reinterpret_cast<const float4*>(o_lin + off);
     const float4 b = *reinterpret_cast<const float4*>(o_sp + off);
-    const float gl = gate_s[wv][tr][hh], gs = gate_s[wv][tr][H + hh];
+    const float gl = gate_s[tr][hh], gs = gate_s[tr][H + hh];
     float r[4] = {a.x * gl + b.x * gs, a.y * gl + b.y * gs, a.z * gl + b.z * gs, a.w * gl + b.w * gs};
     if constexpr (sizeof(T) == 4) {
       *reinterpret_cast<float4*>(out + off) = make_float4(r[0], r[1], r[2], r[3]);
@@ -95,7 +102,7 @@ template <typename T, int D>
 void launch_fuse(const Dims& s, const void* x, const void* w_g, const float* go, const float* ol, const float* osp,
                  void* out, hipStream_t st) {
   const int tiles = (s.Lq + 15) / 16;
-  hipLaunchKernelGGL((fuse_kernel<T, D>), dim3((tiles + 3) / 4), dim3(kFuseThreads), 0, st,
+  hipLaunchKernelGGL((fuse_kernel<T, D>), dim3(tiles), dim3(kFuseThreads), 0, st,
                      reinterpret_cast<const T*>(x), reinterpret_cast<const T*>(w_g), go, ol, osp, s.H, s.Lq,
                      reinterpret_cast<T*>(out));
 }

@@ -45,7 +45,7 @@ hsa_rc derive(const hsa_geom* g, Dims* o) {
 
 ScorePlan score_plan(const Dims& s, int n_pages) {
   ScorePlan p;
-  const int target = 2048;
+  const int target = 640;
   int pc = std::max(1, std::min(cdiv(s.Lp, 16), cdiv(target, std::max(1, n_pages))));
   p.page_rows = cdiv(s.Lp, pc);
   p.page_chunks = cdiv(s.Lp, p.page_rows);
@@ -101,7 +101,8 @@ WsLayout ws_layout(const Dims& s, int n_pages) {
   w.sp_items = 0;
   w.sp_rowinfo = align256((size_t)qp.max_items * 16);
   w.sp_meta = align256(w.sp_rowinfo + (size_t)s.rows * 8);
-  w.sp_part_o = align256(w.sp_meta + 64);
+  w.sp_zeros = align256(w.sp_meta + 64);
+  w.sp_part_o = align256(w.sp_zeros + 1024);
   w.sp_part_ml = align256(w.sp_part_o + (size_t)qp.max_items * s.B * s.d * 4);
   w.sp_end = align256(w.sp_part_ml + (size_t)qp.max_items * s.B * 2 * 4);
   w.total = std::max(std::max(w.score_end, w.lin_end), std::max(w.sel_end, w.sp_end));

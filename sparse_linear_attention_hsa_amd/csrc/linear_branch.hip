@@ -148,6 +148,7 @@ __global__ __launch_bounds__(kProjThreads) void lin_project_kernel(
 }
 
 // Sum the split partials in order; write Ktil [H][r][d] and Vtil^T [H][d][r] (float32).
+// grid = (2H, ceil(r*D/1024)); each thread sums one float4 column group over the splits.
 __global__ __launch_bounds__(256) void lin_reduce_kernel(const float* __restrict__ partial, int H, int D, int r,
                                                          int splits, float* __restrict__ k_proj,
                                                          float* __restrict__ v_proj) {
@@ -155,13 +156,29 @@ __global__ __launch_bounds__(256) void lin_reduce_kernel(const float* __restrict
   const bool is_v = which >= H;
   const int h = is_v ? which - H : which;
   const int rpad = (r + 15) / 16 * 16;
-  for (int e = threadIdx.x; e < r * D; e += 256) {
-    const int rr = e / D, col = e % D;
-    float s = 0.f;
-    for (int sp = 0; sp < splits; ++sp)
-      s += partial[(((size_t)sp * 2 * H + which) * rpad + rr) * D + col];
-    if (is_v) v_proj[((size_t)h * D + col) * r + rr] = s;
-    else k_proj[((size_t)h * r + rr) * D + col] = s;
+  const int e4 = blockIdx.y * 256 + threadIdx.x;  // float4 index inside [r][D]
+  if (e4 * 4 >= r * D) return;
+  const int rr = (e4 * 4) / D, col = (e4 * 4) % D;
+  const size_t stride = (size_t)2 * H * rpad * D;
+  const float* p = partial + ((size_t)which * rpad + rr) * D + col;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  int sp = 0;
+  for (; sp + 4 <= splits; sp += 4) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(p + (size_t)(sp + u) * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w; }
+  }
+  for (; sp < splits; ++sp) {
+    const float4 v = *reinterpret_cast<const float4*>(p + (size_t)sp * stride);
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  if (is_v) {
+    float* o = v_proj + ((size_t)h * D + col) * r + rr;
+    o[0] = s.x; o[r] = s.y; o[2 * r] = s.z; o[3 * r] = s.w;
+  } else {
+    *reinterpret_cast<float4*>(k_proj + ((size_t)h * r + rr) * D + col) = s;
   }
 }
 
@@ -310,7 +327,7 @@ void launch_linear(const Dims& s, const void* q, const void* k_act, const void* 
                        reinterpret_cast<const T*>(k_act), reinterpret_cast<const T*>(v_act),
                        reinterpret_cast<const T*>(e_k), reinterpret_cast<const T*>(e_v), s.H, s.L, s.r, pp.steps,
                        pp.splits, partial);
-    hipLaunchKernelGGL(lin_reduce_kernel, dim3(2 * s.H), dim3(256), 0, st, partial, s.H, D, s.r, pp.splits,
+    hipLaunchKernelGGL(lin_reduce_kernel, dim3(2 * s.H, (s.r * D / 4 + 255) / 256), dim3(256), 0, st, partial, s.H, D, s.r, pp.splits,
                        reinterpret_cast<float*>(k_proj), reinterpret_cast<float*>(v_proj));
   }
   if (flags & HSA_LIN_PROJ_ONLY) return;

@@ -99,51 +99,61 @@ __global__ __launch_bounds__(kScoreThreads) void score_partial_kernel(
   }
 }
 
-// One workgroup per page (and one more for the queries): fixed-order sum of
-// the chunk partials, divided by the token count.
+// grid = (n_pages + 1, ceil(hd / 256)): one thread per column of one page (the
+// last x-index is the query buffer); fixed-order sum of the chunk partials,
+// divided by the token count.
 __global__ __launch_bounds__(kScoreThreads) void score_means_kernel(
     const float* __restrict__ partial, PageTable pages, int n_pages, int page_chunks, int q_chunks,
     int hd, int Lp, int Lq, float* __restrict__ page_kmean, float* __restrict__ kbar,
     float* __restrict__ qbar) {
   const int j = blockIdx.x;
-  if (j < n_pages) {
-    float* dst = kbar + (size_t)j * hd;
-    if (pages.p[j] == nullptr) {
-      for (int c = threadIdx.x; c < hd; c += kScoreThreads) dst[c] = page_kmean[(size_t)j * hd + c];
-      return;
-    }
-    const float inv = 1.f / (float)Lp;
-    for (int c = threadIdx.x; c < hd; c += kScoreThreads) {
-      float s = 0.f;
-      for (int u = 0; u < page_chunks; ++u) s += partial[((size_t)j * page_chunks + u) * hd + c];
-      const float m = s * inv;
-      dst[c] = m;
-      if (page_kmean) page_kmean[(size_t)j * hd + c] = m;
-    }
+  const int c = blockIdx.y * kScoreThreads + threadIdx.x;
+  if (c >= hd) return;
+  const bool is_q = j == n_pages;
+  if (!is_q && pages.p[j] == nullptr) {
+    kbar[(size_t)j * hd + c] = page_kmean[(size_t)j * hd + c];
+    return;
+  }
+  const int n = is_q ? q_chunks : page_chunks;
+  const float* p = partial + ((size_t)j * page_chunks) * hd + c;  // query partials follow the pages
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  int u = 0;
+  for (; u + 4 <= n; u += 4) {
+    s0 += p[(size_t)(u + 0) * hd];
+    s1 += p[(size_t)(u + 1) * hd];
+    s2 += p[(size_t)(u + 2) * hd];
+    s3 += p[(size_t)(u + 3) * hd];
+  }
+  for (; u < n; ++u) s0 += p[(size_t)u * hd];
+  const float m = ((s0 + s1) + (s2 + s3)) / (float)(is_q ? Lq : Lp);
+  if (is_q) {
+    qbar[c] = m;
   } else {
-    const float inv = 1.f / (float)Lq;
-    const size_t base = (size_t)n_pages * page_chunks;
-    for (int c = threadIdx.x; c < hd; c += kScoreThreads) {
-      float s = 0.f;
-      for (int u = 0; u < q_chunks; ++u) s += partial[(base + u) * hd + c];
-      qbar[c] = s * inv;
-    }
+    kbar[(size_t)j * hd + c] = m;
+    if (page_kmean) page_kmean[(size_t)j * hd + c] = m;
   }
 }
+
+constexpr int kTopkThreads = 1024;
 
 // Scores and the top-K_p set.  One wave per page computes the dot product in
 // a fixed order; page j is selected iff fewer than K_p pages rank above it
 // (higher score, or equal score and lower id); the selected ids are written
 // in ascending order.
-__global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(
+__global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int n_pages, int hd, float scale,
     int kp, float* __restrict__ scores, int32_t* __restrict__ sel) {
   __shared__ float alpha[kMaxPages];
   __shared__ int chosen[kMaxPages];
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  for (int j = w; j < n_pages; j += kScoreThreads / kWave) {
+  for (int j = w; j < n_pages; j += kTopkThreads / kWave) {
+    const float4* kb = reinterpret_cast<const float4*>(kbar + (size_t)j * hd);
+    const float4* qb = reinterpret_cast<const float4*>(qbar);
     float s = 0.f;
-    for (int c = lane; c < hd; c += kWave) s += qbar[c] * kbar[(size_t)j * hd + c];
+    for (int c = lane; c < hd / 4; c += kWave) {
+      const float4 a = qb[c], b = kb[c];
+      s += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
     if (lane == 0) alpha[j] = s * scale;
@@ -182,10 +192,10 @@ void launch_score(const Dims& s, const void* q, const PageTable& tab, int n_page
                      reinterpret_cast<const T*>(q), tab, n_pages, s.Lp, s.Lq, cpr, sp.page_chunks,
                      sp.page_rows, sp.q_rows, m.cols, m.par, partial);
   const int hd = s.H * s.d;
-  hipLaunchKernelGGL(score_means_kernel, dim3(n_pages + 1), dim3(kScoreThreads), 0, st, partial, tab,
+  hipLaunchKernelGGL(score_means_kernel, dim3(n_pages + 1, (hd + kScoreThreads - 1) / kScoreThreads), dim3(kScoreThreads), 0, st, partial, tab,
                      n_pages, sp.page_chunks, sp.q_chunks, hd, s.Lp, s.Lq, page_kmean, kbar, qbar);
   const float scale = 1.f / ((float)s.H * sqrtf((float)s.d));
-  hipLaunchKernelGGL(score_topk_kernel, dim3(1), dim3(kScoreThreads), 0, st, qbar, kbar, n_pages, hd,
+  hipLaunchKernelGGL(score_topk_kernel, dim3(1), dim3(kTopkThreads), 0, st, qbar, kbar, n_pages, hd,
                      scale, s.Kp, scores, sel);
 }
 

@@ -28,6 +28,7 @@ namespace hsa {
 namespace {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kZeroChunks = 64;  // 1 KB of zeros in the workspace
 
 __device__ int scan_incl_1024(int v, int* buf) {
   const int t = threadIdx.x;
@@ -48,10 +49,11 @@ __device__ int scan_incl_1024(int v, int* buf) {
 // rowinfo[row] = {segments, first slot}; meta = {items, slots}.
 __global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
     const int32_t* __restrict__ blk_count, int rows, int nKB, int gpb, int gps, int seg_granules,
-    int4* __restrict__ items, int2* __restrict__ rowinfo, int* __restrict__ meta) {
+    int4* __restrict__ items, int2* __restrict__ rowinfo, int* __restrict__ meta, uint4* __restrict__ zeros) {
   __shared__ int buf[kPlanThreads];
   __shared__ int carry_items, carry_slots;
   const int t = threadIdx.x;
+  if (t < kZeroChunks) zeros[t] = make_uint4(0, 0, 0, 0);  // source of masked granules
   if (t == 0) carry_items = carry_slots = 0;
   __syncthreads();
   for (int base = 0; base < rows; base += kPlanThreads) {
@@ -90,30 +92,51 @@ __global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
   }
 }
 
-template <typename T, int D, int NW, int QPW>
-__global__ __launch_bounds__(NW * kWave) void sparse_attn_kernel(
+// LDS staging of one step (KS keys), written by direct global->LDS loads
+// (each wave instruction writes 1 KB: 64 lanes x 16 bytes, contiguous).
+//  * K: rows of D elements; the 16-byte chunk c of key row rho sits in slot
+//    c ^ kswz(rho), so the operand reads of a wave (16 rows, same chunk) hit
+//    distinct banks.
+//  * V: the step's granules as regions [granule][part][D rows][16 bytes];
+//    region g is exactly what lane group g reads for the V^T operand.
+template <typename T> __device__ __forceinline__ int kswz(int rho, int cpr);
+template <> __device__ __forceinline__ int kswz<bf16_t>(int rho, int cpr) {
+  return ((rho & 3) | (((rho >> 3) & 3) << 2)) & (cpr - 1);
+}
+template <> __device__ __forceinline__ int kswz<float>(int rho, int cpr) { return rho & 15 & (cpr - 1); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void load_lds16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+
+// wait until this wave's direct-to-LDS loads have landed
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+
+template <typename T, int D, int NW, int QPW, int WPE>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void sparse_attn_kernel(
     const T* __restrict__ q, const T* __restrict__ k_act, const T* __restrict__ v_act,
     const int32_t* __restrict__ blk_idx, const int4* __restrict__ items, const int* __restrict__ meta,
-    int H, int B, int L, int nKB, int nQB, float scale_log2, float* __restrict__ o_sp,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
+    const uint4* __restrict__ zeros, int H, int B, int L, int nKB, int nQB, float scale_log2,
+    float* __restrict__ o_sp, float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int E = Vec<T>::N;          // elements per 16-byte chunk
   constexpr int KS = Mma<T>::K;         // keys per step
   constexpr int GPS = KS / 16;          // granules per step
-  constexpr int DCH = D / E;            // chunks per key row
+  constexpr int CPR = D / E;            // chunks per key row
   constexpr int DSTEPS = D / KS;        // contraction steps over d in S^T = K Q^T
   constexpr int DT = D / 16;            // output d-tiles
-  constexpr int KSTR = D + E;           // LDS row stride of the K stage (padded)
-  constexpr int VSTR = KS + E;          // LDS row stride of the V^T stage (padded)
-  constexpr int KSTAGE = KS * KSTR;
-  constexpr int VSTAGE = D * VSTR;
-  constexpr int NT = NW * kWave;
-  constexpr int CK = GPS * 16 * DCH;    // K chunks per step
-  constexpr int CV = GPS * D * (16 / E);
-  constexpr int NLD = (CK + CV + NT - 1) / NT;
-  constexpr int PV = 16 / E;            // chunks per 16-token granule row of V
+  constexpr int PV = 16 / E;            // 16-byte parts per granule row of V
+  constexpr int KBYTES = KS * CPR * 16; // K stage bytes
+  constexpr int VBYTES = GPS * PV * D * 16;
+  constexpr int KINST = KBYTES / 1024;  // 1 KB direct-load instructions
+  constexpr int VINST = VBYTES / 1024;
+  constexpr int ROWS_PER_INST = 64 / CPR;
+  constexpr float kLazy = 8.f;          // rescale only when the row max grows by more than 2^8
 
-  __shared__ __align__(16) T lds_k[2][KSTAGE];
-  __shared__ __align__(16) T lds_v[2][VSTAGE];
+  __shared__ __align__(1024) unsigned char lds_k[2][KBYTES];
+  __shared__ __align__(1024) unsigned char lds_v[2][VBYTES];
 
   const int item = xcd_remap(blockIdx.x, meta[0]);
   if (item < 0) return;
@@ -151,8 +174,10 @@ __global__ __launch_bounds__(NW * kWave) void sparse_attn_kernel(
   }
 
   const int nsub = (gcount + GPS - 1) / GPS;
+  const T* kh = k_act + (size_t)h * L * D;
+  const T* vh = v_act + (size_t)h * (L / 16) * D * 16;
 
-  // key offset of granule `j` of step `sub`, or -1 when it is past the end or its block id is invalid
+  // key offset of granule j of step `sub`, or -1 (past the end, or invalid block id)
   auto granule_key = [&](int sub, int j) -> int {
     const int gi = sub * GPS + j;
     if (gi >= gcount) return -1;
@@ -162,58 +187,52 @@ __global__ __launch_bounds__(NW * kWave) void sparse_attn_kernel(
     return blk * B + (ga % gpb) * 16;
   };
 
-  uint4 pre[NLD];
-  auto load_step = [&](int sub) {
+  auto issue = [&](int sub, int buf) {
     int kofs[GPS];
 #pragma unroll
     for (int j = 0; j < GPS; ++j) kofs[j] = granule_key(sub, j);
+    // K: instruction i writes rows i*ROWS_PER_INST .. +ROWS_PER_INST-1
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int cidx = tid + u * NT;
-      pre[u] = make_uint4(0, 0, 0, 0);
-      if (cidx < CK) {
-        const int j = cidx / (16 * DCH), rr = (cidx / DCH) % 16, cc = cidx % DCH;
-        if (kofs[j] >= 0) pre[u] = ld16(k_act + ((size_t)h * L + kofs[j] + rr) * D + cc * E);
-      } else if (cidx < CK + CV) {
-        const int c2 = cidx - CK;
-        const int j = c2 / (D * PV), rem = c2 % (D * PV);
-        const int drow = rem / PV, part = rem % PV;
-        if (kofs[j] >= 0)
-          pre[u] = ld16(v_act + (((size_t)h * (L / 16) + kofs[j] / 16) * D + drow) * 16 + part * E);
-      }
+    for (int i = w; i < KINST; i += NW) {
+      const int rho = i * ROWS_PER_INST + lane / CPR;
+      const int slotc = lane % CPR;
+      const int chunk = slotc ^ kswz<T>(rho, CPR);
+      const int j = rho / 16;
+      const void* src = kofs[j] >= 0 ? (const void*)(kh + (size_t)(kofs[j] + (rho % 16)) * D + chunk * E)
+                                     : (const void*)(zeros + lane);
+      load_lds16(src, lds_k[buf] + i * 1024);
     }
-  };
-  auto store_step = [&](int buf) {
+    // V: instruction i covers region r = i / (D/64) (granule r / PV, part r % PV), rows (i % (D/64))*64 + lane
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int cidx = tid + u * NT;
-      if (cidx < CK) {
-        const int j = cidx / (16 * DCH), rr = (cidx / DCH) % 16, cc = cidx % DCH;
-        st16(&lds_k[buf][(16 * j + rr) * KSTR + cc * E], pre[u]);
-      } else if (cidx < CK + CV) {
-        const int c2 = cidx - CK;
-        const int j = c2 / (D * PV), rem = c2 % (D * PV);
-        const int drow = rem / PV, part = rem % PV;
-        st16(&lds_v[buf][drow * VSTR + 16 * j + part * E], pre[u]);
-      }
+    for (int i = w; i < VINST; i += NW) {
+      const int region = i / (D / 64);
+      const int rowv = (i % (D / 64)) * 64 + lane;
+      const int j = region / PV, part = region % PV;
+      const void* src = kofs[j] >= 0
+                            ? (const void*)(vh + ((size_t)(kofs[j] / 16) * D + rowv) * 16 + part * E)
+                            : (const void*)(zeros + lane);
+      load_lds16(src, lds_v[buf] + i * 1024);
     }
   };
 
-  load_step(0);
-  store_step(0);
+  issue(0, 0);
+  wait_vm();
   __syncthreads();
 
   for (int sub = 0; sub < nsub; ++sub) {
     const int buf = sub & 1;
     const bool more = sub + 1 < nsub;
-    if (more) load_step(sub + 1);
-
-    // validity of this lane's keys: for bf16 lane group g holds keys of granule g/2
-    bool valid = true;
-    if (GPS == 2) valid = (sub * GPS + (g >> 1)) < gcount && granule_key(sub, g >> 1) >= 0;
-    else valid = granule_key(sub, 0) >= 0;
+    if (more) issue(sub + 1, buf ^ 1);
 
     if (w * QPW < QT) {
+      // masked keys only on a ragged or invalid step (wave-uniform test)
+      bool gval[GPS];
+      bool all_valid = true;
+#pragma unroll
+      for (int j = 0; j < GPS; ++j) {
+        gval[j] = granule_key(sub, j) >= 0;
+        all_valid = all_valid && gval[j];
+      }
       f32x4 sacc[QPW][GPS];
 #pragma unroll
       for (int t = 0; t < QPW; ++t)
@@ -221,56 +240,78 @@ __global__ __launch_bounds__(NW * kWave) void sparse_attn_kernel(
         for (int kt = 0; kt < GPS; ++kt) sacc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kt = 0; kt < GPS; ++kt) {
-        const T* krow = &lds_k[buf][perm_row<T>(kt, c) * KSTR];
+        const int rho = perm_row<T>(kt, c);
+        const unsigned char* krow = lds_k[buf] + rho * CPR * 16;
+        const int sw = kswz<T>(rho, CPR);
 #pragma unroll
         for (int s = 0; s < DSTEPS; ++s) {
-          const uint4 a = *reinterpret_cast<const uint4*>(krow + (4 * s + g) * E);
+          const uint4 a = *reinterpret_cast<const uint4*>(krow + (((4 * s + g) ^ sw) * 16));
 #pragma unroll
           for (int t = 0; t < QPW; ++t)
             if (t < ntile) Mma<T>::run(sacc[t][kt], a, qreg[t][s]);
         }
       }
+      if (!all_valid) {
+        // lane group g holds keys of granule g/2 (bf16) or granule 0 (f32)
+        const bool ok = gval[GPS == 2 ? (g >> 1) : 0];
+        if (!ok) {
+#pragma unroll
+          for (int t = 0; t < QPW; ++t)
+#pragma unroll
+            for (int kt = 0; kt < GPS; ++kt) sacc[t][kt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        }
+      }
       uint4 pk[QPW];
+      float alpha[QPW];
+      bool need_any = false;
 #pragma unroll
       for (int t = 0; t < QPW; ++t) {
+        alpha[t] = 1.f;
         if (t < ntile) {
           float mx = -INFINITY;
 #pragma unroll
           for (int kt = 0; kt < GPS; ++kt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if (!valid) sacc[t][kt][i] = -INFINITY;
-              mx = fmaxf(mx, sacc[t][kt][i]);
-            }
-          mx = max4g(mx);
-          const float m_new = fmaxf(m_run[t], mx * scale_log2);
-          const float alpha = exp2f(m_run[t] - m_new);
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[t][kt][i]);
+          mx = max4g(mx) * scale_log2;
+          const bool need = mx > m_run[t] + kLazy;
+          if (need) {
+            alpha[t] = exp2f(m_run[t] - mx);
+            m_run[t] = mx;
+          }
+          need_any = need_any || need;
+          const float mref = m_run[t] == -INFINITY ? 0.f : m_run[t];
           float ls = 0.f;
           f32x4 p[GPS];
 #pragma unroll
           for (int kt = 0; kt < GPS; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float e = exp2f(sacc[t][kt][i] * scale_log2 - m_new);
+              const float e = exp2f(fmaf(sacc[t][kt][i], scale_log2, -mref));
               p[kt][i] = e;
               ls += e;
             }
-          l_run[t] = l_run[t] * alpha + ls;
-          m_run[t] = m_new;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
+          l_run[t] = l_run[t] * alpha[t] + ls;
           pk[t] = pack_p<T>(p);
         }
       }
+      if (__any(need_any)) {
+#pragma unroll
+        for (int t = 0; t < QPW; ++t)
+          if (t < ntile)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha[t];
+      }
+      const unsigned char* vreg = lds_v[buf] + g * (D * 16);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint4 a = *reinterpret_cast<const uint4*>(&lds_v[buf][(16 * dt + c) * VSTR + g * E]);
+        const uint4 a = *reinterpret_cast<const uint4*>(vreg + (16 * dt + c) * 16);
 #pragma unroll
         for (int t = 0; t < QPW; ++t)
           if (t < ntile) Mma<T>::run(o[t][dt], a, pk[t]);
       }
     }
-    if (more) store_step(buf ^ 1);
+    wait_vm();
     __syncthreads();
   }
 
@@ -281,7 +322,7 @@ __global__ __launch_bounds__(NW * kWave) void sparse_attn_kernel(
       const float l_tot = sum4g(l_run[t]);
       const int r = (w * QPW + t) * 16 + c;  // query row inside the block
       if (slot < 0) {
-        const float inv = 1.f / l_tot;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         float* dst = o_sp + (((size_t)qb * B + r) * H + h) * D + 4 * g;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -322,6 +363,7 @@ __global__ __launch_bounds__(256) void sparse_combine_kernel(
     }
     float M = -INFINITY;
     for (int s = 0; s < nseg; ++s) M = fmaxf(M, part_ml[((size_t)(s0 + s) * B + r) * 2]);
+    if (M == -INFINITY) M = 0.f;
     float den = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s = 0; s < nseg; ++s) {
@@ -331,31 +373,32 @@ __global__ __launch_bounds__(256) void sparse_combine_kernel(
       const float4 v = reinterpret_cast<const float4*>(part_o + sr * D)[c4];
       acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
     }
-    const float inv = 1.f / den;
+    const float inv = den > 0.f ? 1.f / den : 0.f;
     *dst = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
 }
 
 template <typename T, int D, int NW, int QPW>
 void launch_attn(const Dims& s, const SparsePlan& pl, const void* q, const void* k_act, const void* v_act,
-                 const int32_t* idx, const int4* items, const int* meta, float* o_sp, float* po, float* pml,
-                 hipStream_t st) {
+                 const int32_t* idx, const int4* items, const int* meta, const uint4* zeros, float* o_sp,
+                 float* po, float* pml, hipStream_t st) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
-  hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW>), dim3(pl.grid), dim3(NW * kWave), 0, st,
+  constexpr int WPE = sizeof(T) == 2 ? 2 : 1;
+  hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE>), dim3(pl.grid), dim3(NW * kWave), 0, st,
                      reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act),
-                     reinterpret_cast<const T*>(v_act), idx, items, meta, s.H, s.B, s.L, s.nKB, s.nQB,
+                     reinterpret_cast<const T*>(v_act), idx, items, meta, zeros, s.H, s.B, s.L, s.nKB, s.nQB,
                      scale_log2, o_sp, po, pml);
 }
 
 template <typename T, int D>
 void dispatch_attn(const Dims& s, const SparsePlan& pl, const void* q, const void* k_act, const void* v_act,
-                   const int32_t* idx, const int4* items, const int* meta, float* o_sp, float* po, float* pml,
-                   hipStream_t st) {
+                   const int32_t* idx, const int4* items, const int* meta, const uint4* zeros, float* o_sp,
+                   float* po, float* pml, hipStream_t st) {
   const int QT = s.B / 16;
   const int nw = (QT + 2) / 3;
   const int qpw = (QT + nw - 1) / nw;
 #define HSA_ATTN_CASE(NW_, QPW_) \
-  if (nw == NW_ && qpw == QPW_) return launch_attn<T, D, NW_, QPW_>(s, pl, q, k_act, v_act, idx, items, meta, o_sp, po, pml, st);
+  if (nw == NW_ && qpw == QPW_) return launch_attn<T, D, NW_, QPW_>(s, pl, q, k_act, v_act, idx, items, meta, zeros, o_sp, po, pml, st);
   HSA_ATTN_CASE(1, 1)
   HSA_ATTN_CASE(1, 2)
   HSA_ATTN_CASE(1, 3)
@@ -387,15 +430,16 @@ extern "C" hsa_rc hsa_sparse_attn(const hsa_geom* geom, const void* q, const voi
   int* meta = reinterpret_cast<int*>(wsb + w.sp_meta);
   float* po = reinterpret_cast<float*>(wsb + w.sp_part_o);
   float* pml = reinterpret_cast<float*>(wsb + w.sp_part_ml);
+  uint4* zeros = reinterpret_cast<uint4*>(wsb + w.sp_zeros);
   const int gps = s.bf16 ? 2 : 1;
   hipLaunchKernelGGL(sparse_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, blk_count, s.rows, s.nKB,
-                     pl.granules_per_block, gps, pl.seg_granules, items, rowinfo, meta);
+                     pl.granules_per_block, gps, pl.seg_granules, items, rowinfo, meta, zeros);
   if (s.bf16) {
-    if (s.d == 128) dispatch_attn<bf16_t, 128>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
-    else dispatch_attn<bf16_t, 64>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
+    if (s.d == 128) dispatch_attn<bf16_t, 128>(s, pl, q, k_act, v_act, blk_idx, items, meta, zeros, o_sp, po, pml, st);
+    else dispatch_attn<bf16_t, 64>(s, pl, q, k_act, v_act, blk_idx, items, meta, zeros, o_sp, po, pml, st);
   } else {
-    if (s.d == 128) dispatch_attn<float, 128>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
-    else dispatch_attn<float, 64>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
+    if (s.d == 128) dispatch_attn<float, 128>(s, pl, q, k_act, v_act, blk_idx, items, meta, zeros, o_sp, po, pml, st);
+    else dispatch_attn<float, 64>(s, pl, q, k_act, v_act, blk_idx, items, meta, zeros, o_sp, po, pml, st);
   }
   if (s.d == 128)
     hipLaunchKernelGGL(sparse_combine_kernel<128>, dim3(s.rows), dim3(256), 0, st, rowinfo, po, pml, s.H, s.B, s.nQB, o_sp);
