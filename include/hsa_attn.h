@@ -54,6 +54,7 @@ extern "C" {
 #define HSA_ATTN_ABI_VERSION 1
 #define HSA_MAX_PAGES 128      /* pages per call (pointer tables travel as launch arguments) */
 #define HSA_MAX_KBLOCKS 2048   /* nKB limit of the block selection (one sort per row in LDS) */
+#define HSA_MAX_ROWS 4096      /* H * nQB limit (selection rows; the sparse branch plans them in LDS) */
 
 typedef enum {
   HSA_OK = 0,

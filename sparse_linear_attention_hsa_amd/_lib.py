@@ -16,6 +16,7 @@ HSA_F32, HSA_BF16 = 0, 1
 HSA_LIN_REUSE_PROJ, HSA_LIN_PROJ_ONLY = 1, 2
 HSA_MAX_PAGES = 128
 HSA_MAX_KBLOCKS = 2048
+HSA_MAX_ROWS = 4096
 
 RC_NAMES = {0: "HSA_OK", 1: "HSA_ERR_NULL_ARG", 2: "HSA_ERR_BAD_SHAPE", 3: "HSA_ERR_BAD_DTYPE",
             4: "HSA_ERR_BAD_PARAM", 5: "HSA_ERR_WORKSPACE", 6: "HSA_ERR_HIP"}
@@ -48,6 +49,9 @@ SIGNATURES = {
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    # torch ships its own HIP runtime under the same soname; load it first so
+    # the library binds to the runtime that owns torch's streams and memory.
+    import torch  # noqa: F401
     if not os.path.exists(path):
         raise ImportError(
             f"HSA HIP library not built: {path} is missing "

@@ -15,6 +15,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kWave = 64;
 constexpr int kMaxPages = HSA_MAX_PAGES;
 
+// 1 KB of zeros in device memory: the source of masked 16-byte lanes of the
+// direct global->LDS loads (each lane reads kZeroPage[lane]).
+__device__ const uint4 kZeroPage[64] = {};
+
 // Page pointer tables travel by value as launch arguments.
 struct PageTable {
   const void* p[kMaxPages];
@@ -135,6 +139,11 @@ __device__ __forceinline__ float sum4g(float v) {
 }
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// 2^x with the hardware instruction (no range fix-ups): used for softmax
+// weights whose arguments are <= 8 here; results below the float range flush
+// to 0, which is what the softmax wants.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // The 8 XCDs of an MI355X receive consecutive workgroup ids round-robin.
 // Remapping blockIdx so that each XCD walks one contiguous range of work

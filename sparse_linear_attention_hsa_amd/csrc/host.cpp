@@ -33,6 +33,7 @@ hsa_rc derive(const hsa_geom* g, Dims* o) {
       Lq * D > (1LL << 31) || Lp * D > (1LL << 31))
     return HSA_ERR_BAD_SHAPE;
   if (L / B > HSA_MAX_KBLOCKS) return HSA_ERR_BAD_SHAPE;
+  if (1LL * g->n_heads * (Lq / B) > HSA_MAX_ROWS) return HSA_ERR_BAD_SHAPE;
   Dims s;
   s.H = g->n_heads; s.d = g->head_dim; s.D = (int)D;
   s.Lp = (int)Lp; s.Lq = (int)Lq; s.B = (int)B; s.Kp = g->n_sel_pages; s.L = (int)L;
@@ -59,8 +60,9 @@ ScorePlan score_plan(const Dims& s, int n_pages) {
 ProjPlan proj_plan(const Dims& s) {
   ProjPlan p;
   const int K = s.bf16 ? 32 : 16;
-  p.steps = cdiv(s.L, K);
-  p.splits = std::max(1, std::min(p.steps, cdiv(512, 2 * s.H)));
+  p.steps = cdiv(s.L, 2 * K);   // stages of two contraction steps
+  // about one workgroup (8 waves, two heads) per CU
+  p.splits = std::max(1, std::min(p.steps, cdiv(256, 2 * ((s.H + 1) / 2))));
   p.rtiles = cdiv(s.r, 16);
   p.rpad = cdiv(s.r, K) * K;
   return p;

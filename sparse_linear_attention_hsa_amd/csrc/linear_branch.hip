@@ -6,138 +6,179 @@
 //
 // Kernels:
 //  * project: split-K matrix-core product over the sequence axis.  One
-//    workgroup (4 waves) computes the full r x d output of one (head, K|V)
-//    for one slice of the sequence, so every active K/V element is read from
-//    memory exactly once; E (shared by all heads) is re-read from L2/MALL.
-//    Contraction over tokens needs tokens contiguous per operand lane: V is
-//    already token-contiguous (d-major granules); K tiles are transposed
-//    through LDS.  Partials are float32.
+//    workgroup computes the full r x d outputs of two heads (K or V) for one
+//    slice of the sequence, so every active K/V element is read from memory
+//    exactly once and each E tile serves two heads.  Contraction over tokens
+//    needs tokens contiguous per operand lane: V is already token-contiguous
+//    (d-major granules); K tiles are transposed through LDS.  Partials are
+//    float32.
 //  * reduce : fixed-order sum of the slices, written as Ktil [H][r][d] and
 //    Vtil^T [H][d][r] in float32.
-//  * attend : per (head, 16-query tile) wave, S^T = Ktil Q^T over all r
-//    rows at once (exact softmax, no online rescaling), then O^T = Vtil^T P^T.
+//  * attend : 128 queries of one head per workgroup; rank chunks of Ktil and
+//    Vtil^T staged in LDS, online softmax over the chunks, O^T = Vtil^T P^T.
 #include "common.h"
 #include "host.h"
 
 namespace hsa {
 namespace {
 
-constexpr int kProjThreads = 256;  // 4 waves
-constexpr int kMaxRT = 16;         // r-tiles of 16 per workgroup (r <= 256)
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-// grid = (2*H, splits).  x < H: keys of head x, else values of head x-H.
-// Software pipeline: the global loads of step n+1 are in flight while step n
-// is multiplied; the transposed K tile is double buffered in LDS (one
-// barrier per step).
+// Projection of the sequence axis, split over S slices of the active keys.
+// Work item = (slice, K|V, head pair); the two heads of a pair share one E
+// tile.  Items run slice-major and each XCD takes a contiguous range of them,
+// so the workgroups that need the same E slice sit behind the same L2.
+// Workgroup = 8 waves: wave w works on head (w / 4) of the pair and on r-tiles
+// 4*(w % 4) .. +3, all D columns (128 float32 accumulators per lane).
+// Per stage (2 contraction steps, ST tokens), staged in LDS and double
+// buffered:
+//  * E tile [256 rows][ST tokens] by direct global->LDS loads; chunk slot
+//    swizzled by the row so the operand reads are bank-conflict free;
+//  * X^T tiles [D][ST tokens] per head in regions [granule][part][D][16 B]:
+//    values arrive that way from the active buffer (direct loads); keys are
+//    loaded to registers one stage ahead and written transposed.
+constexpr int kProjThreads = 512;  // 8 waves
+constexpr int kProjHeads = 2;
+
+__device__ __forceinline__ int eswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
 template <typename T, int D>
-__global__ __launch_bounds__(kProjThreads) void lin_project_kernel(
+__global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lin_project_kernel(
     const T* __restrict__ k_act, const T* __restrict__ v_act, const T* __restrict__ e_k,
-    const T* __restrict__ e_v, int H, int L, int r, int steps, int splits, float* __restrict__ partial) {
+    const T* __restrict__ e_v, int H, int L, int r, int splits, float* __restrict__ partial) {
   constexpr int E = Vec<T>::N;
-  constexpr int KS = Mma<T>::K;      // tokens per step
+  constexpr int KS = Mma<T>::K;          // tokens per contraction step
+  constexpr int ST = 2 * KS;             // tokens per stage
   constexpr int DT = D / 16;
-  constexpr int RPW = kMaxRT / 4;    // r-tiles per wave
-  constexpr int TSTR = KS + E;       // LDS row stride (elements) of the transposed K tile
-  constexpr int KCH = KS * (D / E);  // 16-byte chunks of one K step
-  constexpr int KPT = (KCH + kProjThreads - 1) / kProjThreads;
-  __shared__ __align__(16) T kt_s[2][D * TSTR];
+  constexpr int PV = 16 / E;             // 16-byte parts per granule row
+  constexpr int NREG = ST / 16 * PV;     // X^T regions per stage (8)
+  constexpr int XBYTES = NREG * D * 16;  // X^T tile bytes per head
+  constexpr int EBYTES = 256 * ST * (int)sizeof(T);  // 256 rows x 128 bytes
+  constexpr int KCH = ST * (D / E);      // 16-byte key chunks per head per stage
+  constexpr int KPT = (kProjHeads * KCH) / kProjThreads;
+  __shared__ __align__(1024) unsigned char lds_e[2][EBYTES];
+  __shared__ __align__(1024) unsigned char lds_x[2][kProjHeads][XBYTES];
 
-  const int which = blockIdx.x;
-  const bool is_v = which >= H;
-  const int h = is_v ? which - H : which;
-  const int split = blockIdx.y;
-  const int st0 = (int)((long long)steps * split / splits);
-  const int st1 = (int)((long long)steps * (split + 1) / splits);
-  const T* e = is_v ? e_v : e_k;
-  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int HP = (H + 1) / 2;
+  const int n_items = splits * 2 * HP;
+  const int item = xcd_remap(blockIdx.x, n_items);
+  if (item < 0) return;
+  const int split = item / (2 * HP);
+  const int kv = (item / HP) % 2;
+  const int hp = item % HP;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g = lane >> 4, c = lane & 15;
+  const int hs = w / 4, rg = w % 4;            // head slot, r-group of this wave
+  const int h = hp * 2 + hs;                   // may be == H for an odd head count
+  const bool h_ok = h < H;
   const int rtiles = (r + 15) / 16;
+  const int nst = (L + ST - 1) / ST;
+  const int st0 = (int)((long long)nst * split / splits);
+  const int st1 = (int)((long long)nst * (split + 1) / splits);
+  const T* e = kv ? e_v : e_k;
 
-  f32x4 acc[RPW][DT];
+  f32x4 acc[4][DT];
 #pragma unroll
-  for (int a = 0; a < RPW; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[a][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 aop[RPW], bop[DT], kch[KPT];
-  // issue the global loads of one step
-  auto load = [&](int stp) {
-    const int tok0 = stp * KS;
-    const int tk = tok0 + g * E;
-#pragma unroll
-    for (int a = 0; a < RPW; ++a) {
-      const int rr = 16 * (w * RPW + a) + c;
-      aop[a] = (rr < r && tk < L) ? ld16(e + (size_t)rr * L + tk) : make_uint4(0, 0, 0, 0);
+  uint4 kreg[KPT > 0 ? KPT : 1];
+  // direct loads of one stage (E for all rows, values for both heads), key rows to registers
+  auto issue = [&](int stg, int buf) {
+    const int tok0 = stg * ST;
+    // E: instruction i covers rows 8i .. 8i+7 (128 bytes each)
+    for (int i = w; i < rtiles * 2; i += kProjThreads / kWave) {
+      const int row = 8 * i + lane / 8;
+      const int chunk = (lane % 8) ^ eswz(row);
+      const int tk = tok0 + chunk * E;
+      const void* src = (row < r && tk < L) ? (const void*)(e + (size_t)row * L + tk) : (const void*)(kZeroPage + lane);
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(lds_e[buf] + i * 1024), 16, 0, 0);
     }
-    if (is_v) {
-      // v_act granules [L/16][D][16]: chunk g covers tokens tk .. tk+E-1
+    if (kv) {
+      // values: region = (granule, part), D/64 instructions per region, per head
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        bop[dt] = tk < L ? ld16(v_act + (((size_t)h * (L / 16) + tk / 16) * D + 16 * dt + c) * 16 + (tk % 16))
-                         : make_uint4(0, 0, 0, 0);
+      for (int ii = 0; ii < (kProjHeads * NREG * D / 64) / (kProjThreads / kWave); ++ii) {
+        const int i = ii * (kProjThreads / kWave) + w;
+        const int hsl = i / (NREG * D / 64);
+        const int rem = i % (NREG * D / 64);
+        const int region = rem / (D / 64);
+        const int rowv = (rem % (D / 64)) * 64 + lane;
+        const int gr = region / PV, part = region % PV;
+        const int hh = hp * 2 + hsl;
+        const int tk = tok0 + gr * 16;
+        const void* src = (hh < H && tk < L)
+                              ? (const void*)(v_act + (((size_t)hh * (L / 16) + tk / 16) * D + rowv) * 16 + part * E)
+                              : (const void*)(kZeroPage + lane);
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(lds_x[buf][hsl] + (size_t)region * D * 16 + (rem % (D / 64)) * 1024), 16, 0, 0);
+      }
     } else {
 #pragma unroll
       for (int u = 0; u < KPT; ++u) {
         const int ci = tid + u * kProjThreads;
-        const int tr = ci / (D / E), cc = ci % (D / E);
-        kch[u] = (ci < KCH && tok0 + tr < L) ? ld16(k_act + ((size_t)h * L + tok0 + tr) * D + cc * E)
-                                             : make_uint4(0, 0, 0, 0);
+        const int hsl = ci / KCH, cr = ci % KCH;
+        const int tr = cr / (D / E), cc = cr % (D / E);
+        const int hh = hp * 2 + hsl;
+        kreg[u] = (hh < H && tok0 + tr < L) ? ld16(k_act + ((size_t)hh * L + tok0 + tr) * D + cc * E)
+                                           : make_uint4(0, 0, 0, 0);
       }
     }
   };
-  // K only: write the loaded rows transposed, kt_s[buf][col][token]
-  auto stage = [&](int buf) {
+  // keys only: write the registers of a stage transposed into the X^T regions
+  auto stage_keys = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
       const int ci = tid + u * kProjThreads;
-      if (ci < KCH) {
-        const int tr = ci / (D / E), cc = ci % (D / E);
-        float f[E];
-        unpack16<T>(kch[u], f);
+      const int hsl = ci / KCH, cr = ci % KCH;
+      const int tr = cr / (D / E), cc = cr % (D / E);
+      const int region = (tr / 16) * PV + (tr % 16) / E;
+      unsigned char* base = lds_x[buf][hsl] + (size_t)region * D * 16 + (tr % E) * sizeof(T);
+      float f[E];
+      unpack16<T>(kreg[u], f);
 #pragma unroll
-        for (int x = 0; x < E; ++x) kt_s[buf][(cc * E + x) * TSTR + tr] = from_f32<T>(f[x]);
-      }
+      for (int x = 0; x < E; ++x) *reinterpret_cast<T*>(base + (cc * E + x) * 16) = from_f32<T>(f[x]);
     }
   };
 
   if (st0 < st1) {
-    load(st0);
-    if (!is_v) {
-      stage(0);
-      __syncthreads();
-    }
+    issue(st0, 0);
+    if (!kv) stage_keys(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
   }
-  for (int stp = st0; stp < st1; ++stp) {
-    const int buf = (stp - st0) & 1;
-    uint4 a_cur[RPW], b_cur[DT];
+  for (int stg = st0; stg < st1; ++stg) {
+    const int buf = (stg - st0) & 1;
+    const bool more = stg + 1 < st1;
+    if (more) issue(stg + 1, buf ^ 1);
+    if (h_ok && rg * 4 < rtiles) {
 #pragma unroll
-    for (int a = 0; a < RPW; ++a) a_cur[a] = aop[a];
-    if (is_v) {
+      for (int ks = 0; ks < 2; ++ks) {
+        uint4 bop[DT];
+        const unsigned char* xr = lds_x[buf][hs] + (size_t)(ks * 4 + g) * D * 16;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) b_cur[dt] = bop[dt];
-    } else {
+        for (int dt = 0; dt < DT; ++dt) bop[dt] = *reinterpret_cast<const uint4*>(xr + (16 * dt + c) * 16);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) b_cur[dt] = *reinterpret_cast<const uint4*>(&kt_s[buf][(16 * dt + c) * TSTR + g * E]);
-    }
-    const bool more = stp + 1 < st1;
-    if (more) load(stp + 1);
+        for (int a = 0; a < 4; ++a) {
+          const int row = 16 * (rg * 4 + a) + c;
+          const int slot = (ks * 4 + g) ^ eswz(row);
+          const uint4 aop = *reinterpret_cast<const uint4*>(lds_e[buf] + row * 128 + slot * 16);
 #pragma unroll
-    for (int a = 0; a < RPW; ++a) {
-      if (w * RPW + a < rtiles) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) Mma<T>::run(acc[a][dt], a_cur[a], b_cur[dt]);
+          for (int dt = 0; dt < DT; ++dt) Mma<T>::run(acc[a][dt], aop, bop[dt]);
+        }
       }
     }
-    if (!is_v && more) {
-      stage(buf ^ 1);
-      __syncthreads();
-    }
+    if (more && !kv) stage_keys(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
   }
-  // partial[split][which][rt*16 + row][D]; lane holds rows 4g+i, column c of each tile
+  // partial[split][kv*H + h][rt*16 + row][D]; lane holds rows 4g+i, column c of each tile
+  if (!h_ok) return;
+  const int which = kv * H + h;
   float* out = partial + (((size_t)split * 2 * H + which) * (size_t)(rtiles * 16)) * D;
 #pragma unroll
-  for (int a = 0; a < RPW; ++a) {
-    const int rt = w * RPW + a;
+  for (int a = 0; a < 4; ++a) {
+    const int rt = rg * 4 + a;
     if (rt < rtiles) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -182,137 +223,157 @@ __global__ __launch_bounds__(256) void lin_reduce_kernel(const float* __restrict
   }
 }
 
-// A operand of the matrix cores from float32 storage (one chunk of Vec<T>::N
-// contraction elements).  For bf16 the value is split into hi = bf16(x) and
-// lo = bf16(x - hi): two products carry ~16 mantissa bits, so the projected
-// keys keep float32-like precision in the logits even when |Q| is large.
-template <typename T> struct F32Operand;
-template <> struct F32Operand<float> {
-  static constexpr bool kSplit = false;
-  __device__ __forceinline__ static void load(const float* p, bool ok, uint4& hi, uint4& lo) {
-    hi = ok ? ld16(p) : make_uint4(0, 0, 0, 0);
-    lo = make_uint4(0, 0, 0, 0);
-  }
-  __device__ __forceinline__ static uint4 load_round(const float* p, int n_ok) {
-    float f[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) f[x] = x < n_ok ? p[x] : 0.f;
-    return pack16<float>(f);
-  }
-};
-template <> struct F32Operand<bf16_t> {
-  static constexpr bool kSplit = true;
-  __device__ __forceinline__ static void load(const float* p, bool ok, uint4& hi, uint4& lo) {
-    float f[8];
-    if (ok) {
-      const float4 a = reinterpret_cast<const float4*>(p)[0];
-      const float4 b = reinterpret_cast<const float4*>(p)[1];
-      f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-    } else {
-#pragma unroll
-      for (int x = 0; x < 8; ++x) f[x] = 0.f;
-    }
-    hi = pack16<bf16_t>(f);
-    float fh[8];
-    unpack16<bf16_t>(hi, fh);
-#pragma unroll
-    for (int x = 0; x < 8; ++x) f[x] -= fh[x];
-    lo = pack16<bf16_t>(f);
-  }
-  __device__ __forceinline__ static uint4 load_round(const float* p, int n_ok) {
-    float f[8];
-#pragma unroll
-    for (int x = 0; x < 8; ++x) f[x] = x < n_ok ? p[x] : 0.f;
-    return pack16<bf16_t>(f);
-  }
-};
+// Attention over the r projected keys.  A workgroup (4 waves x 2 query tiles
+// = 128 queries of one head) walks the rank axis in chunks of KS rows; each
+// chunk of Ktil (as a bf16 high/low pair, so the logits keep float32-like
+// precision) and of Vtil^T (bf16) is staged once in LDS, double buffered, and
+// shared by all 128 queries; an online softmax runs over the chunks.  Chunk
+// rows past r are zero and masked.
+constexpr int kAttQT = 2;                      // query tiles per wave
+constexpr int kAttThreads = 256;               // 4 waves
+constexpr int kAttRows = 4 * kAttQT * 16;      // queries per workgroup
 
-// One wave per (head, 16-query tile).  S^T tiles cover all (padded) r rows.
-// Control flow around the matrix-core products is uniform per wave: rows past
-// r load zeros and are masked before the softmax.
-template <typename T, int D, int RT>
-__global__ __launch_bounds__(256) void lin_attend_kernel(
+template <typename T, int D>
+__global__ __launch_bounds__(kAttThreads) void lin_attend_kernel(
     const T* __restrict__ q, const float* __restrict__ k_proj, const float* __restrict__ v_proj, int H, int Lq,
     int r, float scale_log2, float* __restrict__ o_lin) {
   constexpr int E = Vec<T>::N;
-  constexpr int KS = Mma<T>::K;
+  constexpr int KS = Mma<T>::K;        // rank rows per chunk (= one PV contraction step)
+  constexpr int GPS = KS / 16;         // 16-row tiles per chunk
   constexpr int DSTEPS = D / KS;
   constexpr int DT = D / 16;
-  constexpr int GPS = KS / 16;         // r-tiles per contraction step of the PV product
+  constexpr bool SPLIT = sizeof(T) == 2;
+  constexpr int KSTR = D + E;          // padded LDS rows (elements)
+  constexpr int VSTR = KS + E;
+  __shared__ __align__(16) T k_hi[2][KS * KSTR];
+  __shared__ __align__(16) T k_lo[2][SPLIT ? KS * KSTR : E];
+  __shared__ __align__(16) T v_t[2][D * VSTR];
+
   const int tid = threadIdx.x, lane = tid % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g = lane >> 4, c = lane & 15;
-  const int tiles_q = (Lq + 15) / 16;
-  const int wid = blockIdx.x * 4 + tid / kWave;
-  if (wid >= tiles_q * H) return;
-  const int h = wid / tiles_q, qt = wid % tiles_q;
-  const int qrow = qt * 16 + c;
+  const int h = blockIdx.y;
+  const int q0 = blockIdx.x * kAttRows + w * kAttQT * 16;
+  const float* kp = k_proj + (size_t)h * r * D;
+  const float* vp = v_proj + (size_t)h * D * r;
+  const int nchunk = (r + KS - 1) / KS;
 
-  uint4 qreg[DSTEPS];
+  uint4 qreg[kAttQT][DSTEPS];
 #pragma unroll
-  for (int s = 0; s < DSTEPS; ++s)
-    qreg[s] = qrow < Lq ? ld16(q + ((size_t)qrow * H + h) * D + (4 * s + g) * E) : make_uint4(0, 0, 0, 0);
+  for (int t = 0; t < kAttQT; ++t) {
+    const int qrow = q0 + 16 * t + c;
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s)
+      qreg[t][s] = qrow < Lq ? ld16(q + ((size_t)qrow * H + h) * D + (4 * s + g) * E) : make_uint4(0, 0, 0, 0);
+  }
 
-  // S^T[r][q]: tile rt row c loads Ktil row 16*(rt - rt%GPS) + perm_row(rt%GPS, c)
-  f32x4 sacc[RT];
+  // staging: Ktil rows r0..r0+KS-1 (all D columns) and Vtil^T columns r0..r0+KS-1
+  auto stage = [&](int ch, int buf) {
+    const int r0 = ch * KS;
+    for (int e = tid; e < KS * (D / 4); e += kAttThreads) {
+      const int rr = e / (D / 4), c4 = e % (D / 4);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (r0 + rr < r) v = reinterpret_cast<const float4*>(kp + (size_t)(r0 + rr) * D)[c4];
+      const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    sacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (16 * (rt - rt % GPS) < r) {  // wave-uniform
-      const int rr = 16 * (rt - rt % GPS) + perm_row<T>(rt % GPS, c);
-      const bool ok = rr < r;
-      const float* kp = k_proj + ((size_t)h * r + (ok ? rr : 0)) * D;
+      for (int x = 0; x < 4; ++x) {
+        const T hi = from_f32<T>(f[x]);
+        k_hi[buf][rr * KSTR + 4 * c4 + x] = hi;
+        if (SPLIT) k_lo[buf][rr * KSTR + 4 * c4 + x] = from_f32<T>(f[x] - to_f32<T>(hi));
+      }
+    }
+    for (int e = tid; e < D * KS; e += kAttThreads) {
+      const int dr = e / KS, rr = e % KS;
+      const float v = r0 + rr < r ? vp[(size_t)dr * r + r0 + rr] : 0.f;
+      v_t[buf][dr * VSTR + rr] = from_f32<T>(v);
+    }
+  };
+
+  f32x4 o[kAttQT][DT];
+  float m_run[kAttQT], l_run[kAttQT];
+#pragma unroll
+  for (int t = 0; t < kAttQT; ++t) {
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  stage(0, 0);
+  __syncthreads();
+  for (int ch = 0; ch < nchunk; ++ch) {
+    const int buf = ch & 1;
+    if (ch + 1 < nchunk) stage(ch + 1, buf ^ 1);
+    f32x4 sacc[kAttQT][GPS];
+#pragma unroll
+    for (int t = 0; t < kAttQT; ++t)
+#pragma unroll
+      for (int kt = 0; kt < GPS; ++kt) sacc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < GPS; ++kt) {
+      const int rho = perm_row<T>(kt, c);
 #pragma unroll
       for (int s = 0; s < DSTEPS; ++s) {
-        uint4 hi, lo;
-        F32Operand<T>::load(kp + (4 * s + g) * E, ok, hi, lo);
-        Mma<T>::run(sacc[rt], hi, qreg[s]);
-        if (F32Operand<T>::kSplit) Mma<T>::run(sacc[rt], lo, qreg[s]);
+        const uint4 ah = *reinterpret_cast<const uint4*>(&k_hi[buf][rho * KSTR + (4 * s + g) * E]);
+#pragma unroll
+        for (int t = 0; t < kAttQT; ++t) Mma<T>::run(sacc[t][kt], ah, qreg[t][s]);
+        if (SPLIT) {
+          const uint4 al = *reinterpret_cast<const uint4*>(&k_lo[buf][rho * KSTR + (4 * s + g) * E]);
+#pragma unroll
+          for (int t = 0; t < kAttQT; ++t) Mma<T>::run(sacc[t][kt], al, qreg[t][s]);
+        }
       }
     }
+    const bool ragged = (ch + 1) * KS > r;  // uniform
+    uint4 pk[kAttQT];
+#pragma unroll
+    for (int t = 0; t < kAttQT; ++t) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < GPS; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (ragged && ch * KS + perm_row<T>(kt, 4 * g + i) >= r) sacc[t][kt][i] = -INFINITY;
+          mx = fmaxf(mx, sacc[t][kt][i]);
+        }
+      mx = max4g(mx) * scale_log2;
+      const float m_new = fmaxf(m_run[t], mx);
+      const float alpha = fast_exp2(m_run[t] - m_new);
+      float ls = 0.f;
+      f32x4 p[GPS];
+#pragma unroll
+      for (int kt = 0; kt < GPS; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = fast_exp2(fmaf(sacc[t][kt][i], scale_log2, -m_new));
+          p[kt][i] = e;
+          ls += e;
+        }
+      l_run[t] = l_run[t] * alpha + ls;
+      m_run[t] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
+      pk[t] = pack_p<T>(p);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint4 a = *reinterpret_cast<const uint4*>(&v_t[buf][(16 * dt + c) * VSTR + g * E]);
+#pragma unroll
+      for (int t = 0; t < kAttQT; ++t) Mma<T>::run(o[t][dt], a, pk[t]);
+    }
+    __syncthreads();
   }
-  // exact softmax over the r rows (rows >= r masked)
-  float mx = -INFINITY;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+  for (int t = 0; t < kAttQT; ++t) {
+    const int qrow = q0 + 16 * t + c;
+    if (qrow < Lq) {
+      const float inv = 1.f / sum4g(l_run[t]);
+      float* dst = o_lin + ((size_t)qrow * H + h) * D + 4 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = 16 * (rt - rt % GPS) + perm_row<T>(rt % GPS, 4 * g + i);
-      if (rr >= r) sacc[rt][i] = -INFINITY;
-      mx = fmaxf(mx, sacc[rt][i]);
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<float4*>(dst + 16 * dt) =
+            make_float4(o[t][dt][0] * inv, o[t][dt][1] * inv, o[t][dt][2] * inv, o[t][dt][3] * inv);
     }
-  mx = max4g(mx) * scale_log2;
-  float ls = 0.f;
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float e = exp2f(sacc[rt][i] * scale_log2 - mx);
-      sacc[rt][i] = e;
-      ls += e;
-    }
-  const float inv = 1.f / sum4g(ls);
-  // O^T[d][q] = Vtil^T[d][r] P^T[r][q]; step covers r-tiles GPS*st .. +GPS-1
-  f32x4 o[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int stp = 0; stp < RT / GPS; ++stp) {
-    if (stp * KS < r) {  // wave-uniform
-      const uint4 pb = pack_p<T>(&sacc[stp * GPS]);
-      const int r0 = stp * KS + g * E;  // r chunk of this lane group
-      const int n_ok = r0 >= r ? 0 : min(E, r - r0);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const float* vp = v_proj + ((size_t)h * D + 16 * dt + c) * r + (n_ok > 0 ? r0 : 0);
-        Mma<T>::run(o[dt], F32Operand<T>::load_round(vp, n_ok), pb);
-      }
-    }
-  }
-  if (qrow < Lq) {
-    float* dst = o_lin + ((size_t)qrow * H + h) * D + 4 * g;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<float4*>(dst + 16 * dt) = make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
   }
 }
 
@@ -323,27 +384,19 @@ void launch_linear(const Dims& s, const void* q, const void* k_act, const void* 
   const ProjPlan pp = proj_plan(s);
   float* partial = reinterpret_cast<float*>(ws + w.lin_partial);
   if (!(flags & HSA_LIN_REUSE_PROJ)) {
-    hipLaunchKernelGGL((lin_project_kernel<T, D>), dim3(2 * s.H, pp.splits), dim3(kProjThreads), 0, st,
+    const int n_items = pp.splits * 2 * ((s.H + 1) / 2);
+    hipLaunchKernelGGL((lin_project_kernel<T, D>), dim3((n_items + 7) / 8 * 8), dim3(kProjThreads), 0, st,
                        reinterpret_cast<const T*>(k_act), reinterpret_cast<const T*>(v_act),
-                       reinterpret_cast<const T*>(e_k), reinterpret_cast<const T*>(e_v), s.H, s.L, s.r, pp.steps,
-                       pp.splits, partial);
+                       reinterpret_cast<const T*>(e_k), reinterpret_cast<const T*>(e_v), s.H, s.L, s.r, pp.splits,
+                       partial);
     hipLaunchKernelGGL(lin_reduce_kernel, dim3(2 * s.H, (s.r * D / 4 + 255) / 256), dim3(256), 0, st, partial, s.H, D, s.r, pp.splits,
                        reinterpret_cast<float*>(k_proj), reinterpret_cast<float*>(v_proj));
   }
   if (flags & HSA_LIN_PROJ_ONLY) return;
-  const int tiles_q = (s.Lq + 15) / 16;
-  const int nblk = (tiles_q * s.H + 3) / 4;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
-  const int rt = pp.rpad / 16;  // r-tiles covering the padded rank
-#define HSA_LIN_CASE(RT_) \
-  if (rt <= RT_) { hipLaunchKernelGGL((lin_attend_kernel<T, D, RT_>), dim3(nblk), dim3(256), 0, st, \
-      reinterpret_cast<const T*>(q), reinterpret_cast<const float*>(k_proj), reinterpret_cast<const float*>(v_proj), \
-      s.H, s.Lq, s.r, scale_log2, o_lin); return; }
-  HSA_LIN_CASE(2)
-  HSA_LIN_CASE(4)
-  HSA_LIN_CASE(8)
-  HSA_LIN_CASE(16)
-#undef HSA_LIN_CASE
+  hipLaunchKernelGGL((lin_attend_kernel<T, D>), dim3((s.Lq + kAttRows - 1) / kAttRows, s.H), dim3(kAttThreads), 0, st,
+                     reinterpret_cast<const T*>(q), reinterpret_cast<const float*>(k_proj),
+                     reinterpret_cast<const float*>(v_proj), s.H, s.Lq, s.r, scale_log2, o_lin);
 }
 
 }  // namespace

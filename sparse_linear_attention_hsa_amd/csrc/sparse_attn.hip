@@ -19,8 +19,10 @@
 //    one query column), an online softmax per query, and O^T += V^T P^T.
 //    Keeping queries on the lane-column axis puts the softmax state and the
 //    output column of a query in the same lane: no cross-lane rescaling.
-//  * XCD-aware item order: each XCD runs a contiguous range of rows, i.e.
-//    mostly one head, so the K/V blocks its workgroups share stay in its L2.
+//  * XCD-aware item order: items are laid out (head, segment, query block) and
+//    each XCD runs one contiguous range of them, so the workgroups running
+//    together on an XCD read the same head's key/value blocks in the same
+//    order and share them through that XCD's L2.
 #include "common.h"
 #include "host.h"
 
@@ -45,51 +47,87 @@ __device__ int scan_incl_1024(int v, int* buf) {
   return r;
 }
 
+// Work items are (row, segment) pairs; a row (head h, query block i) with G
+// granules gets nseg = ceil(G / seg_granules) balanced segments.  Items are
+// laid out head by head, then by segment index, then by query block, so the
+// workgroups that run together on one XCD walk the same head and the same
+// part of their (ascending) block lists at the same time, and share the key
+// and value blocks through that XCD's L2.
 // items[k] = {row, first granule, granules, partial slot or -1};
 // rowinfo[row] = {segments, first slot}; meta = {items, slots}.
+constexpr int kMaxPlanRows = HSA_MAX_ROWS;
+constexpr int kMaxPlanSegs = 64;
 __global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
-    const int32_t* __restrict__ blk_count, int rows, int nKB, int gpb, int gps, int seg_granules,
-    int4* __restrict__ items, int2* __restrict__ rowinfo, int* __restrict__ meta, uint4* __restrict__ zeros) {
+    const int32_t* __restrict__ blk_count, int rows, int nQB, int nKB, int gpb, int gps, int seg_granules,
+    int max_segs, int4* __restrict__ items, int2* __restrict__ rowinfo, int* __restrict__ meta,
+    uint4* __restrict__ zeros) {
+  __shared__ short nseg_s[kMaxPlanRows];
+  __shared__ int per_s[kMaxPlanRows];
+  __shared__ int off_s[32 * kMaxPlanSegs];   // (head, segment) offsets
   __shared__ int buf[kPlanThreads];
-  __shared__ int carry_items, carry_slots;
+  __shared__ int carry_slots;
   const int t = threadIdx.x;
+  const int H = rows / nQB;
   if (t < kZeroChunks) zeros[t] = make_uint4(0, 0, 0, 0);  // source of masked granules
-  if (t == 0) carry_items = carry_slots = 0;
+  if (t == 0) carry_slots = 0;
+  // 1) segments per row
+  for (int row = t; row < rows; row += kPlanThreads) {
+    int n = blk_count[row];
+    n = n < 0 ? 0 : (n > nKB ? nKB : n);
+    const int G = n * gpb;
+    int nseg = 0, per = 0;
+    if (G > 0) {
+      nseg = (G + seg_granules - 1) / seg_granules;
+      per = (G + nseg - 1) / nseg;
+      per = (per + gps - 1) / gps * gps;
+      nseg = (G + per - 1) / per;
+    }
+    nseg_s[row] = (short)nseg;
+    per_s[row] = per;
+  }
   __syncthreads();
+  // 2) items per (head, segment) and their offsets, in (head, segment) order
+  for (int hs = t; hs < H * max_segs; hs += kPlanThreads) {
+    const int h = hs / max_segs, sg = hs % max_segs;
+    int c = 0;
+    for (int i = 0; i < nQB; ++i) c += nseg_s[h * nQB + i] > sg;
+    off_s[hs] = c;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int hs = 0; hs < H * max_segs; ++hs) {
+      const int c = off_s[hs];
+      off_s[hs] = run;
+      run += c;
+    }
+    meta[0] = run;
+  }
+  __syncthreads();
+  // 3) write the items; partial slots are contiguous per split row
   for (int base = 0; base < rows; base += kPlanThreads) {
     const int row = base + t;
-    int nseg = 0, per = 0, G = 0;
-    if (row < rows) {
-      int n = blk_count[row];
-      n = n < 0 ? 0 : (n > nKB ? nKB : n);
-      G = n * gpb;
-      if (G > 0) {
-        nseg = (G + seg_granules - 1) / seg_granules;
-        per = (G + nseg - 1) / nseg;
-        per = (per + gps - 1) / gps * gps;
-        nseg = (G + per - 1) / per;
-      }
-    }
+    const int nseg = row < rows ? nseg_s[row] : 0;
     const int nslot = nseg > 1 ? nseg : 0;
-    const int ci = scan_incl_1024(nseg, buf) - nseg;
     const int cs = scan_incl_1024(nslot, buf) - nslot;
-    const int i0 = carry_items + ci, s0 = carry_slots + cs;
+    const int s0 = carry_slots + cs;
     if (row < rows) {
-      for (int s = 0; s < nseg; ++s)
-        items[i0 + s] = make_int4(row, s * per, min(per, G - s * per), nslot ? s0 + s : -1);
+      const int h = row / nQB, i = row % nQB;
+      const int per = per_s[row];
+      const int G = blk_count[row] < 0 ? 0 : min(blk_count[row], nKB) * gpb;
+      for (int sg = 0; sg < nseg; ++sg) {
+        int rank = 0;
+        for (int i2 = 0; i2 < i; ++i2) rank += nseg_s[h * nQB + i2] > sg;
+        items[off_s[h * max_segs + sg] + rank] =
+            make_int4(row, sg * per, min(per, G - sg * per), nslot ? s0 + sg : -1);
+      }
       rowinfo[row] = make_int2(nseg, s0);
     }
     __syncthreads();
-    if (t == kPlanThreads - 1) {
-      carry_items += ci + nseg;
-      carry_slots += cs + nslot;
-    }
+    if (t == kPlanThreads - 1) carry_slots += cs + nslot;
     __syncthreads();
   }
-  if (t == 0) {
-    meta[0] = carry_items;
-    meta[1] = carry_slots;
-  }
+  if (t == 0) meta[1] = carry_slots;
 }
 
 // LDS staging of one step (KS keys), written by direct global->LDS loads
@@ -115,7 +153,9 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds_wave_base) {
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 
-template <typename T, int D, int NW, int QPW, int WPE>
+// FULL: every wave owns exactly QPW query tiles (B == 16*NW*QPW), so the tile
+// loops carry no run-time guards and the matrix-core chains stay branch-free.
+template <typename T, int D, int NW, int QPW, int WPE, bool FULL>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void sparse_attn_kernel(
     const T* __restrict__ q, const T* __restrict__ k_act, const T* __restrict__ v_act,
     const int32_t* __restrict__ blk_idx, const int4* __restrict__ items, const int* __restrict__ meta,
@@ -146,10 +186,11 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
   const int gpb = B / 16;
   const int32_t* list = blk_idx + (size_t)row * nKB;
 
-  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave index, kept in a scalar register
   const int g = lane >> 4, c = lane & 15;
   const int QT = B / 16;
-  const int ntile = min(QPW, QT - w * QPW);
+  const int ntile = FULL ? QPW : min(QPW, QT - w * QPW);  // wave-uniform
 
   // Q^T operand: lane (g, c) holds Q[row c of tile][chunk 4s+g] for step s.
   uint4 qreg[QPW][DSTEPS];
@@ -193,7 +234,9 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
     for (int j = 0; j < GPS; ++j) kofs[j] = granule_key(sub, j);
     // K: instruction i writes rows i*ROWS_PER_INST .. +ROWS_PER_INST-1
 #pragma unroll
-    for (int i = w; i < KINST; i += NW) {
+    for (int ii = 0; ii < (KINST + NW - 1) / NW; ++ii) {
+      const int i = ii * NW + w;
+      if (KINST % NW != 0 && i >= KINST) break;
       const int rho = i * ROWS_PER_INST + lane / CPR;
       const int slotc = lane % CPR;
       const int chunk = slotc ^ kswz<T>(rho, CPR);
@@ -204,7 +247,9 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
     }
     // V: instruction i covers region r = i / (D/64) (granule r / PV, part r % PV), rows (i % (D/64))*64 + lane
 #pragma unroll
-    for (int i = w; i < VINST; i += NW) {
+    for (int ii = 0; ii < (VINST + NW - 1) / NW; ++ii) {
+      const int i = ii * NW + w;
+      if (VINST % NW != 0 && i >= VINST) break;
       const int region = i / (D / 64);
       const int rowv = (i % (D / 64)) * 64 + lane;
       const int j = region / PV, part = region % PV;
@@ -224,7 +269,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
     const bool more = sub + 1 < nsub;
     if (more) issue(sub + 1, buf ^ 1);
 
-    if (w * QPW < QT) {
+    if (FULL || w * QPW < QT) {
       // masked keys only on a ragged or invalid step (wave-uniform test)
       bool gval[GPS];
       bool all_valid = true;
@@ -248,7 +293,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
           const uint4 a = *reinterpret_cast<const uint4*>(krow + (((4 * s + g) ^ sw) * 16));
 #pragma unroll
           for (int t = 0; t < QPW; ++t)
-            if (t < ntile) Mma<T>::run(sacc[t][kt], a, qreg[t][s]);
+            if (FULL || t < ntile) Mma<T>::run(sacc[t][kt], a, qreg[t][s]);
         }
       }
       if (!all_valid) {
@@ -267,7 +312,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
 #pragma unroll
       for (int t = 0; t < QPW; ++t) {
         alpha[t] = 1.f;
-        if (t < ntile) {
+        if (FULL || t < ntile) {
           float mx = -INFINITY;
 #pragma unroll
           for (int kt = 0; kt < GPS; ++kt)
@@ -275,10 +320,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
             for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[t][kt][i]);
           mx = max4g(mx) * scale_log2;
           const bool need = mx > m_run[t] + kLazy;
-          if (need) {
-            alpha[t] = exp2f(m_run[t] - mx);
-            m_run[t] = mx;
-          }
+          alpha[t] = need ? fast_exp2(m_run[t] - mx) : 1.f;
+          m_run[t] = need ? mx : m_run[t];
           need_any = need_any || need;
           const float mref = m_run[t] == -INFINITY ? 0.f : m_run[t];
           float ls = 0.f;
@@ -287,7 +330,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
           for (int kt = 0; kt < GPS; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float e = exp2f(fmaf(sacc[t][kt][i], scale_log2, -mref));
+              const float e = fast_exp2(fmaf(sacc[t][kt][i], scale_log2, -mref));
               p[kt][i] = e;
               ls += e;
             }
@@ -298,7 +341,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
       if (__any(need_any)) {
 #pragma unroll
         for (int t = 0; t < QPW; ++t)
-          if (t < ntile)
+          if (FULL || t < ntile)
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha[t];
       }
@@ -308,7 +351,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
         const uint4 a = *reinterpret_cast<const uint4*>(vreg + (16 * dt + c) * 16);
 #pragma unroll
         for (int t = 0; t < QPW; ++t)
-          if (t < ntile) Mma<T>::run(o[t][dt], a, pk[t]);
+          if (FULL || t < ntile) Mma<T>::run(o[t][dt], a, pk[t]);
       }
     }
     wait_vm();
@@ -384,7 +427,13 @@ void launch_attn(const Dims& s, const SparsePlan& pl, const void* q, const void*
                  float* po, float* pml, hipStream_t st) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
   constexpr int WPE = sizeof(T) == 2 ? 2 : 1;
-  hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE>), dim3(pl.grid), dim3(NW * kWave), 0, st,
+  if (s.B == 16 * NW * QPW)
+    hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE, true>), dim3(pl.grid), dim3(NW * kWave), 0, st,
+                       reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act),
+                       reinterpret_cast<const T*>(v_act), idx, items, meta, zeros, s.H, s.B, s.L, s.nKB, s.nQB,
+                       scale_log2, o_sp, po, pml);
+  else
+  hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE, false>), dim3(pl.grid), dim3(NW * kWave), 0, st,
                      reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act),
                      reinterpret_cast<const T*>(v_act), idx, items, meta, zeros, s.H, s.B, s.L, s.nKB, s.nQB,
                      scale_log2, o_sp, po, pml);
@@ -432,8 +481,8 @@ extern "C" hsa_rc hsa_sparse_attn(const hsa_geom* geom, const void* q, const voi
   float* pml = reinterpret_cast<float*>(wsb + w.sp_part_ml);
   uint4* zeros = reinterpret_cast<uint4*>(wsb + w.sp_zeros);
   const int gps = s.bf16 ? 2 : 1;
-  hipLaunchKernelGGL(sparse_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, blk_count, s.rows, s.nKB,
-                     pl.granules_per_block, gps, pl.seg_granules, items, rowinfo, meta, zeros);
+  hipLaunchKernelGGL(sparse_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, blk_count, s.rows, s.nQB, s.nKB,
+                     pl.granules_per_block, gps, pl.seg_granules, pl.max_segs, items, rowinfo, meta, zeros);
   if (s.bf16) {
     if (s.d == 128) dispatch_attn<bf16_t, 128>(s, pl, q, k_act, v_act, blk_idx, items, meta, zeros, o_sp, po, pml, st);
     else dispatch_attn<bf16_t, 64>(s, pl, q, k_act, v_act, blk_idx, items, meta, zeros, o_sp, po, pml, st);
