@@ -64,12 +64,14 @@ template <typename T> __device__ __forceinline__ uint4 pack16(const float* in);
 template <> __device__ __forceinline__ uint4 pack16<float>(const float* in) {
   return make_uint4(__float_as_uint(in[0]), __float_as_uint(in[1]), __float_as_uint(in[2]), __float_as_uint(in[3]));
 }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// two floats -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest even)
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
 template <> __device__ __forceinline__ uint4 pack16<bf16_t>(const float* in) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = static_cast<uint32_t>(f32_to_bf16(in[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(in[2 * i + 1])) << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  return make_uint4(pack2_bf16(in[0], in[1]), pack2_bf16(in[2], in[3]), pack2_bf16(in[4], in[5]), pack2_bf16(in[6], in[7]));
 }
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }

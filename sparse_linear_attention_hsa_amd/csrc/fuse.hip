@@ -91,9 +91,7 @@ __global__ __launch_bounds__(kFuseThreads) void fuse_kernel(
     if constexpr (sizeof(T) == 4) {
       *reinterpret_cast<float4*>(out + off) = make_float4(r[0], r[1], r[2], r[3]);
     } else {
-      const uint32_t lo = (uint32_t)f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16);
-      *reinterpret_cast<uint2*>(out + off) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(out + off) = make_uint2(pack2_bf16(r[0], r[1]), pack2_bf16(r[2], r[3]));
     }
   }
 }

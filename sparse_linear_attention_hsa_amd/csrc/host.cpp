@@ -103,8 +103,7 @@ WsLayout ws_layout(const Dims& s, int n_pages) {
   w.sp_items = 0;
   w.sp_rowinfo = align256((size_t)qp.max_items * 16);
   w.sp_meta = align256(w.sp_rowinfo + (size_t)s.rows * 8);
-  w.sp_zeros = align256(w.sp_meta + 64);
-  w.sp_part_o = align256(w.sp_zeros + 1024);
+  w.sp_part_o = align256(w.sp_meta + 64);
   w.sp_part_ml = align256(w.sp_part_o + (size_t)qp.max_items * s.B * s.d * 4);
   w.sp_end = align256(w.sp_part_ml + (size_t)qp.max_items * s.B * 2 * 4);
   w.total = std::max(std::max(w.score_end, w.lin_end), std::max(w.sel_end, w.sp_end));

@@ -58,7 +58,7 @@ struct WsLayout {
   // select
   size_t sel_qbar, sel_kbar, sel_end;
   // sparse
-  size_t sp_items, sp_rowinfo, sp_meta, sp_zeros, sp_part_o, sp_part_ml, sp_end;
+  size_t sp_items, sp_rowinfo, sp_meta, sp_part_o, sp_part_ml, sp_end;
   size_t total;
 };
 WsLayout ws_layout(const Dims& s, int n_pages);

@@ -23,6 +23,38 @@ namespace hsa {
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+// 32-bit LDS address of a pointer into shared memory
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// N transposing 64-bit LDS reads (ds_read_b64_tr_b16) issued back to back,
+// with the wait for all of them inside the same asm statement, so the
+// outputs are complete when the statement ends.
+template <int N> __device__ __forceinline__ void tr_read_b16(const uint32_t* addr, uint2* out);
+template <> __device__ __forceinline__ void tr_read_b16<16>(const uint32_t* a, uint2* o) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n ds_read_b64_tr_b16 %1, %17\n ds_read_b64_tr_b16 %2, %18\n"
+      "ds_read_b64_tr_b16 %3, %19\n ds_read_b64_tr_b16 %4, %20\n ds_read_b64_tr_b16 %5, %21\n"
+      "ds_read_b64_tr_b16 %6, %22\n ds_read_b64_tr_b16 %7, %23\n ds_read_b64_tr_b16 %8, %24\n"
+      "ds_read_b64_tr_b16 %9, %25\n ds_read_b64_tr_b16 %10, %26\n ds_read_b64_tr_b16 %11, %27\n"
+      "ds_read_b64_tr_b16 %12, %28\n ds_read_b64_tr_b16 %13, %29\n ds_read_b64_tr_b16 %14, %30\n"
+      "ds_read_b64_tr_b16 %15, %31\n s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7]),
+        "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]), "=&v"(o[12]), "=&v"(o[13]), "=&v"(o[14]), "=&v"(o[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(a[8]),
+        "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]), "v"(a[15])
+      : "memory");
+}
+template <> __device__ __forceinline__ void tr_read_b16<8>(const uint32_t* a, uint2* o) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n ds_read_b64_tr_b16 %1, %9\n ds_read_b64_tr_b16 %2, %10\n"
+      "ds_read_b64_tr_b16 %3, %11\n ds_read_b64_tr_b16 %4, %12\n ds_read_b64_tr_b16 %5, %13\n"
+      "ds_read_b64_tr_b16 %6, %14\n ds_read_b64_tr_b16 %7, %15\n s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
 
 // Projection of the sequence axis, split over S slices of the active keys.
 // Work item = (slice, K|V, head pair); the two heads of a pair share one E
@@ -30,34 +62,41 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // so the workgroups that need the same E slice sit behind the same L2.
 // Workgroup = 8 waves: wave w works on head (w / 4) of the pair and on r-tiles
 // 4*(w % 4) .. +3, all D columns (128 float32 accumulators per lane).
-// Per stage (2 contraction steps, ST tokens), staged in LDS and double
-// buffered:
-//  * E tile [256 rows][ST tokens] by direct global->LDS loads; chunk slot
-//    swizzled by the row so the operand reads are bank-conflict free;
-//  * X^T tiles [D][ST tokens] per head in regions [granule][part][D][16 B]:
-//    values arrive that way from the active buffer (direct loads); keys are
-//    loaded to registers one stage ahead and written transposed.
+// One stage = two contraction steps (ST tokens), staged in LDS by direct
+// global->LDS loads, double buffered.  The main loop is unrolled by two so
+// that every LDS operand read names a fixed buffer: the compiler can then see
+// that the loads in flight (other buffer) do not alias the reads, and does not
+// stall the reads on them.
+//  * E tile [256 rows][ST tokens] (128-byte rows, chunk slot swizzled by row);
+//  * values: X^T tile [D][ST tokens] in regions [granule][part][D][16 B], as
+//    they arrive from the active buffer;
+//  * keys: rows [ST tokens][D], chunk slot swizzled by the token's lane group,
+//    read back transposed (ds_read_b64_tr_b16 for bf16).
 constexpr int kProjThreads = 512;  // 8 waves
 constexpr int kProjHeads = 2;
-
-__device__ __forceinline__ int eswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 template <typename T, int D>
 __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lin_project_kernel(
     const T* __restrict__ k_act, const T* __restrict__ v_act, const T* __restrict__ e_k,
     const T* __restrict__ e_v, int H, int L, int r, int splits, float* __restrict__ partial) {
   constexpr int E = Vec<T>::N;
-  constexpr int KS = Mma<T>::K;          // tokens per contraction step
-  constexpr int ST = 2 * KS;             // tokens per stage
+  constexpr int KS = Mma<T>::K;                      // tokens per contraction step
+  constexpr int ST = 2 * KS;                         // tokens per stage
   constexpr int DT = D / 16;
-  constexpr int PV = 16 / E;             // 16-byte parts per granule row
-  constexpr int NREG = ST / 16 * PV;     // X^T regions per stage (8)
-  constexpr int XBYTES = NREG * D * 16;  // X^T tile bytes per head
-  constexpr int EBYTES = 256 * ST * (int)sizeof(T);  // 256 rows x 128 bytes
-  constexpr int KCH = ST * (D / E);      // 16-byte key chunks per head per stage
-  constexpr int KPT = (kProjHeads * KCH) / kProjThreads;
-  __shared__ __align__(1024) unsigned char lds_e[2][EBYTES];
-  __shared__ __align__(1024) unsigned char lds_x[2][kProjHeads][XBYTES];
+  constexpr int PV = 16 / E;                         // 16-byte parts per granule row
+  constexpr int NW = kProjThreads / kWave;
+  constexpr int EROW = ST * (int)sizeof(T);          // 128 bytes
+  constexpr int EBYTES = 256 * EROW;                 // 32 KB
+  constexpr int XBYTES = ST * D * (int)sizeof(T);    // per head
+  constexpr int EINST = EBYTES / 1024;
+  constexpr int XINST = kProjHeads * XBYTES / 1024;
+  constexpr int KROWS = 1024 / (D * (int)sizeof(T)); // key rows per 1 KB instruction
+  // one LDS object per buffer, so alias analysis can tell the buffer being
+  // read from the one being filled
+  __shared__ __align__(1024) unsigned char lds_e0[EBYTES];
+  __shared__ __align__(1024) unsigned char lds_e1[EBYTES];
+  __shared__ __align__(1024) unsigned char lds_x0[kProjHeads * XBYTES];
+  __shared__ __align__(1024) unsigned char lds_x1[kProjHeads * XBYTES];
 
   const int HP = (H + 1) / 2;
   const int n_items = splits * 2 * HP;
@@ -77,6 +116,16 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2,
   const int st0 = (int)((long long)nst * split / splits);
   const int st1 = (int)((long long)nst * (split + 1) / splits);
   const T* e = kv ? e_v : e_k;
+  // E rows: 16-byte chunk slot XOR eswz(row): the 16 rows read together by a
+  // lane group land on distinct banks
+  auto eswz = [](int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); };
+  // keys: 16-byte chunk slot XOR kslot(token); for bf16 this moves whole
+  // 32-byte column groups, so the 16 rows of one transposing read spread over
+  // the banks.  (For f32 the XOR only separates the gathered lane groups.)
+  auto kslot = [](int tr) {
+    if (sizeof(T) == 2) return 2 * (((tr & 3) | (((tr >> 3) & 1) << 2)) & (D / 16 - 1));
+    return ((tr % KS) / E) * PV;
+  };
 
   f32x4 acc[4][DT];
 #pragma unroll
@@ -84,94 +133,132 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[a][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 kreg[KPT > 0 ? KPT : 1];
-  // direct loads of one stage (E for all rows, values for both heads), key rows to registers
-  auto issue = [&](int stg, int buf) {
+  auto issue = [&](int stg, unsigned char* le, unsigned char* lx) {
     const int tok0 = stg * ST;
-    // E: instruction i covers rows 8i .. 8i+7 (128 bytes each)
-    for (int i = w; i < rtiles * 2; i += kProjThreads / kWave) {
-      const int row = 8 * i + lane / 8;
-      const int chunk = (lane % 8) ^ eswz(row);
+#pragma unroll
+    for (int ii = 0; ii < EINST / NW; ++ii) {
+      const int i = ii * NW + w;
+      const int row = (1024 / EROW) * i + lane / (EROW / 16);
+      const int chunk = (lane % (EROW / 16)) ^ eswz(row);
       const int tk = tok0 + chunk * E;
       const void* src = (row < r && tk < L) ? (const void*)(e + (size_t)row * L + tk) : (const void*)(kZeroPage + lane);
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(lds_e[buf] + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(le + i * 1024), 16, 0, 0);
     }
-    if (kv) {
-      // values: region = (granule, part), D/64 instructions per region, per head
 #pragma unroll
-      for (int ii = 0; ii < (kProjHeads * NREG * D / 64) / (kProjThreads / kWave); ++ii) {
-        const int i = ii * (kProjThreads / kWave) + w;
-        const int hsl = i / (NREG * D / 64);
-        const int rem = i % (NREG * D / 64);
-        const int region = rem / (D / 64);
-        const int rowv = (rem % (D / 64)) * 64 + lane;
+    for (int ii = 0; ii < XINST / NW; ++ii) {
+      const int i = ii * NW + w;
+      const int hsl = i / (XBYTES / 1024);
+      const int j = i % (XBYTES / 1024);            // 1 KB piece of this head's tile
+      const int hh = hp * 2 + hsl;
+      const void* src;
+      if (kv) {
+        // regions [granule][part][D rows][16 B]; piece j = region j/(D/64), rows (j%(D/64))*64 + lane
+        const int region = j / (D / 64);
+        const int rowv = (j % (D / 64)) * 64 + lane;
         const int gr = region / PV, part = region % PV;
-        const int hh = hp * 2 + hsl;
         const int tk = tok0 + gr * 16;
-        const void* src = (hh < H && tk < L)
-                              ? (const void*)(v_act + (((size_t)hh * (L / 16) + tk / 16) * D + rowv) * 16 + part * E)
-                              : (const void*)(kZeroPage + lane);
-        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(lds_x[buf][hsl] + (size_t)region * D * 16 + (rem % (D / 64)) * 1024), 16, 0, 0);
+        src = (hh < H && tk < L)
+                  ? (const void*)(v_act + (((size_t)hh * (L / 16) + tk / 16) * D + rowv) * 16 + part * E)
+                  : (const void*)(kZeroPage + lane);
+      } else {
+        const int tr = j * KROWS + lane / (D / E);
+        const int chunk = (lane % (D / E)) ^ kslot(tr);
+        src = (hh < H && tok0 + tr < L) ? (const void*)(k_act + ((size_t)hh * L + tok0 + tr) * D + chunk * E)
+                                        : (const void*)(kZeroPage + lane);
       }
-    } else {
-#pragma unroll
-      for (int u = 0; u < KPT; ++u) {
-        const int ci = tid + u * kProjThreads;
-        const int hsl = ci / KCH, cr = ci % KCH;
-        const int tr = cr / (D / E), cc = cr % (D / E);
-        const int hh = hp * 2 + hsl;
-        kreg[u] = (hh < H && tok0 + tr < L) ? ld16(k_act + ((size_t)hh * L + tok0 + tr) * D + cc * E)
-                                           : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  // keys only: write the registers of a stage transposed into the X^T regions
-  auto stage_keys = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int ci = tid + u * kProjThreads;
-      const int hsl = ci / KCH, cr = ci % KCH;
-      const int tr = cr / (D / E), cc = cr % (D / E);
-      const int region = (tr / 16) * PV + (tr % 16) / E;
-      unsigned char* base = lds_x[buf][hsl] + (size_t)region * D * 16 + (tr % E) * sizeof(T);
-      float f[E];
-      unpack16<T>(kreg[u], f);
-#pragma unroll
-      for (int x = 0; x < E; ++x) *reinterpret_cast<T*>(base + (cc * E + x) * 16) = from_f32<T>(f[x]);
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(lx + hsl * XBYTES + j * 1024), 16, 0, 0);
     }
   };
 
-  if (st0 < st1) {
-    issue(st0, 0);
-    if (!kv) stage_keys(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-  }
-  for (int stg = st0; stg < st1; ++stg) {
-    const int buf = (stg - st0) & 1;
-    const bool more = stg + 1 < st1;
-    if (more) issue(stg + 1, buf ^ 1);
-    if (h_ok && rg * 4 < rtiles) {
+  // A operands of one contraction step: E rows of this wave's four r-tiles
+  auto load_a = [&](const unsigned char* le, int ks, uint4* aop) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        uint4 bop[DT];
-        const unsigned char* xr = lds_x[buf][hs] + (size_t)(ks * 4 + g) * D * 16;
+    for (int a = 0; a < 4; ++a) {
+      const int row = 16 * (rg * 4 + a) + c;
+      aop[a] = *reinterpret_cast<const uint4*>(le + row * EROW + (((ks * 4 + g) ^ eswz(row)) * 16));
+    }
+  };
+  auto compute_v = [&](const unsigned char* le, const unsigned char* lx) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) bop[dt] = *reinterpret_cast<const uint4*>(xr + (16 * dt + c) * 16);
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 aop[4];
+      load_a(le, ks, aop);
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int row = 16 * (rg * 4 + a) + c;
-          const int slot = (ks * 4 + g) ^ eswz(row);
-          const uint4 aop = *reinterpret_cast<const uint4*>(lds_e[buf] + row * 128 + slot * 16);
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint4 bop = *reinterpret_cast<const uint4*>(lx + (size_t)(ks * 4 + g) * D * 16 + (16 * dt + c) * 16);
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) Mma<T>::run(acc[a][dt], aop, bop[dt]);
+        for (int a = 0; a < 4; ++a) Mma<T>::run(acc[a][dt], aop[a], bop);
+      }
+    }
+  };
+  auto compute_k = [&](const unsigned char* le, const unsigned char* lx) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 aop[4];
+      load_a(le, ks, aop);
+      if constexpr (sizeof(T) == 2) {
+        // transposing LDS reads: lane j of a 16-lane group reads 4 columns
+        // 16*dt + 4*(j%4) of token row T0 + j/4; lane c then holds column
+        // 16*dt + c of tokens T0 .. T0+3.  Two reads cover the 8 tokens of
+        // lane group g.  Four d-tiles per batch of reads.
+        const int jc = c & 3, jr = c >> 2;
+#pragma unroll
+        for (int half = 0; half < DT / 4; ++half) {
+          uint32_t addr[8];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int dt = 4 * half + q;
+              const int tr = ks * KS + g * 8 + hh * 4 + jr;
+              const int chunk = 2 * dt + (jc >> 1);
+              addr[2 * q + hh] = lds_addr(lx + (size_t)tr * D * 2 + ((chunk ^ kslot(tr)) * 16) + 8 * (jc & 1));
+            }
+          uint4 bop[4];
+          tr_read_b16<8>(addr, reinterpret_cast<uint2*>(bop));
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) Mma<T>::run(acc[a][4 * half + q], aop[a], bop[q]);
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int col = 16 * dt + c;
+          T v[E];
+#pragma unroll
+          for (int x = 0; x < E; ++x) {
+            const int tr = ks * KS + g * E + x;
+            v[x] = *reinterpret_cast<const T*>(lx + (size_t)tr * D * sizeof(T) +
+                                               (((col / E) ^ kslot(tr)) * 16) + (col % E) * sizeof(T));
+          }
+          const uint4 bop = *reinterpret_cast<const uint4*>(v);
+#pragma unroll
+          for (int a = 0; a < 4; ++a) Mma<T>::run(acc[a][dt], aop[a], bop);
         }
       }
     }
-    if (more && !kv) stage_keys(buf ^ 1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-  }
+  };
+  const bool active = h_ok && rg * 4 < rtiles;  // wave-uniform
+  // double-buffered main loop, unrolled by two so every LDS buffer is a fixed object
+  auto run = [&](auto&& compute) {
+    if (st0 < st1) {
+      issue(st0, lds_e0, lds_x0);
+      __syncthreads();
+    }
+    for (int stg = st0; stg < st1; stg += 2) {
+      if (stg + 1 < st1) issue(stg + 1, lds_e1, lds_x1);
+      if (active) compute(lds_e0, lds_x0 + hs * XBYTES);
+      __syncthreads();
+      if (stg + 1 >= st1) break;
+      if (stg + 2 < st1) issue(stg + 2, lds_e0, lds_x0);
+      if (active) compute(lds_e1, lds_x1 + hs * XBYTES);
+      __syncthreads();
+    }
+  };
+  if (kv) run(compute_v);
+  else run(compute_k);
+
   // partial[split][kv*H + h][rt*16 + row][D]; lane holds rows 4g+i, column c of each tile
   if (!h_ok) return;
   const int which = kv * H + h;

@@ -30,7 +30,6 @@ namespace hsa {
 namespace {
 
 constexpr int kPlanThreads = 1024;
-constexpr int kZeroChunks = 64;  // 1 KB of zeros in the workspace
 
 __device__ int scan_incl_1024(int v, int* buf) {
   const int t = threadIdx.x;
@@ -57,77 +56,84 @@ __device__ int scan_incl_1024(int v, int* buf) {
 // rowinfo[row] = {segments, first slot}; meta = {items, slots}.
 constexpr int kMaxPlanRows = HSA_MAX_ROWS;
 constexpr int kMaxPlanSegs = 64;
+constexpr int kMaxPlanHS = 32 * kMaxPlanSegs;  // (head, segment) pairs, H <= 32
+
 __global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
     const int32_t* __restrict__ blk_count, int rows, int nQB, int nKB, int gpb, int gps, int seg_granules,
-    int max_segs, int4* __restrict__ items, int2* __restrict__ rowinfo, int* __restrict__ meta,
-    uint4* __restrict__ zeros) {
+    int max_segs, int4* __restrict__ items, int2* __restrict__ rowinfo, int* __restrict__ meta) {
   __shared__ short nseg_s[kMaxPlanRows];
   __shared__ int per_s[kMaxPlanRows];
-  __shared__ int off_s[32 * kMaxPlanSegs];   // (head, segment) offsets
+  __shared__ int slot_s[kMaxPlanRows];
+  __shared__ int off_s[kMaxPlanHS];
   __shared__ int buf[kPlanThreads];
-  __shared__ int carry_slots;
+  __shared__ int carry;
   const int t = threadIdx.x;
   const int H = rows / nQB;
-  if (t < kZeroChunks) zeros[t] = make_uint4(0, 0, 0, 0);  // source of masked granules
-  if (t == 0) carry_slots = 0;
-  // 1) segments per row
-  for (int row = t; row < rows; row += kPlanThreads) {
-    int n = blk_count[row];
-    n = n < 0 ? 0 : (n > nKB ? nKB : n);
-    const int G = n * gpb;
-    int nseg = 0, per = 0;
-    if (G > 0) {
-      nseg = (G + seg_granules - 1) / seg_granules;
-      per = (G + nseg - 1) / nseg;
-      per = (per + gps - 1) / gps * gps;
-      nseg = (G + per - 1) / per;
-    }
-    nseg_s[row] = (short)nseg;
-    per_s[row] = per;
-  }
+  const int nhs = H * max_segs;
+  if (t == 0) carry = 0;
   __syncthreads();
-  // 2) items per (head, segment) and their offsets, in (head, segment) order
-  for (int hs = t; hs < H * max_segs; hs += kPlanThreads) {
+  // 1) segments of every row; partial slots are contiguous per split row
+  for (int base = 0; base < rows; base += kPlanThreads) {
+    const int row = base + t;
+    int nseg = 0, per = 0;
+    if (row < rows) {
+      int n = blk_count[row];
+      n = n < 0 ? 0 : (n > nKB ? nKB : n);
+      const int G = n * gpb;
+      if (G > 0) {
+        nseg = (G + seg_granules - 1) / seg_granules;
+        per = (G + nseg - 1) / nseg;
+        per = (per + gps - 1) / gps * gps;
+        nseg = (G + per - 1) / per;
+      }
+    }
+    const int nslot = nseg > 1 ? nseg : 0;
+    const int cs = scan_incl_1024(nslot, buf) - nslot;
+    if (row < rows) {
+      nseg_s[row] = (short)nseg;
+      per_s[row] = per;
+      slot_s[row] = carry + cs;
+      rowinfo[row] = make_int2(nseg, carry + cs);
+    }
+    __syncthreads();
+    if (t == kPlanThreads - 1) carry += cs + nslot;
+    __syncthreads();
+  }
+  if (t == 0) meta[1] = carry;
+  // 2) items per (head, segment index)
+  for (int hs = t; hs < nhs; hs += kPlanThreads) {
     const int h = hs / max_segs, sg = hs % max_segs;
     int c = 0;
     for (int i = 0; i < nQB; ++i) c += nseg_s[h * nQB + i] > sg;
     off_s[hs] = c;
   }
   __syncthreads();
-  if (t == 0) {
-    int run = 0;
-    for (int hs = 0; hs < H * max_segs; ++hs) {
-      const int c = off_s[hs];
-      off_s[hs] = run;
-      run += c;
-    }
-    meta[0] = run;
+  // 3) exclusive scan of the counts in (head, segment) order (two entries per thread)
+  {
+    const int a0 = 2 * t < nhs ? off_s[2 * t] : 0;
+    const int a1 = 2 * t + 1 < nhs ? off_s[2 * t + 1] : 0;
+    const int incl = scan_incl_1024(a0 + a1, buf);
+    if (2 * t < nhs) off_s[2 * t] = incl - a0 - a1;
+    if (2 * t + 1 < nhs) off_s[2 * t + 1] = incl - a1;
+    if (t == kPlanThreads - 1) meta[0] = incl;
   }
   __syncthreads();
-  // 3) write the items; partial slots are contiguous per split row
-  for (int base = 0; base < rows; base += kPlanThreads) {
-    const int row = base + t;
-    const int nseg = row < rows ? nseg_s[row] : 0;
-    const int nslot = nseg > 1 ? nseg : 0;
-    const int cs = scan_incl_1024(nslot, buf) - nslot;
-    const int s0 = carry_slots + cs;
-    if (row < rows) {
-      const int h = row / nQB, i = row % nQB;
-      const int per = per_s[row];
-      const int G = blk_count[row] < 0 ? 0 : min(blk_count[row], nKB) * gpb;
-      for (int sg = 0; sg < nseg; ++sg) {
-        int rank = 0;
-        for (int i2 = 0; i2 < i; ++i2) rank += nseg_s[h * nQB + i2] > sg;
-        items[off_s[h * max_segs + sg] + rank] =
-            make_int4(row, sg * per, min(per, G - sg * per), nslot ? s0 + sg : -1);
+  // 4) each (head, segment) walker writes its items in query-block order
+  for (int hs = t; hs < nhs; hs += kPlanThreads) {
+    const int h = hs / max_segs, sg = hs % max_segs;
+    int pos = off_s[hs];
+    for (int i = 0; i < nQB; ++i) {
+      const int row = h * nQB + i;
+      const int nseg = nseg_s[row];
+      if (nseg > sg) {
+        const int per = per_s[row];
+        int n = blk_count[row];
+        n = n < 0 ? 0 : (n > nKB ? nKB : n);
+        const int G = n * gpb;
+        items[pos++] = make_int4(row, sg * per, min(per, G - sg * per), nseg > 1 ? slot_s[row] + sg : -1);
       }
-      rowinfo[row] = make_int2(nseg, s0);
     }
-    __syncthreads();
-    if (t == kPlanThreads - 1) carry_slots += cs + nslot;
-    __syncthreads();
   }
-  if (t == 0) meta[1] = carry_slots;
 }
 
 // LDS staging of one step (KS keys), written by direct global->LDS loads
@@ -159,7 +165,7 @@ template <typename T, int D, int NW, int QPW, int WPE, bool FULL>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void sparse_attn_kernel(
     const T* __restrict__ q, const T* __restrict__ k_act, const T* __restrict__ v_act,
     const int32_t* __restrict__ blk_idx, const int4* __restrict__ items, const int* __restrict__ meta,
-    const uint4* __restrict__ zeros, int H, int B, int L, int nKB, int nQB, float scale_log2,
+    int H, int B, int L, int nKB, int nQB, float scale_log2,
     float* __restrict__ o_sp, float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int E = Vec<T>::N;          // elements per 16-byte chunk
   constexpr int KS = Mma<T>::K;         // keys per step
@@ -228,34 +234,45 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
     return blk * B + (ga % gpb) * 16;
   };
 
+  // per-lane parts of the direct-load addresses (element offsets from the
+  // start of the granule); only the granule's key offset changes per step
+  constexpr int KPW = (KINST + NW - 1) / NW, VPW = (VINST + NW - 1) / NW;
+  int koff[KPW], kgran[KPW], voff[VPW], vgran[VPW];
+#pragma unroll
+  for (int ii = 0; ii < KPW; ++ii) {
+    const int i = ii * NW + w;
+    const int rho = i * ROWS_PER_INST + lane / CPR;
+    const int chunk = (lane % CPR) ^ kswz<T>(rho, CPR);
+    kgran[ii] = rho / 16;
+    koff[ii] = (rho % 16) * D + chunk * E;
+  }
+#pragma unroll
+  for (int ii = 0; ii < VPW; ++ii) {
+    const int i = ii * NW + w;
+    const int region = i / (D / 64);
+    const int rowv = (i % (D / 64)) * 64 + lane;
+    vgran[ii] = region / PV;
+    voff[ii] = rowv * 16 + (region % PV) * E;
+  }
+
   auto issue = [&](int sub, int buf) {
     int kofs[GPS];
 #pragma unroll
     for (int j = 0; j < GPS; ++j) kofs[j] = granule_key(sub, j);
-    // K: instruction i writes rows i*ROWS_PER_INST .. +ROWS_PER_INST-1
 #pragma unroll
-    for (int ii = 0; ii < (KINST + NW - 1) / NW; ++ii) {
+    for (int ii = 0; ii < KPW; ++ii) {
       const int i = ii * NW + w;
       if (KINST % NW != 0 && i >= KINST) break;
-      const int rho = i * ROWS_PER_INST + lane / CPR;
-      const int slotc = lane % CPR;
-      const int chunk = slotc ^ kswz<T>(rho, CPR);
-      const int j = rho / 16;
-      const void* src = kofs[j] >= 0 ? (const void*)(kh + (size_t)(kofs[j] + (rho % 16)) * D + chunk * E)
-                                     : (const void*)(zeros + lane);
+      const int kg = kofs[kgran[ii]];
+      const void* src = kg >= 0 ? (const void*)(kh + (size_t)kg * D + koff[ii]) : (const void*)(kZeroPage + lane);
       load_lds16(src, lds_k[buf] + i * 1024);
     }
-    // V: instruction i covers region r = i / (D/64) (granule r / PV, part r % PV), rows (i % (D/64))*64 + lane
 #pragma unroll
-    for (int ii = 0; ii < (VINST + NW - 1) / NW; ++ii) {
+    for (int ii = 0; ii < VPW; ++ii) {
       const int i = ii * NW + w;
       if (VINST % NW != 0 && i >= VINST) break;
-      const int region = i / (D / 64);
-      const int rowv = (i % (D / 64)) * 64 + lane;
-      const int j = region / PV, part = region % PV;
-      const void* src = kofs[j] >= 0
-                            ? (const void*)(vh + ((size_t)(kofs[j] / 16) * D + rowv) * 16 + part * E)
-                            : (const void*)(zeros + lane);
+      const int kg = kofs[vgran[ii]];
+      const void* src = kg >= 0 ? (const void*)(vh + (size_t)kg * D + voff[ii]) : (const void*)(kZeroPage + lane);
       load_lds16(src, lds_v[buf] + i * 1024);
     }
   };
@@ -387,67 +404,77 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
 }
 
 // Merge the partial outputs of split rows (fixed segment order); rows with
-// no selected block get zeros.
+// no selected block get zeros.  The per-segment weights exp2(m_s - M) / sum
+// go through LDS, then every thread streams its float4 columns once.
+constexpr int kCombThreads = 256;
+constexpr int kCombMaxSegs = 64;
+
 template <int D>
-__global__ __launch_bounds__(256) void sparse_combine_kernel(
+__global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
     const int2* __restrict__ rowinfo, const float* __restrict__ part_o, const float* __restrict__ part_ml,
     int H, int B, int nQB, float* __restrict__ o_sp) {
+  __shared__ float wgt[kCombMaxSegs * 192];
   const int row = blockIdx.x;
   const int2 ri = rowinfo[row];
   const int nseg = ri.x, s0 = ri.y;
   if (nseg == 1) return;
   const int h = row / nQB, qb = row % nQB;
-  for (int e = threadIdx.x; e < B * (D / 4); e += 256) {
+  if (nseg > 1) {
+    for (int r = threadIdx.x; r < B; r += kCombThreads) {
+      float M = -INFINITY;
+      for (int sg = 0; sg < nseg; ++sg) M = fmaxf(M, part_ml[((size_t)(s0 + sg) * B + r) * 2]);
+      if (M == -INFINITY) M = 0.f;
+      float den = 0.f;
+      for (int sg = 0; sg < nseg; ++sg) {
+        const size_t sr = (size_t)(s0 + sg) * B + r;
+        const float wv = exp2f(part_ml[sr * 2] - M);
+        wgt[sg * B + r] = wv;
+        den += wv * part_ml[sr * 2 + 1];
+      }
+      const float inv = den > 0.f ? 1.f / den : 0.f;
+      for (int sg = 0; sg < nseg; ++sg) wgt[sg * B + r] *= inv;
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < B * (D / 4); e += kCombThreads) {
     const int r = e / (D / 4), c4 = e % (D / 4);
-    float4* dst = reinterpret_cast<float4*>(o_sp + (((size_t)qb * B + r) * H + h) * D) + c4;
-    if (nseg == 0) {
-      *dst = make_float4(0.f, 0.f, 0.f, 0.f);
-      continue;
-    }
-    float M = -INFINITY;
-    for (int s = 0; s < nseg; ++s) M = fmaxf(M, part_ml[((size_t)(s0 + s) * B + r) * 2]);
-    if (M == -INFINITY) M = 0.f;
-    float den = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < nseg; ++s) {
-      const size_t sr = (size_t)(s0 + s) * B + r;
-      const float wgt = exp2f(part_ml[sr * 2] - M);
-      den += wgt * part_ml[sr * 2 + 1];
-      const float4 v = reinterpret_cast<const float4*>(part_o + sr * D)[c4];
-      acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
+    for (int sg = 0; sg < nseg; ++sg) {
+      const float wv = wgt[sg * B + r];
+      const float4 v = reinterpret_cast<const float4*>(part_o + ((size_t)(s0 + sg) * B + r) * D)[c4];
+      acc.x += wv * v.x; acc.y += wv * v.y; acc.z += wv * v.z; acc.w += wv * v.w;
     }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    *dst = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    reinterpret_cast<float4*>(o_sp + (((size_t)qb * B + r) * H + h) * D)[c4] = acc;
   }
 }
 
 template <typename T, int D, int NW, int QPW>
 void launch_attn(const Dims& s, const SparsePlan& pl, const void* q, const void* k_act, const void* v_act,
-                 const int32_t* idx, const int4* items, const int* meta, const uint4* zeros, float* o_sp,
+                 const int32_t* idx, const int4* items, const int* meta, float* o_sp,
                  float* po, float* pml, hipStream_t st) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
   constexpr int WPE = sizeof(T) == 2 ? 2 : 1;
   if (s.B == 16 * NW * QPW)
     hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE, true>), dim3(pl.grid), dim3(NW * kWave), 0, st,
                        reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act),
-                       reinterpret_cast<const T*>(v_act), idx, items, meta, zeros, s.H, s.B, s.L, s.nKB, s.nQB,
+                       reinterpret_cast<const T*>(v_act), idx, items, meta, s.H, s.B, s.L, s.nKB, s.nQB,
                        scale_log2, o_sp, po, pml);
   else
   hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE, false>), dim3(pl.grid), dim3(NW * kWave), 0, st,
                      reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act),
-                     reinterpret_cast<const T*>(v_act), idx, items, meta, zeros, s.H, s.B, s.L, s.nKB, s.nQB,
+                     reinterpret_cast<const T*>(v_act), idx, items, meta, s.H, s.B, s.L, s.nKB, s.nQB,
                      scale_log2, o_sp, po, pml);
 }
 
 template <typename T, int D>
 void dispatch_attn(const Dims& s, const SparsePlan& pl, const void* q, const void* k_act, const void* v_act,
-                   const int32_t* idx, const int4* items, const int* meta, const uint4* zeros, float* o_sp,
+                   const int32_t* idx, const int4* items, const int* meta, float* o_sp,
                    float* po, float* pml, hipStream_t st) {
   const int QT = s.B / 16;
   const int nw = (QT + 2) / 3;
   const int qpw = (QT + nw - 1) / nw;
 #define HSA_ATTN_CASE(NW_, QPW_) \
-  if (nw == NW_ && qpw == QPW_) return launch_attn<T, D, NW_, QPW_>(s, pl, q, k_act, v_act, idx, items, meta, zeros, o_sp, po, pml, st);
+  if (nw == NW_ && qpw == QPW_) return launch_attn<T, D, NW_, QPW_>(s, pl, q, k_act, v_act, idx, items, meta, o_sp, po, pml, st);
   HSA_ATTN_CASE(1, 1)
   HSA_ATTN_CASE(1, 2)
   HSA_ATTN_CASE(1, 3)
@@ -479,20 +506,19 @@ extern "C" hsa_rc hsa_sparse_attn(const hsa_geom* geom, const void* q, const voi
   int* meta = reinterpret_cast<int*>(wsb + w.sp_meta);
   float* po = reinterpret_cast<float*>(wsb + w.sp_part_o);
   float* pml = reinterpret_cast<float*>(wsb + w.sp_part_ml);
-  uint4* zeros = reinterpret_cast<uint4*>(wsb + w.sp_zeros);
   const int gps = s.bf16 ? 2 : 1;
   hipLaunchKernelGGL(sparse_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, blk_count, s.rows, s.nQB, s.nKB,
-                     pl.granules_per_block, gps, pl.seg_granules, pl.max_segs, items, rowinfo, meta, zeros);
+                     pl.granules_per_block, gps, pl.seg_granules, pl.max_segs, items, rowinfo, meta);
   if (s.bf16) {
-    if (s.d == 128) dispatch_attn<bf16_t, 128>(s, pl, q, k_act, v_act, blk_idx, items, meta, zeros, o_sp, po, pml, st);
-    else dispatch_attn<bf16_t, 64>(s, pl, q, k_act, v_act, blk_idx, items, meta, zeros, o_sp, po, pml, st);
+    if (s.d == 128) dispatch_attn<bf16_t, 128>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
+    else dispatch_attn<bf16_t, 64>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
   } else {
-    if (s.d == 128) dispatch_attn<float, 128>(s, pl, q, k_act, v_act, blk_idx, items, meta, zeros, o_sp, po, pml, st);
-    else dispatch_attn<float, 64>(s, pl, q, k_act, v_act, blk_idx, items, meta, zeros, o_sp, po, pml, st);
+    if (s.d == 128) dispatch_attn<float, 128>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
+    else dispatch_attn<float, 64>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
   }
   if (s.d == 128)
-    hipLaunchKernelGGL(sparse_combine_kernel<128>, dim3(s.rows), dim3(256), 0, st, rowinfo, po, pml, s.H, s.B, s.nQB, o_sp);
+    hipLaunchKernelGGL(sparse_combine_kernel<128>, dim3(s.rows), dim3(kCombThreads), 0, st, rowinfo, po, pml, s.H, s.B, s.nQB, o_sp);
   else
-    hipLaunchKernelGGL(sparse_combine_kernel<64>, dim3(s.rows), dim3(256), 0, st, rowinfo, po, pml, s.H, s.B, s.nQB, o_sp);
+    hipLaunchKernelGGL(sparse_combine_kernel<64>, dim3(s.rows), dim3(kCombThreads), 0, st, rowinfo, po, pml, s.H, s.B, s.nQB, o_sp);
   return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
 }
