@@ -14,7 +14,8 @@
 //    kernel (fixed order, no atomics).
 //  * Workgroup = NW waves; wave w owns QPW 16-row query tiles of the block.
 //    Per step it stages KS keys (32 for bf16, 16 for f32) of K (row-major)
-//    and of V (d-major, as the gather lays V out) in LDS, double buffered,
+//    and of V (d-major, as the gather lays V out) in LDS, in a ring of two
+//    or three stages fed by direct global->LDS loads,
 //    and every wave computes S^T = K Q^T (keys on the rows, so each lane owns
 //    one query column), an online softmax per query, and O^T += V^T P^T.
 //    Keeping queries on the lane-column axis puts the softmax state and the
@@ -157,11 +158,24 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds_wave_base) {
 
 // wait until this wave's direct-to-LDS loads have landed
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Workgroup barrier for the staging ring: this wave's LDS reads are done and
+// at most N of its direct-to-LDS loads are still in flight, then all waves
+// meet.  (gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt[5:4] << 14.)  The empty asm statements keep the compiler from moving
+// LDS accesses across the barrier, which __builtin_amdgcn_s_barrier alone
+// does not; unlike __syncthreads they do not force every load to land.
+template <int N> __device__ __forceinline__ void ring_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | ((N >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 
 // FULL: every wave owns exactly QPW query tiles (B == 16*NW*QPW), so the tile
 // loops carry no run-time guards and the matrix-core chains stay branch-free.
-template <typename T, int D, int NW, int QPW, int WPE, bool FULL>
+template <typename T, int D, int NW, int QPW, int WPE, int RING, bool FULL>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void sparse_attn_kernel(
     const T* __restrict__ q, const T* __restrict__ k_act, const T* __restrict__ v_act,
     const int32_t* __restrict__ blk_idx, const int4* __restrict__ items, const int* __restrict__ meta,
@@ -180,9 +194,13 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
   constexpr int VINST = VBYTES / 1024;
   constexpr int ROWS_PER_INST = 64 / CPR;
   constexpr float kLazy = 8.f;          // rescale only when the row max grows by more than 2^8
+  static_assert(RING == 2 || RING == 3, "staging ring depth");
 
-  __shared__ __align__(1024) unsigned char lds_k[2][KBYTES];
-  __shared__ __align__(1024) unsigned char lds_v[2][VBYTES];
+  // RING stages of K and V, each buffer its own object so the compiler can
+  // tell an operand read of one stage from the loads still in flight into
+  // the others (a third buffer goes unused when RING == 2)
+  __shared__ __align__(1024) unsigned char lds_k0[KBYTES], lds_k1[KBYTES], lds_k2[RING == 3 ? KBYTES : 16];
+  __shared__ __align__(1024) unsigned char lds_v0[VBYTES], lds_v1[VBYTES], lds_v2[RING == 3 ? VBYTES : 16];
 
   const int item = xcd_remap(blockIdx.x, meta[0]);
   if (item < 0) return;
@@ -190,13 +208,17 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
   const int row = it.x, g0 = it.y, gcount = it.z, slot = it.w;
   const int h = row / nQB, qb = row % nQB;
   const int gpb = B / 16;
-  const int32_t* list = blk_idx + (size_t)row * nKB;
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave index, kept in a scalar register
   const int g = lane >> 4, c = lane & 15;
   const int QT = B / 16;
   const int ntile = FULL ? QPW : min(QPW, QT - w * QPW);  // wave-uniform
+
+  // The segment's block ids, one per lane (a segment spans at most 33 blocks).
+  const int b0 = g0 / gpb;
+  const int nblk = gcount > 0 ? (g0 + gcount - 1) / gpb - b0 + 1 : 0;
+  const int blk_lane = lane < nblk ? blk_idx[(size_t)row * nKB + b0 + lane] : -1;
 
   // Q^T operand: lane (g, c) holds Q[row c of tile][chunk 4s+g] for step s.
   uint4 qreg[QPW][DSTEPS];
@@ -224,19 +246,11 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
   const T* kh = k_act + (size_t)h * L * D;
   const T* vh = v_act + (size_t)h * (L / 16) * D * 16;
 
-  // key offset of granule j of step `sub`, or -1 (past the end, or invalid block id)
-  auto granule_key = [&](int sub, int j) -> int {
-    const int gi = sub * GPS + j;
-    if (gi >= gcount) return -1;
-    const int ga = g0 + gi;
-    const int blk = list[ga / gpb];
-    if (blk < 0 || blk >= nKB) return -1;
-    return blk * B + (ga % gpb) * 16;
-  };
-
   // per-lane parts of the direct-load addresses (element offsets from the
   // start of the granule); only the granule's key offset changes per step
   constexpr int KPW = (KINST + NW - 1) / NW, VPW = (VINST + NW - 1) / NW;
+  // direct loads every wave issues per stage, at least
+  constexpr int PER_STAGE = KINST / NW + VINST / NW;
   int koff[KPW], kgran[KPW], voff[VPW], vgran[VPW];
 #pragma unroll
   for (int ii = 0; ii < KPW; ++ii) {
@@ -255,17 +269,35 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
     voff[ii] = rowv * 16 + (region % PV) * E;
   }
 
-  auto issue = [&](int sub, int buf) {
+  // Issue cursor over the segment's granules (scalar state): stages are
+  // issued strictly in order, GPS granules each.
+  int cur_blk = 0, cur_gran = g0 - b0 * gpb, issued = 0;
+  // Stage the next GPS granules into (lk, lv); returns their validity bits.
+  auto issue = [&](unsigned char* lk, unsigned char* lv) -> unsigned {
     int kofs[GPS];
+    unsigned mask = 0;
 #pragma unroll
-    for (int j = 0; j < GPS; ++j) kofs[j] = granule_key(sub, j);
+    for (int j = 0; j < GPS; ++j) {
+      int key = -1;
+      if (issued < gcount) {
+        const int blk = __builtin_amdgcn_readlane(blk_lane, cur_blk);
+        if (blk >= 0 && blk < nKB) key = blk * B + cur_gran * 16;
+      }
+      kofs[j] = key;
+      mask |= (key >= 0 ? 1u : 0u) << j;
+      ++issued;
+      if (++cur_gran == gpb) {
+        cur_gran = 0;
+        ++cur_blk;
+      }
+    }
 #pragma unroll
     for (int ii = 0; ii < KPW; ++ii) {
       const int i = ii * NW + w;
       if (KINST % NW != 0 && i >= KINST) break;
       const int kg = kofs[kgran[ii]];
       const void* src = kg >= 0 ? (const void*)(kh + (size_t)kg * D + koff[ii]) : (const void*)(kZeroPage + lane);
-      load_lds16(src, lds_k[buf] + i * 1024);
+      load_lds16(src, lk + i * 1024);
     }
 #pragma unroll
     for (int ii = 0; ii < VPW; ++ii) {
@@ -273,106 +305,116 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
       if (VINST % NW != 0 && i >= VINST) break;
       const int kg = kofs[vgran[ii]];
       const void* src = kg >= 0 ? (const void*)(vh + (size_t)kg * D + voff[ii]) : (const void*)(kZeroPage + lane);
-      load_lds16(src, lds_v[buf] + i * 1024);
+      load_lds16(src, lv + i * 1024);
+    }
+    return mask;
+  };
+
+  constexpr unsigned kAllValid = (1u << GPS) - 1;
+  auto compute = [&](const unsigned char* lk, const unsigned char* lv, unsigned mask) {
+    if (!(FULL || w * QPW < QT)) return;
+    f32x4 sacc[QPW][GPS];
+#pragma unroll
+    for (int t = 0; t < QPW; ++t)
+#pragma unroll
+      for (int kt = 0; kt < GPS; ++kt) sacc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < GPS; ++kt) {
+      const int rho = perm_row<T>(kt, c);
+      const unsigned char* krow = lk + rho * CPR * 16;
+      const int sw = kswz<T>(rho, CPR);
+#pragma unroll
+      for (int s = 0; s < DSTEPS; ++s) {
+        const uint4 a = *reinterpret_cast<const uint4*>(krow + (((4 * s + g) ^ sw) * 16));
+#pragma unroll
+        for (int t = 0; t < QPW; ++t)
+          if (FULL || t < ntile) Mma<T>::run(sacc[t][kt], a, qreg[t][s]);
+      }
+    }
+    if (mask != kAllValid) {
+      // masked keys only on a ragged or invalid step (wave-uniform test);
+      // lane group g holds keys of granule g/2 (bf16) or granule 0 (f32)
+      const bool ok = (mask >> (GPS == 2 ? (g >> 1) : 0)) & 1u;
+      if (!ok) {
+#pragma unroll
+        for (int t = 0; t < QPW; ++t)
+#pragma unroll
+          for (int kt = 0; kt < GPS; ++kt) sacc[t][kt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      }
+    }
+    uint4 pk[QPW];
+    float alpha[QPW];
+    bool need_any = false;
+#pragma unroll
+    for (int t = 0; t < QPW; ++t) {
+      alpha[t] = 1.f;
+      if (FULL || t < ntile) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < GPS; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[t][kt][i]);
+        mx = max4g(mx) * scale_log2;
+        const bool need = mx > m_run[t] + kLazy;
+        alpha[t] = need ? fast_exp2(m_run[t] - mx) : 1.f;
+        m_run[t] = need ? mx : m_run[t];
+        need_any = need_any || need;
+        const float mref = m_run[t] == -INFINITY ? 0.f : m_run[t];
+        float ls = 0.f;
+        f32x4 p[GPS];
+#pragma unroll
+        for (int kt = 0; kt < GPS; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float e = fast_exp2(fmaf(sacc[t][kt][i], scale_log2, -mref));
+            p[kt][i] = e;
+            ls += e;
+          }
+        l_run[t] = l_run[t] * alpha[t] + ls;
+        pk[t] = pack_p<T>(p);
+      }
+    }
+    if (__any(need_any)) {
+#pragma unroll
+      for (int t = 0; t < QPW; ++t)
+        if (FULL || t < ntile)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha[t];
+    }
+    const unsigned char* vreg = lv + g * (D * 16);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint4 a = *reinterpret_cast<const uint4*>(vreg + (16 * dt + c) * 16);
+#pragma unroll
+      for (int t = 0; t < QPW; ++t)
+        if (FULL || t < ntile) Mma<T>::run(o[t][dt], a, pk[t]);
     }
   };
 
-  issue(0, 0);
-  wait_vm();
-  __syncthreads();
+  // One step: wait for this stage (this wave's loads, then every wave's),
+  // refill the ring slot that the previous step finished with, compute.
+  auto step = [&](int sub, const unsigned char* lk, const unsigned char* lv, unsigned mask,
+                  unsigned char* nk, unsigned char* nv, unsigned& nmask) {
+    if (RING == 3 && sub + 1 < nsub) ring_barrier<PER_STAGE>();  // the next stage may stay in flight
+    else ring_barrier<0>();
+    if (sub + RING - 1 < nsub) nmask = issue(nk, nv);
+    compute(lk, lv, mask);
+  };
 
-  for (int sub = 0; sub < nsub; ++sub) {
-    const int buf = sub & 1;
-    const bool more = sub + 1 < nsub;
-    if (more) issue(sub + 1, buf ^ 1);
-
-    if (FULL || w * QPW < QT) {
-      // masked keys only on a ragged or invalid step (wave-uniform test)
-      bool gval[GPS];
-      bool all_valid = true;
-#pragma unroll
-      for (int j = 0; j < GPS; ++j) {
-        gval[j] = granule_key(sub, j) >= 0;
-        all_valid = all_valid && gval[j];
-      }
-      f32x4 sacc[QPW][GPS];
-#pragma unroll
-      for (int t = 0; t < QPW; ++t)
-#pragma unroll
-        for (int kt = 0; kt < GPS; ++kt) sacc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kt = 0; kt < GPS; ++kt) {
-        const int rho = perm_row<T>(kt, c);
-        const unsigned char* krow = lds_k[buf] + rho * CPR * 16;
-        const int sw = kswz<T>(rho, CPR);
-#pragma unroll
-        for (int s = 0; s < DSTEPS; ++s) {
-          const uint4 a = *reinterpret_cast<const uint4*>(krow + (((4 * s + g) ^ sw) * 16));
-#pragma unroll
-          for (int t = 0; t < QPW; ++t)
-            if (FULL || t < ntile) Mma<T>::run(sacc[t][kt], a, qreg[t][s]);
-        }
-      }
-      if (!all_valid) {
-        // lane group g holds keys of granule g/2 (bf16) or granule 0 (f32)
-        const bool ok = gval[GPS == 2 ? (g >> 1) : 0];
-        if (!ok) {
-#pragma unroll
-          for (int t = 0; t < QPW; ++t)
-#pragma unroll
-            for (int kt = 0; kt < GPS; ++kt) sacc[t][kt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-        }
-      }
-      uint4 pk[QPW];
-      float alpha[QPW];
-      bool need_any = false;
-#pragma unroll
-      for (int t = 0; t < QPW; ++t) {
-        alpha[t] = 1.f;
-        if (FULL || t < ntile) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int kt = 0; kt < GPS; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[t][kt][i]);
-          mx = max4g(mx) * scale_log2;
-          const bool need = mx > m_run[t] + kLazy;
-          alpha[t] = need ? fast_exp2(m_run[t] - mx) : 1.f;
-          m_run[t] = need ? mx : m_run[t];
-          need_any = need_any || need;
-          const float mref = m_run[t] == -INFINITY ? 0.f : m_run[t];
-          float ls = 0.f;
-          f32x4 p[GPS];
-#pragma unroll
-          for (int kt = 0; kt < GPS; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float e = fast_exp2(fmaf(sacc[t][kt][i], scale_log2, -mref));
-              p[kt][i] = e;
-              ls += e;
-            }
-          l_run[t] = l_run[t] * alpha[t] + ls;
-          pk[t] = pack_p<T>(p);
-        }
-      }
-      if (__any(need_any)) {
-#pragma unroll
-        for (int t = 0; t < QPW; ++t)
-          if (FULL || t < ntile)
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha[t];
-      }
-      const unsigned char* vreg = lds_v[buf] + g * (D * 16);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const uint4 a = *reinterpret_cast<const uint4*>(vreg + (16 * dt + c) * 16);
-#pragma unroll
-        for (int t = 0; t < QPW; ++t)
-          if (FULL || t < ntile) Mma<T>::run(o[t][dt], a, pk[t]);
-      }
+  unsigned m0 = 0, m1 = 0, m2 = 0;
+  if (nsub > 0) m0 = issue(lds_k0, lds_v0);
+  if (RING == 3) {
+    if (nsub > 1) m1 = issue(lds_k1, lds_v1);
+    for (int sub = 0; sub < nsub; sub += 3) {
+      step(sub, lds_k0, lds_v0, m0, lds_k2, lds_v2, m2);
+      if (sub + 1 < nsub) step(sub + 1, lds_k1, lds_v1, m1, lds_k0, lds_v0, m0);
+      if (sub + 2 < nsub) step(sub + 2, lds_k2, lds_v2, m2, lds_k1, lds_v1, m1);
     }
-    wait_vm();
-    __syncthreads();
+  } else {
+    for (int sub = 0; sub < nsub; sub += 2) {
+      step(sub, lds_k0, lds_v0, m0, lds_k1, lds_v1, m1);
+      if (sub + 1 < nsub) step(sub + 1, lds_k1, lds_v1, m1, lds_k0, lds_v0, m0);
+    }
   }
 
   // epilogue
@@ -454,13 +496,16 @@ void launch_attn(const Dims& s, const SparsePlan& pl, const void* q, const void*
                  float* po, float* pml, hipStream_t st) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
   constexpr int WPE = sizeof(T) == 2 ? 2 : 1;
+  // a third stage only where it still leaves room for four workgroups per CU
+  constexpr int STAGE = 2 * Mma<T>::K * D * (int)sizeof(T);
+  constexpr int RING = 3 * STAGE <= 24576 ? 3 : 2;
   if (s.B == 16 * NW * QPW)
-    hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE, true>), dim3(pl.grid), dim3(NW * kWave), 0, st,
+    hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE, RING, true>), dim3(pl.grid), dim3(NW * kWave), 0, st,
                        reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act),
                        reinterpret_cast<const T*>(v_act), idx, items, meta, s.H, s.B, s.L, s.nKB, s.nQB,
                        scale_log2, o_sp, po, pml);
   else
-  hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE, false>), dim3(pl.grid), dim3(NW * kWave), 0, st,
+  hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE, RING, false>), dim3(pl.grid), dim3(NW * kWave), 0, st,
                      reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act),
                      reinterpret_cast<const T*>(v_act), idx, items, meta, s.H, s.B, s.L, s.nKB, s.nQB,
                      scale_log2, o_sp, po, pml);
