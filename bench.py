@@ -13,6 +13,7 @@ the same line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -45,6 +46,32 @@ def stage_model(cfg, n_sel_total: int):
         "sparse": dict(bound="mfma", flops=4 * B * B * d * n_sel_total),
         "fuse": dict(bound="hbm", bytes=Lq * D * es + 2 * Lq * D * 4 + Lq * D * es),
     }
+
+
+ATTN_SOURCE = os.path.join(ROOT, "sparse_linear_attention_hsa_amd", "csrc", "sparse_attn.hip")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the attention kernel from the committed counter
+    summary (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by the copy-kernel
+    calibration), or None when there is none for this workload or the kernel
+    source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"sparse_attn_kernel_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    with open(ATTN_SOURCE, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if kv.get("source_sha256") != digest:
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(cfg, w, arrays):
@@ -101,6 +128,8 @@ def main():
     ap.add_argument("--config", default="c1_full")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step as one HIP graph")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run three device-to-device copies of 1 GiB (calibrates the HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
@@ -109,6 +138,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+        return
     from synth import CONFIGS, Workload
     from sparse_linear_attention_hsa_amd.ops import make_geom
     from sparse_linear_attention_hsa_amd.step import HsaStep
@@ -117,21 +155,28 @@ def main():
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     w = Workload(cfg)
     s = w.small_inputs()
-    pk_np = [w.page_k(j) for j in range(cfg.n_pages)]
-    pv_np = [w.page_v(j) for j in range(cfg.n_pages)]
     up = lambda a: torch.from_numpy(a).to(tdt).cuda()
     q, x, e_k, e_v, w_g = (up(s[k]) for k in ("q", "x", "e_k", "e_v", "w_g"))
     tau = torch.from_numpy(s["tau"]).cuda()
-    pk = [up(a) for a in pk_np]
-    pv = [up(a) for a in pv_np]
+    keep_host = not args.no_cpu_baseline  # the oracle's scoring reads every page
+    pk_np, pv_np, pk, pv = [], [], [], []
+    for j in range(cfg.n_pages):
+        kj, vj = w.page_k(j), w.page_v(j)
+        pk.append(up(kj))
+        pv.append(up(vj))
+        if keep_host:
+            pk_np.append(kj)
+            pv_np.append(vj)
+        if (j + 1) % 8 == 0 or j + 1 == cfg.n_pages:
+            print(f"bench: generated {j + 1}/{cfg.n_pages} pages", file=sys.stderr, flush=True)
     geom = make_geom(cfg.n_heads, cfg.head_dim, cfg.frame_h, cfg.frame_w, cfg.frames_per_page,
                      cfg.query_frames, cfg.tile, cfg.n_sel_pages, cfg.rank, cfg.dtype)
     st = HsaStep(geom, cfg.n_pages)
     stream = torch.cuda.current_stream()
 
-    def one_step(ev=None):
+    def one_step(ev=None, kev=None):
         calls = (lambda: st.score(q, pk), lambda: st.gather(pk, pv), lambda: st.linear(q, e_k, e_v),
-                 lambda: st.select(q, tau), lambda: st.sparse(q), lambda: st.fuse(x, w_g))
+                 lambda: st.select(q, tau), lambda: st.sparse(q, kernel_events=kev), lambda: st.fuse(x, w_g))
         for i, fn in enumerate(calls):
             if ev is not None:
                 ev[i][0].record(stream)
@@ -167,14 +212,18 @@ def main():
     ms = t_start.elapsed_time(t_end) / args.steps
 
     # per-stage HIP events over a second timed pass (same launches, events between calls)
+    # plus, inside the sparse stage, events around the attention kernel alone
+    # (recorded by the library on the same stream)
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in STAGES]
            for _ in range(args.steps)]
+    kevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     for k in range(args.steps):
-        one_step(evs[k])
+        one_step(evs[k], kevs[k])
     torch.cuda.synchronize()
     stage_ms = {name: float(np.mean([evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(args.steps)]))
                 for i, name in enumerate(STAGES)}
+    attn_kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in kevs]))
 
     counts = st.blk_count.cpu().numpy()
     n_sel_total = int(counts.sum())
@@ -183,16 +232,13 @@ def main():
     lin_tf = model["linear"]["flops"] / (stage_ms["linear"] * 1e-3) / 1e12
     peak_tf = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
 
-    dom = max(STAGES, key=lambda k: stage_ms[k])
-    dm = model[dom]
-    if dm["bound"] == "mfma":
-        ach = dm["flops"] / (stage_ms[dom] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak_tf, "unit": "TFLOP/s",
-                "frac": round(ach / peak_tf, 4), "traffic": None, "stage": dom}
-    else:
-        ach = dm["bytes"] / (stage_ms[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "stage": dom}
+    # Roofline of the dominant kernel: the block-sparse attention kernel
+    # (algorithmic flops 4*B*B*d per selected (query block, key block) pair,
+    # all pairs of the step in one launch) over its own event-timed duration.
+    ach = model["sparse"]["flops"] / (attn_kernel_ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak_tf, "unit": "TFLOP/s",
+            "frac": round(ach / peak_tf, 4), "traffic": measured_traffic(cfg.name),
+            "kernel": "sparse_attn_kernel", "kernel_ms": round(attn_kernel_ms, 4)}
 
     out = {
         "metric": METRIC, "value": round(ms, 4), "unit": "ms/chunk", "n_gpus": 1, "steps": args.steps,

@@ -79,6 +79,7 @@ typedef struct {
 } hsa_geom;
 
 typedef struct ihipStream_t* hsa_stream;  /* a hipStream_t */
+typedef struct ihipEvent_t* hsa_event;    /* a hipEvent_t  */
 
 /* Linear-branch flags. */
 #define HSA_LIN_REUSE_PROJ 1  /* skip the projection: k_proj / v_proj are inputs        */
@@ -194,6 +195,17 @@ hsa_rc hsa_block_select(const hsa_geom* geom, const void* q, const void* k_act, 
 hsa_rc hsa_sparse_attn(const hsa_geom* geom, const void* q, const void* k_act, const void* v_act,
                        const int32_t* blk_count, const int32_t* blk_idx, float* o_sp,
                        void* ws, size_t ws_bytes, hsa_stream stream);
+
+/* The same call, additionally recording ev_begin / ev_end on `stream`
+ * immediately before and after the attention kernel itself (between the
+ * small work-planning kernel that precedes it and the merge of split rows
+ * that follows), so a caller can time the dominant kernel alone.  Either
+ * event may be NULL (not recorded); both are caller-created hipEvent_t.
+ * Errors as hsa_sparse_attn, plus HSA_ERR_HIP if recording fails. */
+hsa_rc hsa_sparse_attn_timed(const hsa_geom* geom, const void* q, const void* k_act, const void* v_act,
+                             const int32_t* blk_count, const int32_t* blk_idx, float* o_sp,
+                             void* ws, size_t ws_bytes, hsa_stream stream,
+                             hsa_event ev_begin, hsa_event ev_end);
 
 /* ---------------------------------------------------------------------------
  * S6 -- gated fusion.  Paper section 3.3, "Gated fusion of two branches";

@@ -40,6 +40,7 @@ SIGNATURES = {
     "hsa_linear_branch": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
     "hsa_block_select": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "hsa_sparse_attn": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "hsa_sparse_attn_timed": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),
     "hsa_fuse": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "hsa_workspace_bytes": (_sz, [_GP, _i32]),
     "hsa_geom_check": (_i32, [_GP]),

@@ -533,9 +533,9 @@ void dispatch_attn(const Dims& s, const SparsePlan& pl, const void* q, const voi
 }  // namespace
 }  // namespace hsa
 
-extern "C" hsa_rc hsa_sparse_attn(const hsa_geom* geom, const void* q, const void* k_act, const void* v_act,
-                                  const int32_t* blk_count, const int32_t* blk_idx, float* o_sp, void* ws,
-                                  size_t ws_bytes, hsa_stream stream) {
+extern "C" hsa_rc hsa_sparse_attn_timed(const hsa_geom* geom, const void* q, const void* k_act, const void* v_act,
+                                        const int32_t* blk_count, const int32_t* blk_idx, float* o_sp, void* ws,
+                                        size_t ws_bytes, hsa_stream stream, hsa_event ev_begin, hsa_event ev_end) {
   using namespace hsa;
   Dims s;
   hsa_rc rc = derive(geom, &s);
@@ -554,6 +554,7 @@ extern "C" hsa_rc hsa_sparse_attn(const hsa_geom* geom, const void* q, const voi
   const int gps = s.bf16 ? 2 : 1;
   hipLaunchKernelGGL(sparse_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, blk_count, s.rows, s.nQB, s.nKB,
                      pl.granules_per_block, gps, pl.seg_granules, pl.max_segs, items, rowinfo, meta);
+  if (ev_begin && hipEventRecord(reinterpret_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return HSA_ERR_HIP;
   if (s.bf16) {
     if (s.d == 128) dispatch_attn<bf16_t, 128>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
     else dispatch_attn<bf16_t, 64>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
@@ -561,9 +562,17 @@ extern "C" hsa_rc hsa_sparse_attn(const hsa_geom* geom, const void* q, const voi
     if (s.d == 128) dispatch_attn<float, 128>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
     else dispatch_attn<float, 64>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
   }
+  if (ev_end && hipEventRecord(reinterpret_cast<hipEvent_t>(ev_end), st) != hipSuccess) return HSA_ERR_HIP;
   if (s.d == 128)
     hipLaunchKernelGGL(sparse_combine_kernel<128>, dim3(s.rows), dim3(kCombThreads), 0, st, rowinfo, po, pml, s.H, s.B, s.nQB, o_sp);
   else
     hipLaunchKernelGGL(sparse_combine_kernel<64>, dim3(s.rows), dim3(kCombThreads), 0, st, rowinfo, po, pml, s.H, s.B, s.nQB, o_sp);
   return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
+}
+
+extern "C" hsa_rc hsa_sparse_attn(const hsa_geom* geom, const void* q, const void* k_act, const void* v_act,
+                                  const int32_t* blk_count, const int32_t* blk_idx, float* o_sp, void* ws,
+                                  size_t ws_bytes, hsa_stream stream) {
+  return hsa_sparse_attn_timed(geom, q, k_act, v_act, blk_count, blk_idx, o_sp, ws, ws_bytes, stream, nullptr,
+                               nullptr);
 }

@@ -108,6 +108,22 @@ def hsa_sparse_attn(geom, q, k_act, v_act, blk_count, blk_idx, o_sp, ws, stream=
         _p(ws), ws.numel() * ws.element_size(), _s(stream)))
 
 
+def hsa_sparse_attn_timed(geom, q, k_act, v_act, blk_count, blk_idx, o_sp, ws, ev_begin, ev_end, stream=None):
+    """hsa_sparse_attn that also records two torch.cuda.Event objects (created
+    with enable_timing=True) around the attention kernel alone."""
+    handles = []
+    for ev in (ev_begin, ev_end):
+        if ev is None:
+            handles.append(None)
+            continue
+        if not ev.cuda_event:  # torch creates the underlying event on first use
+            ev.record(torch.cuda.current_stream() if stream is None else stream)
+        handles.append(ctypes.c_void_p(ev.cuda_event))
+    check("hsa_sparse_attn_timed", lib().hsa_sparse_attn_timed(
+        ctypes.byref(geom), _p(q), _p(k_act), _p(v_act), _p(blk_count), _p(blk_idx), _p(o_sp),
+        _p(ws), ws.numel() * ws.element_size(), _s(stream), handles[0], handles[1]))
+
+
 def hsa_fuse(geom, x, w_g, gate_override, o_lin, o_sp, out, stream=None):
     check("hsa_fuse", lib().hsa_fuse(
         ctypes.byref(geom), _p(x), _p(w_g), _p(gate_override), _p(o_lin), _p(o_sp), _p(out), _s(stream)))

@@ -1,0 +1,169 @@
+"""Summaries of rocprofv3 output for the profiles/ folder.
+
+    python -m sparse_linear_attention_hsa_amd.profiling stats <stats_dir> <out.txt> --cmd "<command>" \
+        [--bench-log <log of the profiled bench run>]
+    python -m sparse_linear_attention_hsa_amd.profiling traffic --fetch <dir> --write <dir> \
+        --copy-fetch <dir> --copy-write <dir> --copy-bytes N --kernel <regex> --workload <name> \
+        --out <out.txt> --cmd "<command>"
+
+`stats` condenses a `rocprofv3 --kernel-trace --stats --output-format csv`
+run into a per-kernel table (calls, average / min / max duration, share).
+
+`traffic` turns two counter runs (`--pmc FETCH_SIZE`, then `--pmc
+WRITE_SIZE`, both `--output-format csv`) into HBM bytes per launch of one
+kernel.  Each counter is scaled by what it reads for a device-to-device copy
+of known size (`bench.py --copy-probe` under the same two counters), so the
+figure is in real bytes.  The summary records the SHA-256 of the attention
+kernel's source; the benchmark reports the traffic only while that source is
+unchanged.
+
+Only CSV files are read; nothing here touches the GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import re
+import sys
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ATTN_SOURCE = os.path.join(PKG, "csrc", "sparse_attn.hip")
+
+
+def _one(pattern: str) -> str:
+    hits = sorted(glob.glob(pattern, recursive=True))
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def _short(name: str) -> str:
+    name = re.sub(r"\(anonymous namespace\)::", "", name)
+    name = re.sub(r"\(.*\)$", "", name)  # drop the parameter list
+    return name.replace("void ", "", 1)
+
+
+def kernel_stats(stats_dir: str):
+    """[(name, calls, avg_us, min_us, max_us, percent)] from *_kernel_stats.csv."""
+    path = _one(os.path.join(stats_dir, "**", "*kernel_stats.csv"))
+    rows = []
+    for r in csv.DictReader(open(path)):
+        rows.append((_short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                     float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    rows.sort(key=lambda t: -t[5])
+    return rows
+
+
+def counter_per_dispatch(pmc_dir: str, counter: str, kernel_regex: str) -> float:
+    """Average value of one counter over the dispatches of the matching kernel."""
+    path = _one(os.path.join(pmc_dir, "**", "*counter_collection.csv"))
+    vals = defaultdict(float)  # per dispatch (a counter can be split over rows)
+    rx = re.compile(kernel_regex)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter and rx.search(r["Kernel_Name"]):
+            vals[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    if not vals:
+        raise ValueError(f"no {counter} rows for /{kernel_regex}/ in {path}")
+    return sum(vals.values()) / len(vals)
+
+
+def source_digest() -> str:
+    with open(ATTN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def trace_durations(stats_dir: str, kernel_regex: str):
+    """Durations (us) of the matching kernel's dispatches, in dispatch order."""
+    path = _one(os.path.join(stats_dir, "**", "*kernel_trace.csv"))
+    rx = re.compile(kernel_regex)
+    rows = [r for r in csv.DictReader(open(path)) if rx.search(r["Kernel_Name"])]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    return [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+
+
+def bench_line(log: str) -> dict:
+    """The benchmark's JSON line from its log."""
+    import json
+    for line in reversed(open(log).read().splitlines()):
+        if line.startswith("{") and '"metric"' in line:
+            return json.loads(line)
+    raise ValueError(f"no benchmark line in {log}")
+
+
+def write_stats(stats_dir: str, out: str, cmd: str, bench_log: str = None) -> None:
+    rows = kernel_stats(stats_dir)
+    with open(out, "w") as f:
+        f.write(f"# rocprofv3 kernel statistics\n# command: {cmd}\n")
+        f.write(f"{'kernel':<72} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'share%':>7}\n")
+        for name, calls, avg, mn, mx, pct in rows:
+            f.write(f"{name[:72]:<72} {calls:>6} {avg:>10.1f} {mn:>10.1f} {mx:>10.1f} {pct:>7.2f}\n")
+        if bench_log:
+            # The benchmark times the attention kernel with HIP events in its
+            # last pass of `steps` steps; compare with the same dispatches here.
+            b = bench_line(bench_log)
+            k = b["roofline"].get("kernel", "sparse_attn_kernel")
+            n = int(b["steps"])
+            d = trace_durations(stats_dir, k)[-n:]
+            prof_us = sum(d) / len(d)
+            ev_us = 1e3 * float(b["roofline"]["kernel_ms"])
+            f.write(f"# {k}: HIP-event average in the benchmark's own line {ev_us:.1f} us; "
+                    f"rocprofv3 average of the same {len(d)} dispatches {prof_us:.1f} us "
+                    f"(difference {100 * (ev_us - prof_us) / prof_us:+.1f}%)\n")
+            f.write(f"# benchmark line under the profiler: value {b['value']} {b['unit']}, "
+                    f"roofline achieved {b['roofline']['achieved']} {b['roofline']['unit']}\n")
+
+
+def write_traffic(a) -> None:
+    fetch_kib = counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel)
+    write_kib = counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel)
+    copy_rx = r"copyBuffer"
+    cf = counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", copy_rx)
+    cw = counter_per_dispatch(a.copy_write, "WRITE_SIZE", copy_rx)
+    f_fetch = a.copy_bytes / (cf * 1024.0)
+    f_write = a.copy_bytes / (cw * 1024.0)
+    traffic = fetch_kib * 1024.0 * f_fetch + write_kib * 1024.0 * f_write
+    with open(a.out, "w") as f:
+        f.write(f"# HBM traffic per launch of /{a.kernel}/, workload {a.workload}\n")
+        f.write(f"# command: {a.cmd}\n")
+        f.write(f"workload: {a.workload}\n")
+        f.write(f"fetch_kib_per_dispatch: {fetch_kib:.1f}\n")
+        f.write(f"write_kib_per_dispatch: {write_kib:.1f}\n")
+        f.write(f"copy_bytes: {a.copy_bytes}\n")
+        f.write(f"copy_fetch_kib: {cf:.1f}\n")
+        f.write(f"copy_write_kib: {cw:.1f}\n")
+        f.write(f"fetch_scale: {f_fetch:.4f}\n")
+        f.write(f"write_scale: {f_write:.4f}\n")
+        f.write(f"traffic_bytes_per_launch: {traffic:.0f}\n")
+        f.write(f"source_sha256: {source_digest()}\n")
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("stats_dir")
+    s.add_argument("out")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--bench-log", default=None, help="log of the profiled benchmark run (its JSON line)")
+    t = sub.add_parser("traffic")
+    for k in ("fetch", "write", "copy_fetch", "copy_write"):
+        t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--cmd", required=True)
+    a = ap.parse_args(argv)
+    if a.what == "stats":
+        write_stats(a.stats_dir, a.out, a.cmd, a.bench_log)
+    else:
+        write_traffic(a)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -65,9 +65,13 @@ class HsaStep:
         ops.hsa_block_select(self.geom, q, self.k_act, self.kblk_mean if use_kblk_mean else None, tau,
                              self.blk_count, self.blk_idx, self.blk_mass, self.ws, stream)
 
-    def sparse(self, q, stream=None):
-        ops.hsa_sparse_attn(self.geom, q, self.k_act, self.v_act, self.blk_count, self.blk_idx, self.o_sp, self.ws,
-                            stream)
+    def sparse(self, q, stream=None, kernel_events=None):
+        if kernel_events is None:
+            ops.hsa_sparse_attn(self.geom, q, self.k_act, self.v_act, self.blk_count, self.blk_idx, self.o_sp,
+                                self.ws, stream)
+        else:
+            ops.hsa_sparse_attn_timed(self.geom, q, self.k_act, self.v_act, self.blk_count, self.blk_idx,
+                                      self.o_sp, self.ws, kernel_events[0], kernel_events[1], stream)
 
     def fuse(self, x, w_g, stream=None):
         ops.hsa_fuse(self.geom, x, w_g, None, self.o_lin, self.o_sp, self.out, stream)

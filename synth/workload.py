@@ -141,7 +141,8 @@ class Workload:
             coef = rs.normal(0.0, c.struct_scale, size=(c.n_heads, c.n_qblocks, 8))
             coef -= coef.mean(axis=1, keepdims=True)
             add = np.einsum("hdk,hik->ihd", self.plant.U, coef)          # [nQB][H][d]
-            q += np.repeat(add, c.block, axis=0).astype(np.float32)
+            # every token of query block i gets add[i] (in place, block by block)
+            q.reshape(c.n_qblocks, c.block, c.n_heads, c.head_dim)[...] += add.astype(np.float32)[:, None]
         elif c.structure == "imbalance":
             g = self._hot_dirs()                                          # [H][nQB][d]
             for h in heads:
@@ -168,7 +169,8 @@ class Workload:
             coef = rs.normal(0.0, c.struct_scale, size=(c.n_heads, c.blocks_per_page, 8))
             coef -= coef.mean(axis=1, keepdims=True)
             add = np.einsum("hdk,hbk->bhd", self.plant.U, coef)
-            k += np.repeat(add, c.block, axis=0).astype(np.float32)
+            # every token of key block b gets add[b] (in place, block by block)
+            k.reshape(c.blocks_per_page, c.block, c.n_heads, c.head_dim)[...] += add.astype(np.float32)[:, None]
         elif c.structure == "imbalance" and in_T:
             slot = int(np.searchsorted(self.plant.target_pages, j))
             g = self._hot_dirs()
