@@ -120,6 +120,84 @@ def cpu_baseline(cfg, w, arrays):
             "stages_ms": {k: round(1e3 * v, 1) for k, v in t.items()}}
 
 
+def run_stack(args, cfg):
+    """A whole chunk of a layer stack (every layer x every denoising step),
+    with the configured share of the selected pages starting in pinned host
+    memory and streamed in on a side stream.  The same chunk also runs with
+    every page resident; the difference is the exposed host-to-device time."""
+    import torch
+    from synth import layer_arrays, stack_host_pages
+    from sparse_linear_attention_hsa_amd.ops import make_geom
+    from sparse_linear_attention_hsa_amd.stack import HsaStack, LayerInputs, make_layer_inputs
+
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    geom = make_geom(cfg.n_heads, cfg.head_dim, cfg.frame_h, cfg.frame_w, cfg.frames_per_page,
+                     cfg.query_frames, cfg.tile, cfg.n_sel_pages, cfg.rank, cfg.dtype)
+    host_ids = stack_host_pages(cfg)
+    up = lambda a: torch.from_numpy(a).to(tdt).cuda()
+    streamed, resident = [], []
+    for l in range(cfg.layers):
+        a = layer_arrays(cfg, l, cfg.steps, workers=16)
+        pk = [up(x) for x in a["pages_k"]]
+        pv = [up(x) for x in a["pages_v"]]
+        qs = [up(x) for x in a["q"]]
+        xs = [up(x) for x in a["x"]]
+        e_k, e_v, w_g = up(a["e_k"]), up(a["e_v"]), up(a["w_g"])
+        tau = torch.from_numpy(a["tau"]).cuda()
+        del a
+        lay = make_layer_inputs(geom, pk, pv, host_ids[l], e_k, e_v, w_g, tau, qs, xs)
+        streamed.append(lay)
+        resident.append(LayerInputs(pages_k=pk, pages_v=pv, host_k={}, host_v={}, e_k=e_k, e_v=e_v, w_g=w_g,
+                                    tau=tau, page_kmean=lay.page_kmean, q=lay.q, x=lay.x))
+        print(f"bench: layer {l + 1}/{cfg.layers} ready ({len(host_ids[l])} host pages)", file=sys.stderr, flush=True)
+    max_host = max(len(h) for h in host_ids)
+    stack = HsaStack(geom, cfg.n_pages, cfg.layers, max_host)
+    stream = torch.cuda.current_stream()
+
+    def timed(inputs, k):
+        for _ in range(args.warmup):
+            stack.run_chunk(inputs, cfg.steps, {})
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(k):
+            stack.run_chunk(inputs, cfg.steps, {})
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / k
+
+    ms = timed(streamed, args.steps)
+    ms_res = timed(resident, args.steps)
+    # the host-to-device copies alone: every non-resident page of the chunk, back to back
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for lay in streamed:
+        for n, j in enumerate(sorted(lay.host_k)):
+            stack.stage_k[0][n].copy_(lay.host_k[j], non_blocking=True)
+            stack.stage_v[0][n].copy_(lay.host_v[j], non_blocking=True)
+    b.record(stream)
+    torch.cuda.synchronize()
+    h2d_ms = a.elapsed_time(b)
+    h2d_bytes = sum(2 * cfg.page_tokens * cfg.model_dim * (2 if cfg.dtype == "bf16" else 4) * len(h) for h in host_ids)
+    out = {
+        "metric": METRIC, "value": round(ms, 3), "unit": "ms/chunk", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "layers": cfg.layers, "denoise_steps": cfg.steps, "heads": cfg.n_heads,
+                   "head_dim": cfg.head_dim, "retrieved_tokens": cfg.active_tokens,
+                   "query_tokens": cfg.query_tokens, "history_pages": cfg.n_pages, "block": cfg.block,
+                   "rank": cfg.rank, "host_pages": int(sum(len(h) for h in host_ids))},
+        "ms_per_layer_step": round(ms / (cfg.layers * cfg.steps), 4),
+        "ms_all_resident": round(ms_res, 3),
+        "exposed_h2d_ms": round(ms - ms_res, 3),
+        "h2d_bytes": int(h2d_bytes),
+        "h2d_ms_alone": round(h2d_ms, 3),
+        "h2d_gbs": round(h2d_bytes / (h2d_ms * 1e-3) / 1e9, 1),
+        "staging_slots": stack.n_slots,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +230,8 @@ def main():
     from sparse_linear_attention_hsa_amd.step import HsaStep
 
     cfg = CONFIGS[args.config]
+    if cfg.layers > 1 or cfg.steps > 1:
+        return run_stack(args, cfg)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     w = Workload(cfg)
     s = w.small_inputs()

@@ -130,7 +130,10 @@ M5 = Config(name="m5_bf16_imbalance", n_heads=4, head_dim=128, frame_h=12, frame
             n_sel_pages=4, rank=32, dtype="bf16", structure="imbalance",
             tau=(0.9,) * 4, uniform_heads=1, hot_per_row=2, seed=2005)
 
-CONFIGS = {c.name: c for c in (C0, C1, C2, C3, C4, M1, M2, M3, M4, M5)}
+# Small layer stack: the chunk schedule (projection reuse, host-resident pages
+# streamed through two staging slots) at parity-test size.
+M6 = replace(M1, name="m6_stack", layers=4, steps=2, host_page_frac=0.5, seed=2006)
+CONFIGS = {c.name: c for c in (C0, C1, C2, C3, C4, M1, M2, M3, M4, M5, M6)}
 BY_INDEX = (C0, C1, C2, C3, C4)
 
 for _c in CONFIGS.values():

@@ -235,3 +235,37 @@ class Workload:
 
     def pages(self):
         return [self.page_k(j) for j in range(self.cfg.n_pages)], [self.page_v(j) for j in range(self.cfg.n_pages)]
+
+
+def layer_arrays(cfg: Config, layer: int, n_steps: int, workers: int = 8) -> Dict[str, object]:
+    """All inputs of one layer of a stack, as float32 arrays: pages (generated
+    on a thread pool), the layer's projections, gate weights and thresholds,
+    and the per-step queries and gate inputs."""
+    from concurrent.futures import ThreadPoolExecutor
+    w = Workload(cfg, layer)
+    with ThreadPoolExecutor(max(1, workers)) as ex:
+        pk = list(ex.map(w.page_k, range(cfg.n_pages)))
+        pv = list(ex.map(w.page_v, range(cfg.n_pages)))
+        qs = list(ex.map(w.q, range(n_steps)))
+        xs = list(ex.map(w.x, range(n_steps)))
+    return dict(pages_k=pk, pages_v=pv, e_k=w.e_k(), e_v=w.e_v(), w_g=w.w_g(), tau=w.tau(), q=qs, x=xs,
+                target_pages=w.plant.target_pages)
+
+
+def stack_host_pages(cfg: Config) -> List[np.ndarray]:
+    """Per layer, the page ids that start in pinned host memory (layer stack).
+
+    A seeded round(host_page_frac * layers * n_sel_pages) of the
+    (layer, target page) pairs are chosen over the whole stack (for the
+    30-layer stack: 36 of 120); the target pages are the ones the planted
+    retrieval structure makes the scoring select."""
+    n_pairs = cfg.layers * cfg.n_sel_pages
+    n_host = int(round(cfg.host_page_frac * n_pairs))
+    targets = [Workload(cfg, layer).plant.target_pages for layer in range(cfg.layers)]
+    rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, TID["host"], 1_000_000]))
+    pick = np.sort(rng.choice(n_pairs, size=n_host, replace=False)) if n_host else np.zeros(0, np.int64)
+    out = [[] for _ in range(cfg.layers)]
+    for p in pick:
+        layer, slot = divmod(int(p), cfg.n_sel_pages)
+        out[layer].append(int(targets[layer][slot]))
+    return [np.asarray(sorted(v), dtype=np.int64) for v in out]

@@ -1,0 +1,134 @@
+"""The chunk schedule of a layer stack (several layers x denoising steps).
+
+Page scoring, gather and the linear-branch projection run once per layer,
+in the first step, on that step's queries; later steps reuse them and run
+the linear attention, block selection, sparse branch and fusion on their
+own queries and gate inputs.  Pages of the configured share start in pinned
+host memory and reach the gather through two device staging slots filled on
+a side stream.  The oracle runs every (layer, step) with the first step's
+page selection, and the streamed run must equal a run with every page
+resident, bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import hsa_oracle as orc
+from synth import CONFIGS, layer_arrays, stack_host_pages
+
+from gpu_harness import TOL, assert_close, check_block_selection, geom_of
+
+pytestmark = pytest.mark.gpu
+
+
+def _build(cfg, layers_needed_host=()):
+    """Device inputs of every layer; returns (streamed, resident, arrays of the requested layers)."""
+    from sparse_linear_attention_hsa_amd.stack import LayerInputs, make_layer_inputs
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(tdt).cuda()
+    geom = geom_of(cfg)
+    host_ids = stack_host_pages(cfg)
+    streamed, resident, keep = [], [], {}
+    for l in range(cfg.layers):
+        a = layer_arrays(cfg, l, cfg.steps, workers=16)
+        if l in layers_needed_host:
+            keep[l] = a
+        pk = [up(x) for x in a["pages_k"]]
+        pv = [up(x) for x in a["pages_v"]]
+        qs = [up(x) for x in a["q"]]
+        xs = [up(x) for x in a["x"]]
+        e_k, e_v, w_g = up(a["e_k"]), up(a["e_v"]), up(a["w_g"])
+        tau = torch.from_numpy(a["tau"]).cuda()
+        lay = make_layer_inputs(geom, pk, pv, host_ids[l], e_k, e_v, w_g, tau, qs, xs)
+        streamed.append(lay)
+        resident.append(LayerInputs(pages_k=pk, pages_v=pv, host_k={}, host_v={}, e_k=e_k, e_v=e_v, w_g=w_g,
+                                    tau=tau, page_kmean=lay.page_kmean, q=lay.q, x=lay.x))
+    return geom, host_ids, streamed, resident, keep
+
+
+def _run(cfg, geom, host_ids, inputs, pairs, n_slots=4):
+    """Run one chunk; return per (layer, step) in `pairs`: out, o_lin, o_sp, counts, lists; and per layer the pages."""
+    from sparse_linear_attention_hsa_amd.stack import HsaStack
+    st = HsaStack(geom, cfg.n_pages, cfg.layers, max(len(h) for h in host_ids), n_slots=n_slots)
+    outs = {p: torch.empty(cfg.query_tokens, cfg.n_heads, cfg.head_dim, dtype=inputs[0].q[0].dtype, device="cuda")
+            for p in pairs}
+    cap = {}
+
+    def probe(l, s):
+        if (l, s) in outs:
+            cap[(l, s)] = (st.o_lin.clone(), st.o_sp.clone(), st.blk_count.clone(), st.blk_idx.clone())
+
+    st.run_chunk(inputs, cfg.steps, outs, probe)
+    torch.cuda.synchronize()
+    res = {}
+    for p in pairs:
+        o_lin, o_sp, cnt, idx = (t.cpu().numpy() for t in cap[p])
+        res[p] = dict(out=outs[p].float().cpu().numpy(), o_lin=o_lin, o_sp=o_sp, cnt=cnt, idx=idx)
+    sel = [st.layers[l].sel_pages.cpu().numpy().astype(np.int64) for l in range(cfg.layers)]
+    return res, sel
+
+
+def _check_layer_step(cfg, a, s, gpu_sel, r, rows=None):
+    """Oracle for one (layer, step) with the first step's pages; rows = sampled (h, query block) or all."""
+    B, H = cfg.block, cfg.n_heads
+    sc = orc.score_and_select(a["q"][0], a["pages_k"], cfg.n_sel_pages)
+    if not np.array_equal(gpu_sel, sc["sel"]):
+        assert sc["tie"] and orc.valid_page_selection(sc["alpha"], gpu_sel, cfg.n_sel_pages)
+    k_act = orc.gather_active(a["pages_k"], gpu_sel)
+    v_act = orc.gather_active(a["pages_v"], gpu_sel)
+    q, x = a["q"][s], a["x"][s]
+    bs = orc.block_selection(q, k_act, a["tau"], B)
+    gl = [[r["idx"][h, i, :r["cnt"][h, i]].astype(np.int64) for i in range(cfg.n_qblocks)] for h in range(H)]
+    check_block_selection(bs, gl, a["tau"])
+    ktil, vtil = orc.project(a["e_k"], k_act), orc.project(a["e_v"], v_act)
+    qblocks = range(cfg.n_qblocks) if rows is None else sorted({i for _, i in rows})
+    tok = np.concatenate([np.arange(i * B, (i + 1) * B) for i in qblocks])
+    o_lin_ref = orc.linear_attention(q[tok], ktil, vtil)
+    o_sp_ref = np.empty((len(tok), H, cfg.head_dim))
+    for h in range(H):
+        for n, i in enumerate(qblocks):
+            o_sp_ref[n * B:(n + 1) * B, h, :] = orc.sparse_row(q[i * B:(i + 1) * B, h, :], k_act[h], v_act[h],
+                                                               gl[h][i], B)
+    out_ref = orc.fuse(x[tok], a["w_g"], o_lin_ref, o_sp_ref)
+    assert_close("o_lin", r["o_lin"][tok], o_lin_ref, cfg)
+    assert_close("o_sp", r["o_sp"][tok], o_sp_ref, cfg)
+    assert_close("out", r["out"][tok], out_ref, cfg)
+
+
+@pytest.mark.parametrize("n_slots", [2, 4])
+def test_stack_small_every_layer_step(n_slots):
+    cfg = CONFIGS["m6_stack"]
+    print(f"\n[stack] {cfg.name}: {cfg.layers} layers x {cfg.steps} steps, {n_slots} staging slots, host pages "
+          f"{[h.tolist() for h in stack_host_pages(cfg)]}", flush=True)
+    geom, host_ids, streamed, resident, keep = _build(cfg, layers_needed_host=range(cfg.layers))
+    pairs = [(l, s) for l in range(cfg.layers) for s in range(cfg.steps)]
+    got, sel = _run(cfg, geom, host_ids, streamed, pairs, n_slots=n_slots)
+    ref, sel_r = _run(cfg, geom, host_ids, resident, pairs)
+    for p in pairs:
+        for k in ("out", "o_lin", "o_sp", "cnt", "idx"):
+            assert np.array_equal(got[p][k], ref[p][k]), f"streamed != resident at {p} ({k})"
+    for l in range(cfg.layers):
+        assert np.array_equal(sel[l], sel_r[l])
+        for s in range(cfg.steps):
+            _check_layer_step(cfg, keep[l], s, sel[l], got[(l, s)])
+
+
+def test_stack_c4_sampled():
+    cfg = CONFIGS["c4_stack"]
+    last = cfg.layers - 1
+    print(f"\n[stack] {cfg.name}: {cfg.layers} layers x {cfg.steps} steps, "
+          f"{sum(len(h) for h in stack_host_pages(cfg))} host pages", flush=True)
+    geom, host_ids, streamed, _, keep = _build(cfg, layers_needed_host=(0, last))
+    pairs = [(0, 0), (0, cfg.steps - 1), (last, 0), (last, cfg.steps - 1)]
+    got, sel = _run(cfg, geom, host_ids, streamed, pairs)
+    rng = np.random.default_rng(11)
+    for (l, s) in pairs:
+        cnt = got[(l, s)]["cnt"]
+        flat = cnt.reshape(-1)
+        pick = {int(np.argmax(flat)), int(np.argmin(flat))} | set(int(i) for i in rng.choice(flat.size, 3, replace=False))
+        rows = [(i // cfg.n_qblocks, i % cfg.n_qblocks) for i in pick]
+        print(f"  layer {l} step {s}: pages {sel[l].tolist()} (host {host_ids[l].tolist()}), "
+              f"selected pairs {int(flat.sum())}", flush=True)
+        _check_layer_step(cfg, keep[l], s, sel[l], got[(l, s)], rows=rows)
