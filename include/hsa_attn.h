@@ -150,6 +150,9 @@ hsa_rc hsa_gather_pages(const hsa_geom* geom, const void* const* page_k, const v
  *  o_lin        [Lq][H][d] float32 out (untouched with HSA_LIN_PROJ_ONLY).
  *  flags        0, HSA_LIN_REUSE_PROJ or HSA_LIN_PROJ_ONLY.
  *  With HSA_LIN_REUSE_PROJ, k_act, v_act, e_k and e_v may be NULL.
+ *  ws           workspace of ws_bytes >= hsa_workspace_bytes(geom, 1), with
+ *               every flag (the projection keeps its per-slice partial sums
+ *               there, the attention its element-type copies of Ktil/Vtil).
  * ------------------------------------------------------------------------- */
 hsa_rc hsa_linear_branch(const hsa_geom* geom, const void* q, const void* k_act, const void* v_act,
                          const void* e_k, const void* e_v, void* k_proj, void* v_proj, float* o_lin,

@@ -7,11 +7,11 @@
 // Two kernels:
 //  * pool:   mean of every B-token query block (and key block, unless the
 //            gather already produced the key-block means), float32;
-//  * select: one workgroup per (head, query block): pooled logits
-//            qbar.kbar_j/sqrt(d), softmax over the key blocks, a bitonic sort
-//            in LDS on (mass descending, block id ascending), a prefix sum of
-//            the sorted masses, the first prefix that reaches tau_h, and the
-//            selected ids compacted in ascending order.
+//  * select: pooled logits qbar.kbar_j/sqrt(d) of 16 query blocks at a time
+//            on the matrix cores, then per (head, query block) one wave:
+//            softmax over the key blocks, the minimal mass-ordered prefix that
+//            reaches tau_h (found by a search over the mass values rather
+//            than a sort), and the selected ids in ascending order.
 // Everything is float32 and in a fixed order, so the selection is bitwise
 // reproducible; no atomics.
 #include "common.h"
@@ -21,7 +21,6 @@ namespace hsa {
 namespace {
 
 constexpr int kPoolThreads = 256;
-constexpr int kSelThreads = 256;
 
 // grid.x = H * (nQB + nKB_to_pool): the first H*nQB workgroups pool query
 // blocks, the rest pool key blocks of k_act.
@@ -76,171 +75,204 @@ __global__ __launch_bounds__(kPoolThreads) void pool_blocks_kernel(
   }
 }
 
-// Block-wide inclusive scan of one float per thread (Hillis-Steele in LDS).
-__device__ float block_scan_incl(float v, float* buf) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int o = 1; o < kSelThreads; o <<= 1) {
-    const float a = t >= o ? buf[t - o] : 0.f;
-    __syncthreads();
-    buf[t] += a;
-    __syncthreads();
-  }
-  return buf[t];
-}
-
-__device__ int block_scan_incl_int(int v, int* buf) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int o = 1; o < kSelThreads; o <<= 1) {
-    const int a = t >= o ? buf[t - o] : 0;
-    __syncthreads();
-    buf[t] += a;
-    __syncthreads();
-  }
-  return buf[t];
-}
+// Pooled logits s_ij = qbar_i . kbar_j / sqrt(d) on the float64 matrix
+// cores: products of float32 values are exact in float64 and the sums round
+// at 2^-53, so each logit is the float32 rounding of the exact dot product --
+// the selection does not depend on a summation order.  A workgroup (4 waves)
+// takes 64 key blocks x 16 query blocks of one head; wave w computes the
+// 16 x 16 tile of key blocks 16*(4x + w) .. as S^T = Kbar Qbar^T (keys on
+// the rows, one query per accumulator column); lane (g, c) supplies key row c
+// and query column c at contraction elements 16s + 4g .. 16s + 4g + 3 of step s.
+// grid (ceil(nKB/64), ceil(nQB/16), H); logits [H][nQB][nKB].
+constexpr int kLogitThreads = 4 * kWave;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
+__global__ __launch_bounds__(kLogitThreads) void block_logits_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar, int nQB, int nKB, float scale,
+    float* __restrict__ logits) {
+  const int h = blockIdx.z, q0 = blockIdx.y * 16;
+  const int lane = threadIdx.x % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int g = lane >> 4, c = lane & 15;
+  const int kt = blockIdx.x * 4 + w;
+  const int key = kt * 16 + c, qi = q0 + c;
+  const float4* kp = reinterpret_cast<const float4*>(kbar + ((size_t)h * nKB + (key < nKB ? key : 0)) * D);
+  const float4* qp = reinterpret_cast<const float4*>(qbar + ((size_t)h * nQB + (qi < nQB ? qi : 0)) * D);
+  // every operand chunk is loaded before the first product (one memory latency)
+  uint4 av[D / 16], bv[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    av[st] = ld16_masked(kp + 4 * st + g, key < nKB);
+    bv[st] = ld16_masked(qp + 4 * st + g, qi < nQB);
+  }
+  f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    const uint4 a = av[st], b = bv[st];
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)__uint_as_float(a.x), (double)__uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)__uint_as_float(a.y), (double)__uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)__uint_as_float(a.z), (double)__uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)__uint_as_float(a.w), (double)__uint_as_float(b.w), acc, 0, 0, 0);
+  }
+  // the float64 16x16x4 product leaves D[g + 4i][c] in register i of lane
+  // (g, c): key blocks 16*kt + g + 4i for query block q0 + c
+  if (qi < nQB) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kk = kt * 16 + g + 4 * i;
+      if (kk < nKB) logits[((size_t)h * nQB + qi) * nKB + kk] = (float)(acc[i] * (double)scale);
+    }
+  }
+}
+
+// Selection: one wave per (head, query block) row, kSelRows rows per
+// workgroup.  Lane l holds the blocks j = l + 64k in registers: softmax with
+// wave-wide max and sum; then the boundary mass s_n of the minimal prefix
+// (masses in decreasing order) whose sum reaches tau, found as the largest
+// float bit pattern b with F(b) = sum of the masses whose bits are >= b still
+// >= tau (31 halving steps; F only changes at actual masses, so b is the
+// pattern of s_n).  Every block above s_n is kept, and of the blocks equal to
+// s_n the lowest ids until the sum reaches tau -- the (mass descending, id
+// ascending) prefix rule.  The kept ids are compacted in ascending order with
+// ballots; the rest of the row is padded with -1.
+constexpr int kSelRows = 4;
+constexpr int kSelThreads = kSelRows * kWave;
+// NPL: blocks per lane, a fixed bucket >= ceil(nKB/64) so the per-block loops
+// carry no run-time guards; the padding blocks have mass 0.
+
+// Wave-wide reductions with DPP moves (no LDS round trip): two quad
+// permutations and the half-row and row mirrors leave every lane with the
+// total of its 16-lane row; the four row totals are read as scalars.  The
+// order is fixed, so results are reproducible.
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL> __device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// value of lane l of a float (the readlane builtin moves 32-bit integers)
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<kQuadSwap1>(v);
+  v += dpp_f<kQuadSwap2>(v);
+  v += dpp_f<kRowHalfMirror>(v);
+  v += dpp_f<kRowMirror>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<kQuadSwap1>(v));
+  v = fmaxf(v, dpp_f<kQuadSwap2>(v));
+  v = fmaxf(v, dpp_f<kRowHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kRowMirror>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+__device__ __forceinline__ int wave_sum_int(int v) {
+  v += dpp_i<kQuadSwap1>(v);
+  v += dpp_i<kQuadSwap2>(v);
+  v += dpp_i<kRowHalfMirror>(v);
+  v += dpp_i<kRowMirror>(v);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
+template <int NPL>
 __global__ __launch_bounds__(kSelThreads) void select_rows_kernel(
-    const float* __restrict__ qbar, const float* __restrict__ kbar, const float* __restrict__ tau,
-    int nQB, int nKB, int n2, float scale, int32_t* __restrict__ blk_count, int32_t* __restrict__ blk_idx,
-    float* __restrict__ blk_mass) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint64_t* key = reinterpret_cast<uint64_t*>(smem);                 // [n2] sort keys
-  float* mval = reinterpret_cast<float*>(smem + (size_t)n2 * 8);     // [nKB] logits, then masses
-  int* flag = reinterpret_cast<int*>(mval + nKB);                    // [nKB]
-  __shared__ float q_s[D];
-  __shared__ float fbuf[kSelThreads];
-  __shared__ int ibuf[kSelThreads];
-  __shared__ float red[kSelThreads / kWave];
-  __shared__ int nsel_s;
-
-  const int row = blockIdx.x;  // h * nQB + i
+    const float* __restrict__ logits, const float* __restrict__ tau, int rows, int nQB, int nKB,
+    int32_t* __restrict__ blk_count, int32_t* __restrict__ blk_idx, float* __restrict__ blk_mass) {
+  const int lane = threadIdx.x % kWave;
+  const int row = blockIdx.x * kSelRows + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (row >= rows) return;
   const int h = row / nQB;
-  const int t = threadIdx.x, lane = t % kWave, wv = t / kWave;
-  const float th = tau[h];
+  const float* lr = logits + (size_t)row * nKB;
 
-  for (int c = t; c < D; c += kSelThreads) q_s[c] = qbar[(size_t)row * D + c];
-  __syncthreads();
-
-  // pooled logits
-  const float* kb = kbar + (size_t)h * nKB * D;
+  // tau <= 0 (or NaN) keeps one block: the first prefix already reaches it
+  const float th = fmaxf(tau[h], 1.17549435e-38f);
+  float m[NPL];
   float lmax = -INFINITY;
-  for (int j = t; j < nKB; j += kSelThreads) {
-    const float4* kr = reinterpret_cast<const float4*>(kb + (size_t)j * D);
-    float s = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < D / 4; ++c) {
-      const float4 k4 = kr[c];
-      s += q_s[4 * c] * k4.x + q_s[4 * c + 1] * k4.y + q_s[4 * c + 2] * k4.z + q_s[4 * c + 3] * k4.w;
-    }
-    s *= scale;
-    mval[j] = s;
-    lmax = fmaxf(lmax, s);
-  }
-  // block max
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, o));
-  if (lane == 0) red[wv] = lmax;
-  __syncthreads();
-  float gmax = red[0];
-  for (int k = 1; k < kSelThreads / kWave; ++k) gmax = fmaxf(gmax, red[k]);
-  __syncthreads();
-  // exp and sum (per-thread sequential, then a fixed tree)
+  for (int k = 0; k < NPL; ++k) {
+    const int j = k * kWave + lane;
+    const float v = lr[j < nKB ? j : nKB - 1];  // always issued, in bounds
+    m[k] = j < nKB ? v : -INFINITY;
+    lmax = fmaxf(lmax, m[k]);
+  }
+  const float gmax = wave_max(lmax);
   float lsum = 0.f;
-  for (int j = t; j < nKB; j += kSelThreads) {
-    const float e = expf(mval[j] - gmax);
-    mval[j] = e;
-    lsum += e;
-  }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
-  if (lane == 0) red[wv] = lsum;
-  __syncthreads();
-  float gsum = 0.f;
-  for (int k = 0; k < kSelThreads / kWave; ++k) gsum += red[k];
-  const float inv = 1.f / gsum;
-  for (int j = t; j < n2; j += kSelThreads) {
-    if (j < nKB) {
-      const float m = mval[j] * inv;
-      mval[j] = m;
-      // non-negative floats order like their bit patterns; the low word puts
-      // lower ids first among equal masses when sorting descending
-      key[j] = ((uint64_t)__float_as_uint(m) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)j);
-      flag[j] = 0;
-      if (blk_mass) blk_mass[(size_t)row * nKB + j] = m;
-    } else {
-      key[j] = 0;  // padding sorts last
-    }
+  for (int k = 0; k < NPL; ++k) {
+    const int j = k * kWave + lane;
+    m[k] = j < nKB ? expf(m[k] - gmax) : 0.f;
+    lsum += m[k];
   }
-  __syncthreads();
-
-  // bitonic sort, descending
-  for (int k = 2; k <= n2; k <<= 1) {
-    for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      for (int i = t; i < n2; i += kSelThreads) {
-        const int ixj = i ^ jj;
-        if (ixj > i) {
-          const uint64_t a = key[i], b = key[ixj];
-          const bool desc = (i & k) == 0;
-          if (desc ? (a < b) : (a > b)) {
-            key[i] = b;
-            key[ixj] = a;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-
-  // prefix sums of the sorted masses: thread t owns a contiguous range
-  const int per = (nKB + kSelThreads - 1) / kSelThreads;
-  const int lo = min(nKB, t * per), hi = min(nKB, lo + per);
-  float local = 0.f;
-  for (int p = lo; p < hi; ++p) local += __uint_as_float((uint32_t)(key[p] >> 32));
-  const float incl = block_scan_incl(local, fbuf);
-  float run = incl - local;
-  int first = nKB;  // first position whose prefix reaches tau
-  if (th < 1.f) {
-    for (int p = lo; p < hi; ++p) {
-      run += __uint_as_float((uint32_t)(key[p] >> 32));
-      if (run >= th) {
-        first = p;
-        break;
-      }
-    }
-  }
-  // minimum over threads of `first`
-  int f = first;
+  const float inv = 1.f / wave_sum(lsum);
+  float ltot = 0.f;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) f = min(f, __shfl_xor(f, o));
-  if (lane == 0) ibuf[wv] = f;
-  __syncthreads();
-  if (t == 0) {
-    int m = ibuf[0];
-    for (int k = 1; k < kSelThreads / kWave; ++k) m = min(m, ibuf[k]);
-    nsel_s = th >= 1.f ? nKB : (m < nKB ? m + 1 : nKB);
+  for (int k = 0; k < NPL; ++k) {
+    const int j = k * kWave + lane;
+    m[k] *= inv;  // padding blocks stay 0
+    ltot += m[k];
+    if (blk_mass && j < nKB) blk_mass[(size_t)row * nKB + j] = m[k];
   }
-  __syncthreads();
-  const int nsel = nsel_s;
-  for (int p = t; p < nsel; p += kSelThreads) flag[0xFFFFFFFFu - (uint32_t)(key[p] & 0xFFFFFFFFu)] = 1;
-  __syncthreads();
+  const float total = wave_sum(ltot);
 
-  // compact the selected ids in ascending order
-  int cnt = 0;
-  for (int j = lo; j < hi; ++j) cnt += flag[j];
-  const int cincl = block_scan_incl_int(cnt, ibuf);
-  int pos = cincl - cnt;
+  // boundary: b_lo = largest bit pattern with F(b) >= th
+  bool all = th >= 1.f || total < th;
+  uint32_t b_lo = 0;
+  int k_t = 0;  // tied blocks to keep
+  if (!all) {
+    uint32_t hi = 0x7F800000u;  // F(+inf) = 0 < th  (th > 0 here or the max is taken)
+    while (hi - b_lo > 1) {
+      const uint32_t mid = b_lo + ((hi - b_lo) >> 1);
+      float part = 0.f;
+#pragma unroll
+      for (int k = 0; k < NPL; ++k) part += __float_as_uint(m[k]) >= mid ? m[k] : 0.f;
+      if (wave_sum(part) >= th) b_lo = mid;
+      else hi = mid;
+    }
+    float sgt = 0.f;
+    int nties = 0;
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      const int j = k * kWave + lane;
+      const uint32_t b = __float_as_uint(m[k]);
+      if (j < nKB && b > b_lo) sgt += m[k];
+      if (j < nKB && b == b_lo) ++nties;
+    }
+    const float sum_gt = wave_sum(sgt);
+    nties = wave_sum_int(nties);
+    const float v = __uint_as_float(b_lo);
+    int need = v > 0.f ? (int)ceilf((th - sum_gt) / v) : 1;
+    k_t = max(1, min(nties, need));
+  }
+
+  // compaction in ascending id order
   int32_t* out = blk_idx + (size_t)row * nKB;
-  for (int j = lo; j < hi; ++j) {
-    if (flag[j]) out[pos++] = j;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int base = 0, tie_base = 0;
+#pragma unroll
+  for (int k = 0; k < NPL; ++k) {
+    const int j = k * kWave + lane;
+    const uint32_t b = __float_as_uint(m[k]);
+    const bool valid = j < nKB;
+    const bool tie = valid && !all && b == b_lo;
+    const uint64_t tb = __ballot(tie);
+    const int tie_rank = tie_base + __popcll(tb & below);
+    tie_base += __popcll(tb);
+    const bool keep = valid && (all || b > b_lo || (tie && tie_rank < k_t));
+    const uint64_t kb = __ballot(keep);
+    if (keep) out[base + __popcll(kb & below)] = j;
+    base += __popcll(kb);
   }
-  __syncthreads();
-  for (int p = nsel + t; p < nKB; p += kSelThreads) out[p] = -1;
-  if (t == 0) blk_count[row] = nsel;
+  for (int p = base + lane; p < nKB; p += kWave) out[p] = -1;
+  if (lane == 0) blk_count[row] = base;
 }
 
 template <typename T, int D>
@@ -252,11 +284,24 @@ void launch_select(const Dims& s, const void* q, const void* k_act, const float*
   hipLaunchKernelGGL((pool_blocks_kernel<T, D>), dim3(s.H * (s.nQB + pool_k)), dim3(kPoolThreads), 0, st,
                      reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act), s.H, s.B, s.L, s.nQB,
                      s.nKB, qbar, kbar);
-  int n2 = 1;
-  while (n2 < s.nKB) n2 <<= 1;
-  const size_t smem = (size_t)n2 * 8 + (size_t)s.nKB * 8;
-  hipLaunchKernelGGL((select_rows_kernel<D>), dim3(s.rows), dim3(kSelThreads), smem, st, qbar, kbar, tau,
-                     s.nQB, s.nKB, n2, 1.f / sqrtf((float)s.d), cnt, idx, mass);
+  float* logits = reinterpret_cast<float*>(ws + w.sel_logit);
+  hipLaunchKernelGGL((block_logits_kernel<D>), dim3((s.nKB + 63) / 64, (s.nQB + 15) / 16, s.H), dim3(kLogitThreads),
+                     0, st, qbar, kbar, s.nQB, s.nKB, 1.f / sqrtf((float)s.d), logits);
+  const int npl = (s.nKB + kWave - 1) / kWave;
+  const dim3 grid((s.rows + kSelRows - 1) / kSelRows);
+#define HSA_SEL_CASE(N)                                                                                  \
+  if (npl <= N) {                                                                                        \
+    hipLaunchKernelGGL(select_rows_kernel<N>, grid, dim3(kSelThreads), 0, st, logits, tau, s.rows, s.nQB, s.nKB, \
+                       cnt, idx, mass);                                                                  \
+    return;                                                                                              \
+  }
+  HSA_SEL_CASE(4)
+  HSA_SEL_CASE(8)
+  HSA_SEL_CASE(12)
+  HSA_SEL_CASE(16)
+  HSA_SEL_CASE(24)
+  HSA_SEL_CASE(32)
+#undef HSA_SEL_CASE
 }
 
 }  // namespace

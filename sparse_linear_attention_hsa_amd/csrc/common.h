@@ -77,6 +77,14 @@ template <> __device__ __forceinline__ uint4 pack16<bf16_t>(const float* in) {
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// 16-byte load that is always issued, zeroed where `ok` is false.  The
+// address must be valid in every lane (callers clamp it); a load under a
+// per-lane condition is otherwise split into dword loads, each waited for.
+__device__ __forceinline__ uint4 ld16_masked(const void* p, bool ok) {
+  const uint4 v = ld16(p);
+  return ok ? v : make_uint4(0, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // 16x16 matrix-core step.  Lane l = 16*g + c (g = l/16 in 0..3, c = l%16)
 // supplies one 16-byte chunk of A row c and one of B column c; both chunks
@@ -141,6 +149,29 @@ __device__ __forceinline__ float sum4g(float v) {
 }
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// Direct global->LDS loads: one wave instruction moves 64 lanes x 16 bytes
+// into 1 KB of contiguous LDS (lane l -> bytes 16l..16l+15 of the wave base).
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void load_lds16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+
+// wait until this wave's direct-to-LDS (and other vector memory) loads have landed
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Swizzle of row-major operand tiles in LDS: the 16-byte chunk c of row rho
+// sits in slot c ^ kswz(rho).  A matrix-core A operand is read as 16 rows
+// (perm_row(kt, c) for lanes c = 0..15, see above) at one chunk index; the
+// swizzle sends those 16 reads to distinct banks.
+template <typename T> __device__ __forceinline__ int kswz(int rho, int cpr);
+template <> __device__ __forceinline__ int kswz<bf16_t>(int rho, int cpr) {
+  return ((rho & 3) | (((rho >> 3) & 3) << 2)) & (cpr - 1);
+}
+template <> __device__ __forceinline__ int kswz<float>(int rho, int cpr) { return rho & 15 & (cpr - 1); }
 
 // 2^x with the hardware instruction (no range fix-ups): used for softmax
 // weights whose arguments are <= 8 here; results below the float range flush

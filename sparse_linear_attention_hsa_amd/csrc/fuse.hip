@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kFuseThreads) void fuse_kernel(
       for (int n = 0; n < kMaxGateTiles; ++n) {
         if (n < ntile) {
           const int col = 16 * n + c;
-          const uint4 a = col < G2 ? ld16(w_g + (size_t)col * Dm + k0 + g * E) : make_uint4(0, 0, 0, 0);
+          const uint4 a = ld16_masked(w_g + (size_t)min(col, G2 - 1) * Dm + k0 + g * E, col < G2);
           Mma<T>::run(acc[n], a, b);
         }
       }

@@ -68,6 +68,17 @@ ProjPlan proj_plan(const Dims& s) {
   return p;
 }
 
+AttendPlan attend_plan(const Dims& s) {
+  AttendPlan p;
+  p.units = cdiv(s.Lq, 32);
+  // one round of workgroups over the 256 CUs (a workgroup holds a head's
+  // projected keys in LDS, so one fits per CU at the largest rank)
+  const int per_head = std::max(1, std::min(p.units, 256 / std::max(1, s.H)));
+  p.units_per_wg = cdiv(p.units, per_head);
+  p.wg_per_head = cdiv(p.units, p.units_per_wg);
+  return p;
+}
+
 SparsePlan sparse_plan(const Dims& s) {
   SparsePlan p;
   p.granules_per_block = s.B / 16;
@@ -93,11 +104,16 @@ WsLayout ws_layout(const Dims& s, int n_pages) {
   // linear
   ProjPlan pp = proj_plan(s);
   w.lin_partial = 0;
-  w.lin_end = align256((size_t)pp.splits * 2 * s.H * pp.rtiles * 16 * s.d * 4);
+  const size_t kbytes = (size_t)s.H * pp.rpad * s.d * s.esize;  // one [H][rpad][d] operand
+  w.lin_khi = align256((size_t)pp.splits * 2 * s.H * pp.rtiles * 16 * s.d * 4);
+  w.lin_klo = align256(w.lin_khi + kbytes);
+  w.lin_vt = align256(w.lin_klo + kbytes);
+  w.lin_end = align256(w.lin_vt + kbytes);
   // select
   w.sel_qbar = 0;
   w.sel_kbar = align256((size_t)s.H * s.nQB * s.d * 4);
-  w.sel_end = align256(w.sel_kbar + (size_t)s.H * s.nKB * s.d * 4);
+  w.sel_logit = align256(w.sel_kbar + (size_t)s.H * s.nKB * s.d * 4);
+  w.sel_end = align256(w.sel_logit + (size_t)s.rows * s.nKB * 4);
   // sparse
   SparsePlan qp = sparse_plan(s);
   w.sp_items = 0;

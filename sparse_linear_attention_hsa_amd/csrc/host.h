@@ -38,6 +38,15 @@ struct ProjPlan {
 };
 ProjPlan proj_plan(const Dims& s);
 
+// Linear-branch attention split: units of 32 queries of one head; a
+// workgroup takes a run of units_per_wg of them.
+struct AttendPlan {
+  int units;         // ceil(Lq / 32) per head
+  int units_per_wg;
+  int wg_per_head;
+};
+AttendPlan attend_plan(const Dims& s);
+
 // Sparse-branch segmentation of the selected-block rows.
 struct SparsePlan {
   int granules_per_block;  // B / 16
@@ -54,9 +63,9 @@ struct WsLayout {
   // score
   size_t score_partial, score_qbar, score_kbar, score_end;
   // linear
-  size_t lin_partial, lin_end;
+  size_t lin_partial, lin_khi, lin_klo, lin_vt, lin_end;
   // select
-  size_t sel_qbar, sel_kbar, sel_end;
+  size_t sel_qbar, sel_kbar, sel_logit, sel_end;
   // sparse
   size_t sp_items, sp_rowinfo, sp_meta, sp_part_o, sp_part_ml, sp_end;
   size_t total;

@@ -22,7 +22,6 @@
 namespace hsa {
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 // 32-bit LDS address of a pointer into shared memory
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -310,156 +309,199 @@ __global__ __launch_bounds__(256) void lin_reduce_kernel(const float* __restrict
   }
 }
 
-// Attention over the r projected keys.  A workgroup (4 waves x 2 query tiles
-// = 128 queries of one head) walks the rank axis in chunks of KS rows; each
-// chunk of Ktil (as a bf16 high/low pair, so the logits keep float32-like
-// precision) and of Vtil^T (bf16) is staged once in LDS, double buffered, and
-// shared by all 128 queries; an online softmax runs over the chunks.  Chunk
-// rows past r are zero and masked.
-constexpr int kAttQT = 2;                      // query tiles per wave
-constexpr int kAttThreads = 256;               // 4 waves
-constexpr int kAttRows = 4 * kAttQT * 16;      // queries per workgroup
+// Operands of the attention over the rank axis, prepared once per call from
+// the float32 projections: Ktil as element-type rows [H][rpad][D] (for bf16 a
+// high part plus the bf16 rounding of the remainder, so the two products
+// together keep float32-like logits) and Vtil^T as [H][D][rpad]; rows and
+// columns past r are zero.  grid (ceil(rpad*D/256), H, 2): z = 0 Ktil, 1 Vtil^T.
+template <typename T>
+__global__ __launch_bounds__(256) void lin_prep_kernel(const float* __restrict__ k_proj,
+                                                       const float* __restrict__ v_proj, int D, int r, int rpad,
+                                                       T* __restrict__ khi, T* __restrict__ klo, T* __restrict__ vt) {
+  const int h = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= rpad * D) return;
+  if (blockIdx.z == 0) {
+    const int rr = e / D, col = e % D;
+    const float v = rr < r ? k_proj[((size_t)h * r + rr) * D + col] : 0.f;
+    const T hi = from_f32<T>(v);
+    khi[(size_t)h * rpad * D + e] = hi;
+    if (sizeof(T) == 2) klo[(size_t)h * rpad * D + e] = from_f32<T>(v - to_f32<T>(hi));
+  } else {
+    const int col = e / rpad, rr = e % rpad;
+    const float v = rr < r ? v_proj[((size_t)h * D + col) * r + rr] : 0.f;
+    vt[(size_t)h * D * rpad + e] = from_f32<T>(v);
+  }
+}
+
+// Attention over the r projected keys.  A workgroup (8 waves) takes a run of
+// 32-query units of one head.  It first stages the head's whole Ktil (and
+// for bf16 its low part) in LDS with direct loads, swizzled by kswz, behind a
+// single barrier; then every wave walks its units independently: S^T =
+// Ktil Q^T chunk by chunk over the rank axis (keys on the rows, one query
+// per accumulator column), an online softmax, and O^T += Vtil^T P^T with the
+// Vtil^T operand read straight from memory (a head's Vtil^T is 64 KB and
+// stays in L2), one chunk ahead.  Chunk rows past r are masked.
+constexpr int kAttWaves = 8;
+constexpr int kAttThreads = kAttWaves * kWave;
+constexpr int kAttMaxRank = 256;
+constexpr int kAttUnit = 32;  // queries per unit: two 16-row tiles share every Ktil operand read
 
 template <typename T, int D>
-__global__ __launch_bounds__(kAttThreads) void lin_attend_kernel(
-    const T* __restrict__ q, const float* __restrict__ k_proj, const float* __restrict__ v_proj, int H, int Lq,
-    int r, float scale_log2, float* __restrict__ o_lin) {
+__global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lin_attend_kernel(
+    const T* __restrict__ q, const T* __restrict__ khi, const T* __restrict__ klo, const T* __restrict__ vt, int H,
+    int Lq, int r, int rpad, int units_per_wg, float scale_log2, float* __restrict__ o_lin) {
   constexpr int E = Vec<T>::N;
   constexpr int KS = Mma<T>::K;        // rank rows per chunk (= one PV contraction step)
   constexpr int GPS = KS / 16;         // 16-row tiles per chunk
+  constexpr int CPR = D / E;           // 16-byte chunks per Ktil row
   constexpr int DSTEPS = D / KS;
   constexpr int DT = D / 16;
+  constexpr int QT = kAttUnit / 16;
   constexpr bool SPLIT = sizeof(T) == 2;
-  constexpr int KSTR = D + E;          // padded LDS rows (elements)
-  constexpr int VSTR = KS + E;
-  __shared__ __align__(16) T k_hi[2][KS * KSTR];
-  __shared__ __align__(16) T k_lo[2][SPLIT ? KS * KSTR : E];
-  __shared__ __align__(16) T v_t[2][D * VSTR];
+  constexpr int ROWB = D * (int)sizeof(T);
+  constexpr int RPI = 1024 / ROWB;     // Ktil rows per direct-load instruction
+  constexpr int PART = kAttMaxRank * ROWB;
+  constexpr bool PREFETCH_V = SPLIT;   // the float32 variant has no registers to spare
+  __shared__ __align__(1024) unsigned char lds_k[SPLIT ? 2 * PART : PART];
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g = lane >> 4, c = lane & 15;
   const int h = blockIdx.y;
-  const int q0 = blockIdx.x * kAttRows + w * kAttQT * 16;
-  const float* kp = k_proj + (size_t)h * r * D;
-  const float* vp = v_proj + (size_t)h * D * r;
-  const int nchunk = (r + KS - 1) / KS;
+  const int nchunk = rpad / KS;
 
-  uint4 qreg[kAttQT][DSTEPS];
+  // stage Ktil (high and low parts) of head h
+  const int ninst = rpad / RPI;
 #pragma unroll
-  for (int t = 0; t < kAttQT; ++t) {
-    const int qrow = q0 + 16 * t + c;
-#pragma unroll
-    for (int s = 0; s < DSTEPS; ++s)
-      qreg[t][s] = qrow < Lq ? ld16(q + ((size_t)qrow * H + h) * D + (4 * s + g) * E) : make_uint4(0, 0, 0, 0);
-  }
-
-  // staging: Ktil rows r0..r0+KS-1 (all D columns) and Vtil^T columns r0..r0+KS-1
-  auto stage = [&](int ch, int buf) {
-    const int r0 = ch * KS;
-    for (int e = tid; e < KS * (D / 4); e += kAttThreads) {
-      const int rr = e / (D / 4), c4 = e % (D / 4);
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (r0 + rr < r) v = reinterpret_cast<const float4*>(kp + (size_t)(r0 + rr) * D)[c4];
-      const float f[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const T hi = from_f32<T>(f[x]);
-        k_hi[buf][rr * KSTR + 4 * c4 + x] = hi;
-        if (SPLIT) k_lo[buf][rr * KSTR + 4 * c4 + x] = from_f32<T>(f[x] - to_f32<T>(hi));
-      }
+  for (int part = 0; part < (SPLIT ? 2 : 1); ++part) {
+    const T* src = (part ? klo : khi) + (size_t)h * rpad * D;
+    for (int i = w; i < ninst; i += kAttWaves) {
+      const int row = i * RPI + lane / CPR;
+      const int chunk = (lane % CPR) ^ kswz<T>(row, CPR);
+      load_lds16(src + (size_t)row * D + chunk * E, lds_k + part * PART + i * 1024);
     }
-    for (int e = tid; e < D * KS; e += kAttThreads) {
-      const int dr = e / KS, rr = e % KS;
-      const float v = r0 + rr < r ? vp[(size_t)dr * r + r0 + rr] : 0.f;
-      v_t[buf][dr * VSTR + rr] = from_f32<T>(v);
-    }
-  };
-
-  f32x4 o[kAttQT][DT];
-  float m_run[kAttQT], l_run[kAttQT];
-#pragma unroll
-  for (int t = 0; t < kAttQT; ++t) {
-    m_run[t] = -INFINITY;
-    l_run[t] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-
-  stage(0, 0);
+  wait_vm();
   __syncthreads();
-  for (int ch = 0; ch < nchunk; ++ch) {
-    const int buf = ch & 1;
-    if (ch + 1 < nchunk) stage(ch + 1, buf ^ 1);
-    f32x4 sacc[kAttQT][GPS];
+
+  const int units = (Lq + kAttUnit - 1) / kAttUnit;
+  const int u_begin = blockIdx.x * units_per_wg;
+  const int u_end = min(units, u_begin + units_per_wg);
+  const T* vh = vt + (size_t)h * D * rpad;
+  for (int u = u_begin + w; u < u_end; u += kAttWaves) {
+    const int qbase = u * kAttUnit;
+    uint4 qreg[QT][DSTEPS];
 #pragma unroll
-    for (int t = 0; t < kAttQT; ++t)
+    for (int t = 0; t < QT; ++t) {
+      const int qrow = qbase + 16 * t + c;
 #pragma unroll
-      for (int kt = 0; kt < GPS; ++kt) sacc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < DSTEPS; ++s)
+        qreg[t][s] = ld16_masked(q + ((size_t)min(qrow, Lq - 1) * H + h) * D + (4 * s + g) * E, qrow < Lq);
+    }
+    f32x4 o[QT][DT];
+    float m_run[QT], l_run[QT];
 #pragma unroll
-    for (int kt = 0; kt < GPS; ++kt) {
-      const int rho = perm_row<T>(kt, c);
+    for (int t = 0; t < QT; ++t) {
+      m_run[t] = -INFINITY;
+      l_run[t] = 0.f;
 #pragma unroll
-      for (int s = 0; s < DSTEPS; ++s) {
-        const uint4 ah = *reinterpret_cast<const uint4*>(&k_hi[buf][rho * KSTR + (4 * s + g) * E]);
+      for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // Vtil^T operand of chunk ch: lane (g, c) holds row 16*dt + c, ranks ch*KS + g*E ...
+    uint4 vop[DT];
 #pragma unroll
-        for (int t = 0; t < kAttQT; ++t) Mma<T>::run(sacc[t][kt], ah, qreg[t][s]);
-        if (SPLIT) {
-          const uint4 al = *reinterpret_cast<const uint4*>(&k_lo[buf][rho * KSTR + (4 * s + g) * E]);
+    for (int dt = 0; dt < DT; ++dt) vop[dt] = ld16(vh + (size_t)(16 * dt + c) * rpad + g * E);
+    for (int ch = 0; ch < nchunk; ++ch) {
+      uint4 vnext[DT];
+      if (PREFETCH_V && ch + 1 < nchunk) {
 #pragma unroll
-          for (int t = 0; t < kAttQT; ++t) Mma<T>::run(sacc[t][kt], al, qreg[t][s]);
+        for (int dt = 0; dt < DT; ++dt) vnext[dt] = ld16(vh + (size_t)(16 * dt + c) * rpad + (ch + 1) * KS + g * E);
+      }
+      f32x4 sacc[QT][GPS];
+#pragma unroll
+      for (int t = 0; t < QT; ++t)
+#pragma unroll
+        for (int kt = 0; kt < GPS; ++kt) sacc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < GPS; ++kt) {
+        const int row = ch * KS + perm_row<T>(kt, c);
+        const int sw = kswz<T>(row, CPR);
+        const unsigned char* krow = lds_k + row * ROWB;
+#pragma unroll
+        for (int s = 0; s < DSTEPS; ++s) {
+          const int off = ((4 * s + g) ^ sw) * 16;
+          const uint4 ah = *reinterpret_cast<const uint4*>(krow + off);
+#pragma unroll
+          for (int t = 0; t < QT; ++t) Mma<T>::run(sacc[t][kt], ah, qreg[t][s]);
+          if (SPLIT) {
+            const uint4 al = *reinterpret_cast<const uint4*>(krow + PART + off);
+#pragma unroll
+            for (int t = 0; t < QT; ++t) Mma<T>::run(sacc[t][kt], al, qreg[t][s]);
+          }
         }
       }
-    }
-    const bool ragged = (ch + 1) * KS > r;  // uniform
-    uint4 pk[kAttQT];
+      const bool ragged = (ch + 1) * KS > r;  // uniform
+      uint4 pk[QT];
+      float alpha[QT];
+      bool need_any = false;
 #pragma unroll
-    for (int t = 0; t < kAttQT; ++t) {
-      float mx = -INFINITY;
+      for (int t = 0; t < QT; ++t) {
+        float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < GPS; ++kt)
+        for (int kt = 0; kt < GPS; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (ragged && ch * KS + perm_row<T>(kt, 4 * g + i) >= r) sacc[t][kt][i] = -INFINITY;
-          mx = fmaxf(mx, sacc[t][kt][i]);
-        }
-      mx = max4g(mx) * scale_log2;
-      const float m_new = fmaxf(m_run[t], mx);
-      const float alpha = fast_exp2(m_run[t] - m_new);
-      float ls = 0.f;
-      f32x4 p[GPS];
+          for (int i = 0; i < 4; ++i) {
+            if (ragged && ch * KS + perm_row<T>(kt, 4 * g + i) >= r) sacc[t][kt][i] = -INFINITY;
+            mx = fmaxf(mx, sacc[t][kt][i]);
+          }
+        mx = max4g(mx) * scale_log2;
+        // lazy rescale: the reference max moves only when the new maximum
+        // exceeds it by more than 2^8 (weights stay <= 256, exact in fp32)
+        const bool need = mx > m_run[t] + 8.f;
+        alpha[t] = need ? fast_exp2(m_run[t] - mx) : 1.f;
+        m_run[t] = need ? mx : m_run[t];
+        need_any = need_any || need;
+        float ls = 0.f;
+        f32x4 p[GPS];
 #pragma unroll
-      for (int kt = 0; kt < GPS; ++kt)
+        for (int kt = 0; kt < GPS; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = fast_exp2(fmaf(sacc[t][kt][i], scale_log2, -m_new));
-          p[kt][i] = e;
-          ls += e;
-        }
-      l_run[t] = l_run[t] * alpha + ls;
-      m_run[t] = m_new;
+          for (int i = 0; i < 4; ++i) {
+            const float e = fast_exp2(fmaf(sacc[t][kt][i], scale_log2, -m_run[t]));
+            p[kt][i] = e;
+            ls += e;
+          }
+        l_run[t] = l_run[t] * alpha[t] + ls;
+        pk[t] = pack_p<T>(p);
+      }
+      if (__any(need_any)) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
-      pk[t] = pack_p<T>(p);
-    }
+        for (int t = 0; t < QT; ++t)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint4 a = *reinterpret_cast<const uint4*>(&v_t[buf][(16 * dt + c) * VSTR + g * E]);
-#pragma unroll
-      for (int t = 0; t < kAttQT; ++t) Mma<T>::run(o[t][dt], a, pk[t]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int t = 0; t < kAttQT; ++t) {
-    const int qrow = q0 + 16 * t + c;
-    if (qrow < Lq) {
-      const float inv = 1.f / sum4g(l_run[t]);
-      float* dst = o_lin + ((size_t)qrow * H + h) * D + 4 * g;
+          for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha[t];
+      }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<float4*>(dst + 16 * dt) =
-            make_float4(o[t][dt][0] * inv, o[t][dt][1] * inv, o[t][dt][2] * inv, o[t][dt][3] * inv);
+#pragma unroll
+        for (int t = 0; t < QT; ++t) Mma<T>::run(o[t][dt], vop[dt], pk[t]);
+      if (ch + 1 < nchunk) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          vop[dt] = PREFETCH_V ? vnext[dt] : ld16(vh + (size_t)(16 * dt + c) * rpad + (ch + 1) * KS + g * E);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      const int qrow = qbase + 16 * t + c;
+      if (qrow < Lq) {
+        const float inv = 1.f / sum4g(l_run[t]);
+        float* dst = o_lin + ((size_t)qrow * H + h) * D + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<float4*>(dst + 16 * dt) =
+              make_float4(o[t][dt][0] * inv, o[t][dt][1] * inv, o[t][dt][2] * inv, o[t][dt][3] * inv);
+      }
     }
   }
 }
@@ -480,10 +522,18 @@ void launch_linear(const Dims& s, const void* q, const void* k_act, const void* 
                        reinterpret_cast<float*>(k_proj), reinterpret_cast<float*>(v_proj));
   }
   if (flags & HSA_LIN_PROJ_ONLY) return;
+  // MFMA-ready operands of the attention, then the attention
+  T* khi = reinterpret_cast<T*>(ws + w.lin_khi);
+  T* klo = reinterpret_cast<T*>(ws + w.lin_klo);
+  T* vt = reinterpret_cast<T*>(ws + w.lin_vt);
+  hipLaunchKernelGGL((lin_prep_kernel<T>), dim3((pp.rpad * D + 255) / 256, s.H, 2), dim3(256), 0, st,
+                     reinterpret_cast<const float*>(k_proj), reinterpret_cast<const float*>(v_proj), D, s.r, pp.rpad,
+                     khi, klo, vt);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
-  hipLaunchKernelGGL((lin_attend_kernel<T, D>), dim3((s.Lq + kAttRows - 1) / kAttRows, s.H), dim3(kAttThreads), 0, st,
-                     reinterpret_cast<const T*>(q), reinterpret_cast<const float*>(k_proj),
-                     reinterpret_cast<const float*>(v_proj), s.H, s.Lq, s.r, scale_log2, o_lin);
+  const AttendPlan ap = attend_plan(s);
+  hipLaunchKernelGGL((lin_attend_kernel<T, D>), dim3(ap.wg_per_head, s.H), dim3(kAttThreads), 0, st,
+                     reinterpret_cast<const T*>(q), khi, klo, vt, s.H, s.Lq, s.r, pp.rpad, ap.units_per_wg,
+                     scale_log2, o_lin);
 }
 
 }  // namespace
@@ -502,7 +552,7 @@ extern "C" hsa_rc hsa_linear_branch(const hsa_geom* geom, const void* q, const v
   if (!(flags & HSA_LIN_REUSE_PROJ) && (!k_act || !v_act || !e_k || !e_v)) return HSA_ERR_NULL_ARG;
   if (!(flags & HSA_LIN_PROJ_ONLY) && (!q || !o_lin)) return HSA_ERR_NULL_ARG;
   const WsLayout w = ws_layout(s, 1);
-  if (!(flags & HSA_LIN_REUSE_PROJ) && (!ws || ws_bytes < w.lin_end)) return HSA_ERR_WORKSPACE;
+  if (!ws || ws_bytes < w.lin_end) return HSA_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* wsb = static_cast<char*>(ws);
   if (s.bf16) {

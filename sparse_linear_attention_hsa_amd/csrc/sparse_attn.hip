@@ -139,25 +139,10 @@ __global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
 
 // LDS staging of one step (KS keys), written by direct global->LDS loads
 // (each wave instruction writes 1 KB: 64 lanes x 16 bytes, contiguous).
-//  * K: rows of D elements; the 16-byte chunk c of key row rho sits in slot
-//    c ^ kswz(rho), so the operand reads of a wave (16 rows, same chunk) hit
-//    distinct banks.
+//  * K: rows of D elements, 16-byte chunks swizzled by kswz (common.h).
 //  * V: the step's granules as regions [granule][part][D rows][16 bytes];
 //    region g is exactly what lane group g reads for the V^T operand.
-template <typename T> __device__ __forceinline__ int kswz(int rho, int cpr);
-template <> __device__ __forceinline__ int kswz<bf16_t>(int rho, int cpr) {
-  return ((rho & 3) | (((rho >> 3) & 3) << 2)) & (cpr - 1);
-}
-template <> __device__ __forceinline__ int kswz<float>(int rho, int cpr) { return rho & 15 & (cpr - 1); }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ void load_lds16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_wave_base, 16, 0, 0);
-}
-
-// wait until this wave's direct-to-LDS loads have landed
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // Workgroup barrier for the staging ring: this wave's LDS reads are done and
 // at most N of its direct-to-LDS loads are still in flight, then all waves
 // meet.  (gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
