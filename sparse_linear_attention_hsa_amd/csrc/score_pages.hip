@@ -99,33 +99,40 @@ __global__ __launch_bounds__(kScoreThreads) void score_partial_kernel(
   }
 }
 
-// grid = (n_pages + 1, ceil(hd / 256)): one thread per column of one page (the
-// last x-index is the query buffer); fixed-order sum of the chunk partials,
-// divided by the token count.
+// grid = (n_pages + 1, ceil(hd / 64)): 64 columns of one page per workgroup
+// (the last x-index is the query buffer); thread group s (of 4) sums the
+// chunk partials u = s, s+4, ... of its column, and the four sums are added
+// in a fixed order (bitwise reproducible), divided by the token count.
+constexpr int kMeanCols = 64;
 __global__ __launch_bounds__(kScoreThreads) void score_means_kernel(
     const float* __restrict__ partial, PageTable pages, int n_pages, int page_chunks, int q_chunks,
     int hd, int Lp, int Lq, float* __restrict__ page_kmean, float* __restrict__ kbar,
     float* __restrict__ qbar) {
+  constexpr int kGroups = kScoreThreads / kMeanCols;
+  static_assert(kGroups == 4, "the final sum adds four group sums");
+  __shared__ float part[kGroups][kMeanCols];
   const int j = blockIdx.x;
-  const int c = blockIdx.y * kScoreThreads + threadIdx.x;
-  if (c >= hd) return;
+  const int cl = threadIdx.x % kMeanCols, grp = threadIdx.x / kMeanCols;
+  const int c = blockIdx.y * kMeanCols + cl;
   const bool is_q = j == n_pages;
-  if (!is_q && pages.p[j] == nullptr) {
-    kbar[(size_t)j * hd + c] = page_kmean[(size_t)j * hd + c];
+  const bool resident = is_q || pages.p[j] != nullptr;  // uniform
+  if (!resident) {
+    if (grp == 0 && c < hd) kbar[(size_t)j * hd + c] = page_kmean[(size_t)j * hd + c];
     return;
   }
   const int n = is_q ? q_chunks : page_chunks;
-  const float* p = partial + ((size_t)j * page_chunks) * hd + c;  // query partials follow the pages
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-  int u = 0;
-  for (; u + 4 <= n; u += 4) {
-    s0 += p[(size_t)(u + 0) * hd];
-    s1 += p[(size_t)(u + 1) * hd];
-    s2 += p[(size_t)(u + 2) * hd];
-    s3 += p[(size_t)(u + 3) * hd];
+  const float* p = partial + ((size_t)j * page_chunks) * hd + (c < hd ? c : 0);  // query partials follow the pages
+  float s0 = 0.f, s1 = 0.f;
+  int u = grp;
+  for (; u + kGroups < n; u += 2 * kGroups) {
+    s0 += p[(size_t)u * hd];
+    s1 += p[(size_t)(u + kGroups) * hd];
   }
-  for (; u < n; ++u) s0 += p[(size_t)u * hd];
-  const float m = ((s0 + s1) + (s2 + s3)) / (float)(is_q ? Lq : Lp);
+  if (u < n) s0 += p[(size_t)u * hd];
+  part[grp][cl] = s0 + s1;
+  __syncthreads();
+  if (grp != 0 || c >= hd) return;
+  const float m = ((part[0][cl] + part[1][cl]) + (part[2][cl] + part[3][cl])) / (float)(is_q ? Lq : Lp);
   if (is_q) {
     qbar[c] = m;
   } else {
@@ -192,7 +199,7 @@ void launch_score(const Dims& s, const void* q, const PageTable& tab, int n_page
                      reinterpret_cast<const T*>(q), tab, n_pages, s.Lp, s.Lq, cpr, sp.page_chunks,
                      sp.page_rows, sp.q_rows, m.cols, m.par, partial);
   const int hd = s.H * s.d;
-  hipLaunchKernelGGL(score_means_kernel, dim3(n_pages + 1, (hd + kScoreThreads - 1) / kScoreThreads), dim3(kScoreThreads), 0, st, partial, tab,
+  hipLaunchKernelGGL(score_means_kernel, dim3(n_pages + 1, (hd + kMeanCols - 1) / kMeanCols), dim3(kScoreThreads), 0, st, partial, tab,
                      n_pages, sp.page_chunks, sp.q_chunks, hd, s.Lp, s.Lq, page_kmean, kbar, qbar);
   const float scale = 1.f / ((float)s.H * sqrtf((float)s.d));
   hipLaunchKernelGGL(score_topk_kernel, dim3(1), dim3(kTopkThreads), 0, st, qbar, kbar, n_pages, hd,

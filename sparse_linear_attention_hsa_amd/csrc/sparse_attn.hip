@@ -64,6 +64,7 @@ __global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
     int max_segs, int4* __restrict__ items, int2* __restrict__ rowinfo, int* __restrict__ meta) {
   __shared__ short nseg_s[kMaxPlanRows];
   __shared__ int per_s[kMaxPlanRows];
+  __shared__ int gran_s[kMaxPlanRows];  // granules of every row
   __shared__ int slot_s[kMaxPlanRows];
   __shared__ int off_s[kMaxPlanHS];
   __shared__ int buf[kPlanThreads];
@@ -76,11 +77,12 @@ __global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
   // 1) segments of every row; partial slots are contiguous per split row
   for (int base = 0; base < rows; base += kPlanThreads) {
     const int row = base + t;
-    int nseg = 0, per = 0;
+    int nseg = 0, per = 0, G_row = 0;
     if (row < rows) {
       int n = blk_count[row];
       n = n < 0 ? 0 : (n > nKB ? nKB : n);
       const int G = n * gpb;
+      G_row = G;
       if (G > 0) {
         nseg = (G + seg_granules - 1) / seg_granules;
         per = (G + nseg - 1) / nseg;
@@ -93,6 +95,7 @@ __global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
     if (row < rows) {
       nseg_s[row] = (short)nseg;
       per_s[row] = per;
+      gran_s[row] = G_row;
       slot_s[row] = carry + cs;
       rowinfo[row] = make_int2(nseg, carry + cs);
     }
@@ -128,9 +131,7 @@ __global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
       const int nseg = nseg_s[row];
       if (nseg > sg) {
         const int per = per_s[row];
-        int n = blk_count[row];
-        n = n < 0 ? 0 : (n > nKB ? nKB : n);
-        const int G = n * gpb;
+        const int G = gran_s[row];
         items[pos++] = make_int4(row, sg * per, min(per, G - sg * per), nseg > 1 ? slot_s[row] + sg : -1);
       }
     }
@@ -434,41 +435,59 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
 // no selected block get zeros.  The per-segment weights exp2(m_s - M) / sum
 // go through LDS, then every thread streams its float4 columns once.
 constexpr int kCombThreads = 256;
-constexpr int kCombMaxSegs = 64;
 
 template <int D>
 __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
     const int2* __restrict__ rowinfo, const float* __restrict__ part_o, const float* __restrict__ part_ml,
     int H, int B, int nQB, float* __restrict__ o_sp) {
-  __shared__ float wgt[kCombMaxSegs * 192];
+  // (running max, sum) of every segment row, then (weight, -) in place;
+  // max_segs x B entries (dynamic)
+  extern __shared__ float2 ml[];
   const int row = blockIdx.x;
   const int2 ri = rowinfo[row];
   const int nseg = ri.x, s0 = ri.y;
   if (nseg == 1) return;
   const int h = row / nQB, qb = row % nQB;
   if (nseg > 1) {
+    // all (max, sum) pairs of the row in one parallel step
+    const float2* pml = reinterpret_cast<const float2*>(part_ml) + (size_t)s0 * B;
+    for (int e = threadIdx.x; e < nseg * B; e += kCombThreads) ml[e] = pml[e];
+    __syncthreads();
     for (int r = threadIdx.x; r < B; r += kCombThreads) {
       float M = -INFINITY;
-      for (int sg = 0; sg < nseg; ++sg) M = fmaxf(M, part_ml[((size_t)(s0 + sg) * B + r) * 2]);
+      for (int sg = 0; sg < nseg; ++sg) M = fmaxf(M, ml[sg * B + r].x);
       if (M == -INFINITY) M = 0.f;
       float den = 0.f;
       for (int sg = 0; sg < nseg; ++sg) {
-        const size_t sr = (size_t)(s0 + sg) * B + r;
-        const float wv = exp2f(part_ml[sr * 2] - M);
-        wgt[sg * B + r] = wv;
-        den += wv * part_ml[sr * 2 + 1];
+        const float2 v = ml[sg * B + r];
+        const float wv = exp2f(v.x - M);
+        ml[sg * B + r].x = wv;
+        den += wv * v.y;
       }
       const float inv = den > 0.f ? 1.f / den : 0.f;
-      for (int sg = 0; sg < nseg; ++sg) wgt[sg * B + r] *= inv;
+      for (int sg = 0; sg < nseg; ++sg) ml[sg * B + r].x *= inv;
     }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < B * (D / 4); e += kCombThreads) {
     const int r = e / (D / 4), c4 = e % (D / 4);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sg = 0; sg < nseg; ++sg) {
-      const float wv = wgt[sg * B + r];
-      const float4 v = reinterpret_cast<const float4*>(part_o + ((size_t)(s0 + sg) * B + r) * D)[c4];
+    const float4* src = reinterpret_cast<const float4*>(part_o + ((size_t)s0 * B + r) * D) + c4;
+    const size_t seg_stride = (size_t)B * D / 4;  // float4s between the partials of consecutive segments
+    int sg = 0;
+    for (; sg + 4 <= nseg; sg += 4) {  // four loads in flight, summed in segment order
+      float4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = src[(size_t)(sg + k) * seg_stride];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float wv = ml[(sg + k) * B + r].x;
+        acc.x += wv * v[k].x; acc.y += wv * v[k].y; acc.z += wv * v[k].z; acc.w += wv * v[k].w;
+      }
+    }
+    for (; sg < nseg; ++sg) {
+      const float wv = ml[sg * B + r].x;
+      const float4 v = src[(size_t)sg * seg_stride];
       acc.x += wv * v.x; acc.y += wv * v.y; acc.z += wv * v.z; acc.w += wv * v.w;
     }
     reinterpret_cast<float4*>(o_sp + (((size_t)qb * B + r) * H + h) * D)[c4] = acc;
@@ -548,10 +567,13 @@ extern "C" hsa_rc hsa_sparse_attn_timed(const hsa_geom* geom, const void* q, con
     else dispatch_attn<float, 64>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
   }
   if (ev_end && hipEventRecord(reinterpret_cast<hipEvent_t>(ev_end), st) != hipSuccess) return HSA_ERR_HIP;
-  if (s.d == 128)
-    hipLaunchKernelGGL(sparse_combine_kernel<128>, dim3(s.rows), dim3(kCombThreads), 0, st, rowinfo, po, pml, s.H, s.B, s.nQB, o_sp);
-  else
-    hipLaunchKernelGGL(sparse_combine_kernel<64>, dim3(s.rows), dim3(kCombThreads), 0, st, rowinfo, po, pml, s.H, s.B, s.nQB, o_sp);
+  const size_t comb_lds = (size_t)pl.max_segs * s.B * sizeof(float2);
+  auto comb = s.d == 128 ? sparse_combine_kernel<128> : sparse_combine_kernel<64>;
+  if (comb_lds > 65536 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(comb), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)comb_lds) != hipSuccess)
+    return HSA_ERR_HIP;
+  hipLaunchKernelGGL(comb, dim3(s.rows), dim3(kCombThreads), comb_lds, st, rowinfo, po, pml, s.H, s.B, s.nQB, o_sp);
   return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
 }
 
