@@ -15,8 +15,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kWave = 64;
 constexpr int kMaxPages = HSA_MAX_PAGES;
 
-// 1 KB of zeros in device memory: the source of masked 16-byte lanes of the
-// direct global->LDS loads (each lane reads kZeroPage[lane]).
+// 1 KB of zeros in device memory: the source of the 16-byte lanes of direct
+// global->LDS loads whose contraction elements must be zero (each lane reads
+// kZeroPage[lane]).
 __device__ const uint4 kZeroPage[64] = {};
 
 // Page pointer tables travel by value as launch arguments.
@@ -136,16 +137,24 @@ template <> __device__ __forceinline__ uint4 pack_p<float>(const f32x4* p) {
   return make_uint4(__float_as_uint(p[0][0]), __float_as_uint(p[0][1]), __float_as_uint(p[0][2]), __float_as_uint(p[0][3]));
 }
 
-// Cross-lane reductions over the four lanes (g = 0..3) that share c = l%16.
+// Cross-lane reductions over the four lanes (g = 0..3) that share c = l%16,
+// with the gfx950 row swaps (plain VALU, no LDS round trip).  With both
+// operands equal, v_permlane16_swap returns the rows exchanged in pairs
+// (0,1) / (2,3) across its two results, v_permlane32_swap in pairs (0,2) /
+// (1,3); combining its two results reduces over lanes l and l^16 (l^32) in
+// every lane, in the same order in all four lanes.
+__device__ __forceinline__ float max_nn(float a, float b) { return a > b ? a : b; }  // no NaNs here
 __device__ __forceinline__ float max4g(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = max_nn(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max_nn(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 __device__ __forceinline__ float sum4g(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }

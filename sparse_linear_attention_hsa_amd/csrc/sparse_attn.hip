@@ -269,7 +269,9 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
         const int blk = __builtin_amdgcn_readlane(blk_lane, cur_blk);
         if (blk >= 0 && blk < nKB) key = blk * B + cur_gran * 16;
       }
-      kofs[j] = key;
+      // a masked granule (past the segment or an invalid block id) loads the
+      // head's first granule: its scores are set to -inf, so it adds nothing
+      kofs[j] = key >= 0 ? key : 0;
       mask |= (key >= 0 ? 1u : 0u) << j;
       ++issued;
       if (++cur_gran == gpb) {
@@ -282,7 +284,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
       const int i = ii * NW + w;
       if (KINST % NW != 0 && i >= KINST) break;
       const int kg = kofs[kgran[ii]];
-      const void* src = kg >= 0 ? (const void*)(kh + (size_t)kg * D + koff[ii]) : (const void*)(kZeroPage + lane);
+      const void* src = kh + (size_t)kg * D + koff[ii];
       load_lds16(src, lk + i * 1024);
     }
 #pragma unroll
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
       const int i = ii * NW + w;
       if (VINST % NW != 0 && i >= VINST) break;
       const int kg = kofs[vgran[ii]];
-      const void* src = kg >= 0 ? (const void*)(vh + (size_t)kg * D + voff[ii]) : (const void*)(kZeroPage + lane);
+      const void* src = vh + (size_t)kg * D + voff[ii];
       load_lds16(src, lv + i * 1024);
     }
     return mask;
