@@ -179,7 +179,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
   constexpr int KINST = KBYTES / 1024;  // 1 KB direct-load instructions
   constexpr int VINST = VBYTES / 1024;
   constexpr int ROWS_PER_INST = 64 / CPR;
-  constexpr float kLazy = 8.f;          // rescale only when the row max grows by more than 2^8
+  constexpr float kLazy = 8.f;          // rescale only when the row max grows by more than 2^8 (log2 units)
   static_assert(RING == 2 || RING == 3, "staging ring depth");
 
   // RING stages of K and V, each buffer its own object so the compiler can
@@ -218,15 +218,22 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
     }
   }
 
-  f32x4 o[QPW][DT];
-  float m_run[QPW], l_run[QPW];
+  // Output accumulators, plus one more 16-row tile per query tile fed by an
+  // all-ones operand: its rows are the running softmax denominators (the sum
+  // of exactly the bf16-rounded weights the numerator uses), in every lane
+  // group, with no cross-lane reduction.  The running max starts at a finite
+  // -1e30, so weights of masked keys are exp2(-inf) = 0 without a special case.
+  f32x4 o[QPW][DT], lacc[QPW];
+  float m_run[QPW];
 #pragma unroll
   for (int t = 0; t < QPW; ++t) {
-    m_run[t] = -INFINITY;
-    l_run[t] = 0.f;
+    m_run[t] = -1e30f;
+    lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const uint4 ones = sizeof(T) == 2 ? make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u)
+                                    : make_uint4(0x3F800000u, 0x3F800000u, 0x3F800000u, 0x3F800000u);
 
   const int nsub = (gcount + GPS - 1) / GPS;
   const T* kh = k_act + (size_t)h * L * D;
@@ -331,11 +338,13 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
       }
     }
     uint4 pk[QPW];
-    float alpha[QPW];
+    float mnew[QPW];
+    bool need[QPW];
     bool need_any = false;
 #pragma unroll
     for (int t = 0; t < QPW; ++t) {
-      alpha[t] = 1.f;
+      need[t] = false;
+      mnew[t] = m_run[t];
       if (FULL || t < ntile) {
         float mx = -INFINITY;
 #pragma unroll
@@ -343,31 +352,32 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[t][kt][i]);
         mx = max4g(mx) * scale_log2;
-        const bool need = mx > m_run[t] + kLazy;
-        alpha[t] = need ? fast_exp2(m_run[t] - mx) : 1.f;
-        m_run[t] = need ? mx : m_run[t];
-        need_any = need_any || need;
-        const float mref = m_run[t] == -INFINITY ? 0.f : m_run[t];
-        float ls = 0.f;
+        need[t] = mx > m_run[t] + kLazy;
+        mnew[t] = need[t] ? mx : m_run[t];
+        need_any = need_any || need[t];
+      }
+    }
+    if (__any(need_any)) {  // rare: the reference max moves
+#pragma unroll
+      for (int t = 0; t < QPW; ++t)
+        if (FULL || t < ntile) {
+          const float alpha = need[t] ? fast_exp2(m_run[t] - mnew[t]) : 1.f;
+          lacc[t] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < QPW; ++t) {
+      m_run[t] = mnew[t];
+      if (FULL || t < ntile) {
         f32x4 p[GPS];
 #pragma unroll
         for (int kt = 0; kt < GPS; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float e = fast_exp2(fmaf(sacc[t][kt][i], scale_log2, -mref));
-            p[kt][i] = e;
-            ls += e;
-          }
-        l_run[t] = l_run[t] * alpha[t] + ls;
+          for (int i = 0; i < 4; ++i) p[kt][i] = fast_exp2(fmaf(sacc[t][kt][i], scale_log2, -m_run[t]));
         pk[t] = pack_p<T>(p);
       }
-    }
-    if (__any(need_any)) {
-#pragma unroll
-      for (int t = 0; t < QPW; ++t)
-        if (FULL || t < ntile)
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha[t];
     }
     const unsigned char* vreg = lv + g * (D * 16);
 #pragma unroll
@@ -377,6 +387,9 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
       for (int t = 0; t < QPW; ++t)
         if (FULL || t < ntile) Mma<T>::run(o[t][dt], a, pk[t]);
     }
+#pragma unroll
+    for (int t = 0; t < QPW; ++t)
+      if (FULL || t < ntile) Mma<T>::run(lacc[t], ones, pk[t]);
   };
 
   // One step: wait for this stage (this wave's loads, then every wave's),
@@ -409,7 +422,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
 #pragma unroll
   for (int t = 0; t < QPW; ++t) {
     if (t < ntile) {
-      const float l_tot = sum4g(l_run[t]);
+      const float l_tot = lacc[t][0];  // every row of the ones tile holds the denominator
       const int r = (w * QPW + t) * 16 + c;  // query row inside the block
       if (slot < 0) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -458,7 +471,7 @@ __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
     for (int r = threadIdx.x; r < B; r += kCombThreads) {
       float M = -INFINITY;
       for (int sg = 0; sg < nseg; ++sg) M = fmaxf(M, ml[sg * B + r].x);
-      if (M == -INFINITY) M = 0.f;
+      if (M == -INFINITY) M = 0.f;  // (running maxima start at -1e30; kept for any caller)
       float den = 0.f;
       for (int sg = 0; sg < nseg; ++sg) {
         const float2 v = ml[sg * B + r];
