@@ -12,7 +12,8 @@
 //    segments out; segments of a split row write un-normalised partial
 //    outputs with their running max and sum, merged exactly by a combine
 //    kernel (fixed order, no atomics).
-//  * Workgroup = NW waves; wave w owns QPW 16-row query tiles of the block.
+//  * Workgroup = NW waves; wave w owns QPW (at most two) 16-row query tiles
+//    of the block, which keeps a wave at 168 registers: three waves per SIMD.
 //    Per step it stages KS keys (32 for bf16, 16 for f32) of K (row-major)
 //    and of V (d-major, as the gather lays V out) in LDS, in a ring of two
 //    or three stages fed by direct global->LDS loads,
@@ -514,7 +515,8 @@ void launch_attn(const Dims& s, const SparsePlan& pl, const void* q, const void*
                  const int32_t* idx, const int4* items, const int* meta, float* o_sp,
                  float* po, float* pml, hipStream_t st) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
-  constexpr int WPE = sizeof(T) == 2 ? 2 : 1;
+  // bf16: two query tiles per wave fit 168 registers, three waves per SIMD
+  constexpr int WPE = sizeof(T) == 2 ? (QPW <= 2 ? 3 : 2) : 1;
   // a third stage only where it still leaves room for four workgroups per CU
   constexpr int STAGE = 2 * Mma<T>::K * D * (int)sizeof(T);
   constexpr int RING = 3 * STAGE <= 24576 ? 3 : 2;
@@ -535,17 +537,17 @@ void dispatch_attn(const Dims& s, const SparsePlan& pl, const void* q, const voi
                    const int32_t* idx, const int4* items, const int* meta, float* o_sp,
                    float* po, float* pml, hipStream_t st) {
   const int QT = s.B / 16;
-  const int nw = (QT + 2) / 3;
+  const int nw = (QT + 1) / 2;  // at most two 16-row query tiles per wave
   const int qpw = (QT + nw - 1) / nw;
 #define HSA_ATTN_CASE(NW_, QPW_) \
   if (nw == NW_ && qpw == QPW_) return launch_attn<T, D, NW_, QPW_>(s, pl, q, k_act, v_act, idx, items, meta, o_sp, po, pml, st);
   HSA_ATTN_CASE(1, 1)
   HSA_ATTN_CASE(1, 2)
-  HSA_ATTN_CASE(1, 3)
   HSA_ATTN_CASE(2, 2)
-  HSA_ATTN_CASE(2, 3)
-  HSA_ATTN_CASE(3, 3)
-  HSA_ATTN_CASE(4, 3)
+  HSA_ATTN_CASE(3, 2)
+  HSA_ATTN_CASE(4, 2)
+  HSA_ATTN_CASE(5, 2)
+  HSA_ATTN_CASE(6, 2)
 #undef HSA_ATTN_CASE
 }
 
