@@ -41,6 +41,7 @@ __global__ __launch_bounds__(kFuseThreads) void fuse_kernel(
     // G^T[col][tok] = W[col][:] . X[tok][:] ; A = W rows (gate column), B = X^T (token)
     const int tk = tok0 + c;
     const T* xr = x + (size_t)min(tk, Lq - 1) * Dm;
+#pragma unroll 4
     for (int k0 = wv * KS; k0 < Dm; k0 += 4 * KS) {
       const uint4 b = ld16(xr + k0 + g * E);
 #pragma unroll
@@ -76,22 +77,34 @@ __global__ __launch_bounds__(kFuseThreads) void fuse_kernel(
     }
   }
   __syncthreads();
-  // blend: 16 tokens x H heads x D, 4 floats per thread step
+  // blend: 16 tokens x H heads x D, 4 floats per element; kBlendU elements per
+  // thread in flight (loads from clamped, always valid positions)
+  constexpr int kBlendU = 4;
   const int per_tok = H * D / 4;
-  for (int e = tid; e < 16 * per_tok; e += kFuseThreads) {
-    const int tr = e / per_tok, rem = e % per_tok;
-    const int tk = tok0 + tr;
-    if (tk >= Lq) break;
-    const int hh = (rem * 4) / D;
-    const size_t off = (size_t)tk * H * D + rem * 4;
-    const float4 a = *reinterpret_cast<const float4*>(o_lin + off);
-    const float4 b = *reinterpret_cast<const float4*>(o_sp + off);
-    const float gl = gate_s[tr][hh], gs = gate_s[tr][H + hh];
-    float r[4] = {a.x * gl + b.x * gs, a.y * gl + b.y * gs, a.z * gl + b.z * gs, a.w * gl + b.w * gs};
-    if constexpr (sizeof(T) == 4) {
-      *reinterpret_cast<float4*>(out + off) = make_float4(r[0], r[1], r[2], r[3]);
-    } else {
-      *reinterpret_cast<uint2*>(out + off) = make_uint2(pack2_bf16(r[0], r[1]), pack2_bf16(r[2], r[3]));
+  const int total = min(16, Lq - tok0) * per_tok;
+  const size_t base = (size_t)tok0 * H * D;
+  for (int e0 = tid; e0 < total; e0 += kBlendU * kFuseThreads) {
+    float4 a[kBlendU], b[kBlendU];
+#pragma unroll
+    for (int u = 0; u < kBlendU; ++u) {
+      const int e = min(e0 + u * kFuseThreads, total - 1);
+      a[u] = reinterpret_cast<const float4*>(o_lin + base)[e];
+      b[u] = reinterpret_cast<const float4*>(o_sp + base)[e];
+    }
+#pragma unroll
+    for (int u = 0; u < kBlendU; ++u) {
+      const int e = e0 + u * kFuseThreads;
+      if (e < total) {
+        const int tr = e / per_tok, hh = (e % per_tok) * 4 / D;
+        const float gl = gate_s[tr][hh], gs = gate_s[tr][H + hh];
+        const float r0 = a[u].x * gl + b[u].x * gs, r1 = a[u].y * gl + b[u].y * gs;
+        const float r2 = a[u].z * gl + b[u].z * gs, r3 = a[u].w * gl + b[u].w * gs;
+        if constexpr (sizeof(T) == 4) {
+          reinterpret_cast<float4*>(out + base)[e] = make_float4(r0, r1, r2, r3);
+        } else {
+          reinterpret_cast<uint2*>(out + base)[e] = make_uint2(pack2_bf16(r0, r1), pack2_bf16(r2, r3));
+        }
+      }
     }
   }
 }
