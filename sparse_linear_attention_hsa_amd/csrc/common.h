@@ -172,6 +172,20 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds_wave_base) {
 // wait until this wave's direct-to-LDS (and other vector memory) loads have landed
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Workgroup barrier for the staging ring: this wave's LDS reads are done and
+// at most N of its direct-to-LDS loads are still in flight, then all waves
+// meet.  (gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt[5:4] << 14.)  The empty asm statements keep the compiler from moving
+// LDS accesses across the barrier, which __builtin_amdgcn_s_barrier alone
+// does not; unlike __syncthreads they do not force every load to land.
+template <int N> __device__ __forceinline__ void ring_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | ((N >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Swizzle of row-major operand tiles in LDS: the 16-byte chunk c of row rho
 // sits in slot c ^ kswz(rho).  A matrix-core A operand is read as 16 rows
 // (perm_row(kt, c) for lanes c = 0..15, see above) at one chunk index; the

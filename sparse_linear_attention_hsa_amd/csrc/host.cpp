@@ -60,9 +60,11 @@ ScorePlan score_plan(const Dims& s, int n_pages) {
 ProjPlan proj_plan(const Dims& s) {
   ProjPlan p;
   const int K = s.bf16 ? 32 : 16;
-  p.steps = cdiv(s.L, 2 * K);   // stages of two contraction steps
-  // about one workgroup (8 waves, two heads) per CU
-  p.splits = std::max(1, std::min(p.steps, cdiv(256, 2 * ((s.H + 1) / 2))));
+  p.steps = cdiv(s.L, K);       // stages of one contraction step
+  // At most one workgroup (8 waves, two heads, 128 KB of LDS) fits on a CU,
+  // so the items must not exceed the 256 CUs: one item more would run in a
+  // second round and double the kernel's time.
+  p.splits = std::max(1, std::min(p.steps, 256 / (2 * ((s.H + 1) / 2))));
   p.rtiles = cdiv(s.r, 16);
   p.rpad = cdiv(s.r, K) * K;
   return p;

@@ -28,8 +28,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // N transposing 64-bit LDS reads (ds_read_b64_tr_b16) issued back to back,
-// with the wait for all of them inside the same asm statement, so the
-// outputs are complete when the statement ends.
+// with the wait for all of them inside the same asm statement, so the outputs
+// are complete when the statement ends.  (The compiler's own form of this
+// read carries no alias information, so it would wait for every
+// direct-to-LDS load in flight before it.)
 template <int N> __device__ __forceinline__ void tr_read_b16(const uint32_t* addr, uint2* out);
 template <> __device__ __forceinline__ void tr_read_b16<16>(const uint32_t* a, uint2* o) {
   asm volatile(
@@ -61,41 +63,50 @@ template <> __device__ __forceinline__ void tr_read_b16<8>(const uint32_t* a, ui
 // so the workgroups that need the same E slice sit behind the same L2.
 // Workgroup = 8 waves: wave w works on head (w / 4) of the pair and on r-tiles
 // 4*(w % 4) .. +3, all D columns (128 float32 accumulators per lane).
-// One stage = two contraction steps (ST tokens), staged in LDS by direct
-// global->LDS loads, double buffered.  The main loop is unrolled by two so
-// that every LDS operand read names a fixed buffer: the compiler can then see
-// that the loads in flight (other buffer) do not alias the reads, and does not
-// stall the reads on them.
-//  * E tile [256 rows][ST tokens] (128-byte rows, chunk slot swizzled by row);
-//  * values: X^T tile [D][ST tokens] in regions [granule][part][D][16 B], as
+// One stage = one contraction step (KS tokens), staged in LDS by direct
+// global->LDS loads into a ring of kProjRing slots: while one stage is
+// multiplied, the loads of the next kProjRing-1 stages are in flight.  Every
+// slot is its own LDS object and the main loop is unrolled over the ring, so
+// each operand read names a fixed slot: the compiler can then see that the
+// loads in flight (other slots) do not alias the reads and does not stall the
+// reads on them.  The waits count the loads still allowed in flight
+// (ring_barrier) instead of draining them all at each barrier.
+//  * E tile [256 rows][KS tokens] (64-byte rows, chunk slot swizzled by row);
+//  * values: X^T tile [D][KS tokens] in regions [granule][part][D][16 B], as
 //    they arrive from the active buffer;
-//  * keys: rows [ST tokens][D], chunk slot swizzled by the token's lane group,
+//  * keys: rows [KS tokens][D], chunk slot swizzled by the token's lane group,
 //    read back transposed (ds_read_b64_tr_b16 for bf16).
 constexpr int kProjThreads = 512;  // 8 waves
 constexpr int kProjHeads = 2;
+constexpr int kProjRing = 4;
 
 template <typename T, int D>
 __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lin_project_kernel(
     const T* __restrict__ k_act, const T* __restrict__ v_act, const T* __restrict__ e_k,
     const T* __restrict__ e_v, int H, int L, int r, int splits, float* __restrict__ partial) {
   constexpr int E = Vec<T>::N;
-  constexpr int KS = Mma<T>::K;                      // tokens per contraction step
-  constexpr int ST = 2 * KS;                         // tokens per stage
+  constexpr int KS = Mma<T>::K;                      // tokens per stage (one contraction step)
   constexpr int DT = D / 16;
   constexpr int PV = 16 / E;                         // 16-byte parts per granule row
   constexpr int NW = kProjThreads / kWave;
-  constexpr int EROW = ST * (int)sizeof(T);          // 128 bytes
-  constexpr int EBYTES = 256 * EROW;                 // 32 KB
-  constexpr int XBYTES = ST * D * (int)sizeof(T);    // per head
+  constexpr int EROW = KS * (int)sizeof(T);          // 64 bytes
+  constexpr int EBYTES = 256 * EROW;                 // 16 KB
+  constexpr int XBYTES = KS * D * (int)sizeof(T);    // per head
   constexpr int EINST = EBYTES / 1024;
   constexpr int XINST = kProjHeads * XBYTES / 1024;
   constexpr int KROWS = 1024 / (D * (int)sizeof(T)); // key rows per 1 KB instruction
-  // one LDS object per buffer, so alias analysis can tell the buffer being
-  // read from the one being filled
+  constexpr int PER = EINST / NW + XINST / NW;       // loads per wave per stage
+  static_assert(EROW == 64 && EINST % NW == 0 && XINST % NW == 0, "stage tiling");
+  static_assert((kProjRing - 2) * PER < 64, "vmcnt range");
+  // one LDS object per slot (see above)
   __shared__ __align__(1024) unsigned char lds_e0[EBYTES];
   __shared__ __align__(1024) unsigned char lds_e1[EBYTES];
+  __shared__ __align__(1024) unsigned char lds_e2[EBYTES];
+  __shared__ __align__(1024) unsigned char lds_e3[EBYTES];
   __shared__ __align__(1024) unsigned char lds_x0[kProjHeads * XBYTES];
   __shared__ __align__(1024) unsigned char lds_x1[kProjHeads * XBYTES];
+  __shared__ __align__(1024) unsigned char lds_x2[kProjHeads * XBYTES];
+  __shared__ __align__(1024) unsigned char lds_x3[kProjHeads * XBYTES];
 
   const int HP = (H + 1) / 2;
   const int n_items = splits * 2 * HP;
@@ -111,13 +122,14 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2,
   const int h = hp * 2 + hs;                   // may be == H for an odd head count
   const bool h_ok = h < H;
   const int rtiles = (r + 15) / 16;
-  const int nst = (L + ST - 1) / ST;
+  const int nst = (L + KS - 1) / KS;
   const int st0 = (int)((long long)nst * split / splits);
   const int st1 = (int)((long long)nst * (split + 1) / splits);
   const T* e = kv ? e_v : e_k;
-  // E rows: 16-byte chunk slot XOR eswz(row): the 16 rows read together by a
-  // lane group land on distinct banks
-  auto eswz = [](int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); };
+  // E rows (four 16-byte chunks): chunk slot XOR ((row >> 2) & 3); the 16
+  // rows one lane group reads at one chunk index then cover 16 distinct
+  // 16-byte bank groups
+  auto eswz = [](int row) { return (row >> 2) & 3; };
   // keys: 16-byte chunk slot XOR kslot(token); for bf16 this moves whole
   // 32-byte column groups, so the 16 rows of one transposing read spread over
   // the banks.  (For f32 the XOR only separates the gathered lane groups.)
@@ -132,8 +144,9 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[a][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // exactly PER loads per wave (tails read the zero page), so the waits can count them
   auto issue = [&](int stg, unsigned char* le, unsigned char* lx) {
-    const int tok0 = stg * ST;
+    const int tok0 = stg * KS;
 #pragma unroll
     for (int ii = 0; ii < EINST / NW; ++ii) {
       const int i = ii * NW + w;
@@ -169,90 +182,97 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2,
     }
   };
 
-  // A operands of one contraction step: E rows of this wave's four r-tiles
-  auto load_a = [&](const unsigned char* le, int ks, uint4* aop) {
+  // A operands: E rows of this wave's four r-tiles at chunk g
+  auto load_a = [&](const unsigned char* le, uint4* aop) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int row = 16 * (rg * 4 + a) + c;
-      aop[a] = *reinterpret_cast<const uint4*>(le + row * EROW + (((ks * 4 + g) ^ eswz(row)) * 16));
+      aop[a] = *reinterpret_cast<const uint4*>(le + row * EROW + ((g ^ eswz(row)) * 16));
     }
   };
-  auto compute_v = [&](const unsigned char* le, const unsigned char* lx) {
+  // Every operand of a stage is read before its products, so one wait covers
+  // the LDS latency of the stage instead of one wait per pair of d-tiles.
+  auto mma_all = [&](const uint4* aop, const uint4* bop) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint4 aop[4];
-      load_a(le, ks, aop);
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) Mma<T>::run(acc[a][dt], aop[a], bop[dt]);
+  };
+  auto compute_v = [&](const unsigned char* le, const unsigned char* lxs) {
+    const unsigned char* lx = lxs + hs * XBYTES;
+    uint4 aop[4], bop[DT];
+    load_a(le, aop);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      bop[dt] = *reinterpret_cast<const uint4*>(lx + (size_t)g * D * 16 + (16 * dt + c) * 16);
+    mma_all(aop, bop);
+    // keep the reads ahead of the products (the scheduler would otherwise
+    // sink each read to its first use)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 + DT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * DT, 0);
+  };
+  auto compute_k = [&](const unsigned char* le, const unsigned char* lxs) {
+    const unsigned char* lx = lxs + hs * XBYTES;
+    uint4 aop[4], bop[DT];
+    load_a(le, aop);
+    if constexpr (sizeof(T) == 2) {
+      // transposing LDS reads: lane j of a 16-lane group reads 4 columns
+      // 16*dt + 4*(j%4) of token row T0 + j/4; lane c then holds column
+      // 16*dt + c of tokens T0 .. T0+3.  Two reads cover the 8 tokens of
+      // lane group g.
+      const int jc = c & 3, jr = c >> 2;
+      // the slot base goes through an empty asm so that the 2*DT addresses
+      // are formed here from lane offsets, not kept live per slot
+      uint32_t xb = lds_addr(lx);
+      asm volatile("" : "+v"(xb));
+      uint32_t addr[2 * DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int tr = g * 8 + hh * 4 + jr;
+          const int chunk = 2 * dt + (jc >> 1);
+          addr[2 * dt + hh] = xb + (uint32_t)(tr * D * 2 + ((chunk ^ kslot(tr)) * 16) + 8 * (jc & 1));
+        }
+      tr_read_b16<2 * DT>(addr, reinterpret_cast<uint2*>(bop));
+    } else {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint4 bop = *reinterpret_cast<const uint4*>(lx + (size_t)(ks * 4 + g) * D * 16 + (16 * dt + c) * 16);
+        const int col = 16 * dt + c;
+        T v[E];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) Mma<T>::run(acc[a][dt], aop[a], bop);
+        for (int x = 0; x < E; ++x) {
+          const int tr = g * E + x;
+          v[x] = *reinterpret_cast<const T*>(lx + (size_t)tr * D * sizeof(T) +
+                                             (((col / E) ^ kslot(tr)) * 16) + (col % E) * sizeof(T));
+        }
+        bop[dt] = *reinterpret_cast<const uint4*>(v);
       }
     }
-  };
-  auto compute_k = [&](const unsigned char* le, const unsigned char* lx) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint4 aop[4];
-      load_a(le, ks, aop);
-      if constexpr (sizeof(T) == 2) {
-        // transposing LDS reads: lane j of a 16-lane group reads 4 columns
-        // 16*dt + 4*(j%4) of token row T0 + j/4; lane c then holds column
-        // 16*dt + c of tokens T0 .. T0+3.  Two reads cover the 8 tokens of
-        // lane group g.  Four d-tiles per batch of reads.
-        const int jc = c & 3, jr = c >> 2;
-#pragma unroll
-        for (int half = 0; half < DT / 4; ++half) {
-          uint32_t addr[8];
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const int dt = 4 * half + q;
-              const int tr = ks * KS + g * 8 + hh * 4 + jr;
-              const int chunk = 2 * dt + (jc >> 1);
-              addr[2 * q + hh] = lds_addr(lx + (size_t)tr * D * 2 + ((chunk ^ kslot(tr)) * 16) + 8 * (jc & 1));
-            }
-          uint4 bop[4];
-          tr_read_b16<8>(addr, reinterpret_cast<uint2*>(bop));
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int a = 0; a < 4; ++a) Mma<T>::run(acc[a][4 * half + q], aop[a], bop[q]);
-        }
-      } else {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int col = 16 * dt + c;
-          T v[E];
-#pragma unroll
-          for (int x = 0; x < E; ++x) {
-            const int tr = ks * KS + g * E + x;
-            v[x] = *reinterpret_cast<const T*>(lx + (size_t)tr * D * sizeof(T) +
-                                               (((col / E) ^ kslot(tr)) * 16) + (col % E) * sizeof(T));
-          }
-          const uint4 bop = *reinterpret_cast<const uint4*>(v);
-#pragma unroll
-          for (int a = 0; a < 4; ++a) Mma<T>::run(acc[a][dt], aop[a], bop);
-        }
-      }
-    }
+    mma_all(aop, bop);
   };
   const bool active = h_ok && rg * 4 < rtiles;  // wave-uniform
-  // double-buffered main loop, unrolled by two so every LDS buffer is a fixed object
+  // One ring step: stage i lands (the stages after it, up to two, may stay in
+  // flight), every wave is done with the slot of stage i-1, which then takes
+  // stage i+3, and stage i is multiplied.
+  auto step = [&](int i, const unsigned char* ce, const unsigned char* cx, unsigned char* re, unsigned char* rx,
+                  auto&& compute) {
+    const int later = st1 - 1 - i;  // stages already issued after i: min(later, 2)
+    if (later >= 2) ring_barrier<2 * PER>();
+    else if (later == 1) ring_barrier<PER>();
+    else ring_barrier<0>();
+    if (i + 3 < st1) issue(i + 3, re, rx);
+    if (active) compute(ce, cx);
+  };
   auto run = [&](auto&& compute) {
-    if (st0 < st1) {
-      issue(st0, lds_e0, lds_x0);
-      __syncthreads();
-    }
-    for (int stg = st0; stg < st1; stg += 2) {
-      if (stg + 1 < st1) issue(stg + 1, lds_e1, lds_x1);
-      if (active) compute(lds_e0, lds_x0 + hs * XBYTES);
-      __syncthreads();
-      if (stg + 1 >= st1) break;
-      if (stg + 2 < st1) issue(stg + 2, lds_e0, lds_x0);
-      if (active) compute(lds_e1, lds_x1 + hs * XBYTES);
-      __syncthreads();
+    if (st0 < st1) issue(st0, lds_e0, lds_x0);
+    if (st0 + 1 < st1) issue(st0 + 1, lds_e1, lds_x1);
+    if (st0 + 2 < st1) issue(st0 + 2, lds_e2, lds_x2);
+    for (int i = st0; i < st1; i += kProjRing) {
+      step(i, lds_e0, lds_x0, lds_e3, lds_x3, compute);
+      if (i + 1 < st1) step(i + 1, lds_e1, lds_x1, lds_e0, lds_x0, compute);
+      if (i + 2 < st1) step(i + 2, lds_e2, lds_x2, lds_e1, lds_x1, compute);
+      if (i + 3 < st1) step(i + 3, lds_e3, lds_x3, lds_e2, lds_x2, compute);
     }
   };
   if (kv) run(compute_v);

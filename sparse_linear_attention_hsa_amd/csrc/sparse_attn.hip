@@ -145,21 +145,6 @@ __global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
 //  * V: the step's granules as regions [granule][part][D rows][16 bytes];
 //    region g is exactly what lane group g reads for the V^T operand.
 
-// Workgroup barrier for the staging ring: this wave's LDS reads are done and
-// at most N of its direct-to-LDS loads are still in flight, then all waves
-// meet.  (gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
-// vmcnt[5:4] << 14.)  The empty asm statements keep the compiler from moving
-// LDS accesses across the barrier, which __builtin_amdgcn_s_barrier alone
-// does not; unlike __syncthreads they do not force every load to land.
-template <int N> __device__ __forceinline__ void ring_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | ((N >> 4) << 14));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-
 // FULL: every wave owns exactly QPW query tiles (B == 16*NW*QPW), so the tile
 // loops carry no run-time guards and the matrix-core chains stay branch-free.
 template <typename T, int D, int NW, int QPW, int WPE, int RING, bool FULL>
