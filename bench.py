@@ -201,8 +201,8 @@ def run_stack(args, cfg):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c1_full")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step as one HIP graph")
@@ -254,15 +254,20 @@ def main():
     st = HsaStep(geom, cfg.n_pages)
     stream = torch.cuda.current_stream()
 
-    def one_step(ev=None, kev=None):
+    def one_step():
+        # the step's own schedule: the linear branch on a side stream beside
+        # block selection and the sparse branch, joined before the fusion
+        # (on the current stream, which is the capture stream under --graph)
+        st.run(q, pk, pv, e_k, e_v, w_g, x, tau)
+
+    def one_step_staged(ev, kev):
+        # the same six calls in order on one stream, with events between them
         calls = (lambda: st.score(q, pk), lambda: st.gather(pk, pv), lambda: st.linear(q, e_k, e_v),
                  lambda: st.select(q, tau), lambda: st.sparse(q, kernel_events=kev), lambda: st.fuse(x, w_g))
         for i, fn in enumerate(calls):
-            if ev is not None:
-                ev[i][0].record(stream)
+            ev[i][0].record(stream)
             fn()
-            if ev is not None:
-                ev[i][1].record(stream)
+            ev[i][1].record(stream)
 
     for _ in range(args.warmup):
         one_step()
@@ -277,7 +282,19 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
 
-    # timed region: K whole steps
+    # per-stage HIP events over a pass of the same launches issued in order on
+    # one stream (events between calls), plus, inside the sparse stage, events
+    # around the attention kernel alone (recorded by the library on the same
+    # stream).  This pass runs before the timed region, so the timed steps
+    # find the GPU in its steady state.
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in STAGES]
+           for _ in range(args.steps)]
+    kevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        one_step_staged(evs[k], kevs[k])
+    torch.cuda.synchronize()
+    # timed region: K whole steps in the step's own schedule
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -291,16 +308,6 @@ def main():
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
 
-    # per-stage HIP events over a second timed pass (same launches, events between calls)
-    # plus, inside the sparse stage, events around the attention kernel alone
-    # (recorded by the library on the same stream)
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in STAGES]
-           for _ in range(args.steps)]
-    kevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        one_step(evs[k], kevs[k])
-    torch.cuda.synchronize()
     stage_ms = {name: float(np.mean([evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(args.steps)]))
                 for i, name in enumerate(STAGES)}
     attn_kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in kevs]))

@@ -103,11 +103,12 @@ def write_stats(stats_dir: str, out: str, cmd: str, bench_log: str = None) -> No
             f.write(f"{name[:72]:<72} {calls:>6} {avg:>10.1f} {mn:>10.1f} {mx:>10.1f} {pct:>7.2f}\n")
         if bench_log:
             # The benchmark times the attention kernel with HIP events in its
-            # last pass of `steps` steps; compare with the same dispatches here.
+            # per-stage pass of `steps` steps, which is followed by the timed
+            # pass of `steps` steps: compare with the same dispatches here.
             b = bench_line(bench_log)
             k = b["roofline"].get("kernel", "sparse_attn_kernel")
             n = int(b["steps"])
-            d = trace_durations(stats_dir, k)[-n:]
+            d = trace_durations(stats_dir, k)[-2 * n:-n]
             prof_us = sum(d) / len(d)
             ev_us = 1e3 * float(b["roofline"]["kernel_ms"])
             f.write(f"# {k}: HIP-event average in the benchmark's own line {ev_us:.1f} us; "

@@ -1,9 +1,18 @@
 """One HSA decode step (one layer, one denoising step) over device buffers.
 
 Holds the intermediate buffers of the six stages (allocated once with torch)
-and issues the six C-ABI calls in order on one stream:
+and issues the six C-ABI calls:
 
-    score_pages -> gather_pages -> linear_branch -> block_select -> sparse_attn -> fuse
+    score_pages -> gather_pages -> linear_branch  -------------------.
+                                \-> block_select -> sparse_attn -> fuse
+
+The linear branch reads only the gathered K/V and the queries, and its
+output meets the sparse branch's only in the fusion (WorldAttention paper,
+section 3.3: the two branches are computed side by side and gated
+together).  By default it therefore runs on a side stream (default priority)
+with a workspace of its own, beside block selection and the sparse branch,
+and the fusion waits for both; run(..., concurrent=False) issues all six
+calls in order on one stream.  The two schedules give bit-identical results.
 
 Nothing here computes: every stage runs in the library's HIP kernels, and the
 selections never leave the device.
@@ -44,6 +53,10 @@ class HsaStep:
         if nbytes == 0:
             raise ValueError("invalid geometry")
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        # the linear branch's own workspace and stream, so that it can run
+        # beside block selection and the sparse branch
+        self.ws_lin = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.side = torch.cuda.Stream(device=dev)
 
     # individual stages --------------------------------------------------
     def score(self, q, pages_k: Sequence[Optional[torch.Tensor]], stream=None, use_cache: bool = False):
@@ -53,13 +66,14 @@ class HsaStep:
         ops.hsa_gather_pages(self.geom, pages_k, pages_v, self.sel_pages, self.k_act, self.v_act, self.kblk_mean,
                              stream)
 
-    def linear(self, q, e_k, e_v, flags: int = 0, stream=None):
+    def linear(self, q, e_k, e_v, flags: int = 0, stream=None, ws=None):
+        ws = self.ws if ws is None else ws
         if flags & HSA_LIN_REUSE_PROJ:
             ops.hsa_linear_branch(self.geom, q, None, None, None, None, self.k_proj, self.v_proj, self.o_lin,
-                                  flags, self.ws, stream)
+                                  flags, ws, stream)
         else:
             ops.hsa_linear_branch(self.geom, q, self.k_act, self.v_act, e_k, e_v, self.k_proj, self.v_proj,
-                                  self.o_lin, flags, self.ws, stream)
+                                  self.o_lin, flags, ws, stream)
 
     def select(self, q, tau, use_kblk_mean: bool = True, stream=None):
         ops.hsa_block_select(self.geom, q, self.k_act, self.kblk_mean if use_kblk_mean else None, tau,
@@ -77,11 +91,22 @@ class HsaStep:
         ops.hsa_fuse(self.geom, x, w_g, None, self.o_lin, self.o_sp, self.out, stream)
 
     # the whole step -----------------------------------------------------
-    def run(self, q, pages_k, pages_v, e_k, e_v, w_g, x, tau, stream=None):
-        self.score(q, pages_k, stream)
-        self.gather(pages_k, pages_v, stream)
-        self.linear(q, e_k, e_v, 0, stream)
-        self.select(q, tau, True, stream)
-        self.sparse(q, stream)
-        self.fuse(x, w_g, stream)
+    def run(self, q, pages_k, pages_v, e_k, e_v, w_g, x, tau, stream=None, concurrent: bool = True):
+        main = torch.cuda.current_stream() if stream is None else stream
+        self.score(q, pages_k, main)
+        self.gather(pages_k, pages_v, main)
+        if concurrent:
+            gathered = torch.cuda.Event()
+            gathered.record(main)
+            self.side.wait_event(gathered)
+            self.linear(q, e_k, e_v, 0, self.side, ws=self.ws_lin)
+            linear_done = torch.cuda.Event()
+            linear_done.record(self.side)
+        else:
+            self.linear(q, e_k, e_v, 0, main)
+        self.select(q, tau, True, main)
+        self.sparse(q, main)
+        if concurrent:
+            main.wait_event(linear_done)
+        self.fuse(x, w_g, main)
         return self.out

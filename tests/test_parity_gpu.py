@@ -85,6 +85,19 @@ def test_bitwise_reproducible(ran):
         assert torch.equal(x, y)
 
 
+def test_side_stream_schedule_matches_in_order(ran):
+    """The step's default schedule (linear branch on a side stream beside block
+    selection and the sparse branch) equals the six calls in order on one
+    stream, bit for bit."""
+    st = ran.step
+    names = ("out", "o_sp", "o_lin", "k_proj", "v_proj", "blk_count", "blk_idx", "sel_pages")
+    ran.run(concurrent=True)
+    a = {k: getattr(st, k).clone() for k in names}
+    ran.run(concurrent=False)
+    for k in names:
+        assert torch.equal(a[k], getattr(st, k)), k
+
+
 # --------------------------------------------------------------- special cases
 @pytest.mark.parametrize("cfg", [C0, M1], ids=lambda c: c.name)
 def test_tau_one_gives_dense_attention(cfg):
