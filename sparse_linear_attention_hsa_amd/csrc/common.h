@@ -143,7 +143,13 @@ template <> __device__ __forceinline__ uint4 pack_p<float>(const f32x4* p) {
 // (0,1) / (2,3) across its two results, v_permlane32_swap in pairs (0,2) /
 // (1,3); combining its two results reduces over lanes l and l^16 (l^32) in
 // every lane, in the same order in all four lanes.
-__device__ __forceinline__ float max_nn(float a, float b) { return a > b ? a : b; }  // no NaNs here
+// Maximum of two values that are never NaN, as one v_max_f32 (the plain
+// comparison costs a compare and a select, fmaxf adds canonicalizations).
+__device__ __forceinline__ float max_nn(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float max4g(float v) {
   const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = max_nn(__uint_as_float(p[0]), __uint_as_float(p[1]));

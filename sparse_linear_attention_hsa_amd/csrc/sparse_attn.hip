@@ -470,28 +470,60 @@ __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < B * (D / 4); e += kCombThreads) {
-    const int r = e / (D / 4), c4 = e % (D / 4);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4* src = reinterpret_cast<const float4*>(part_o + ((size_t)s0 * B + r) * D) + c4;
-    const size_t seg_stride = (size_t)B * D / 4;  // float4s between the partials of consecutive segments
+  // Three float4 columns per thread and pass, with the loads of up to four
+  // segments of all three in flight together; each column still sums its
+  // segments in segment order.
+  constexpr int U = 3;
+  const int total = B * (D / 4);
+  const size_t seg_stride = (size_t)B * D / 4;  // float4s between the partials of consecutive segments
+  const float4* base = reinterpret_cast<const float4*>(part_o + (size_t)s0 * B * D);
+  for (int e0 = threadIdx.x; e0 < total; e0 += U * kCombThreads) {
+    int rr[U];
+    bool ok[U];
+    const float4* src[U];
+    float4 acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = e0 + u * kCombThreads;
+      ok[u] = e < total;
+      const int ec = ok[u] ? e : 0;  // clamped: a column past the end reads column 0 and is not stored
+      rr[u] = ec / (D / 4);
+      src[u] = base + (size_t)rr[u] * (D / 4) + ec % (D / 4);
+      acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     int sg = 0;
-    for (; sg + 4 <= nseg; sg += 4) {  // four loads in flight, summed in segment order
-      float4 v[4];
+    for (; sg + 4 <= nseg; sg += 4) {
+      float4 v[U][4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) v[k] = src[(size_t)(sg + k) * seg_stride];
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float wv = ml[(sg + k) * B + r].x;
-        acc.x += wv * v[k].x; acc.y += wv * v[k].y; acc.z += wv * v[k].z; acc.w += wv * v[k].w;
-      }
+        for (int k = 0; k < 4; ++k) v[u][k] = src[u][(size_t)(sg + k) * seg_stride];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float wv = ml[(sg + k) * B + rr[u]].x;
+          acc[u].x += wv * v[u][k].x; acc[u].y += wv * v[u][k].y;
+          acc[u].z += wv * v[u][k].z; acc[u].w += wv * v[u][k].w;
+        }
     }
     for (; sg < nseg; ++sg) {
-      const float wv = ml[sg * B + r].x;
-      const float4 v = src[(size_t)sg * seg_stride];
-      acc.x += wv * v.x; acc.y += wv * v.y; acc.z += wv * v.z; acc.w += wv * v.w;
+      float4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = src[u][(size_t)sg * seg_stride];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wv = ml[sg * B + rr[u]].x;
+        acc[u].x += wv * v[u].x; acc[u].y += wv * v[u].y; acc[u].z += wv * v[u].z; acc[u].w += wv * v[u].w;
+      }
     }
-    reinterpret_cast<float4*>(o_sp + (((size_t)qb * B + r) * H + h) * D)[c4] = acc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ok[u]) {
+        const int e = e0 + u * kCombThreads;
+        reinterpret_cast<float4*>(o_sp + (((size_t)qb * B + rr[u]) * H + h) * D)[e % (D / 4)] = acc[u];
+      }
+    }
   }
 }
 
