@@ -3,13 +3,13 @@
 Holds the intermediate buffers of the six stages (allocated once with torch)
 and issues the six C-ABI calls:
 
-    score_pages -> gather_pages -> linear_branch  -------------------.
-                                \-> block_select -> sparse_attn -> fuse
+    score_pages -> gather_pages -+-> linear_branch ---------------------+-> fuse
+                                 +-> block_select -> sparse_attn ------+
 
 The linear branch reads only the gathered K/V and the queries, and its
-output meets the sparse branch's only in the fusion (WorldAttention paper,
-section 3.3: the two branches are computed side by side and gated
-together).  By default it therefore runs on a side stream (default priority)
+output meets the sparse branch's only in the gated sum (WorldAttention
+paper, section 3.3 "Hybrid Sparse Attention", paragraph on the gated fusion
+of the two branches).  By default it therefore runs on a side stream (default priority)
 with a workspace of its own, beside block selection and the sparse branch,
 and the fusion waits for both; run(..., concurrent=False) issues all six
 calls in order on one stream.  The two schedules give bit-identical results.
