@@ -19,6 +19,11 @@ refilled only after the gather that last read it.  The schedule prefetches
 every non-resident page of the coming layers (the host never sees a
 selection).
 
+As in a single step, each layer-step's linear branch runs on a side stream
+(default priority, its own workspace) beside block selection and the sparse
+branch, and the fusion waits for it; the next linear branch waits for that
+fusion, which is the last reader of the shared per-step O_lin buffer.
+
 Nothing here computes: every stage runs in the library's HIP kernels; this
 module only orders the calls, the copies and the stream events.
 """
@@ -83,6 +88,8 @@ class HsaStack:
         if nbytes == 0:
             raise ValueError("invalid geometry")
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.ws_lin = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.side = torch.cuda.Stream(device=dev)  # default priority
         # staging slots for the non-resident pages of the coming layers
         if n_slots < 2:
             raise ValueError("at least two staging slots")
@@ -126,14 +133,18 @@ class HsaStack:
 
     def run_chunk(self, inputs: Sequence[LayerInputs], n_steps: int,
                   outputs: Dict[Tuple[int, int], torch.Tensor],
-                  probe: Optional[Callable[[int, int], None]] = None) -> None:
-        """All layers x n_steps on the current stream.  outputs[(layer, step)] is a
-        [Lq][H][d] tensor of the element type for every pair the caller wants.
-        probe(layer, step), if given, is called after each layer-step has been
-        enqueued (to copy out the per-step buffers, in stream order)."""
+                  probe: Optional[Callable[[int, int], None]] = None, concurrent: bool = True) -> None:
+        """All layers x n_steps, ending on the current stream.  outputs[(layer, step)]
+        is a [Lq][H][d] tensor of the element type for every pair the caller
+        wants.  probe(layer, step), if given, is called after each layer-step
+        has been enqueued (to copy out the per-step buffers, in stream order).
+        concurrent=False issues every call on the current stream."""
         g, ws = self.geom, self.ws
         L = self.n_layers
         stream = torch.cuda.current_stream()
+        side = self.side if concurrent else stream
+        ws_lin = self.ws_lin if concurrent else ws
+        fused: Optional[torch.cuda.Event] = None  # the last fusion (last reader of O_lin)
         copy_done: List[Optional[torch.cuda.Event]] = [None] * L
         last_reader: List[Optional[torch.cuda.Event]] = [None] * self.n_slots  # per staging slot
         issued = 0  # layers whose prefetch has been issued
@@ -157,17 +168,35 @@ class HsaStack:
                         ev = torch.cuda.Event()
                         ev.record(stream)
                         last_reader[l % self.n_slots] = ev
+                if concurrent:
+                    # the linear branch needs this layer's gathered K/V (or its
+                    # projections) and a free O_lin
+                    ready = torch.cuda.Event()
+                    ready.record(stream)
+                    side.wait_event(ready)
+                    if fused is not None:
+                        side.wait_event(fused)
+                if step == 0:
                     ops.hsa_linear_branch(g, q, st.k_act, st.v_act, inp.e_k, inp.e_v, st.k_proj, st.v_proj,
-                                          self.o_lin, 0, ws)
+                                          self.o_lin, 0, ws_lin, side)
                 else:
                     ops.hsa_linear_branch(g, q, None, None, None, None, st.k_proj, st.v_proj, self.o_lin,
-                                          HSA_LIN_REUSE_PROJ, ws)
+                                          HSA_LIN_REUSE_PROJ, ws_lin, side)
+                if concurrent:
+                    linear_done = torch.cuda.Event()
+                    linear_done.record(side)
                 ops.hsa_block_select(g, q, st.k_act, st.kblk_mean, inp.tau, self.blk_count, self.blk_idx, None, ws)
                 ops.hsa_sparse_attn(g, q, st.k_act, st.v_act, self.blk_count, self.blk_idx, self.o_sp, ws)
+                if concurrent:
+                    stream.wait_event(linear_done)
                 out = outputs.get((l, step), self.scratch_out)
                 ops.hsa_fuse(g, x, inp.w_g, None, self.o_lin, self.o_sp, out)
                 if probe is not None:
                     probe(l, step)
+                if concurrent:
+                    # after the probe's copies too: they also read O_lin
+                    fused = torch.cuda.Event()
+                    fused.record(stream)
 
 
 def make_layer_inputs(geom: Geom, pages_k: List[torch.Tensor], pages_v: List[torch.Tensor], host_ids: Sequence[int],

@@ -6,8 +6,9 @@ the linear attention, block selection, sparse branch and fusion on their
 own queries and gate inputs.  Pages of the configured share start in pinned
 host memory and reach the gather through two device staging slots filled on
 a side stream.  The oracle runs every (layer, step) with the first step's
-page selection, and the streamed run must equal a run with every page
-resident, bit for bit.
+page selection, and the streamed run (linear branch on a side stream) must
+equal a run with every page resident and every call in order on one stream,
+bit for bit.
 """
 from __future__ import annotations
 
@@ -48,7 +49,7 @@ def _build(cfg, layers_needed_host=()):
     return geom, host_ids, streamed, resident, keep
 
 
-def _run(cfg, geom, host_ids, inputs, pairs, n_slots=4):
+def _run(cfg, geom, host_ids, inputs, pairs, n_slots=4, concurrent=True):
     """Run one chunk; return per (layer, step) in `pairs`: out, o_lin, o_sp, counts, lists; and per layer the pages."""
     from sparse_linear_attention_hsa_amd.stack import HsaStack
     st = HsaStack(geom, cfg.n_pages, cfg.layers, max(len(h) for h in host_ids), n_slots=n_slots)
@@ -60,7 +61,7 @@ def _run(cfg, geom, host_ids, inputs, pairs, n_slots=4):
         if (l, s) in outs:
             cap[(l, s)] = (st.o_lin.clone(), st.o_sp.clone(), st.blk_count.clone(), st.blk_idx.clone())
 
-    st.run_chunk(inputs, cfg.steps, outs, probe)
+    st.run_chunk(inputs, cfg.steps, outs, probe, concurrent=concurrent)
     torch.cuda.synchronize()
     res = {}
     for p in pairs:
@@ -105,7 +106,8 @@ def test_stack_small_every_layer_step(n_slots):
     geom, host_ids, streamed, resident, keep = _build(cfg, layers_needed_host=range(cfg.layers))
     pairs = [(l, s) for l in range(cfg.layers) for s in range(cfg.steps)]
     got, sel = _run(cfg, geom, host_ids, streamed, pairs, n_slots=n_slots)
-    ref, sel_r = _run(cfg, geom, host_ids, resident, pairs)
+    # the reference run: every page resident, every call in order on one stream
+    ref, sel_r = _run(cfg, geom, host_ids, resident, pairs, concurrent=False)
     for p in pairs:
         for k in ("out", "o_lin", "o_sp", "cnt", "idx"):
             assert np.array_equal(got[p][k], ref[p][k]), f"streamed != resident at {p} ({k})"
