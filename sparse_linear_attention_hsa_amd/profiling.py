@@ -116,6 +116,23 @@ def write_stats(stats_dir: str, out: str, cmd: str, bench_log: str = None) -> No
                     f"(difference {100 * (ev_us - prof_us) / prof_us:+.1f}%)\n")
             f.write(f"# benchmark line under the profiler: value {b['value']} {b['unit']}, "
                     f"roofline achieved {b['roofline']['achieved']} {b['roofline']['unit']}\n")
+            # The table above averages every dispatch, including the timed pass,
+            # where the linear branch runs beside the sparse branch and waits for
+            # CUs.  Each kernel runs once per step, so the per-stage pass (calls
+            # in order on one stream) is the same window of dispatches for all.
+            f.write(f"# per-kernel averages over the per-stage pass only ({n} steps, calls in order on one stream):\n")
+            names = sorted({r["Kernel_Name"] for r in csv.DictReader(open(_one(os.path.join(stats_dir, "**", "*kernel_trace.csv"))))})
+            rows = []
+            for full in names:
+                d = trace_durations(stats_dir, re.escape(full))
+                if len(d) >= 2 * n:
+                    w = d[-2 * n:-n]
+                    rows.append((_short(full), sum(w) / len(w)))
+            rows.sort(key=lambda t: -t[1])
+            total = sum(us for _, us in rows)
+            for name, us in rows:
+                f.write(f"#   {name[:70]:<70} {us:>9.1f} us\n")
+            f.write(f"#   {'sum of kernel times in one step':<70} {total:>9.1f} us\n")
 
 
 def write_traffic(a) -> None:
