@@ -177,6 +177,9 @@ hsa_rc hsa_linear_branch(const hsa_geom* geom, const void* q, const void* k_act,
  *             entries past the count are -1.
  *  blk_mass   [H][nQB][nKB] float32 out or NULL: the pooled masses m.
  *  Requires nKB <= HSA_MAX_KBLOCKS.
+ *  Precision: pooled means are float32; each pooled logit is accumulated in
+ *  float64 (products of float32 values are exact there) and rounded to
+ *  float32 once, so the selection does not depend on a summation order.
  * ------------------------------------------------------------------------- */
 hsa_rc hsa_block_select(const hsa_geom* geom, const void* q, const void* k_act, const float* kblk_mean,
                         const float* tau, int32_t* blk_count, int32_t* blk_idx, float* blk_mass,
