@@ -192,6 +192,23 @@ template <int N> __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Word 3 of a buffer resource for raw (untyped) buffer loads on gfx9-family
+// chips such as gfx950: 32-bit data format, no swizzle, no stride.  Loads
+// past num_records read zeros.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// One direct buffer->LDS load of 16 bytes per lane: the resource spans
+// [base, base + bytes), the lane reads at byte voffset + soffset (soffset
+// uniform) and lands at lds_wave_base + 16 * lane.  The address of a lane
+// takes one 32-bit register instead of a 64-bit pair.  (Kept out of lambdas:
+// called from one, the builtin made the compiler drop the kernel's host stub.)
+__device__ __forceinline__ void buffer_load_lds16(const void* base, int bytes, void* lds_wave_base, int voffset,
+                                                  int soffset) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferRsrcWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_wave_base, 16, voffset, soffset, 0, 0);
+}
+
 // Swizzle of row-major operand tiles in LDS: the 16-byte chunk c of row rho
 // sits in slot c ^ kswz(rho).  A matrix-core A operand is read as 16 rows
 // (perm_row(kt, c) for lanes c = 0..15, see above) at one chunk index; the

@@ -224,6 +224,12 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
   const int nsub = (gcount + GPS - 1) / GPS;
   const T* kh = k_act + (size_t)h * L * D;
   const T* vh = v_act + (size_t)h * (L / 16) * D * 16;
+  // Direct loads go through buffer resources over the head's K and V: a lane's
+  // address is one 32-bit byte offset and the granule's part a scalar offset
+  // (a global address takes a 64-bit register pair per load).  A head's
+  // active K/V is at most HSA_MAX_KBLOCKS * 192 * 128 * 4 bytes, well within
+  // 32 bits.
+  const int head_bytes = (int)((size_t)L * D * sizeof(T));
 
   // per-lane parts of the direct-load addresses (element offsets from the
   // start of the granule); only the granule's key offset changes per step
@@ -277,16 +283,14 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
       const int i = ii * NW + w;
       if (KINST % NW != 0 && i >= KINST) break;
       const int kg = kofs[kgran[ii]];
-      const void* src = kh + (size_t)kg * D + koff[ii];
-      load_lds16(src, lk + i * 1024);
+      buffer_load_lds16(kh, head_bytes, lk + i * 1024, koff[ii] * (int)sizeof(T), kg * D * (int)sizeof(T));
     }
 #pragma unroll
     for (int ii = 0; ii < VPW; ++ii) {
       const int i = ii * NW + w;
       if (VINST % NW != 0 && i >= VINST) break;
       const int kg = kofs[vgran[ii]];
-      const void* src = vh + (size_t)kg * D + voff[ii];
-      load_lds16(src, lv + i * 1024);
+      buffer_load_lds16(vh, head_bytes, lv + i * 1024, voff[ii] * (int)sizeof(T), kg * D * (int)sizeof(T));
     }
     return mask;
   };
