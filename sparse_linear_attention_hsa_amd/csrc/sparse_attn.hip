@@ -33,19 +33,21 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 
+// Inclusive prefix sum over the 1024 threads of the workgroup: a shuffle
+// scan inside each wave, then the 16 wave totals (buf holds >= 16 ints).
 __device__ int scan_incl_1024(int v, int* buf) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int o = 1; o < kPlanThreads; o <<= 1) {
-    const int a = t >= o ? buf[t - o] : 0;
-    __syncthreads();
-    buf[t] += a;
-    __syncthreads();
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(v, o);
+    if (lane >= o) v += y;
   }
-  const int r = buf[t];
+  if (lane == kWave - 1) buf[wave] = v;
   __syncthreads();
-  return r;
+  int before = 0;
+  for (int k = 0; k < wave; ++k) before += buf[k];
+  __syncthreads();  // buf may be reused by the caller
+  return v + before;
 }
 
 // Work items are (row, segment) pairs; a row (head h, query block i) with G
@@ -105,12 +107,18 @@ __global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
     __syncthreads();
   }
   if (t == 0) meta[1] = carry;
-  // 2) items per (head, segment index)
-  for (int hs = t; hs < nhs; hs += kPlanThreads) {
+  // 2) items per (head, segment index): one wave per pair, rows 64 at a time
+  //    as ballot bits
+  const int lane = t % kWave, wave = t / kWave;
+  constexpr int kWaves = kPlanThreads / kWave;
+  for (int hs = wave; hs < nhs; hs += kWaves) {
     const int h = hs / max_segs, sg = hs % max_segs;
     int c = 0;
-    for (int i = 0; i < nQB; ++i) c += nseg_s[h * nQB + i] > sg;
-    off_s[hs] = c;
+    for (int i0 = 0; i0 < nQB; i0 += kWave) {
+      const int i = i0 + lane;
+      c += __popcll(__ballot(i < nQB && nseg_s[h * nQB + i] > sg));
+    }
+    if (lane == 0) off_s[hs] = c;
   }
   __syncthreads();
   // 3) exclusive scan of the counts in (head, segment) order (two entries per thread)
@@ -123,18 +131,24 @@ __global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
     if (t == kPlanThreads - 1) meta[0] = incl;
   }
   __syncthreads();
-  // 4) each (head, segment) walker writes its items in query-block order
-  for (int hs = t; hs < nhs; hs += kPlanThreads) {
+  // 4) each (head, segment) wave writes its items in query-block order: a
+  //    row's place is the number of earlier rows that have this segment
+  for (int hs = wave; hs < nhs; hs += kWaves) {
     const int h = hs / max_segs, sg = hs % max_segs;
     int pos = off_s[hs];
-    for (int i = 0; i < nQB; ++i) {
+    for (int i0 = 0; i0 < nQB; i0 += kWave) {
+      const int i = i0 + lane;
       const int row = h * nQB + i;
-      const int nseg = nseg_s[row];
-      if (nseg > sg) {
+      const bool has = i < nQB && nseg_s[row] > sg;
+      const unsigned long long bits = __ballot(has);
+      if (has) {
+        const int rank = __popcll(bits & ((1ull << lane) - 1ull));
+        const int nseg = nseg_s[row];
         const int per = per_s[row];
         const int G = gran_s[row];
-        items[pos++] = make_int4(row, sg * per, min(per, G - sg * per), nseg > 1 ? slot_s[row] + sg : -1);
+        items[pos + rank] = make_int4(row, sg * per, min(per, G - sg * per), nseg > 1 ? slot_s[row] + sg : -1);
       }
+      pos += __popcll(bits);
     }
   }
 }

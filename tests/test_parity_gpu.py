@@ -172,3 +172,27 @@ def test_non_resident_page_scored_from_cached_mean():
     assert torch.equal(st.page_kmean, cached)
     assert torch.equal(st.scores, scores)
     assert torch.equal(st.sel_pages, sel)
+
+
+def test_graph_replays_match_eager():
+    """The step (side-stream schedule) captured into a HIP graph: every replay,
+    with eager steps and synchronisations between replays, equals the eager
+    step bit for bit (the library records no memset in a captured step)."""
+    r = Run(M1)
+    st = r.step
+    names = ("out", "o_sp", "o_lin", "blk_count", "blk_idx", "sel_pages", "k_proj")
+    r.run()
+    ref = {k: getattr(st, k).clone() for k in names}
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.run(r.q, r.pk, r.pv, r.e_k, r.e_v, r.w_g, r.x, r.tau)
+    for rep in range(3):
+        for k in names:
+            getattr(st, k).zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in names:
+            assert torch.equal(getattr(st, k), ref[k]), f"replay {rep}: {k}"
+        r.run()  # eager work between replays
+        torch.cuda.synchronize()
