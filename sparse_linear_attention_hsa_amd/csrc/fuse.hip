@@ -33,6 +33,24 @@ __global__ __launch_bounds__(kFuseThreads) void fuse_kernel(
   const int tok0 = blockIdx.x * 16;
   const int G2 = 2 * H;
   const int Dm = H * D;  // model width
+  // blend geometry: 16 tokens x H heads x D, 4 floats per element; kBlendU
+  // elements per thread in flight (loads from clamped, always valid
+  // positions).  The first round of branch-output loads is issued before the
+  // gate product, which does not need them, so the two latencies overlap.
+  constexpr int kBlendU = 8;
+  const int per_tok = H * D / 4;
+  const int total = min(16, Lq - tok0) * per_tok;
+  const size_t base = (size_t)tok0 * H * D;
+  float4 a[kBlendU], b[kBlendU];
+  auto load_round = [&](int e0) {
+#pragma unroll
+    for (int u = 0; u < kBlendU; ++u) {
+      const int e = min(e0 + u * kFuseThreads, total - 1);
+      a[u] = reinterpret_cast<const float4*>(o_lin + base)[e];
+      b[u] = reinterpret_cast<const float4*>(o_sp + base)[e];
+    }
+  };
+  load_round(tid);
   if (x != nullptr) {
     const int ntile = (G2 + 15) / 16;
     f32x4 acc[kMaxGateTiles];
@@ -77,20 +95,8 @@ __global__ __launch_bounds__(kFuseThreads) void fuse_kernel(
     }
   }
   __syncthreads();
-  // blend: 16 tokens x H heads x D, 4 floats per element; kBlendU elements per
-  // thread in flight (loads from clamped, always valid positions)
-  constexpr int kBlendU = 4;
-  const int per_tok = H * D / 4;
-  const int total = min(16, Lq - tok0) * per_tok;
-  const size_t base = (size_t)tok0 * H * D;
   for (int e0 = tid; e0 < total; e0 += kBlendU * kFuseThreads) {
-    float4 a[kBlendU], b[kBlendU];
-#pragma unroll
-    for (int u = 0; u < kBlendU; ++u) {
-      const int e = min(e0 + u * kFuseThreads, total - 1);
-      a[u] = reinterpret_cast<const float4*>(o_lin + base)[e];
-      b[u] = reinterpret_cast<const float4*>(o_sp + base)[e];
-    }
+    if (e0 != tid) load_round(e0);
 #pragma unroll
     for (int u = 0; u < kBlendU; ++u) {
       const int e = e0 + u * kFuseThreads;
