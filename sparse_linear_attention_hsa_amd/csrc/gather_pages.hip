@@ -54,8 +54,8 @@ __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
       const int row = (base + u) * RPP + r0;
       if (base + u < npass && row < B) {
         const size_t off = ((tok0 + row) * H + h) * D + ch * E;
-        kv[u] = ld16(ksrc + off);
-        vv[u] = ld16(vsrc + off);
+        kv[u] = ld16_nt(ksrc + off);  // pages are read once: streaming loads
+        vv[u] = ld16_nt(vsrc + off);
       }
     }
 #pragma unroll

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_partial_kernel(
     for (; r + (kUnroll - 1) * mpar < r1; r += kUnroll * mpar) {
       uint4 v[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) v[u] = ld16(p + (size_t)(r + u * mpar) * row_elems);
+      for (int u = 0; u < kUnroll; ++u) v[u] = ld16_nt(p + (size_t)(r + u * mpar) * row_elems);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         float f[E];
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_partial_kernel(
     }
     for (; r < r1; r += mpar) {
       float f[E];
-      unpack16<T>(ld16(p + (size_t)r * row_elems), f);
+      unpack16<T>(ld16_nt(p + (size_t)r * row_elems), f);
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] += f[e];
     }
