@@ -85,10 +85,6 @@ __device__ __forceinline__ uint4 ld16_nt(const void* p) {
   const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
-__device__ __forceinline__ float4 ld16f_nt(const void* p) {
-  const uint4 v = ld16_nt(p);
-  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
-}
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
 // 16-byte load that is always issued, zeroed where `ok` is false.  The
