@@ -42,10 +42,42 @@ def stage_model(cfg, n_sel_total: int):
         "gather": dict(bound="hbm", bytes=2 * (2 * L * D * es)),
         "linear": dict(bound="mfma", flops=2 * 2 * H * r * L * d + 2 * 2 * H * Lq * r * d,
                        bytes=2 * L * D * es + 2 * r * L * es + Lq * D * es + Lq * D * 4),
-        "select": dict(bound="hbm", bytes=Lq * D * es + H * (L // B) * d * 4),
+        "select": dict(bound="hbm", bytes=Lq * D * es + H * (L // B) * d * 4,
+                       flops=2 * H * (Lq // B) * (L // B) * d),
         "sparse": dict(bound="mfma", flops=4 * B * B * d * n_sel_total),
-        "fuse": dict(bound="hbm", bytes=Lq * D * es + 2 * Lq * D * 4 + Lq * D * es),
+        "fuse": dict(bound="hbm", bytes=Lq * D * es + 2 * Lq * D * 4 + Lq * D * es, flops=2 * Lq * D * 2 * H),
     }
+
+
+def measured_peaks():
+    """What this GPU sustains, measured here (the published peaks are the
+    roofline's denominators; these are reported beside them): the bf16
+    matrix-core rate of a register-only product loop, and the HBM rate of a
+    1 GiB stream copy (read + write bytes), both through the library's probe
+    entry points.  Best of three runs each."""
+    import torch
+    from sparse_linear_attention_hsa_amd import ops
+    n_wg, iters = 256, 2000
+    out = torch.empty(n_wg * 512, dtype=torch.float32, device="cuda")
+    best = float("inf")
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ops.hsa_probe_mfma_bf16(n_wg, iters, out, a, b)
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b))
+    mfma_tf = n_wg * 8 * iters * 32 * 16 * 16 * 32 * 2 / (best * 1e-3) / 1e12
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    y = torch.empty_like(x)
+    ops.hsa_probe_hbm_copy(x, y, None, None)
+    best = float("inf")
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ops.hsa_probe_hbm_copy(x, y, a, b)
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b))
+    del x, y
+    return {"mfma_bf16_tflops": round(mfma_tf, 1), "hbm_copy_gbs": round(2 * n / (best * 1e-3) / 1e9, 1)}
 
 
 ATTN_SOURCE = os.path.join(ROOT, "sparse_linear_attention_hsa_amd", "csrc", "sparse_attn.hip")
@@ -294,19 +326,21 @@ def main():
     for k in range(args.steps):
         one_step_staged(evs[k], kevs[k])
     torch.cuda.synchronize()
-    # timed region: K whole steps in the step's own schedule
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # timed region: K whole steps in the step's own schedule (an event after
+    # every step gives the per-step spread; events do not synchronise)
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    t_start.record(stream)
-    for _ in range(args.steps):
+    step_ev[0].record(stream)
+    for k in range(args.steps):
         if graph is not None:
             graph.replay()
         else:
             one_step()
-    t_end.record(stream)
+        step_ev[k + 1].record(stream)
     torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_end) / args.steps
+    ms = step_ev[0].elapsed_time(step_ev[-1]) / args.steps
+    per_step = np.array([step_ev[k].elapsed_time(step_ev[k + 1]) for k in range(args.steps)])
+    peaks = measured_peaks()
 
     stage_ms = {name: float(np.mean([evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(args.steps)]))
                 for i, name in enumerate(STAGES)}
@@ -335,11 +369,21 @@ def main():
                    "retrieved_tokens": cfg.active_tokens, "query_tokens": cfg.query_tokens,
                    "history_pages": cfg.n_pages, "block": cfg.block, "rank": cfg.rank,
                    "graph": bool(args.graph)},
+        "ms_per_step_stats": {"median": round(float(np.median(per_step)), 4),
+                              "min": round(float(per_step.min()), 4),
+                              "p90": round(float(np.percentile(per_step, 90)), 4)},
+        "step_tflops": round(sum(m.get("flops", 0) for m in model.values()) / (ms * 1e-3) / 1e12, 1),
         "attended_tflops": round(sparse_tf, 1), "mfma_frac_sparse": round(sparse_tf / peak_tf, 4),
+        "peaks_measured": peaks,
+        "mfma_frac_sparse_of_measured": round(sparse_tf / peaks["mfma_bf16_tflops"], 4),
         "selected_block_frac": round(n_sel_total / (cfg.n_heads * cfg.n_qblocks * cfg.n_kblocks), 4),
         "linear_tflops": round(lin_tf, 1),
         "score_gbs": round(model["score"]["bytes"] / (stage_ms["score"] * 1e-3) / 1e9, 1),
         "gather_gbs": round(model["gather"]["bytes"] / (stage_ms["gather"] * 1e-3) / 1e9, 1),
+        "hbm_frac": {k: {"of_8tbs": round(model[k]["bytes"] / (stage_ms[k] * 1e-3) / 8e12, 4),
+                         "of_measured_copy": round(model[k]["bytes"] / (stage_ms[k] * 1e-3) / 1e9
+                                                   / peaks["hbm_copy_gbs"], 4)}
+                     for k in ("score", "gather")},
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "roofline": roof,
     }

@@ -242,6 +242,29 @@ const char* hsa_rc_string(hsa_rc rc);
 /* HSA_ATTN_ABI_VERSION of the built library. */
 int32_t hsa_abi_version(void);
 
+/* ---------------------------------------------------------------------------
+ * Measurement helper, not part of the decode step: the bf16 matrix-core rate
+ * this GPU sustains (the denominator of the "% of measured peak" figures the
+ * benchmark reports beside the published peak).
+ *
+ *  n_workgroups  1 .. 65536 workgroups of 8 waves (one per CU at a time).
+ *  iters         1 .. 2^20 rounds; each wave runs 32 independent
+ *                16x16x32 bf16 products per round (16*16*32*2 flops each).
+ *  out           device float32 buffer of n_workgroups * 512 values (written).
+ *  ev_begin/end  hipEvent_t recorded around the launch, or NULL.
+ * Flops of one call: n_workgroups * 8 * iters * 32 * 16384.
+ * ------------------------------------------------------------------------- */
+hsa_rc hsa_probe_mfma_bf16(int32_t n_workgroups, int32_t iters, float* out, hsa_stream stream,
+                           hsa_event ev_begin, hsa_event ev_end);
+
+/* Measurement helper, not part of the decode step: an HBM stream copy of
+ * `bytes` (a multiple of 16, both pointers 16-byte aligned, buffers not
+ * overlapping) from src to dst, 16 bytes per lane with non-temporal loads
+ * and stores.  It moves 2 * bytes; the benchmark reports its rate as the
+ * measured stream-copy peak. */
+hsa_rc hsa_probe_hbm_copy(const void* src, void* dst, size_t bytes, hsa_stream stream, hsa_event ev_begin,
+                          hsa_event ev_end);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,6 +46,8 @@ SIGNATURES = {
     "hsa_geom_check": (_i32, [_GP]),
     "hsa_rc_string": (ctypes.c_char_p, [_i32]),
     "hsa_abi_version": (_i32, []),
+    "hsa_probe_mfma_bf16": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp]),
+    "hsa_probe_hbm_copy": (_i32, [_vp, _vp, _sz, _vp, _vp, _vp]),
 }
 
 

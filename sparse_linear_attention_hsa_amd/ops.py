@@ -111,17 +111,41 @@ def hsa_sparse_attn(geom, q, k_act, v_act, blk_count, blk_idx, o_sp, ws, stream=
 def hsa_sparse_attn_timed(geom, q, k_act, v_act, blk_count, blk_idx, o_sp, ws, ev_begin, ev_end, stream=None):
     """hsa_sparse_attn that also records two torch.cuda.Event objects (created
     with enable_timing=True) around the attention kernel alone."""
+    handles = _event_handles((ev_begin, ev_end), stream)
+    check("hsa_sparse_attn_timed", lib().hsa_sparse_attn_timed(
+        ctypes.byref(geom), _p(q), _p(k_act), _p(v_act), _p(blk_count), _p(blk_idx), _p(o_sp),
+        _p(ws), ws.numel() * ws.element_size(), _s(stream), handles[0], handles[1]))
+
+
+def _event_handles(events, stream):
     handles = []
-    for ev in (ev_begin, ev_end):
+    for ev in events:
         if ev is None:
             handles.append(None)
             continue
         if not ev.cuda_event:  # torch creates the underlying event on first use
             ev.record(torch.cuda.current_stream() if stream is None else stream)
         handles.append(ctypes.c_void_p(ev.cuda_event))
-    check("hsa_sparse_attn_timed", lib().hsa_sparse_attn_timed(
-        ctypes.byref(geom), _p(q), _p(k_act), _p(v_act), _p(blk_count), _p(blk_idx), _p(o_sp),
-        _p(ws), ws.numel() * ws.element_size(), _s(stream), handles[0], handles[1]))
+    return handles
+
+
+def hsa_probe_mfma_bf16(n_workgroups, iters, out, ev_begin, ev_end, stream=None):
+    """The matrix-core rate probe (a measurement helper, not part of the
+    step): out is a float32 device tensor of n_workgroups * 512 values."""
+    if out.numel() < n_workgroups * 512 or out.dtype != torch.float32:
+        raise ValueError("out must hold n_workgroups * 512 float32 values")
+    h = _event_handles((ev_begin, ev_end), stream)
+    check("hsa_probe_mfma_bf16", lib().hsa_probe_mfma_bf16(n_workgroups, iters, _p(out), _s(stream), h[0], h[1]))
+
+
+def hsa_probe_hbm_copy(src, dst, ev_begin, ev_end, stream=None):
+    """The HBM stream-copy probe (a measurement helper, not part of the step):
+    copies src into dst (same byte size, contiguous device tensors)."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("src and dst must have the same byte size")
+    h = _event_handles((ev_begin, ev_end), stream)
+    check("hsa_probe_hbm_copy", lib().hsa_probe_hbm_copy(_p(src), _p(dst), n, _s(stream), h[0], h[1]))
 
 
 def hsa_fuse(geom, x, w_g, gate_override, o_lin, o_sp, out, stream=None):

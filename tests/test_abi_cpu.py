@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "hsa_attn.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(hsa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(hsa_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -104,6 +104,16 @@ def test_entry_points_reject_bad_arguments_before_launch(lib):
     # geometry errors win before anything else
     bad = c1_geom(dtype=9)
     assert lib.hsa_fuse(ctypes.byref(bad), fake, fake, None, fake, fake, fake, None) == 3
+    # the matrix-core probe: NULL output, workgroup and round counts out of range
+    assert lib.hsa_probe_mfma_bf16(256, 10, None, None, None, None) == 1
+    assert lib.hsa_probe_mfma_bf16(0, 10, fake, None, None, None) == 4
+    assert lib.hsa_probe_mfma_bf16(70000, 10, fake, None, None, None) == 4
+    assert lib.hsa_probe_mfma_bf16(256, 0, fake, None, None, None) == 4
+    # the copy probe: NULL pointers, sizes or alignments it does not take
+    assert lib.hsa_probe_hbm_copy(None, fake, 1 << 20, None, None, None) == 1
+    assert lib.hsa_probe_hbm_copy(fake, fake, 0, None, None, None) == 4
+    assert lib.hsa_probe_hbm_copy(fake, fake, 100, None, None, None) == 4
+    assert lib.hsa_probe_hbm_copy(ctypes.c_void_p(0x1004), fake, 1 << 20, None, None, None) == 4
 
 
 def test_status_strings(lib):
