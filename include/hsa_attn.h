@@ -233,6 +233,12 @@ hsa_rc hsa_fuse(const hsa_geom* geom, const void* x, const void* w_g, const floa
  * geometry is invalid).  One workspace serves all calls on one stream. */
 size_t hsa_workspace_bytes(const hsa_geom* geom, int32_t n_pages);
 
+/* Bytes of workspace hsa_linear_branch alone needs (0 if the geometry is
+ * invalid): a second, smaller workspace lets the linear branch run on its own
+ * stream beside block selection and the sparse branch, which use the first
+ * one (the two branches meet only in hsa_fuse). */
+size_t hsa_linear_workspace_bytes(const hsa_geom* geom);
+
 /* Host-only validation of a geometry (HSA_OK or the reason it is invalid). */
 hsa_rc hsa_geom_check(const hsa_geom* geom);
 

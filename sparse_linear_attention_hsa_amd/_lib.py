@@ -43,6 +43,7 @@ SIGNATURES = {
     "hsa_sparse_attn_timed": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),
     "hsa_fuse": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "hsa_workspace_bytes": (_sz, [_GP, _i32]),
+    "hsa_linear_workspace_bytes": (_sz, [_GP]),
     "hsa_geom_check": (_i32, [_GP]),
     "hsa_rc_string": (ctypes.c_char_p, [_i32]),
     "hsa_abi_version": (_i32, []),

@@ -140,6 +140,12 @@ size_t hsa_workspace_bytes(const hsa_geom* geom, int32_t n_pages) {
   return hsa::ws_layout(s, n_pages).total;
 }
 
+size_t hsa_linear_workspace_bytes(const hsa_geom* geom) {
+  hsa::Dims s;
+  if (hsa::derive(geom, &s) != HSA_OK) return 0;
+  return hsa::ws_layout(s, 1).lin_end;
+}
+
 hsa_rc hsa_geom_check(const hsa_geom* geom) { return hsa::derive(geom, nullptr); }
 
 const char* hsa_rc_string(hsa_rc rc) {

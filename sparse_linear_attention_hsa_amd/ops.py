@@ -74,6 +74,10 @@ def hsa_workspace_bytes(geom: Geom, n_pages: int) -> int:
     return int(lib().hsa_workspace_bytes(ctypes.byref(geom), n_pages))
 
 
+def hsa_linear_workspace_bytes(geom: Geom) -> int:
+    return int(lib().hsa_linear_workspace_bytes(ctypes.byref(geom)))
+
+
 def hsa_geom_check(geom: Geom) -> int:
     return int(lib().hsa_geom_check(ctypes.byref(geom)))
 

@@ -88,7 +88,7 @@ class HsaStack:
         if nbytes == 0:
             raise ValueError("invalid geometry")
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        self.ws_lin = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.ws_lin = torch.empty(ops.hsa_linear_workspace_bytes(geom), dtype=torch.uint8, device=dev)
         self.side = torch.cuda.Stream(device=dev)  # default priority
         # staging slots for the non-resident pages of the coming layers
         if n_slots < 2:

@@ -55,7 +55,7 @@ class HsaStep:
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         # the linear branch's own workspace and stream, so that it can run
         # beside block selection and the sparse branch
-        self.ws_lin = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.ws_lin = torch.empty(ops.hsa_linear_workspace_bytes(geom), dtype=torch.uint8, device=dev)
         self.side = torch.cuda.Stream(device=dev)
 
     # individual stages --------------------------------------------------

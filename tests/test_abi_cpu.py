@@ -68,6 +68,16 @@ def test_workspace_sizes(lib):
     b = lib.hsa_workspace_bytes(ctypes.byref(g), 120)
     assert 0 < a <= b
     assert lib.hsa_workspace_bytes(ctypes.byref(g), _lib.HSA_MAX_PAGES + 1) == 0
+    # the linear branch's own workspace: smaller than the full one, enough for
+    # the linear branch (its check passes with exactly this size, fails below)
+    lin = lib.hsa_linear_workspace_bytes(ctypes.byref(g))
+    assert 0 < lin < a
+    assert lib.hsa_linear_workspace_bytes(ctypes.byref(c1_geom(dtype=9))) == 0
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.hsa_linear_branch(ctypes.byref(g), fake, fake, fake, fake, fake, fake, fake, fake, 8, fake,
+                                 lin - 1, None) == 4  # bad flags still reported first
+    assert lib.hsa_linear_branch(ctypes.byref(g), fake, fake, fake, fake, fake, fake, fake, fake, 0, fake,
+                                 lin - 1, None) == 5
 
 
 def test_entry_points_reject_bad_arguments_before_launch(lib):
