@@ -224,10 +224,12 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
   // group, with no cross-lane reduction.  The running max starts at a finite
   // -1e30, so weights of masked keys are exp2(-inf) = 0 without a special case.
   f32x4 o[QPW][DT], lacc[QPW];
-  float m_run[QPW];
+  float m_run[QPW], thr[QPW];
+  const float inv_scale = 1.f / scale_log2;
 #pragma unroll
   for (int t = 0; t < QPW; ++t) {
     m_run[t] = -1e30f;
+    thr[t] = (-1e30f + kLazy) * inv_scale;
     lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -310,6 +312,25 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
   };
 
   constexpr unsigned kAllValid = (1u << GPS) - 1;
+  // S^T products of one granule half kt (both query tiles share each K read)
+  auto products = [&](const unsigned char* lk, f32x4 (&sacc)[QPW][GPS], int kt) {
+    const int rho = perm_row<T>(kt, c);
+    const unsigned char* krow = lk + rho * CPR * 16;
+    const int sw = kswz<T>(rho, CPR);
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s) {
+      const uint4 a = *reinterpret_cast<const uint4*>(krow + (((4 * s + g) ^ sw) * 16));
+#pragma unroll
+      for (int t = 0; t < QPW; ++t)
+        if (FULL || t < ntile) Mma<T>::run(sacc[t][kt], a, qreg[t][s]);
+    }
+  };
+  // weight of one score under the reference max of tile t
+  auto wt = [&](float sc, int t) { return fast_exp2(fmaf(sc, scale_log2, -m_run[t])); };
+  // packed weights of granule half kt: bf16 pairs for bf16, raw floats for f32
+  auto weights_half = [&](const f32x4& sh, int t) -> uint2 {
+    return make_uint2(pack2_bf16(wt(sh[0], t), wt(sh[1], t)), pack2_bf16(wt(sh[2], t), wt(sh[3], t)));
+  };
   auto compute = [&](const unsigned char* lk, const unsigned char* lv, unsigned mask) {
     if (!(FULL || w * QPW < QT)) return;
     f32x4 sacc[QPW][GPS];
@@ -317,72 +338,78 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
     for (int t = 0; t < QPW; ++t)
 #pragma unroll
       for (int kt = 0; kt < GPS; ++kt) sacc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // bf16: the first half's products, then its weights under the current
+    // reference max while the second half's products run on the matrix
+    // cores; the (rare) move of the reference max below recomputes them.
+    uint2 ph[QPW];
+    products(lk, sacc, 0);
+    if constexpr (GPS == 2) {
 #pragma unroll
-    for (int kt = 0; kt < GPS; ++kt) {
-      const int rho = perm_row<T>(kt, c);
-      const unsigned char* krow = lk + rho * CPR * 16;
-      const int sw = kswz<T>(rho, CPR);
-#pragma unroll
-      for (int s = 0; s < DSTEPS; ++s) {
-        const uint4 a = *reinterpret_cast<const uint4*>(krow + (((4 * s + g) ^ sw) * 16));
-#pragma unroll
-        for (int t = 0; t < QPW; ++t)
-          if (FULL || t < ntile) Mma<T>::run(sacc[t][kt], a, qreg[t][s]);
-      }
+      for (int t = 0; t < QPW; ++t)
+        if (FULL || t < ntile) ph[t] = weights_half(sacc[t][0], t);
+      products(lk, sacc, 1);
     }
     if (mask != kAllValid) {
-      // masked keys only on a ragged or invalid step (wave-uniform test);
-      // lane group g holds keys of granule g/2 (bf16) or granule 0 (f32)
+      // masked keys, only on a ragged or invalid step (wave-uniform test):
+      // lane group g holds keys of granule g/2 (bf16) or granule 0 (f32);
+      // their scores become -inf and the first half's weights exactly 0
       const bool ok = (mask >> (GPS == 2 ? (g >> 1) : 0)) & 1u;
-      if (!ok) {
 #pragma unroll
-        for (int t = 0; t < QPW; ++t)
+      for (int t = 0; t < QPW; ++t) {
 #pragma unroll
-          for (int kt = 0; kt < GPS; ++kt) sacc[t][kt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        for (int kt = 0; kt < GPS; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sacc[t][kt][i] = ok ? sacc[t][kt][i] : -INFINITY;
+        if constexpr (GPS == 2) ph[t] = ok ? ph[t] : make_uint2(0u, 0u);
       }
     }
-    uint4 pk[QPW];
-    float mnew[QPW];
-    bool need[QPW];
-    bool need_any = false;
+    // Lazy test, lane-local: a query's weights can exceed 2^kLazy only if one
+    // of this lane's raw scores exceeds thr = (m + kLazy) / scale.  Only then
+    // is the max reduced across the four lane groups (uniform per query).
+    bool up = false;
 #pragma unroll
-    for (int t = 0; t < QPW; ++t) {
-      need[t] = false;
-      mnew[t] = m_run[t];
+    for (int t = 0; t < QPW; ++t)
       if (FULL || t < ntile) {
         float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < GPS; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[t][kt][i]);
-        mx = max4g(mx) * scale_log2;
-        need[t] = mx > m_run[t] + kLazy;
-        mnew[t] = need[t] ? mx : m_run[t];
-        need_any = need_any || need[t];
+        up = up || mx > thr[t];
       }
-    }
-    if (__any(need_any)) {  // rare: the reference max moves
+    if (__any(up)) {  // rare: the reference max moves
 #pragma unroll
       for (int t = 0; t < QPW; ++t)
         if (FULL || t < ntile) {
-          const float alpha = need[t] ? fast_exp2(m_run[t] - mnew[t]) : 1.f;
-          lacc[t] *= alpha;
+          float mx = -INFINITY;
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
+          for (int kt = 0; kt < GPS; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[t][kt][i]);
+          mx = max4g(mx) * scale_log2;
+          if (mx > m_run[t] + kLazy) {  // uniform across the lane groups of a query
+            const float alpha = fast_exp2(m_run[t] - mx);
+            lacc[t] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
+            m_run[t] = mx;
+            thr[t] = (mx + kLazy) * inv_scale;
+            if constexpr (GPS == 2) ph[t] = weights_half(sacc[t][0], t);
+          }
         }
     }
+    uint4 pk[QPW];
 #pragma unroll
-    for (int t = 0; t < QPW; ++t) {
-      m_run[t] = mnew[t];
+    for (int t = 0; t < QPW; ++t)
       if (FULL || t < ntile) {
-        f32x4 p[GPS];
-#pragma unroll
-        for (int kt = 0; kt < GPS; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) p[kt][i] = fast_exp2(fmaf(sacc[t][kt][i], scale_log2, -m_run[t]));
-        pk[t] = pack_p<T>(p);
+        if constexpr (GPS == 2) {
+          const uint2 p1 = weights_half(sacc[t][1], t);
+          pk[t] = make_uint4(ph[t].x, ph[t].y, p1.x, p1.y);
+        } else {
+          pk[t] = make_uint4(__float_as_uint(wt(sacc[t][0][0], t)), __float_as_uint(wt(sacc[t][0][1], t)),
+                             __float_as_uint(wt(sacc[t][0][2], t)), __float_as_uint(wt(sacc[t][0][3], t)));
+        }
       }
-    }
     const unsigned char* vreg = lv + g * (D * 16);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
