@@ -478,9 +478,12 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
 }
 
 // Merge the partial outputs of split rows (fixed segment order); rows with
-// no selected block get zeros.  The per-segment weights exp2(m_s - M) / sum
-// go through LDS, then every thread streams its float4 columns once.
+// no selected block get zeros.  kCombParts workgroups share a row, each with
+// a quarter of its columns (more loads in flight across the chip).  The
+// per-segment weights exp2(m_s - M) / sum go through LDS, then every thread
+// streams its float4 columns once.
 constexpr int kCombThreads = 256;
+constexpr int kCombParts = 4;
 
 template <int D>
 __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
@@ -489,7 +492,7 @@ __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
   // (running max, sum) of every segment row, then (weight, -) in place;
   // max_segs x B entries (dynamic)
   extern __shared__ float2 ml[];
-  const int row = blockIdx.x;
+  const int row = blockIdx.x / kCombParts, part = blockIdx.x % kCombParts;
   const int2 ri = rowinfo[row];
   const int nseg = ri.x, s0 = ri.y;
   if (nseg == 1) return;
@@ -519,9 +522,10 @@ __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
   // segments of all three in flight together; each column still sums its
   // segments in segment order.
   constexpr int U = 3;
-  const int total = B * (D / 4);
+  constexpr int CW = D / 4 / kCombParts;  // float4 columns of this workgroup per row
+  const int total = B * CW;
   const size_t seg_stride = (size_t)B * D / 4;  // float4s between the partials of consecutive segments
-  const float4* base = reinterpret_cast<const float4*>(part_o + (size_t)s0 * B * D);
+  const float4* base = reinterpret_cast<const float4*>(part_o + (size_t)s0 * B * D) + part * CW;
   for (int e0 = threadIdx.x; e0 < total; e0 += U * kCombThreads) {
     int rr[U];
     bool ok[U];
@@ -532,8 +536,8 @@ __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
       const int e = e0 + u * kCombThreads;
       ok[u] = e < total;
       const int ec = ok[u] ? e : 0;  // clamped: a column past the end reads column 0 and is not stored
-      rr[u] = ec / (D / 4);
-      src[u] = base + (size_t)rr[u] * (D / 4) + ec % (D / 4);
+      rr[u] = ec / CW;
+      src[u] = base + (size_t)rr[u] * (D / 4) + ec % CW;
       acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     int sg = 0;
@@ -566,7 +570,7 @@ __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
     for (int u = 0; u < U; ++u) {
       if (ok[u]) {
         const int e = e0 + u * kCombThreads;
-        reinterpret_cast<float4*>(o_sp + (((size_t)qb * B + rr[u]) * H + h) * D)[e % (D / 4)] = acc[u];
+        reinterpret_cast<float4*>(o_sp + (((size_t)qb * B + rr[u]) * H + h) * D)[part * CW + e % CW] = acc[u];
       }
     }
   }
@@ -652,7 +656,8 @@ extern "C" hsa_rc hsa_sparse_attn_timed(const hsa_geom* geom, const void* q, con
       hipFuncSetAttribute(reinterpret_cast<const void*>(comb), hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)comb_lds) != hipSuccess)
     return HSA_ERR_HIP;
-  hipLaunchKernelGGL(comb, dim3(s.rows), dim3(kCombThreads), comb_lds, st, rowinfo, po, pml, s.H, s.B, s.nQB, o_sp);
+  hipLaunchKernelGGL(comb, dim3(s.rows * kCombParts), dim3(kCombThreads), comb_lds, st, rowinfo, po, pml, s.H, s.B,
+                     s.nQB, o_sp);
   return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
 }
 
