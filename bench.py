@@ -31,14 +31,16 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 STAGES = ("score", "gather", "linear", "select", "sparse", "fuse")
 
 
-def stage_model(cfg, n_sel_total: int):
-    """Algorithmic work of one call of each stage (bytes moved or flops)."""
+def stage_model(cfg, n_sel_total: int, indexed: bool = False):
+    """Algorithmic work of one call of each stage (bytes moved or flops).
+    With the page index, scoring reads the pages' fp32 mean keys instead of
+    their keys."""
     es = 2 if cfg.dtype == "bf16" else 4
     H, d, Lp, Lq, L, B, r, P = (cfg.n_heads, cfg.head_dim, cfg.page_tokens, cfg.query_tokens,
                                 cfg.active_tokens, cfg.block, cfg.rank, cfg.n_pages)
     D = H * d
     return {
-        "score": dict(bound="hbm", bytes=P * Lp * D * es + Lq * D * es),
+        "score": dict(bound="hbm", bytes=(P * D * 4 if indexed else P * Lp * D * es) + Lq * D * es),
         "gather": dict(bound="hbm", bytes=2 * (2 * L * D * es)),
         "linear": dict(bound="mfma", flops=2 * 2 * H * r * L * d + 2 * 2 * H * Lq * r * d,
                        bytes=2 * L * D * es + 2 * r * L * es + Lq * D * es + Lq * D * 4),
@@ -238,6 +240,9 @@ def main():
     ap.add_argument("--config", default="c1_full")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step as one HIP graph")
+    ap.add_argument("--page-index", action="store_true",
+                    help="score from a page index of mean keys built once before the timed steps "
+                         "(as when pages are written) instead of reading every page's keys")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run three device-to-device copies of 1 GiB (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -286,15 +291,21 @@ def main():
     st = HsaStep(geom, cfg.n_pages)
     stream = torch.cuda.current_stream()
 
+    indexed = bool(args.page_index)
+    if indexed:
+        st.index_pages(q, pk)  # the page index, built once (outside the timed steps)
+        torch.cuda.synchronize()
+
     def one_step():
         # the step's own schedule: the linear branch on a side stream beside
         # block selection and the sparse branch, joined before the fusion
         # (on the current stream, which is the capture stream under --graph)
-        st.run(q, pk, pv, e_k, e_v, w_g, x, tau)
+        st.run(q, pk, pv, e_k, e_v, w_g, x, tau, indexed=indexed)
 
     def one_step_staged(ev, kev):
         # the same six calls in order on one stream, with events between them
-        calls = (lambda: st.score(q, pk), lambda: st.gather(pk, pv), lambda: st.linear(q, e_k, e_v),
+        calls = (lambda: st.score(q, pk, use_cache=indexed), lambda: st.gather(pk, pv),
+                 lambda: st.linear(q, e_k, e_v),
                  lambda: st.select(q, tau), lambda: st.sparse(q, kernel_events=kev), lambda: st.fuse(x, w_g))
         for i, fn in enumerate(calls):
             ev[i][0].record(stream)
@@ -348,7 +359,7 @@ def main():
 
     counts = st.blk_count.cpu().numpy()
     n_sel_total = int(counts.sum())
-    model = stage_model(cfg, n_sel_total)
+    model = stage_model(cfg, n_sel_total, indexed)
     sparse_tf = model["sparse"]["flops"] / (stage_ms["sparse"] * 1e-3) / 1e12
     lin_tf = model["linear"]["flops"] / (stage_ms["linear"] * 1e-3) / 1e12
     peak_tf = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -368,7 +379,7 @@ def main():
         "config": {"workload": cfg.name, "heads": cfg.n_heads, "head_dim": cfg.head_dim,
                    "retrieved_tokens": cfg.active_tokens, "query_tokens": cfg.query_tokens,
                    "history_pages": cfg.n_pages, "block": cfg.block, "rank": cfg.rank,
-                   "graph": bool(args.graph)},
+                   "graph": bool(args.graph), "page_index": indexed},
         "ms_per_step_stats": {"median": round(float(np.median(per_step)), 4),
                               "min": round(float(per_step.min()), 4),
                               "p90": round(float(np.percentile(per_step, 90)), 4)},

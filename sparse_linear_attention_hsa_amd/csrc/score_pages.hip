@@ -122,14 +122,21 @@ __global__ __launch_bounds__(kScoreThreads) void score_means_kernel(
   }
   const int n = is_q ? q_chunks : page_chunks;
   const float* p = partial + ((size_t)j * page_chunks) * hd + (c < hd ? c : 0);  // query partials follow the pages
-  float s0 = 0.f, s1 = 0.f;
+  // eight independent sums, so eight loads are in flight per thread (the
+  // query's 128 chunk partials are the longest column)
+  constexpr int kAcc = 8;
+  float acc[kAcc];
+#pragma unroll
+  for (int k = 0; k < kAcc; ++k) acc[k] = 0.f;
   int u = grp;
-  for (; u + kGroups < n; u += 2 * kGroups) {
-    s0 += p[(size_t)u * hd];
-    s1 += p[(size_t)(u + kGroups) * hd];
+  for (; u + (kAcc - 1) * kGroups < n; u += kAcc * kGroups) {
+#pragma unroll
+    for (int k = 0; k < kAcc; ++k) acc[k] += p[(size_t)(u + k * kGroups) * hd];
   }
-  if (u < n) s0 += p[(size_t)u * hd];
-  part[grp][cl] = s0 + s1;
+#pragma unroll
+  for (int k = 0; k < kAcc - 1; ++k)
+    if (u + k * kGroups < n) acc[k] += p[(size_t)(u + k * kGroups) * hd];
+  part[grp][cl] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
   __syncthreads();
   if (grp != 0 || c >= hd) return;
   const float m = ((part[0][cl] + part[1][cl]) + (part[2][cl] + part[3][cl])) / (float)(is_q ? Lq : Lp);

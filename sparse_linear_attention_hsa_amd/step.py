@@ -60,6 +60,15 @@ class HsaStep:
 
     # individual stages --------------------------------------------------
     def score(self, q, pages_k: Sequence[Optional[torch.Tensor]], stream=None, use_cache: bool = False):
+        """use_cache: score every page from the page index (page_kmean,
+        filled by index_pages) instead of reading its keys."""
+        pages = [None] * self.n_pages if use_cache else pages_k
+        ops.hsa_score_pages(self.geom, q, pages, self.page_kmean, self.scores, self.sel_pages, self.ws, stream)
+
+    def index_pages(self, q, pages_k: Sequence[torch.Tensor], stream=None):
+        """Build the page index: every page's mean key (WorldAttention paper,
+        section 3.2, the page index built from the keys), as it would be kept
+        when a page is written.  Runs one scoring call over the pages."""
         ops.hsa_score_pages(self.geom, q, pages_k, self.page_kmean, self.scores, self.sel_pages, self.ws, stream)
 
     def gather(self, pages_k, pages_v, stream=None):
@@ -91,9 +100,12 @@ class HsaStep:
         ops.hsa_fuse(self.geom, x, w_g, None, self.o_lin, self.o_sp, self.out, stream)
 
     # the whole step -----------------------------------------------------
-    def run(self, q, pages_k, pages_v, e_k, e_v, w_g, x, tau, stream=None, concurrent: bool = True):
+    def run(self, q, pages_k, pages_v, e_k, e_v, w_g, x, tau, stream=None, concurrent: bool = True,
+            indexed: bool = False):
+        """indexed: score from the page index (index_pages ran before) rather
+        than from the pages' keys; the gather still copies the pages."""
         main = torch.cuda.current_stream() if stream is None else stream
-        self.score(q, pages_k, main)
+        self.score(q, pages_k, main, use_cache=indexed)
         self.gather(pages_k, pages_v, main)
         if concurrent:
             gathered = torch.cuda.Event()

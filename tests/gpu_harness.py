@@ -81,9 +81,9 @@ class Run:
         self.geom = geom_of(cfg)
         self.step = HsaStep(self.geom, cfg.n_pages)
 
-    def run(self, concurrent: bool = True):
+    def run(self, concurrent: bool = True, indexed: bool = False):
         self.step.run(self.q, self.pk, self.pv, self.e_k, self.e_v, self.w_g, self.x, self.tau,
-                      concurrent=concurrent)
+                      concurrent=concurrent, indexed=indexed)
         torch.cuda.synchronize()
         return self.step
 

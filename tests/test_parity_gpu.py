@@ -98,6 +98,21 @@ def test_side_stream_schedule_matches_in_order(ran):
         assert torch.equal(a[k], getattr(st, k)), k
 
 
+def test_page_index_scoring_matches_page_scan(ran):
+    """Scoring every page from the page index (mean keys kept from an earlier
+    pass over the pages) gives the scores, the selection and the step's
+    outputs of scoring from the pages themselves, bit for bit."""
+    st = ran.step
+    names = ("scores", "sel_pages", "out", "o_sp", "o_lin", "blk_count", "blk_idx")
+    ran.run()
+    a = {k: getattr(st, k).clone() for k in names}
+    st.page_kmean.fill_(float("nan"))  # nothing left over from the run above
+    st.index_pages(ran.q, ran.pk)
+    ran.run(indexed=True)
+    for k in names:
+        assert torch.equal(a[k], getattr(st, k)), k
+
+
 # --------------------------------------------------------------- special cases
 @pytest.mark.parametrize("cfg", [C0, M1], ids=lambda c: c.name)
 def test_tau_one_gives_dense_attention(cfg):
