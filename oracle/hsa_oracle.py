@@ -11,6 +11,10 @@ computes, written from these pages:
         (paper.rainbus.top/paper/2609.34606), method steps (1)-(6)
 
 Steps, in the pages' order:
+  stage 1           [WA §3.2 "Stage 1: prompt-level retrieval"; §4.5 ablation
+                     of candidate chunks; SUM step (2)]: cosine similarity of
+                     prompt embeddings, top-k chunks; then S1 over the pages
+                     of those chunks with the page budget split evenly.
   S1 page scoring   [WA §3.2 "Stage 2: page-level retrieval", score equation;
                      SUM step (3)]: alpha_j = mean_h( Qbar_h . Kbar_{j,h} ) / sqrt(d_k),
                      top-K_p pages.
@@ -140,6 +144,84 @@ def score_and_select(q: np.ndarray, pages_k: Sequence[np.ndarray], k: int):
     alpha = page_scores(qbar, kbars)
     sel, tie = select_pages(alpha, k)
     return dict(qbar=qbar, kbars=kbars, alpha=alpha, sel=sel, tie=tie)
+
+
+# --------------------------------------------------------------------------
+# Stage 1 -- prompt-level retrieval, and page retrieval inside the chosen
+# chunks.  [WA §3.2 "Stage 1: prompt-level retrieval" (cosine similarity of
+# the current prompt embedding with the previous chunks' prompt embeddings,
+# top-1 chunk) and "Stage 2: page-level retrieval" (the pages of the
+# retrieved chunks are scored); §4.5 ablation of prompt-level candidate
+# chunks (Top-2 takes two pages from each chunk, Top-4 one page from each,
+# under the same four-page budget); SUM step (2)]
+# Readings: a zero embedding has similarity 0 with every embedding; the
+# budget K_p is split evenly over the chosen chunks (K_p divisible by their
+# number); a chosen chunk with fewer pages than its share gives its slots to
+# the best remaining pages of the chosen chunks, then to the lowest ids.
+# --------------------------------------------------------------------------
+
+
+def cosine(a: np.ndarray, b: np.ndarray) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    na, nb = math.sqrt(float(a @ a)), math.sqrt(float(b @ b))
+    if na == 0.0 or nb == 0.0:
+        return 0.0
+    return float(a @ b) / (na * nb)
+
+
+def prompt_retrieval(e_cur: np.ndarray, e_past: np.ndarray, k: int):
+    """Cosine similarity of the current prompt embedding [E] with every past
+    chunk's [C][E]; the top-k chunks (ascending ids) and a near-tie flag."""
+    sims = np.array([cosine(e_cur, e) for e in np.asarray(e_past)])
+    sel, tie = select_pages(sims, k)
+    return dict(sims=sims, sel=sel, tie=tie)
+
+
+def select_pages_in_chunks(alpha: np.ndarray, page_chunk: Sequence[int], sel_chunks: Sequence[int], k_p: int):
+    """Pages of the chosen chunks: from each chosen chunk its K_p / n best
+    pages (by alpha, ties to the lower id); slots a short chunk leaves go to
+    the best other pages of the chosen chunks, then to the lowest page ids.
+    Returns (ascending page ids, near-tie flag)."""
+    alpha = np.asarray(alpha, dtype=np.float64)
+    page_chunk = np.asarray(page_chunk)
+    chosen = set(int(c) for c in sel_chunks)
+    n = len(chosen)
+    assert k_p % n == 0, "the page budget is split evenly over the chosen chunks"
+    share = k_p // n
+    P = len(alpha)
+    cand = np.array([int(page_chunk[j]) in chosen for j in range(P)])
+    in_share = np.zeros(P, dtype=bool)
+    tie = False
+    for ch in sorted(chosen):
+        ids = np.flatnonzero(page_chunk == ch)
+        order, _ = top_k_lower_index(alpha[ids], min(share, len(ids)))
+        in_share[ids[order[:share]]] = True
+        if len(ids) > share and alpha[ids[order[share - 1]]] - alpha[ids[order[share]]] < TIE_EPS:
+            tie = True
+    # tiers: within a chunk's share, other pages of the chosen chunks, the rest
+    tier = np.where(in_share, 0, np.where(cand, 1, 2))
+    key_alpha = np.where(cand, alpha, -np.inf)
+    order = sorted(range(P), key=lambda j: (tier[j], -key_alpha[j], j))
+    sel = np.sort(np.array(order[:k_p], dtype=np.int64))
+    n_in = int(in_share.sum())
+    if n_in < k_p < P and tier[order[k_p - 1]] == 1 == tier[order[k_p]]:
+        tie = tie or bool(key_alpha[order[k_p - 1]] - key_alpha[order[k_p]] < TIE_EPS)
+    return sel, tie
+
+
+def score_chunk_pages(q: np.ndarray, pages_k: Sequence[np.ndarray], page_chunk: Sequence[int],
+                      sel_chunks: Sequence[int], k_p: int):
+    """Stage 2 over the chosen chunks only: alpha for their pages (-inf for
+    every other page, whose keys are not read), then the per-chunk budget."""
+    chosen = set(int(c) for c in sel_chunks)
+    qbar = mean_over_tokens(q)
+    alpha = np.full(len(pages_k), -np.inf)
+    for j, p in enumerate(pages_k):
+        if int(page_chunk[j]) in chosen:
+            alpha[j] = page_scores(qbar, mean_over_tokens(p)[None])[0]
+    sel, tie = select_pages_in_chunks(alpha, page_chunk, sel_chunks, k_p)
+    return dict(alpha=alpha, sel=sel, tie=tie)
 
 
 # --------------------------------------------------------------------------

@@ -78,6 +78,66 @@ def test_page_score_invariances():
     assert sorted(best) == base["sel"].tolist()
 
 
+# ------------------------------------------------ stage 1, chunk page budget
+def test_prompt_retrieval_hand_example(golden):
+    g = golden("hw7_prompt_retrieval.json")
+    e_cur, e_past = np.array(g["e_cur"], float), np.array(g["e_past"], float)
+    for case in g["cases"]:
+        r = orc.prompt_retrieval(e_cur, e_past, case["k"])
+        np.testing.assert_allclose(r["sims"], g["sims"], rtol=0, atol=1e-15)
+        assert r["sel"].tolist() == case["sel"]
+        assert not r["tie"]
+
+
+def test_prompt_retrieval_invariances():
+    rng = np.random.default_rng(17)
+    e_cur = rng.standard_normal(24)
+    e_past = rng.standard_normal((9, 24))
+    base = orc.prompt_retrieval(e_cur, e_past, 3)
+    # positive scaling of any embedding, and one permutation of the
+    # embedding axis applied to all, leave every similarity unchanged
+    scaled = orc.prompt_retrieval(3.0 * e_cur, e_past * rng.uniform(0.1, 5.0, size=(9, 1)), 3)
+    np.testing.assert_allclose(scaled["sims"], base["sims"], rtol=1e-12, atol=1e-14)
+    perm = rng.permutation(24)
+    np.testing.assert_allclose(orc.prompt_retrieval(e_cur[perm], e_past[:, perm], 3)["sims"], base["sims"],
+                               rtol=1e-12, atol=1e-14)
+    # bounds, and the best chunk is the one with the largest similarity
+    assert np.all(np.abs(base["sims"]) <= 1.0 + 1e-12)
+    assert orc.prompt_retrieval(e_cur, e_past, 1)["sel"].tolist() == [int(np.argmax(base["sims"]))]
+    # a past embedding equal to the current one (up to scale) is the top-1 chunk
+    e_past[4] = 0.3 * e_cur
+    r = orc.prompt_retrieval(e_cur, e_past, 1)
+    assert r["sel"].tolist() == [4] and abs(r["sims"][4] - 1.0) < 1e-12
+
+
+def test_chunk_pages_hand_examples(golden):
+    g = golden("hw8_chunk_pages.json")
+    for case in g["cases"]:
+        sel, tie = orc.select_pages_in_chunks(np.array(case["alpha"]), case["page_chunk"], case["chunks"],
+                                              case["k_p"])
+        assert sel.tolist() == case["sel"], case
+        assert not tie
+
+
+def test_chunk_pages_special_cases():
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((30, 2, 8))
+    pages = [rng.standard_normal((12, 2, 8)) + rng.standard_normal(8) for _ in range(12)]
+    # one chunk holding every page: plain top-K_p scoring
+    whole = orc.score_chunk_pages(q, pages, [0] * 12, [0], 4)
+    plain = orc.score_and_select(q, pages, 4)
+    assert whole["sel"].tolist() == plain["sel"].tolist()
+    np.testing.assert_allclose(whole["alpha"], plain["alpha"], rtol=1e-12, atol=1e-14)
+    # one page per chunk (Top-K_p chunks): every chosen chunk's argmax page
+    page_chunk = [j // 3 for j in range(12)]
+    r = orc.score_chunk_pages(q, pages, page_chunk, [0, 2, 3], 3)
+    want = sorted(3 * c + int(np.argmax(plain["alpha"][3 * c:3 * c + 3])) for c in (0, 2, 3))
+    assert r["sel"].tolist() == want
+    # pages outside the chosen chunks are never scored or chosen
+    assert np.all(np.isneginf(r["alpha"][3:6]))
+    np.testing.assert_allclose(r["alpha"][:3], plain["alpha"][:3], rtol=1e-12, atol=1e-14)
+
+
 @pytest.mark.parametrize("cfg", [M1, M2, M3, M4, M5])
 def test_planted_pages_are_retrieved(cfg):
     w = Workload(cfg)
