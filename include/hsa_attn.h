@@ -55,6 +55,8 @@ extern "C" {
 #define HSA_MAX_PAGES 128      /* pages per call (pointer tables travel as launch arguments) */
 #define HSA_MAX_KBLOCKS 2048   /* nKB limit of the block selection (one sort per row in LDS) */
 #define HSA_MAX_ROWS 4096      /* H * nQB limit (selection rows; the sparse branch plans them in LDS) */
+#define HSA_MAX_CHUNKS 4096    /* previous chunks in prompt-level retrieval (ranked in LDS) */
+#define HSA_MAX_EMBED 65536    /* prompt embedding width */
 
 typedef enum {
   HSA_OK = 0,
@@ -109,6 +111,52 @@ typedef struct ihipEvent_t* hsa_event;    /* a hipEvent_t  */
 hsa_rc hsa_score_pages(const hsa_geom* geom, const void* q, const void* const* page_k,
                        float* page_kmean, int32_t n_pages, float* scores, int32_t* sel_pages,
                        void* ws, size_t ws_bytes, hsa_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * Stage 1 -- prompt-level retrieval.  Paper section 3.2, "Stage 1:
+ * prompt-level retrieval" (the cosine similarity between the current prompt
+ * embedding and the previous chunks' prompt embeddings picks the top-1 chunk)
+ * and section 4.5, ablation of prompt-level candidate chunks (Top-2, Top-4);
+ * structured summary, method step (2).
+ *
+ *  prompt         [E] float32 device: the current chunk's prompt embedding.
+ *  chunk_prompts  [C][E] float32 device: the previous chunks' embeddings.
+ *  n_chunks       1 <= C <= HSA_MAX_CHUNKS.
+ *  emb_dim        1 <= E <= HSA_MAX_EMBED.
+ *  k_chunks       1 <= k <= C.
+ *  sims           [C] float32 out: cosine similarities, fp32 sums; 0 where
+ *                 either embedding is all zeros.
+ *  sel_chunks     [k] int32 out: the k most similar chunks (ties to the
+ *                 lower id), ascending.
+ * Errors: HSA_ERR_NULL_ARG, HSA_ERR_BAD_PARAM (sizes), HSA_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+hsa_rc hsa_retrieve_chunks(const float* prompt, const float* chunk_prompts, int32_t n_chunks, int32_t emb_dim,
+                           int32_t k_chunks, float* sims, int32_t* sel_chunks, hsa_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * S1 over the retrieved chunks.  Paper section 3.2, "Stage 2: page-level
+ * retrieval" (the pages of the chunks retrieved in stage 1 are scored) and
+ * section 4.5 (under the same K_p-page budget, Top-2 takes two pages from each
+ * chunk and Top-4 one page from each).
+ *
+ *  Arguments as hsa_score_pages, plus:
+ *  page_chunk  [P] int32 device: the chunk of every page.
+ *  sel_chunks  [k_chunks] int32 device: distinct chosen chunk ids (the output
+ *              of hsa_retrieve_chunks).
+ *  k_chunks    1 <= k <= K_p and K_p % k == 0.
+ *  Pages outside the chosen chunks are not read (their page_k entry may be
+ *  NULL, with page_kmean given, as for any NULL entry) and score -inf.  The
+ *  K_p pages are, in this order: the best K_p / k pages of each chosen chunk
+ *  (higher score, ties to the lower id); if a chosen chunk has fewer pages,
+ *  the best remaining pages of the chosen chunks; then the lowest other ids.
+ *  sel_pages is ascending.
+ * Errors: as hsa_score_pages; HSA_ERR_NULL_ARG for a NULL page_chunk or
+ * sel_chunks, HSA_ERR_BAD_PARAM for k_chunks.
+ * ------------------------------------------------------------------------- */
+hsa_rc hsa_score_chunk_pages(const hsa_geom* geom, const void* q, const void* const* page_k, float* page_kmean,
+                             int32_t n_pages, const int32_t* page_chunk, const int32_t* sel_chunks,
+                             int32_t k_chunks, float* scores, int32_t* sel_pages, void* ws, size_t ws_bytes,
+                             hsa_stream stream);
 
 /* ---------------------------------------------------------------------------
  * S2 -- active KV construction.  Paper section 3.2, "Active KV construction";

@@ -17,6 +17,8 @@ HSA_LIN_REUSE_PROJ, HSA_LIN_PROJ_ONLY = 1, 2
 HSA_MAX_PAGES = 128
 HSA_MAX_KBLOCKS = 2048
 HSA_MAX_ROWS = 4096
+HSA_MAX_CHUNKS = 4096
+HSA_MAX_EMBED = 65536
 
 RC_NAMES = {0: "HSA_OK", 1: "HSA_ERR_NULL_ARG", 2: "HSA_ERR_BAD_SHAPE", 3: "HSA_ERR_BAD_DTYPE",
             4: "HSA_ERR_BAD_PARAM", 5: "HSA_ERR_WORKSPACE", 6: "HSA_ERR_HIP"}
@@ -36,6 +38,9 @@ class Geom(ctypes.Structure):
 _GP = ctypes.POINTER(Geom)
 SIGNATURES = {
     "hsa_score_pages": (_i32, [_GP, _vp, ctypes.POINTER(_vp), _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "hsa_score_chunk_pages": (_i32, [_GP, _vp, ctypes.POINTER(_vp), _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _sz,
+                                     _vp]),
+    "hsa_retrieve_chunks": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "hsa_gather_pages": (_i32, [_GP, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp, _vp]),
     "hsa_linear_branch": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
     "hsa_block_select": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),

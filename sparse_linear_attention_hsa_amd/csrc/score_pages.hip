@@ -8,6 +8,13 @@
 // rows of one page into a float32 partial, then one workgroup per page sums
 // its partials in a fixed order (bitwise reproducible), and a last small
 // kernel scores and ranks the pages.
+//
+// Stage 1 (prompt-level retrieval, same section, "Stage 1"; section 4.5,
+// ablation of candidate chunks): the cosine similarity of the current prompt
+// embedding with every previous chunk's picks the top-k chunks, and the page
+// scoring then runs over those chunks' pages only, K_p / k pages from each.
+// The same three kernels serve it through a candidate filter: pages of other
+// chunks are not read and score -inf.
 #include "common.h"
 #include "host.h"
 
@@ -29,9 +36,24 @@ inline ColMap col_map(int cpr) {
   return m;
 }
 
+// Candidate pages: those whose chunk (page_chunk[j]) is one of the k chosen
+// chunks; every page when page_chunk is null.
+struct ChunkFilter {
+  const int32_t* page_chunk;
+  const int32_t* sel_chunks;
+  int k;
+};
+__device__ __forceinline__ bool candidate(const ChunkFilter& f, int j) {
+  if (f.page_chunk == nullptr) return true;
+  const int c = f.page_chunk[j];
+  bool in = false;
+  for (int i = 0; i < f.k; ++i) in = in || f.sel_chunks[i] == c;
+  return in;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kScoreThreads) void score_partial_kernel(
-    const T* __restrict__ q, PageTable pages, int n_pages, int Lp, int Lq, int cpr,
+    const T* __restrict__ q, PageTable pages, ChunkFilter filt, int n_pages, int Lp, int Lq, int cpr,
     int page_chunks, int page_rows, int q_rows, int mcols, int mpar, float* __restrict__ partial) {
   constexpr int E = Vec<T>::N;
   __shared__ float red[kScoreThreads * E];
@@ -46,6 +68,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_partial_kernel(
   int r0, r1;
   if (unit < n_pages * page_chunks) {
     const int j = unit / page_chunks, c = unit % page_chunks;
+    if (!candidate(filt, j)) return;  // a page outside the chosen chunks is not read
     base = reinterpret_cast<const T*>(pages.p[j]);
     r0 = c * page_rows;
     r1 = min(Lp, r0 + page_rows);
@@ -105,8 +128,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_partial_kernel(
 // in a fixed order (bitwise reproducible), divided by the token count.
 constexpr int kMeanCols = 64;
 __global__ __launch_bounds__(kScoreThreads) void score_means_kernel(
-    const float* __restrict__ partial, PageTable pages, int n_pages, int page_chunks, int q_chunks,
-    int hd, int Lp, int Lq, float* __restrict__ page_kmean, float* __restrict__ kbar,
+    const float* __restrict__ partial, PageTable pages, ChunkFilter filt, int n_pages, int page_chunks,
+    int q_chunks, int hd, int Lp, int Lq, float* __restrict__ page_kmean, float* __restrict__ kbar,
     float* __restrict__ qbar) {
   constexpr int kGroups = kScoreThreads / kMeanCols;
   static_assert(kGroups == 4, "the final sum adds four group sums");
@@ -115,6 +138,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_means_kernel(
   const int cl = threadIdx.x % kMeanCols, grp = threadIdx.x / kMeanCols;
   const int c = blockIdx.y * kMeanCols + cl;
   const bool is_q = j == n_pages;
+  if (!is_q && !candidate(filt, j)) return;  // scored -inf by the ranking kernel
   const bool resident = is_q || pages.p[j] != nullptr;  // uniform
   if (!resident) {
     if (grp == 0 && c < hd) kbar[(size_t)j * hd + c] = page_kmean[(size_t)j * hd + c];
@@ -154,35 +178,59 @@ constexpr int kTopkThreads = 1024;
 // a fixed order; page j is selected iff fewer than K_p pages rank above it
 // (higher score, or equal score and lower id); the selected ids are written
 // in ascending order.
+// With a chunk filter the order has three tiers: the best K_p / k pages of
+// each chosen chunk, the other pages of the chosen chunks, then every other
+// page (score -inf, by id); within a tier, higher score then lower id.
 __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
-    const float* __restrict__ qbar, const float* __restrict__ kbar, int n_pages, int hd, float scale,
-    int kp, float* __restrict__ scores, int32_t* __restrict__ sel) {
+    const float* __restrict__ qbar, const float* __restrict__ kbar, ChunkFilter filt, int n_pages, int hd,
+    float scale, int kp, float* __restrict__ scores, int32_t* __restrict__ sel) {
   __shared__ float alpha[kMaxPages];
+  __shared__ int tier[kMaxPages];
+  __shared__ int chunk_of[kMaxPages];
   __shared__ int chosen[kMaxPages];
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   for (int j = w; j < n_pages; j += kTopkThreads / kWave) {
-    const float4* kb = reinterpret_cast<const float4*>(kbar + (size_t)j * hd);
-    const float4* qb = reinterpret_cast<const float4*>(qbar);
+    const bool cand = candidate(filt, j);  // wave-uniform
     float s = 0.f;
-    for (int c = lane; c < hd / 4; c += kWave) {
-      const float4 a = qb[c], b = kb[c];
-      s += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
-    }
+    if (cand) {
+      const float4* kb = reinterpret_cast<const float4*>(kbar + (size_t)j * hd);
+      const float4* qb = reinterpret_cast<const float4*>(qbar);
+      for (int c = lane; c < hd / 4; c += kWave) {
+        const float4 a = qb[c], b = kb[c];
+        s += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+      }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-    if (lane == 0) alpha[j] = s * scale;
+      for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+    }
+    if (lane == 0) {
+      alpha[j] = cand ? s * scale : -INFINITY;
+      tier[j] = cand ? 1 : 2;
+      chunk_of[j] = filt.page_chunk ? filt.page_chunk[j] : 0;
+    }
   }
   __syncthreads();
   const int j = threadIdx.x;
-  if (j < n_pages) {
-    const float a = alpha[j];
-    int rank = 0;
-    for (int i = 0; i < n_pages; ++i) {
-      const float b = alpha[i];
-      rank += (b > a) || (b == a && i < j);
+  auto above = [&](int i, int jj) {  // page i ranks above page jj (same tier)
+    return alpha[i] > alpha[jj] || (alpha[i] == alpha[jj] && i < jj);
+  };
+  if (filt.page_chunk != nullptr) {
+    // tier 0: a chosen chunk's best K_p / k pages
+    const int share = kp / filt.k;
+    int t = 2;
+    if (j < n_pages && tier[j] == 1) {
+      int r = 0;
+      for (int i = 0; i < n_pages; ++i) r += tier[i] != 2 && chunk_of[i] == chunk_of[j] && above(i, j);
+      t = r < share ? 0 : 1;
     }
+    __syncthreads();
+    if (j < n_pages) tier[j] = t;
+    __syncthreads();
+  }
+  if (j < n_pages) {
+    int rank = 0;
+    for (int i = 0; i < n_pages; ++i) rank += tier[i] < tier[j] || (tier[i] == tier[j] && above(i, j));
     chosen[j] = rank < kp;
-    scores[j] = a;
+    scores[j] = alpha[j];
   }
   __syncthreads();
   if (j < n_pages && chosen[j]) {
@@ -192,9 +240,61 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
   }
 }
 
+// Stage 1: cosine similarity of the current prompt embedding with every
+// previous chunk's (one wave per chunk, fixed-order sums), then the top-k
+// chunks, ascending; a zero embedding has similarity 0.
+constexpr int kRetrThreads = 1024;
+__global__ __launch_bounds__(kRetrThreads) void retrieve_chunks_kernel(
+    const float* __restrict__ prompt, const float* __restrict__ chunk_prompts, int n_chunks, int emb_dim,
+    int k, float* __restrict__ sims, int32_t* __restrict__ sel) {
+  __shared__ float sim_s[HSA_MAX_CHUNKS];
+  __shared__ int chosen[HSA_MAX_CHUNKS];
+  __shared__ float cur_s;
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  if (w == 0) {
+    float n = 0.f;
+    for (int i = lane; i < emb_dim; i += kWave) n += prompt[i] * prompt[i];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o);
+    if (lane == 0) cur_s = n;
+  }
+  __syncthreads();
+  const float ncur = cur_s;
+  for (int c = w; c < n_chunks; c += kRetrThreads / kWave) {
+    const float* e = chunk_prompts + (size_t)c * emb_dim;
+    float dot = 0.f, n = 0.f;
+    for (int i = lane; i < emb_dim; i += kWave) {
+      const float x = e[i];
+      dot += prompt[i] * x;
+      n += x * x;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      dot += __shfl_xor(dot, o);
+      n += __shfl_xor(n, o);
+    }
+    if (lane == 0) sim_s[c] = (ncur > 0.f && n > 0.f) ? dot / (sqrtf(ncur) * sqrtf(n)) : 0.f;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < n_chunks; c += kRetrThreads) {
+    const float a = sim_s[c];
+    int rank = 0;
+    for (int i = 0; i < n_chunks; ++i) rank += sim_s[i] > a || (sim_s[i] == a && i < c);
+    chosen[c] = rank < k;
+    sims[c] = a;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < n_chunks; c += kRetrThreads) {
+    if (!chosen[c]) continue;
+    int pos = 0;
+    for (int i = 0; i < c; ++i) pos += chosen[i];
+    if (pos < k) sel[pos] = c;
+  }
+}
+
 template <typename T>
-void launch_score(const Dims& s, const void* q, const PageTable& tab, int n_pages, float* page_kmean,
-                  float* scores, int32_t* sel, char* ws, const WsLayout& w, hipStream_t st) {
+void launch_score(const Dims& s, const void* q, const PageTable& tab, const ChunkFilter& filt, int n_pages,
+                  float* page_kmean, float* scores, int32_t* sel, char* ws, const WsLayout& w, hipStream_t st) {
   const ScorePlan sp = score_plan(s, n_pages);
   const int cpr = s.H * s.d * s.esize / 16;
   const ColMap m = col_map(cpr);
@@ -203,23 +303,26 @@ void launch_score(const Dims& s, const void* q, const PageTable& tab, int n_page
   float* qbar = reinterpret_cast<float*>(ws + w.score_qbar);
   float* kbar = reinterpret_cast<float*>(ws + w.score_kbar);
   hipLaunchKernelGGL(score_partial_kernel<T>, grid, dim3(kScoreThreads), 0, st,
-                     reinterpret_cast<const T*>(q), tab, n_pages, s.Lp, s.Lq, cpr, sp.page_chunks,
+                     reinterpret_cast<const T*>(q), tab, filt, n_pages, s.Lp, s.Lq, cpr, sp.page_chunks,
                      sp.page_rows, sp.q_rows, m.cols, m.par, partial);
   const int hd = s.H * s.d;
-  hipLaunchKernelGGL(score_means_kernel, dim3(n_pages + 1, (hd + kMeanCols - 1) / kMeanCols), dim3(kScoreThreads), 0, st, partial, tab,
-                     n_pages, sp.page_chunks, sp.q_chunks, hd, s.Lp, s.Lq, page_kmean, kbar, qbar);
+  hipLaunchKernelGGL(score_means_kernel, dim3(n_pages + 1, (hd + kMeanCols - 1) / kMeanCols), dim3(kScoreThreads),
+                     0, st, partial, tab, filt, n_pages, sp.page_chunks, sp.q_chunks, hd, s.Lp, s.Lq, page_kmean,
+                     kbar, qbar);
   const float scale = 1.f / ((float)s.H * sqrtf((float)s.d));
-  hipLaunchKernelGGL(score_topk_kernel, dim3(1), dim3(kTopkThreads), 0, st, qbar, kbar, n_pages, hd,
+  hipLaunchKernelGGL(score_topk_kernel, dim3(1), dim3(kTopkThreads), 0, st, qbar, kbar, filt, n_pages, hd,
                      scale, s.Kp, scores, sel);
 }
 
 }  // namespace
 }  // namespace hsa
 
-extern "C" hsa_rc hsa_score_pages(const hsa_geom* geom, const void* q, const void* const* page_k,
-                                  float* page_kmean, int32_t n_pages, float* scores, int32_t* sel_pages,
-                                  void* ws, size_t ws_bytes, hsa_stream stream) {
-  using namespace hsa;
+namespace hsa {
+namespace {
+
+hsa_rc score_entry(const hsa_geom* geom, const void* q, const void* const* page_k, float* page_kmean,
+                   int32_t n_pages, const ChunkFilter& filt, float* scores, int32_t* sel_pages, void* ws,
+                   size_t ws_bytes, hsa_stream stream) {
   Dims s;
   hsa_rc rc = derive(geom, &s);
   if (rc != HSA_OK) return rc;
@@ -236,8 +339,46 @@ extern "C" hsa_rc hsa_score_pages(const hsa_geom* geom, const void* q, const voi
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* wsb = static_cast<char*>(ws);
   if (s.bf16)
-    launch_score<bf16_t>(s, q, tab, n_pages, page_kmean, scores, sel_pages, wsb, w, st);
+    launch_score<bf16_t>(s, q, tab, filt, n_pages, page_kmean, scores, sel_pages, wsb, w, st);
   else
-    launch_score<float>(s, q, tab, n_pages, page_kmean, scores, sel_pages, wsb, w, st);
+    launch_score<float>(s, q, tab, filt, n_pages, page_kmean, scores, sel_pages, wsb, w, st);
+  return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace hsa
+
+extern "C" hsa_rc hsa_score_pages(const hsa_geom* geom, const void* q, const void* const* page_k,
+                                  float* page_kmean, int32_t n_pages, float* scores, int32_t* sel_pages,
+                                  void* ws, size_t ws_bytes, hsa_stream stream) {
+  return hsa::score_entry(geom, q, page_k, page_kmean, n_pages, hsa::ChunkFilter{nullptr, nullptr, 1}, scores,
+                          sel_pages, ws, ws_bytes, stream);
+}
+
+extern "C" hsa_rc hsa_score_chunk_pages(const hsa_geom* geom, const void* q, const void* const* page_k,
+                                        float* page_kmean, int32_t n_pages, const int32_t* page_chunk,
+                                        const int32_t* sel_chunks, int32_t k_chunks, float* scores,
+                                        int32_t* sel_pages, void* ws, size_t ws_bytes, hsa_stream stream) {
+  using namespace hsa;
+  if (!page_chunk || !sel_chunks) return HSA_ERR_NULL_ARG;
+  Dims s;
+  hsa_rc rc = derive(geom, &s);
+  if (rc != HSA_OK) return rc;
+  if (k_chunks < 1 || k_chunks > s.Kp || s.Kp % k_chunks != 0) return HSA_ERR_BAD_PARAM;
+  return score_entry(geom, q, page_k, page_kmean, n_pages, ChunkFilter{page_chunk, sel_chunks, k_chunks}, scores,
+                     sel_pages, ws, ws_bytes, stream);
+}
+
+extern "C" hsa_rc hsa_retrieve_chunks(const float* prompt, const float* chunk_prompts, int32_t n_chunks,
+                                      int32_t emb_dim, int32_t k_chunks, float* sims, int32_t* sel_chunks,
+                                      hsa_stream stream) {
+  using namespace hsa;
+  if (!prompt || !chunk_prompts || !sims || !sel_chunks) return HSA_ERR_NULL_ARG;
+  if (n_chunks < 1 || n_chunks > HSA_MAX_CHUNKS || emb_dim < 1 || emb_dim > HSA_MAX_EMBED || k_chunks < 1 ||
+      k_chunks > n_chunks)
+    return HSA_ERR_BAD_PARAM;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(retrieve_chunks_kernel, dim3(1), dim3(kRetrThreads), 0, st, prompt, chunk_prompts, n_chunks,
+                     emb_dim, k_chunks, sims, sel_chunks);
   return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
 }

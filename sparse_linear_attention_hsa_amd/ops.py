@@ -88,6 +88,21 @@ def hsa_score_pages(geom, q, pages_k, page_kmean, scores, sel_pages, ws, stream=
         _p(ws), ws.numel() * ws.element_size(), _s(stream)))
 
 
+def hsa_retrieve_chunks(prompt, chunk_prompts, k_chunks, sims, sel_chunks, stream=None):
+    """prompt [E] and chunk_prompts [C][E] float32 device tensors."""
+    n_chunks, emb_dim = chunk_prompts.shape
+    check("hsa_retrieve_chunks", lib().hsa_retrieve_chunks(
+        _p(prompt), _p(chunk_prompts), n_chunks, emb_dim, k_chunks, _p(sims), _p(sel_chunks), _s(stream)))
+
+
+def hsa_score_chunk_pages(geom, q, pages_k, page_kmean, page_chunk, sel_chunks, scores, sel_pages, ws,
+                          stream=None):
+    check("hsa_score_chunk_pages", lib().hsa_score_chunk_pages(
+        ctypes.byref(geom), _p(q), _table(pages_k), _p(page_kmean), len(pages_k), _p(page_chunk),
+        _p(sel_chunks), sel_chunks.numel(), _p(scores), _p(sel_pages), _p(ws), ws.numel() * ws.element_size(),
+        _s(stream)))
+
+
 def hsa_gather_pages(geom, pages_k, pages_v, sel_pages, k_act, v_act, kblk_mean=None, stream=None):
     check("hsa_gather_pages", lib().hsa_gather_pages(
         ctypes.byref(geom), _table(pages_k), _table(pages_v), len(pages_k), _p(sel_pages), _p(k_act), _p(v_act),

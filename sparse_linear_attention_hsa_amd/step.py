@@ -57,6 +57,9 @@ class HsaStep:
         # beside block selection and the sparse branch
         self.ws_lin = torch.empty(ops.hsa_linear_workspace_bytes(geom), dtype=torch.uint8, device=dev)
         self.side = torch.cuda.Stream(device=dev)
+        # prompt-level retrieval outputs (sized on first use)
+        self.chunk_sims: Optional[torch.Tensor] = None
+        self.sel_chunks: Optional[torch.Tensor] = None
 
     # individual stages --------------------------------------------------
     def score(self, q, pages_k: Sequence[Optional[torch.Tensor]], stream=None, use_cache: bool = False):
@@ -64,6 +67,20 @@ class HsaStep:
         filled by index_pages) instead of reading its keys."""
         pages = [None] * self.n_pages if use_cache else pages_k
         ops.hsa_score_pages(self.geom, q, pages, self.page_kmean, self.scores, self.sel_pages, self.ws, stream)
+
+    def retrieve(self, q, pages_k, chunks, stream=None):
+        """Stage 1 and page scoring inside the retrieved chunks (WorldAttention
+        paper, section 3.2, "Stage 1: prompt-level retrieval"; section 4.5,
+        candidate chunks).  chunks = (prompt [E], chunk_prompts [C][E] float32,
+        page_chunk [P] int32, k_chunks), all device tensors but k_chunks."""
+        prompt, chunk_prompts, page_chunk, k_chunks = chunks
+        n_chunks = chunk_prompts.shape[0]
+        if self.chunk_sims is None or self.chunk_sims.numel() != n_chunks or self.sel_chunks.numel() != k_chunks:
+            self.chunk_sims = torch.empty(n_chunks, dtype=torch.float32, device=q.device)
+            self.sel_chunks = torch.empty(k_chunks, dtype=torch.int32, device=q.device)
+        ops.hsa_retrieve_chunks(prompt, chunk_prompts, k_chunks, self.chunk_sims, self.sel_chunks, stream)
+        ops.hsa_score_chunk_pages(self.geom, q, pages_k, self.page_kmean, page_chunk, self.sel_chunks, self.scores,
+                                  self.sel_pages, self.ws, stream)
 
     def index_pages(self, q, pages_k: Sequence[torch.Tensor], stream=None):
         """Build the page index: every page's mean key (WorldAttention paper,
@@ -101,11 +118,16 @@ class HsaStep:
 
     # the whole step -----------------------------------------------------
     def run(self, q, pages_k, pages_v, e_k, e_v, w_g, x, tau, stream=None, concurrent: bool = True,
-            indexed: bool = False):
+            indexed: bool = False, chunks=None):
         """indexed: score from the page index (index_pages ran before) rather
-        than from the pages' keys; the gather still copies the pages."""
+        than from the pages' keys; the gather still copies the pages.
+        chunks: run prompt-level retrieval first and score only the pages of
+        the retrieved chunks (see retrieve)."""
         main = torch.cuda.current_stream() if stream is None else stream
-        self.score(q, pages_k, main, use_cache=indexed)
+        if chunks is not None:
+            self.retrieve(q, [None] * self.n_pages if indexed else pages_k, chunks, main)
+        else:
+            self.score(q, pages_k, main, use_cache=indexed)
         self.gather(pages_k, pages_v, main)
         if concurrent:
             gathered = torch.cuda.Event()

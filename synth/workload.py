@@ -36,7 +36,7 @@ import numpy as np
 
 from .configs import Config
 
-TID = dict(q=1, k=2, v=3, x=4, ek=5, ev=6, wg=7, mu=8, struct=9, tau=10, hot=11, host=12)
+TID = dict(q=1, k=2, v=3, x=4, ek=5, ev=6, wg=7, mu=8, struct=9, tau=10, hot=11, host=12, prompt=13)
 
 
 def round_bf16(a: np.ndarray) -> np.ndarray:
@@ -250,6 +250,23 @@ def layer_arrays(cfg: Config, layer: int, n_steps: int, workers: int = 8) -> Dic
         xs = list(ex.map(w.x, range(n_steps)))
     return dict(pages_k=pk, pages_v=pv, e_k=w.e_k(), e_v=w.e_v(), w_g=w.w_g(), tau=w.tau(), q=qs, x=xs,
                 target_pages=w.plant.target_pages)
+
+
+def chunk_prompts(cfg: Config, pages_per_chunk: int, emb_dim: int = 512, noise: float = 0.5, layer: int = 0):
+    """Prompt-level retrieval inputs for a layer's history: pages are grouped
+    into chunks of pages_per_chunk consecutive ids (the last one may be
+    shorter), every previous chunk gets a seeded N(0, 1) prompt embedding, and
+    the current prompt is the embedding of the chunk holding the first target
+    page plus N(0, noise^2) noise.  Returns (page_chunk [P] int32,
+    current [E] float32, previous [C][E] float32, that chunk's id)."""
+    n_chunks = -(-cfg.n_pages // pages_per_chunk)
+    page_chunk = (np.arange(cfg.n_pages) // pages_per_chunk).astype(np.int32)
+    w = Workload(cfg, layer)
+    target = int(page_chunk[int(w.plant.target_pages[0])])
+    r = w.rng("prompt")
+    prev = r.standard_normal((n_chunks, emb_dim)).astype(np.float32)
+    cur = (prev[target] + noise * r.standard_normal(emb_dim)).astype(np.float32)
+    return page_chunk, cur, prev, target
 
 
 def stack_host_pages(cfg: Config) -> List[np.ndarray]:

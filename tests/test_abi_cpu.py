@@ -93,6 +93,24 @@ def test_entry_points_reject_bad_arguments_before_launch(lib):
     assert lib.hsa_score_pages(ctypes.byref(g), fake, pages, None, 0, fake, fake, fake, 1 << 40, None) == 4
     assert lib.hsa_score_pages(ctypes.byref(g), fake, pages, None, 16, fake, fake, fake, ws_small, None) == 5
     assert lib.hsa_score_pages(ctypes.byref(g), fake, pages, None, 16, fake, fake, None, 1 << 40, None) == 5
+    # chunk-restricted scoring: NULL chunk arrays, k_chunks out of range or
+    # not dividing K_p (4 here), then the page checks of plain scoring
+    sc = lib.hsa_score_chunk_pages
+    assert sc(ctypes.byref(g), fake, pages, None, 16, None, fake, 1, fake, fake, fake, 1 << 40, None) == 1
+    assert sc(ctypes.byref(g), fake, pages, None, 16, fake, None, 1, fake, fake, fake, 1 << 40, None) == 1
+    for k in (0, 3, 5, -1):
+        assert sc(ctypes.byref(g), fake, pages, None, 16, fake, fake, k, fake, fake, fake, 1 << 40, None) == 4, k
+    assert sc(ctypes.byref(g), fake, null_pages, None, 16, fake, fake, 2, fake, fake, fake, 1 << 40, None) == 1
+    assert sc(ctypes.byref(g), fake, pages, None, 16, fake, fake, 2, fake, fake, fake, ws_small, None) == 5
+    # prompt-level retrieval: NULL arrays, sizes, k above the chunk count
+    rc = lib.hsa_retrieve_chunks
+    assert rc(None, fake, 8, 16, 1, fake, fake, None) == 1
+    assert rc(fake, fake, 8, 16, 1, None, fake, None) == 1
+    assert rc(fake, fake, 0, 16, 1, fake, fake, None) == 4
+    assert rc(fake, fake, _lib.HSA_MAX_CHUNKS + 1, 16, 1, fake, fake, None) == 4
+    assert rc(fake, fake, 8, 0, 1, fake, fake, None) == 4
+    assert rc(fake, fake, 8, 16, 9, fake, fake, None) == 4
+    assert rc(fake, fake, 8, 16, 0, fake, fake, None) == 4
     # gather: NULL page entry, NULL outputs
     assert lib.hsa_gather_pages(ctypes.byref(g), null_pages, pages, 16, fake, fake, fake, None, None) == 1
     assert lib.hsa_gather_pages(ctypes.byref(g), pages, pages, 16, fake, None, fake, None, None) == 1

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 from oracle import hsa_oracle as orc
-from synth import C0, M1, M2, M3, M4, M5, with_
+from synth import C0, M1, M2, M3, M4, M5, chunk_prompts, with_
 
 from gpu_harness import (TOL, Run, assert_close, check_block_selection, gpu_block_lists, host, untile_v)
 
@@ -111,6 +111,67 @@ def test_page_index_scoring_matches_page_scan(ran):
     ran.run(indexed=True)
     for k in names:
         assert torch.equal(a[k], getattr(st, k)), k
+
+
+def _chunk_cases(cfg):
+    """(pages per chunk, k) pairs: chunks of 2 pages (short chunks for K_p > 2)
+    and of K_p pages, every k that divides K_p and fits the chunk count."""
+    out = []
+    for ppc in sorted({2, cfg.n_sel_pages}):
+        n_chunks = -(-cfg.n_pages // ppc)
+        out += [(ppc, k) for k in range(1, cfg.n_sel_pages + 1) if cfg.n_sel_pages % k == 0 and k <= n_chunks]
+    return out
+
+
+def _valid_chunk_pages(alpha, page_chunk, chunks, k_p, sel):
+    """A selection that differs from the oracle's only inside near-ties: in
+    every chosen chunk, no unchosen page scores above a chosen one."""
+    sel = set(int(j) for j in sel)
+    if len(sel) != k_p:
+        return False
+    for ch in chunks:
+        ids = [j for j in range(len(alpha)) if page_chunk[j] == ch]
+        chosen = [alpha[j] for j in ids if j in sel]
+        rest = [alpha[j] for j in ids if j not in sel]
+        if chosen and rest and min(chosen) < max(rest) - orc.TIE_EPS:
+            return False
+    return True
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_prompt_retrieval_and_chunk_pages(cfg):
+    """Stage 1 (cosine top-k chunks) and page scoring inside the chosen chunks
+    against the oracle, for every chunk size and k of _chunk_cases; then the
+    whole step on the retrieved pages."""
+    r = Run(cfg)
+    st = r.step
+    q_np = r.np["q"]
+    for ppc, k in _chunk_cases(cfg):
+        page_chunk, cur, prev, _ = chunk_prompts(cfg, ppc)
+        print(f"  pages per chunk {ppc}, k {k}", flush=True)
+        chunks = (torch.from_numpy(cur).cuda(), torch.from_numpy(prev).cuda(),
+                  torch.from_numpy(page_chunk).cuda(), k)
+        st.retrieve(r.q, r.pk, chunks)
+        torch.cuda.synchronize()
+        ref = orc.prompt_retrieval(cur, prev, k)
+        np.testing.assert_allclose(host(st.chunk_sims), ref["sims"], rtol=0, atol=1e-5)
+        gsel = host(st.sel_chunks).astype(np.int64)
+        if not np.array_equal(gsel, ref["sel"]):
+            assert ref["tie"] and orc.valid_page_selection(ref["sims"], gsel, k)
+        sc = orc.score_chunk_pages(q_np, r.pk_np, page_chunk, gsel, cfg.n_sel_pages)
+        scores = host(st.scores)
+        cand = np.isfinite(sc["alpha"])
+        np.testing.assert_allclose(scores[cand], sc["alpha"][cand], rtol=0, atol=2e-5)
+        assert np.all(np.isneginf(scores[~cand]))
+        psel = host(st.sel_pages).astype(np.int64)
+        if not np.array_equal(psel, sc["sel"]):
+            assert sc["tie"] and _valid_chunk_pages(sc["alpha"], page_chunk, gsel, cfg.n_sel_pages, psel)
+    # the whole step with retrieval (last case), against the oracle on its pages
+    r.step.run(r.q, r.pk, r.pv, r.e_k, r.e_v, r.w_g, r.x, r.tau, chunks=chunks)
+    torch.cuda.synchronize()
+    lists, _, _ = gpu_block_lists(st)
+    ref = r.oracle(sel_pages=st.sel_pages.cpu().numpy(), block_sel=lists)
+    assert_close("out", host(st.out), ref["out"], cfg)
 
 
 # --------------------------------------------------------------- special cases
