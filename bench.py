@@ -31,13 +31,14 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 STAGES = ("score", "gather", "linear", "select", "sparse", "fuse")
 
 
-def stage_model(cfg, n_sel_total: int, indexed: bool = False):
+def stage_model(cfg, n_sel_total: int, indexed: bool = False, scored_pages=None):
     """Algorithmic work of one call of each stage (bytes moved or flops).
     With the page index, scoring reads the pages' fp32 mean keys instead of
-    their keys."""
+    their keys; with prompt-level retrieval it reads only scored_pages."""
     es = 2 if cfg.dtype == "bf16" else 4
     H, d, Lp, Lq, L, B, r, P = (cfg.n_heads, cfg.head_dim, cfg.page_tokens, cfg.query_tokens,
-                                cfg.active_tokens, cfg.block, cfg.rank, cfg.n_pages)
+                                cfg.active_tokens, cfg.block, cfg.rank,
+                                cfg.n_pages if scored_pages is None else scored_pages)
     D = H * d
     return {
         "score": dict(bound="hbm", bytes=(P * D * 4 if indexed else P * Lp * D * es) + Lq * D * es),
@@ -240,6 +241,10 @@ def main():
     ap.add_argument("--config", default="c1_full")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step as one HIP graph")
+    ap.add_argument("--chunks", type=int, default=0,
+                    help="prompt-level retrieval first: keep the K most similar chunks and score only their pages "
+                         "(K_p/K pages from each)")
+    ap.add_argument("--pages-per-chunk", type=int, default=8, help="history pages per chunk for --chunks")
     ap.add_argument("--page-index", action="store_true",
                     help="score from a page index of mean keys built once before the timed steps "
                          "(as when pages are written) instead of reading every page's keys")
@@ -295,16 +300,28 @@ def main():
     if indexed:
         st.index_pages(q, pk)  # the page index, built once (outside the timed steps)
         torch.cuda.synchronize()
+    chunks = None
+    if args.chunks:
+        from synth import chunk_prompts
+        page_chunk, cur, prev, _ = chunk_prompts(cfg, args.pages_per_chunk)
+        chunks = (torch.from_numpy(cur).cuda(), torch.from_numpy(prev).cuda(), torch.from_numpy(page_chunk).cuda(),
+                  args.chunks)
+
+    def score_stage():
+        if chunks is not None:
+            st.retrieve(q, [None] * cfg.n_pages if indexed else pk, chunks)
+        else:
+            st.score(q, pk, use_cache=indexed)
 
     def one_step():
         # the step's own schedule: the linear branch on a side stream beside
         # block selection and the sparse branch, joined before the fusion
         # (on the current stream, which is the capture stream under --graph)
-        st.run(q, pk, pv, e_k, e_v, w_g, x, tau, indexed=indexed)
+        st.run(q, pk, pv, e_k, e_v, w_g, x, tau, indexed=indexed, chunks=chunks)
 
     def one_step_staged(ev, kev):
         # the same six calls in order on one stream, with events between them
-        calls = (lambda: st.score(q, pk, use_cache=indexed), lambda: st.gather(pk, pv),
+        calls = (score_stage, lambda: st.gather(pk, pv),
                  lambda: st.linear(q, e_k, e_v),
                  lambda: st.select(q, tau), lambda: st.sparse(q, kernel_events=kev), lambda: st.fuse(x, w_g))
         for i, fn in enumerate(calls):
@@ -359,7 +376,11 @@ def main():
 
     counts = st.blk_count.cpu().numpy()
     n_sel_total = int(counts.sum())
-    model = stage_model(cfg, n_sel_total, indexed)
+    scored_pages = cfg.n_pages
+    if chunks is not None:  # only the retrieved chunks' pages are read
+        pc = chunks[2].cpu().numpy()
+        scored_pages = int(np.isin(pc, st.sel_chunks.cpu().numpy()).sum())
+    model = stage_model(cfg, n_sel_total, indexed, scored_pages)
     sparse_tf = model["sparse"]["flops"] / (stage_ms["sparse"] * 1e-3) / 1e12
     lin_tf = model["linear"]["flops"] / (stage_ms["linear"] * 1e-3) / 1e12
     peak_tf = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -379,7 +400,8 @@ def main():
         "config": {"workload": cfg.name, "heads": cfg.n_heads, "head_dim": cfg.head_dim,
                    "retrieved_tokens": cfg.active_tokens, "query_tokens": cfg.query_tokens,
                    "history_pages": cfg.n_pages, "block": cfg.block, "rank": cfg.rank,
-                   "graph": bool(args.graph), "page_index": indexed},
+                   "graph": bool(args.graph), "page_index": indexed, "chunks": args.chunks,
+                   "pages_per_chunk": args.pages_per_chunk if args.chunks else None},
         "ms_per_step_stats": {"median": round(float(np.median(per_step)), 4),
                               "min": round(float(per_step.min()), 4),
                               "p90": round(float(np.percentile(per_step, 90)), 4)},

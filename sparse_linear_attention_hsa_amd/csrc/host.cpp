@@ -44,10 +44,10 @@ hsa_rc derive(const hsa_geom* g, Dims* o) {
   return HSA_OK;
 }
 
-ScorePlan score_plan(const Dims& s, int n_pages) {
+ScorePlan score_plan(const Dims& s, int n_pages, bool few_pages) {
   ScorePlan p;
   const int target = 640;
-  int pc = std::max(1, std::min(cdiv(s.Lp, 16), cdiv(target, std::max(1, n_pages))));
+  int pc = std::max(1, std::min(cdiv(s.Lp, 16), few_pages ? 64 : cdiv(target, std::max(1, n_pages))));
   p.page_rows = cdiv(s.Lp, pc);
   p.page_chunks = cdiv(s.Lp, p.page_rows);
   int qc = std::max(1, std::min(cdiv(s.Lq, 16), 128));
@@ -98,9 +98,9 @@ WsLayout ws_layout(const Dims& s, int n_pages) {
   WsLayout w;
   const size_t hd = (size_t)s.H * s.d;
   // score
-  ScorePlan sp = score_plan(s, n_pages);
+  const ScorePlan sp = score_plan(s, n_pages), spf = score_plan(s, n_pages, true);
   w.score_partial = 0;
-  w.score_qbar = align256(w.score_partial + (size_t)sp.units * hd * 4);
+  w.score_qbar = align256(w.score_partial + (size_t)std::max(sp.units, spf.units) * hd * 4);
   w.score_kbar = align256(w.score_qbar + hd * 4);
   w.score_end = align256(w.score_kbar + (size_t)n_pages * hd * 4);
   // linear

@@ -27,7 +27,9 @@ struct ScorePlan {
   int q_rows;
   int units;         // n_pages * page_chunks + q_chunks
 };
-ScorePlan score_plan(const Dims& s, int n_pages);
+// few_pages: only a few of the n_pages will be read (scoring restricted to
+// retrieved chunks), so every page is cut finer to keep the chip busy.
+ScorePlan score_plan(const Dims& s, int n_pages, bool few_pages = false);
 
 // Linear-branch projection split over the sequence axis.
 struct ProjPlan {

@@ -295,7 +295,7 @@ __global__ __launch_bounds__(kRetrThreads) void retrieve_chunks_kernel(
 template <typename T>
 void launch_score(const Dims& s, const void* q, const PageTable& tab, const ChunkFilter& filt, int n_pages,
                   float* page_kmean, float* scores, int32_t* sel, char* ws, const WsLayout& w, hipStream_t st) {
-  const ScorePlan sp = score_plan(s, n_pages);
+  const ScorePlan sp = score_plan(s, n_pages, filt.page_chunk != nullptr);
   const int cpr = s.H * s.d * s.esize / 16;
   const ColMap m = col_map(cpr);
   dim3 grid(sp.units, (cpr + m.cols - 1) / m.cols);
