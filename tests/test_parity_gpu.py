@@ -166,6 +166,11 @@ def test_prompt_retrieval_and_chunk_pages(cfg):
         psel = host(st.sel_pages).astype(np.int64)
         if not np.array_equal(psel, sc["sel"]):
             assert sc["tie"] and _valid_chunk_pages(sc["alpha"], page_chunk, gsel, cfg.n_sel_pages, psel)
+        # the same from the page index, every page pointer NULL: bit for bit
+        st.index_pages(r.q, r.pk)
+        st.retrieve(r.q, [None] * cfg.n_pages, chunks)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(st.scores), scores) and np.array_equal(host(st.sel_pages), psel)
     # the whole step with retrieval (last case), against the oracle on its pages
     r.step.run(r.q, r.pk, r.pv, r.e_k, r.e_v, r.w_g, r.x, r.tau, chunks=chunks)
     torch.cuda.synchronize()
