@@ -52,6 +52,12 @@ SIGNATURES = {
     "hsa_geom_check": (_i32, [_GP]),
     "hsa_rc_string": (ctypes.c_char_p, [_i32]),
     "hsa_abi_version": (_i32, []),
+    "hsa_tier_create": (_vp, [_i32, _i32, _i32]),
+    "hsa_tier_destroy": (None, [_vp]),
+    "hsa_tier_seed": (_i32, [_vp, _vp, _i32, _i32, _vp]),
+    "hsa_tier_request": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _vp]),
+    "hsa_tier_locate": (_i32, [_vp, _i32, _vp, _vp]),
+    "hsa_tier_stats": (_i32, [_vp, _vp]),
     "hsa_probe_mfma_bf16": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp]),
     "hsa_probe_hbm_copy": (_i32, [_vp, _vp, _sz, _vp, _vp, _vp]),
 }
