@@ -233,6 +233,95 @@ def run_stack(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+def run_tiers(args, cfg):
+    """Several generated chunks over one history whose pages live in tiers
+    (device slots for one chunk's K_p pages, pinned host slots for half the
+    history, the full backup in pageable host memory).  Per chunk: stage 1
+    and chunk-restricted scoring from the page index, the selected pages made
+    resident, the gather, then the per-step stages repeated R times (a
+    stand-in for the layers and denoising steps of one chunk).  Two runs:
+    pages fetched when selected, and the next chunk's pages predicted by
+    stage 1 on its prompt and prefetched during the current chunk."""
+    import torch
+    from synth import Workload, chunk_prompt_sequence
+    from sparse_linear_attention_hsa_amd import ops
+    from sparse_linear_attention_hsa_amd.ops import make_geom
+    from sparse_linear_attention_hsa_amd.step import HsaStep
+    from sparse_linear_attention_hsa_amd.tiers import PageTiers
+
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    kp, n_chunks_gen, R = cfg.n_sel_pages, args.tiers, args.tiers_steps
+    w = Workload(cfg)
+    s = w.small_inputs()
+    up = lambda a: torch.from_numpy(a).to(tdt).cuda()
+    q, x, e_k, e_v, w_g = (up(s[k]) for k in ("q", "x", "e_k", "e_v", "w_g"))
+    tau = torch.from_numpy(s["tau"]).cuda()
+    pk_np, pv_np = w.pages()
+    geom = make_geom(cfg.n_heads, cfg.head_dim, cfg.frame_h, cfg.frame_w, cfg.frames_per_page,
+                     cfg.query_frames, cfg.tile, cfg.n_sel_pages, cfg.rank, cfg.dtype)
+    page_chunk, prompts, prev, targets = chunk_prompt_sequence(cfg, kp, n_chunks_gen)
+    pc_d, prev_d = torch.from_numpy(page_chunk).cuda(), torch.from_numpy(prev).cuda()
+    prompts_d = [torch.from_numpy(p).cuda() for p in prompts]
+    n_hist = len(prev)
+
+    def run(prefetch: bool):
+        st = HsaStep(geom, cfg.n_pages)
+        # the page index, built when the pages were written
+        st.index_pages(q, [up(p) for p in pk_np])
+        torch.cuda.synchronize()
+        tiers = PageTiers(pk_np, pv_np, l1_slots=kp, l2_slots=cfg.n_pages // 2, dtype=tdt,
+                          l2_pages=range(cfg.n_pages // 2, cfg.n_pages))
+        main = torch.cuda.current_stream()
+        sims = torch.empty(n_hist, dtype=torch.float32, device="cuda")
+        pred = torch.empty(1, dtype=torch.int32, device="cuda")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_chunks_gen + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(main)
+        for t in range(n_chunks_gen):
+            st.retrieve(q, [None] * cfg.n_pages, (prompts_d[t], prev_d, pc_d, 1), main)
+            sel = st.sel_pages.cpu().tolist()  # the host learns the selection
+            tiers.request(sel)
+            main.wait_event(tiers.ready)
+            pk_t, pv_t = tiers.tables()
+            st.gather(pk_t, pv_t, main)
+            gathered = torch.cuda.Event()
+            gathered.record(main)
+            if prefetch and t + 1 < n_chunks_gen:
+                # predict the next chunk's history chunk (stage 1 on its prompt,
+                # on the copy stream) and bring its pages in behind the gather
+                with torch.cuda.stream(tiers.stream):
+                    ops.hsa_retrieve_chunks(prompts_d[t + 1], prev_d, 1, sims, pred, tiers.stream)
+                    nxt = int(pred.cpu())
+                tiers.request([j for j in range(cfg.n_pages) if page_chunk[j] == nxt], after=gathered)
+            for _ in range(R):
+                st.linear(q, e_k, e_v, 0, main)
+                st.select(q, tau, True, main)
+                st.sparse(q, main)
+                st.fuse(x, w_g, main)
+            ev[t + 1].record(main)
+        torch.cuda.synchronize()
+        per = [ev[t].elapsed_time(ev[t + 1]) for t in range(n_chunks_gen)]
+        return per, tiers.policy.stats(), tiers.bytes_moved
+
+    run(False)  # warm-up (allocations, first launches)
+    od, od_stats, od_bytes = run(False)
+    pf, pf_stats, pf_bytes = run(True)
+    ms_od, ms_pf = float(np.mean(od[1:])), float(np.mean(pf[1:]))
+    print(json.dumps({
+        "metric": "ms per generated chunk, pages in tiers", "value": round(ms_pf, 3), "unit": "ms/chunk",
+        "n_gpus": 1, "steps": n_chunks_gen, "warmup": 1, "ms_per_step": round(ms_pf, 3), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name + "+tiers", "history_pages": cfg.n_pages, "pages_per_chunk": kp,
+                   "device_slots": kp, "host_slots": cfg.n_pages // 2, "stage_repeats": R,
+                   "history_chunk_walk": [int(c) for c in targets]},
+        "ms_on_demand": round(ms_od, 3), "ms_prefetch": round(ms_pf, 3),
+        "exposed_fetch_ms": round(ms_od - ms_pf, 3),
+        "per_chunk_ms": {"on_demand": [round(v, 2) for v in od], "prefetch": [round(v, 2) for v in pf]},
+        "tier_stats": {"on_demand": od_stats, "prefetch": pf_stats},
+        "bytes_moved": {"on_demand": od_bytes, "prefetch": pf_bytes},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +334,10 @@ def main():
                     help="prompt-level retrieval first: keep the K most similar chunks and score only their pages "
                          "(K_p/K pages from each)")
     ap.add_argument("--pages-per-chunk", type=int, default=8, help="history pages per chunk for --chunks")
+    ap.add_argument("--tiers", type=int, default=0,
+                    help="run this many generated chunks with the pages in tiers, fetched on demand and prefetched")
+    ap.add_argument("--tiers-steps", type=int, default=120,
+                    help="per-step stages repeated per generated chunk under --tiers (30 layers x 4 steps)")
     ap.add_argument("--page-index", action="store_true",
                     help="score from a page index of mean keys built once before the timed steps "
                          "(as when pages are written) instead of reading every page's keys")
@@ -272,6 +365,8 @@ def main():
     from sparse_linear_attention_hsa_amd.step import HsaStep
 
     cfg = CONFIGS[args.config]
+    if args.tiers:
+        return run_tiers(args, cfg)
     if cfg.layers > 1 or cfg.steps > 1:
         return run_stack(args, cfg)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32

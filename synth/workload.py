@@ -269,6 +269,22 @@ def chunk_prompts(cfg: Config, pages_per_chunk: int, emb_dim: int = 512, noise: 
     return page_chunk, cur, prev, target
 
 
+def chunk_prompt_sequence(cfg: Config, pages_per_chunk: int, n: int, emb_dim: int = 512, noise: float = 0.5):
+    """Prompts of n generated chunks over one history: as chunk_prompts, but
+    the t-th prompt is the embedding of history chunk targets[t] plus noise,
+    with targets a seeded walk that never repeats the previous chunk.
+    Returns (page_chunk [P] int32, prompts [n][E], previous [C][E], targets)."""
+    page_chunk, _, prev, first = chunk_prompts(cfg, pages_per_chunk, emb_dim, noise)
+    r = Workload(cfg).rng("prompt", page=1)
+    n_chunks = len(prev)
+    targets = [first]
+    for _ in range(n - 1):
+        step = int(r.integers(1, n_chunks)) if n_chunks > 1 else 0
+        targets.append((targets[-1] + step) % n_chunks)
+    prompts = np.stack([prev[c] + noise * r.standard_normal(emb_dim) for c in targets]).astype(np.float32)
+    return page_chunk, prompts, prev, np.asarray(targets)
+
+
 def stack_host_pages(cfg: Config) -> List[np.ndarray]:
     """Per layer, the page ids that start in pinned host memory (layer stack).
 
