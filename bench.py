@@ -4,11 +4,20 @@
 
 One step = the whole hot path over one chunk of one layer: page scoring ->
 gather -> linear branch -> block selection -> sparse branch -> fusion (six
-C-ABI calls on one stream), on seeded synthetic inputs already resident in
-HBM.  Prints ONE JSON line.  The metric is ms per chunk (lower is better);
-attended TFLOP/s of the sparse branch, per-stage times, the roofline of the
-dominant kernel and the CPU oracle's time (bounded sample) are reported in
-the same line.
+C-ABI calls; the linear branch on a side stream), on seeded synthetic inputs
+already resident in HBM.  Prints ONE JSON line.  The metric is ms per chunk
+(lower is better); attended TFLOP/s of the sparse branch, per-stage times,
+the roofline of the dominant kernel and the CPU oracle's time (bounded
+sample) are reported in the same line.
+
+Variants (each reports its own line; the default is the headline workload):
+  --config c4_stack        the 30-layer x 4-step chunk with host-resident pages
+  --page-index             score from mean keys kept when pages were written
+  --chunks K               prompt-level retrieval first (top-K chunks), scoring
+                           only their pages (--pages-per-chunk, default 8)
+  --tiers N                N generated chunks over a history in page tiers,
+                           fetched on demand vs predicted and prefetched
+  --graph                  the step replayed as one HIP graph
 """
 from __future__ import annotations
 
