@@ -38,8 +38,22 @@
  *  - Sizes used below: H = n_heads, d = head_dim (64 or 128), D = H*d,
  *    Lp = frames_per_page*frame_h*frame_w (tokens per page),
  *    Lq = query_frames*frame_h*frame_w (query tokens of the chunk),
- *    B = tile_t*tile_h*tile_w, L = n_sel_pages*Lp (active keys),
- *    nKB = L/B, nQB = Lq/B, r = rank, P = n_pages.
+ *    B = tile_t*tile_h*tile_w, r = rank, P = n_pages,
+ *    Lh = n_sel_pages*Lp (keys of the retrieved pages),
+ *    s = intra_split, L = Lh (s = 0) or Lh + Lq (s > 0) active keys,
+ *    Bk = B (s = 0) or B/s (s > 0) tokens per key block, nKB = L/Bk key
+ *    blocks, nQB = Lq/B query blocks, nKBh = Lh/B,
+ *    nC = nKB (s = 0) or nKBh + Lq/Bk (s > 0) selection candidates.
+ *  - Intra-chunk keys (intra_split = s > 0; paper section 3.3, "Inter- and
+ *    intra-chunk sparse granularity": the retrieved history is partitioned
+ *    coarsely, the current chunk's own tokens finely, both through the same
+ *    block-sparse interface).  The chunk's Lq tokens follow the Lh history
+ *    keys in the active buffer.  Key blocks are Bk = B/s tokens: a B-token
+ *    history tile is s consecutive key blocks, selected together as one
+ *    candidate; each Bk-token block of the chunk is a candidate of its own.
+ *    Bk-token blocks of the chunk are consecutive slices of its B-token tiles,
+ *    so the caller orders the tokens inside a tile so that each slice is a
+ *    sub-cube (e.g. a (4,6,4) tile as two (4,3,4) halves).
  */
 #ifndef HSA_ATTN_H
 #define HSA_ATTN_H
@@ -51,9 +65,10 @@
 extern "C" {
 #endif
 
-#define HSA_ATTN_ABI_VERSION 1
+#define HSA_ATTN_ABI_VERSION 2
 #define HSA_MAX_PAGES 128      /* pages per call (pointer tables travel as launch arguments) */
 #define HSA_MAX_KBLOCKS 2048   /* nKB limit of the block selection (one sort per row in LDS) */
+#define HSA_MAX_INTRA_SPLIT 4  /* largest intra_split */
 #define HSA_MAX_ROWS 4096      /* H * nQB limit (selection rows; the sparse branch plans them in LDS) */
 #define HSA_MAX_CHUNKS 4096    /* previous chunks in prompt-level retrieval (ranked in LDS) */
 #define HSA_MAX_EMBED 65536    /* prompt embedding width */
@@ -78,6 +93,10 @@ typedef struct {
                                             B = product, a multiple of 16, at most 192    */
   int32_t n_sel_pages, rank;             /* K_p (pages retrieved), r (linear-branch rank) */
   int32_t dtype;                         /* hsa_dtype                                     */
+  int32_t intra_split;                   /* s: 0 = keys of the retrieved pages only;
+                                            1..HSA_MAX_INTRA_SPLIT = the chunk's own tokens
+                                            follow them in key blocks of B/s tokens
+                                            (B/s a multiple of 16)                         */
 } hsa_geom;
 
 typedef struct ihipStream_t* hsa_stream;  /* a hipStream_t */
@@ -172,12 +191,34 @@ hsa_rc hsa_score_chunk_pages(const hsa_geom* geom, const void* q, const void* co
  *                  16-token granules stored d-major (the transposed layout the
  *                  PV and projection products read).  Element (h, t, c) is at
  *                  ((h*(L/16) + t/16)*d + c)*16 + t%16.
- *  kblk_mean       [H][nKB][d] float32 out or NULL: mean key of every B-token
- *                  block of the active buffer (input of hsa_block_select).
+ *  kblk_mean       [H][nKB][d] float32 out or NULL: mean key of every
+ *                  Bk-token key block of the active buffer (input of
+ *                  hsa_block_select).
+ *  Requires intra_split = 0 (HSA_ERR_BAD_PARAM otherwise): a geometry with
+ *  intra-chunk keys uses hsa_gather_active.
  * ------------------------------------------------------------------------- */
 hsa_rc hsa_gather_pages(const hsa_geom* geom, const void* const* page_k, const void* const* page_v,
                         int32_t n_pages, const int32_t* sel_pages, void* k_act, void* v_act,
                         float* kblk_mean, hsa_stream stream);
+
+/* S2 with the current chunk's own keys.  Paper section 3.3, "Inter- and
+ * intra-chunk sparse granularity" (the current chunk's tokens join the
+ * retrieved history in the block-sparse attention).  As hsa_gather_pages,
+ * and the chunk's own keys and values follow the Lh history keys:
+ *
+ *  k_cur, v_cur  [Lq][H][d] dtype device (token-major, as q): the chunk's
+ *                keys and values.  Required (non-NULL) iff intra_split > 0;
+ *                with intra_split = 0 both must be NULL and the call is
+ *                hsa_gather_pages.
+ *  k_act, v_act  as hsa_gather_pages over L = Lh + Lq keys.
+ *  kblk_mean     [H][nKB][d] float32 out or NULL: the mean of every
+ *                Bk-token key block (history and chunk alike).
+ * Errors: as hsa_gather_pages; HSA_ERR_NULL_ARG for a missing k_cur/v_cur,
+ * HSA_ERR_BAD_PARAM for k_cur/v_cur given with intra_split = 0.
+ * ------------------------------------------------------------------------- */
+hsa_rc hsa_gather_active(const hsa_geom* geom, const void* const* page_k, const void* const* page_v,
+                         int32_t n_pages, const int32_t* sel_pages, const void* k_cur, const void* v_cur,
+                         void* k_act, void* v_act, float* kblk_mean, hsa_stream stream);
 
 /* ---------------------------------------------------------------------------
  * S3 -- linear branch.  Paper section 3.3, "Linear branch" (output equation);
@@ -217,13 +258,22 @@ hsa_rc hsa_linear_branch(const hsa_geom* geom, const void* q, const void* k_act,
  * >= tau_h; tau_h >= 1 keeps every block; at least one block is kept.
  *
  *  q          [Lq][H][d] dtype.
+ *  With intra-chunk keys (intra_split = s > 0) the candidates j are the nC
+ *  blocks of the two granularities: j < nKBh is the B-token history tile j
+ *  (key blocks s*j .. s*j+s-1), j >= nKBh the chunk's Bk-token key block
+ *  s*nKBh + (j - nKBh); each is pooled by the mean over its own tokens, and
+ *  one softmax runs over all nC of them.  The output lists key blocks: a
+ *  selected history tile contributes its s key blocks.
+ *
  *  k_act      [H][L][d] dtype; may be NULL when kblk_mean is given.
- *  kblk_mean  [H][nKB][d] float32 or NULL (computed from k_act when NULL).
+ *  kblk_mean  [H][nKB][d] float32 or NULL (computed from k_act when NULL);
+ *             the mean of a history tile is the mean of its s key-block means.
  *  tau        [H] float32, each > 0.
  *  blk_count  [H][nQB] int32 out: number of selected key blocks.
  *  blk_idx    [H][nQB][nKB] int32 out: selected key-block ids, ascending;
  *             entries past the count are -1.
- *  blk_mass   [H][nQB][nKB] float32 out or NULL: the pooled masses m.
+ *  blk_mass   [H][nQB][nC] float32 out or NULL: the pooled masses m of the
+ *             candidates.
  *  Requires nKB <= HSA_MAX_KBLOCKS.
  *  Precision: pooled means are float32; each pooled logit is accumulated in
  *  float64 (products of float32 values are exact there) and rounded to
@@ -241,6 +291,7 @@ hsa_rc hsa_block_select(const hsa_geom* geom, const void* q, const void* k_act, 
  * selected blocks.
  *
  *  q, k_act, v_act        as above.
+ *  Key block j is the Bk tokens j*Bk .. j*Bk+Bk-1 of the active buffer.
  *  blk_count, blk_idx     as written by hsa_block_select.  Entries outside
  *                         [0, nKB) are skipped; a count is clamped to [0, nKB];
  *                         a row with no valid block gets zeros.

@@ -29,6 +29,10 @@ Steps, in the pages' order:
                      mass reaches tau_h.
   S5 sparse branch  [WA §3.3 "Sparse branch"; appendix A.1.3]: exact softmax
                      attention restricted to the tokens of the selected blocks.
+  intra-chunk keys  [WA §3.3 "Inter- and intra-chunk sparse granularity"]:
+                     the chunk's own tokens follow the history in the active
+                     sequence; the history is selected in B-token tiles, the
+                     chunk in finer b_intra-token blocks, under one softmax.
   S6 fusion         [WA §3.3 "Gated fusion of two branches"; SUM step (6)]:
                      G = X W, sigmoid gates per (token, head) and branch,
                      O = O_lin * g_lin + O_sp * g_sp.
@@ -382,6 +386,66 @@ def sparse_attention(q, k_act, v_act, sel, b):
 
 
 # --------------------------------------------------------------------------
+# Intra-chunk keys.  [WA §3.3 "Inter- and intra-chunk sparse granularity"]:
+# the current chunk's own tokens take part in the block-sparse attention
+# beside the retrieved history, through the same interface, with a finer
+# partition than the history (the page: 128-token (4,8,4) cubes for the
+# history, 64-token (4,4,4) cubes inside the chunk, i.e. half a history cube).
+# Readings: the chunk's keys follow the history keys in the active sequence;
+# the history keeps its B-token tiles as selection candidates and the chunk
+# is cut into b_intra-token blocks (b_intra divides B); every candidate is
+# pooled by the mean over its own tokens and one softmax runs over all of
+# them; the linear branch projects the whole active sequence.
+# --------------------------------------------------------------------------
+
+
+def key_parts(l_hist: int, b_hist: int, l_chunk: int, b_intra: int) -> List[Tuple[int, int]]:
+    """(first token, length) of every selection candidate: the history's
+    b_hist-token tiles, then the chunk's b_intra-token blocks."""
+    return ([(j * b_hist, b_hist) for j in range(l_hist // b_hist)] +
+            [(l_hist + i * b_intra, b_intra) for i in range(l_chunk // b_intra)])
+
+
+def part_means(t: np.ndarray, parts: Sequence[Tuple[int, int]]) -> np.ndarray:
+    """[H][N][d] -> [H][len(parts)][d]: the mean key of every candidate."""
+    t = np.asarray(t, dtype=np.float64)
+    return np.stack([t[:, a:a + n, :].mean(axis=1) for a, n in parts], axis=1)
+
+
+def block_selection_parts(q: np.ndarray, k_act: np.ndarray, tau: Sequence[float], b: int,
+                          parts: Sequence[Tuple[int, int]]):
+    """As block_selection, over the given candidates (query blocks stay b tokens)."""
+    qb = block_means(np.asarray(q).transpose(1, 0, 2), b)     # [H][nQB][d]
+    kb = part_means(k_act, parts)                              # [H][nC][d]
+    H, nqb, _ = qb.shape
+    mass = np.empty((H, nqb, kb.shape[1]))
+    sel: List[List[np.ndarray]] = []
+    flags = np.zeros((H, nqb), dtype=bool)
+    for h in range(H):
+        row = []
+        for i in range(nqb):
+            mass[h, i] = pooled_mass(qb[h, i], kb[h])
+            s_, f = select_blocks(mass[h, i], tau[h])
+            row.append(s_)
+            flags[h, i] = f
+        sel.append(row)
+    counts = np.array([[len(x) for x in r] for r in sel], dtype=np.int64)
+    return dict(qbar=qb, kbar=kb, mass=mass, sel=sel, counts=counts, flags=flags)
+
+
+def sparse_attention_parts(q, k_act, v_act, sel, b, parts):
+    """q [Lq][H][d]; sel[h][i] candidate ids -> O_sp [Lq][H][d]: attention of
+    query block i over exactly the tokens of its selected candidates."""
+    Lq, H, d = q.shape
+    out = np.empty((Lq, H, d))
+    for h in range(H):
+        for i in range(Lq // b):
+            idx = np.concatenate([np.arange(parts[j][0], parts[j][0] + parts[j][1]) for j in sel[h][i]])
+            out[i * b:(i + 1) * b, h, :] = attention(q[i * b:(i + 1) * b, h, :], k_act[h][idx], v_act[h][idx])
+    return out
+
+
+# --------------------------------------------------------------------------
 # S6 -- gated fusion.  [WA §3.3 "Gated fusion of two branches"; SUM step (6)]
 # --------------------------------------------------------------------------
 
@@ -412,18 +476,32 @@ def fuse(x, w_g, o_lin, o_sp):
 
 
 def hsa_step(q, pages_k, pages_v, e_k, e_v, w_g, x, tau, n_sel_pages, block,
-             sel_pages=None, block_sel=None) -> Dict[str, object]:
+             sel_pages=None, block_sel=None, k_cur=None, v_cur=None, b_intra=None) -> Dict[str, object]:
     """Run S1..S6.  `sel_pages` / `block_sel` override the selections (used to
-    re-run the downstream stages with another valid selection at a tie)."""
+    re-run the downstream stages with another valid selection at a tie).
+    With `k_cur`, `v_cur` ([Lq][H][d]) and `b_intra`, the chunk's own keys
+    join the history (intra-chunk keys); `block_sel` then lists candidates
+    of `key_parts`."""
     q = np.asarray(q, dtype=np.float64)
     sc = score_and_select(q, pages_k, n_sel_pages)
     sp = np.asarray(sc["sel"] if sel_pages is None else sel_pages)
     k_act = gather_active([np.asarray(p, np.float64) for p in pages_k], sp)
     v_act = gather_active([np.asarray(p, np.float64) for p in pages_v], sp)
+    parts = None
+    if k_cur is not None:
+        l_hist = k_act.shape[1]
+        k_act = np.concatenate([k_act, np.asarray(k_cur, np.float64).transpose(1, 0, 2)], axis=1)
+        v_act = np.concatenate([v_act, np.asarray(v_cur, np.float64).transpose(1, 0, 2)], axis=1)
+        parts = key_parts(l_hist, block, q.shape[0], b_intra)
     lin = linear_branch(q, k_act, v_act, e_k, e_v)
-    bs = block_selection(q, k_act, tau, block)
-    bsel = bs["sel"] if block_sel is None else block_sel
-    o_sp = sparse_attention(q, k_act, v_act, bsel, block)
+    if parts is None:
+        bs = block_selection(q, k_act, tau, block)
+        bsel = bs["sel"] if block_sel is None else block_sel
+        o_sp = sparse_attention(q, k_act, v_act, bsel, block)
+    else:
+        bs = block_selection_parts(q, k_act, tau, block, parts)
+        bsel = bs["sel"] if block_sel is None else block_sel
+        o_sp = sparse_attention_parts(q, k_act, v_act, bsel, block, parts)
     out = fuse(x, w_g, lin["o_lin"], o_sp)
     return dict(score=sc, sel_pages=sp, k_act=k_act, v_act=v_act, lin=lin,
-                blocks=bs, block_sel=bsel, o_sp=o_sp, out=out)
+                blocks=bs, block_sel=bsel, o_sp=o_sp, out=out, parts=parts)

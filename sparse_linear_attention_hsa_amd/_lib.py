@@ -19,6 +19,7 @@ HSA_MAX_KBLOCKS = 2048
 HSA_MAX_ROWS = 4096
 HSA_MAX_CHUNKS = 4096
 HSA_MAX_EMBED = 65536
+HSA_MAX_INTRA_SPLIT = 4
 
 RC_NAMES = {0: "HSA_OK", 1: "HSA_ERR_NULL_ARG", 2: "HSA_ERR_BAD_SHAPE", 3: "HSA_ERR_BAD_DTYPE",
             4: "HSA_ERR_BAD_PARAM", 5: "HSA_ERR_WORKSPACE", 6: "HSA_ERR_HIP"}
@@ -32,7 +33,8 @@ class Geom(ctypes.Structure):
                 ("frame_h", ctypes.c_int32), ("frame_w", ctypes.c_int32),
                 ("frames_per_page", ctypes.c_int32), ("query_frames", ctypes.c_int32),
                 ("tile_t", ctypes.c_int32), ("tile_h", ctypes.c_int32), ("tile_w", ctypes.c_int32),
-                ("n_sel_pages", ctypes.c_int32), ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("n_sel_pages", ctypes.c_int32), ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("intra_split", ctypes.c_int32)]
 
 
 _GP = ctypes.POINTER(Geom)
@@ -42,6 +44,8 @@ SIGNATURES = {
                                      _vp]),
     "hsa_retrieve_chunks": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "hsa_gather_pages": (_i32, [_GP, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp, _vp]),
+    "hsa_gather_active": (_i32, [_GP, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp]),
     "hsa_linear_branch": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
     "hsa_block_select": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "hsa_sparse_attn": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),

@@ -4,9 +4,11 @@
 // coarse estimate of where the mass lies); structured summary, method step
 // (5) (block pooling, coarse selection).
 //
-// Two kernels:
-//  * pool:   mean of every B-token query block (and key block, unless the
+// Kernels:
+//  * pool:   mean of every B-token query block (and key candidate, unless the
 //            gather already produced the key-block means), float32;
+//  * group:  with intra-chunk keys and given key-block means, the mean of
+//            each B-token history tile from its key-block means;
 //  * select: pooled logits qbar.kbar_j/sqrt(d) of 16 query blocks at a time
 //            on the matrix cores, then per (head, query block) one wave:
 //            softmax over the key blocks, the minimal mass-ordered prefix that
@@ -22,12 +24,14 @@ namespace {
 
 constexpr int kPoolThreads = 256;
 
-// grid.x = H * (nQB + nKB_to_pool): the first H*nQB workgroups pool query
-// blocks, the rest pool key blocks of k_act.
+// grid.x = H * (nQB + nC_to_pool): the first H*nQB workgroups pool query
+// blocks, the rest pool the nC key candidates of k_act (candidate j < nKBh is
+// the B-token history tile j, the others Bk-token blocks after the Lh history
+// keys).
 template <typename T, int D>
 __global__ __launch_bounds__(kPoolThreads) void pool_blocks_kernel(
-    const T* __restrict__ q, const T* __restrict__ k_act, int H, int B, int L, int nQB, int nKB,
-    float* __restrict__ qbar, float* __restrict__ kbar) {
+    const T* __restrict__ q, const T* __restrict__ k_act, int H, int B, int Bk, int L, int Lh, int nQB,
+    int nC, int nKBh, float* __restrict__ qbar, float* __restrict__ kbar) {
   constexpr int E = Vec<T>::N;
   constexpr int CPR = D / E;
   constexpr int RPP = kPoolThreads / CPR;
@@ -37,22 +41,26 @@ __global__ __launch_bounds__(kPoolThreads) void pool_blocks_kernel(
   const T* src;
   size_t stride;  // elements between consecutive tokens
   float* dst;
+  int n;          // tokens pooled
   if (w < H * nQB) {
     const int h = w / nQB, i = w % nQB;
     src = q + ((size_t)i * B * H + h) * D;
     stride = (size_t)H * D;
     dst = qbar + ((size_t)h * nQB + i) * D;
+    n = B;
   } else {
     const int u = w - H * nQB;
-    const int h = u / nKB, j = u % nKB;
-    src = k_act + ((size_t)h * L + (size_t)j * B) * D;
+    const int h = u / nC, j = u % nC;
+    const size_t first = j < nKBh ? (size_t)j * B : (size_t)Lh + (size_t)(j - nKBh) * Bk;
+    src = k_act + ((size_t)h * L + first) * D;
     stride = D;
-    dst = kbar + ((size_t)h * nKB + j) * D;
+    dst = kbar + ((size_t)h * nC + j) * D;
+    n = j < nKBh ? B : Bk;
   }
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int row = r0; row < B; row += RPP) {
+  for (int row = r0; row < n; row += RPP) {
     float f[E];
     unpack16<T>(ld16(src + row * stride + ch * E), f);
 #pragma unroll
@@ -69,10 +77,34 @@ __global__ __launch_bounds__(kPoolThreads) void pool_blocks_kernel(
 #pragma unroll
       for (int e = 0; e < E; ++e) s[e] += red[(ph * CPR + t) * E + e];
     }
-    const float inv = 1.f / (float)B;
+    const float inv = 1.f / (float)n;
 #pragma unroll
     for (int e = 0; e < E; ++e) dst[t * E + e] = s[e] * inv;
   }
+}
+
+// Candidate means from key-block means [H][nKB][D]: history tile j < nKBh is
+// the mean of key blocks grp*j .. grp*j+grp-1 (equal sizes, so the mean of
+// their means), a chunk candidate is its key block's mean.  One thread per
+// (head, candidate, element).
+__global__ __launch_bounds__(256) void group_means_kernel(const float* __restrict__ kblk_mean, int H, int D,
+                                                          int nKB, int nC, int nKBh, int grp,
+                                                          float* __restrict__ kbar) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)H * nC * D) return;
+  const int e = (int)(i % D);
+  const int j = (int)((i / D) % nC);
+  const int h = (int)(i / ((size_t)D * nC));
+  const float* src = kblk_mean + (size_t)h * nKB * D + e;
+  float v;
+  if (j < nKBh) {
+    float acc = 0.f;
+    for (int u = 0; u < grp; ++u) acc += src[(size_t)(grp * j + u) * D];
+    v = acc / (float)grp;
+  } else {
+    v = src[(size_t)(grp * nKBh + (j - nKBh)) * D];
+  }
+  kbar[i] = v;
 }
 
 // Pooled logits s_ij = qbar_i . kbar_j / sqrt(d) on the float64 matrix
@@ -183,10 +215,15 @@ __device__ __forceinline__ int wave_sum_int(int v) {
          (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
 }
 
+// The row has nKB candidates here (the caller's nC); kept candidate j < nKBh
+// is written as the grp key blocks grp*j .. grp*j+grp-1, a later one as key
+// block grp*nKBh + (j - nKBh) (grp = 1 and nKBh = nKB without intra-chunk
+// keys); the output row holds out_stride entries.
 template <int NPL>
 __global__ __launch_bounds__(kSelThreads) void select_rows_kernel(
-    const float* __restrict__ logits, const float* __restrict__ tau, int rows, int nQB, int nKB,
-    int32_t* __restrict__ blk_count, int32_t* __restrict__ blk_idx, float* __restrict__ blk_mass) {
+    const float* __restrict__ logits, const float* __restrict__ tau, int rows, int nQB, int nKB, int nKBh,
+    int grp, int out_stride, int32_t* __restrict__ blk_count, int32_t* __restrict__ blk_idx,
+    float* __restrict__ blk_mass) {
   const int lane = threadIdx.x % kWave;
   const int row = blockIdx.x * kSelRows + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if (row >= rows) return;
@@ -253,8 +290,8 @@ __global__ __launch_bounds__(kSelThreads) void select_rows_kernel(
     k_t = max(1, min(nties, need));
   }
 
-  // compaction in ascending id order
-  int32_t* out = blk_idx + (size_t)row * nKB;
+  // compaction in ascending id order (history tiles expand to grp key blocks)
+  int32_t* out = blk_idx + (size_t)row * out_stride;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int base = 0, tie_base = 0;
 #pragma unroll
@@ -267,11 +304,19 @@ __global__ __launch_bounds__(kSelThreads) void select_rows_kernel(
     const int tie_rank = tie_base + __popcll(tb & below);
     tie_base += __popcll(tb);
     const bool keep = valid && (all || b > b_lo || (tie && tie_rank < k_t));
-    const uint64_t kb = __ballot(keep);
-    if (keep) out[base + __popcll(kb & below)] = j;
-    base += __popcll(kb);
+    const bool hist = j < nKBh;
+    const uint64_t kh = __ballot(keep && hist), kc = __ballot(keep && !hist);
+    if (keep) {
+      const int pos = base + grp * __popcll(kh & below) + __popcll(kc & below);
+      if (hist) {
+        for (int u = 0; u < grp; ++u) out[pos + u] = grp * j + u;
+      } else {
+        out[pos] = grp * nKBh + (j - nKBh);
+      }
+    }
+    base += grp * __popcll(kh) + __popcll(kc);
   }
-  for (int p = base + lane; p < nKB; p += kWave) out[p] = -1;
+  for (int p = base + lane; p < out_stride; p += kWave) out[p] = -1;
   if (lane == 0) blk_count[row] = base;
 }
 
@@ -279,20 +324,30 @@ template <typename T, int D>
 void launch_select(const Dims& s, const void* q, const void* k_act, const float* kblk_mean, const float* tau,
                    int32_t* cnt, int32_t* idx, float* mass, char* ws, const WsLayout& w, hipStream_t st) {
   float* qbar = reinterpret_cast<float*>(ws + w.sel_qbar);
-  float* kbar = kblk_mean ? const_cast<float*>(kblk_mean) : reinterpret_cast<float*>(ws + w.sel_kbar);
-  const int pool_k = kblk_mean ? 0 : s.nKB;
+  // candidate means: the given key-block means as they are (no intra-chunk
+  // keys), grouped from them, or pooled from k_act
+  const bool given = kblk_mean != nullptr;
+  float* kbar = given && !s.split ? const_cast<float*>(kblk_mean) : reinterpret_cast<float*>(ws + w.sel_kbar);
+  const int pool_k = given ? 0 : s.nC;
+  const int grp = s.B / s.Bk;
   hipLaunchKernelGGL((pool_blocks_kernel<T, D>), dim3(s.H * (s.nQB + pool_k)), dim3(kPoolThreads), 0, st,
-                     reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act), s.H, s.B, s.L, s.nQB,
-                     s.nKB, qbar, kbar);
+                     reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act), s.H, s.B, s.Bk, s.L, s.Lh,
+                     s.nQB, s.nC, s.split ? s.nKBh : s.nC, qbar, kbar);
+  if (given && s.split) {
+    const size_t n = (size_t)s.H * s.nC * s.d;
+    hipLaunchKernelGGL(group_means_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, kblk_mean, s.H,
+                       s.d, s.nKB, s.nC, s.nKBh, grp, kbar);
+  }
   float* logits = reinterpret_cast<float*>(ws + w.sel_logit);
-  hipLaunchKernelGGL((block_logits_kernel<D>), dim3((s.nKB + 63) / 64, (s.nQB + 15) / 16, s.H), dim3(kLogitThreads),
-                     0, st, qbar, kbar, s.nQB, s.nKB, 1.f / sqrtf((float)s.d), logits);
-  const int npl = (s.nKB + kWave - 1) / kWave;
+  hipLaunchKernelGGL((block_logits_kernel<D>), dim3((s.nC + 63) / 64, (s.nQB + 15) / 16, s.H), dim3(kLogitThreads),
+                     0, st, qbar, kbar, s.nQB, s.nC, 1.f / sqrtf((float)s.d), logits);
+  const int npl = (s.nC + kWave - 1) / kWave;
+  const int nkbh = s.split ? s.nKBh : s.nC;
   const dim3 grid((s.rows + kSelRows - 1) / kSelRows);
 #define HSA_SEL_CASE(N)                                                                                  \
   if (npl <= N) {                                                                                        \
-    hipLaunchKernelGGL(select_rows_kernel<N>, grid, dim3(kSelThreads), 0, st, logits, tau, s.rows, s.nQB, s.nKB, \
-                       cnt, idx, mass);                                                                  \
+    hipLaunchKernelGGL(select_rows_kernel<N>, grid, dim3(kSelThreads), 0, st, logits, tau, s.rows, s.nQB, s.nC, \
+                       nkbh, grp, s.nKB, cnt, idx, mass);                                                \
     return;                                                                                              \
   }
   HSA_SEL_CASE(4)

@@ -1,10 +1,14 @@
 // S2 -- active KV construction: the K_p retrieved pages, ascending id, copied
 // into one contiguous head-major buffer.  WorldAttention paper, section 3.2
-// "Active KV construction"; structured summary, method step (4).
+// "Active KV construction"; structured summary, method step (4).  With
+// intra-chunk keys (section 3.3, "Inter- and intra-chunk sparse
+// granularity") the current chunk's own keys and values follow the pages.
 //
-// One workgroup moves one B-token block of one head of one selected page:
+// One workgroup moves one B-token block of one head of one selected page (or
+// of the chunk):
 //  * keys   [Lp][H][d] rows -> k_act [H][L][d]   (plain copy, 16-byte chunks),
-//    summing the block's keys on the way (the pooled block means of S4);
+//    summing the keys of each Bk-token key block on the way (the pooled
+//    block means of S4; a B-token block holds B/Bk key blocks);
 //  * values [Lp][H][d] rows -> v_act [H][L/16][d][16] (16-token granules
 //    stored d-major), transposed through LDS, because the PV product and the
 //    low-rank projection contract over tokens and want tokens contiguous.
@@ -19,10 +23,13 @@ namespace {
 constexpr int kGatherThreads = 256;
 constexpr int kBatch = 6;  // passes whose loads are in flight together
 
-template <typename T, int D>
+// NSUB: the largest number of key blocks per B-token block (1 without
+// intra-chunk keys, where key blocks are B tokens).
+template <typename T, int D, int NSUB>
 __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
-    PageTable pk, PageTable pv, int n_pages, const int32_t* __restrict__ sel, int H, int Lp, int B,
-    int L, T* __restrict__ k_act, T* __restrict__ v_act, float* __restrict__ kblk_mean) {
+    PageTable pk, PageTable pv, int n_pages, const int32_t* __restrict__ sel, const T* __restrict__ k_cur,
+    const T* __restrict__ v_cur, int H, int Lp, int Kp, int B, int Bk, int L, int nKB,
+    T* __restrict__ k_act, T* __restrict__ v_act, float* __restrict__ kblk_mean) {
   constexpr int E = Vec<T>::N;
   constexpr int CPR = D / E;                       // 16-byte chunks per (token, head) row
   constexpr int RPP = kGatherThreads / CPR;        // rows per pass
@@ -30,22 +37,37 @@ __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
   constexpr int VS = D + VPAD;                     // LDS row stride (elements)
   extern __shared__ __align__(16) unsigned char smem[];
   T* vs = reinterpret_cast<T*>(smem);                              // [B][VS]
-  float* red = reinterpret_cast<float*>(smem + (size_t)B * VS * sizeof(T));  // [256][E]
+  float* red = reinterpret_cast<float*>(smem + (size_t)B * VS * sizeof(T));  // [nsub][256][E]
 
   const int bpp = Lp / B;
-  const int p = blockIdx.x / bpp, blk = blockIdx.x % bpp, h = blockIdx.y;
-  int page = sel[p];
-  page = page < 0 ? 0 : (page >= n_pages ? n_pages - 1 : page);
-  const T* ksrc = reinterpret_cast<const T*>(pk.p[page]);
-  const T* vsrc = reinterpret_cast<const T*>(pv.p[page]);
+  const int h = blockIdx.y;
+  const T* ksrc;
+  const T* vsrc;
+  size_t tok0, act0;  // first token of the block in its source, and in the active buffer
+  if ((int)blockIdx.x < Kp * bpp) {
+    const int p = blockIdx.x / bpp, blk = blockIdx.x % bpp;
+    int page = sel[p];
+    page = page < 0 ? 0 : (page >= n_pages ? n_pages - 1 : page);
+    ksrc = reinterpret_cast<const T*>(pk.p[page]);
+    vsrc = reinterpret_cast<const T*>(pv.p[page]);
+    tok0 = (size_t)blk * B;
+    act0 = (size_t)p * Lp + tok0;
+  } else {  // the chunk's own tokens, after the Kp pages
+    const int blk = blockIdx.x - Kp * bpp;
+    ksrc = k_cur;
+    vsrc = v_cur;
+    tok0 = (size_t)blk * B;
+    act0 = (size_t)Kp * Lp + tok0;
+  }
   const int t = threadIdx.x;
   const int ch = t % CPR, r0 = t / CPR;
-  const size_t tok0 = (size_t)blk * B;           // first token of the block in the page
-  const size_t act0 = (size_t)p * Lp + tok0;     // first token of the block in the active buffer
+  const int nsub = B / Bk;
 
-  float acc[E];
+  float acc[NSUB][E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[u][e] = 0.f;
   const int npass = (B + RPP - 1) / RPP;
   for (int base = 0; base < npass; base += kBatch) {
     uint4 kv[kBatch], vv[kBatch];
@@ -65,14 +87,21 @@ __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
         st16(k_act + ((size_t)h * L + act0 + row) * D + ch * E, kv[u]);
         float f[E];
         unpack16<T>(kv[u], f);
+        const int sub = NSUB == 1 ? 0 : row / Bk;
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] += f[e];
+        for (int su = 0; su < NSUB; ++su)
+          if (su == sub)
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[su][e] += f[e];
         st16(vs + row * VS + ch * E, vv[u]);
       }
     }
   }
 #pragma unroll
-  for (int e = 0; e < E; ++e) red[t * E + e] = acc[e];
+  for (int su = 0; su < NSUB; ++su)
+    if (su < nsub)
+#pragma unroll
+      for (int e = 0; e < E; ++e) red[(su * kGatherThreads + t) * E + e] = acc[su][e];
   __syncthreads();
 
   // values: [16 tokens][D] granules in LDS -> [D][16] granules in memory
@@ -89,18 +118,19 @@ __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
     st16(v_act + (((size_t)h * (L / 16) + g0 + gr) * D + drow) * 16 + part * E, pack16<T>(f));
   }
 
-  // block mean of the keys (fixed-order sum over the row phases)
-  if (kblk_mean != nullptr && t < CPR) {
+  // key-block means (fixed-order sum over the row phases)
+  if (kblk_mean != nullptr && t < CPR * nsub) {
+    const int su = t / CPR, c = t % CPR;
     float s[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) s[e] = 0.f;
     for (int ph = 0; ph < RPP; ++ph) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) s[e] += red[(ph * CPR + t) * E + e];
+      for (int e = 0; e < E; ++e) s[e] += red[(su * kGatherThreads + ph * CPR + c) * E + e];
     }
-    const float inv = 1.f / (float)B;
-    const int j = (int)(act0 / B);
-    float* dst = kblk_mean + ((size_t)h * (L / B) + j) * D + t * E;
+    const float inv = 1.f / (float)Bk;
+    const int j = (int)(act0 / Bk) + su;
+    float* dst = kblk_mean + ((size_t)h * nKB + j) * D + c * E;
 #pragma unroll
     for (int e = 0; e < E; ++e) dst[e] = s[e] * inv;
   }
@@ -108,26 +138,35 @@ __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
 
 template <typename T, int D>
 void launch_gather(const Dims& s, const PageTable& pk, const PageTable& pv, int n_pages, const int32_t* sel,
-                   void* k_act, void* v_act, float* kblk_mean, hipStream_t st) {
+                   const void* k_cur, const void* v_cur, void* k_act, void* v_act, float* kblk_mean,
+                   hipStream_t st) {
   constexpr int E = Vec<T>::N;
-  const size_t smem = (size_t)s.B * (D + E) * sizeof(T) + (size_t)kGatherThreads * E * sizeof(float);
-  dim3 grid(s.Kp * (s.Lp / s.B), s.H);
-  hipLaunchKernelGGL((gather_block_kernel<T, D>), grid, dim3(kGatherThreads), smem, st, pk, pv, n_pages,
-                     sel, s.H, s.Lp, s.B, s.L, reinterpret_cast<T*>(k_act), reinterpret_cast<T*>(v_act),
-                     kblk_mean);
+  const int nsub = s.B / s.Bk;
+  const size_t smem = (size_t)s.B * (D + E) * sizeof(T) + (size_t)nsub * kGatherThreads * E * sizeof(float);
+  dim3 grid(s.Kp * (s.Lp / s.B) + (s.split ? s.Lq / s.B : 0), s.H);
+  auto kern = nsub == 1 ? gather_block_kernel<T, D, 1> : gather_block_kernel<T, D, HSA_MAX_INTRA_SPLIT>;
+  if (smem > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)smem);
+  hipLaunchKernelGGL(kern, grid, dim3(kGatherThreads), smem, st, pk, pv, n_pages, sel,
+                     reinterpret_cast<const T*>(k_cur), reinterpret_cast<const T*>(v_cur), s.H, s.Lp, s.Kp, s.B,
+                     s.Bk, s.L, s.nKB, reinterpret_cast<T*>(k_act), reinterpret_cast<T*>(v_act), kblk_mean);
 }
 
 }  // namespace
 }  // namespace hsa
 
-extern "C" hsa_rc hsa_gather_pages(const hsa_geom* geom, const void* const* page_k, const void* const* page_v,
-                                   int32_t n_pages, const int32_t* sel_pages, void* k_act, void* v_act,
-                                   float* kblk_mean, hsa_stream stream) {
+extern "C" hsa_rc hsa_gather_active(const hsa_geom* geom, const void* const* page_k, const void* const* page_v,
+                                    int32_t n_pages, const int32_t* sel_pages, const void* k_cur,
+                                    const void* v_cur, void* k_act, void* v_act, float* kblk_mean,
+                                    hsa_stream stream) {
   using namespace hsa;
   Dims s;
   hsa_rc rc = derive(geom, &s);
   if (rc != HSA_OK) return rc;
   if (!page_k || !page_v || !sel_pages || !k_act || !v_act) return HSA_ERR_NULL_ARG;
+  if (s.split && (!k_cur || !v_cur)) return HSA_ERR_NULL_ARG;
+  if (!s.split && (k_cur || v_cur)) return HSA_ERR_BAD_PARAM;
   if (n_pages < 1 || n_pages > HSA_MAX_PAGES || s.Kp > n_pages) return HSA_ERR_BAD_PARAM;
   PageTable pk, pv;
   for (int j = 0; j < kMaxPages; ++j) pk.p[j] = pv.p[j] = nullptr;
@@ -138,11 +177,19 @@ extern "C" hsa_rc hsa_gather_pages(const hsa_geom* geom, const void* const* page
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (s.bf16) {
-    if (s.d == 128) launch_gather<bf16_t, 128>(s, pk, pv, n_pages, sel_pages, k_act, v_act, kblk_mean, st);
-    else launch_gather<bf16_t, 64>(s, pk, pv, n_pages, sel_pages, k_act, v_act, kblk_mean, st);
+    if (s.d == 128) launch_gather<bf16_t, 128>(s, pk, pv, n_pages, sel_pages, k_cur, v_cur, k_act, v_act, kblk_mean, st);
+    else launch_gather<bf16_t, 64>(s, pk, pv, n_pages, sel_pages, k_cur, v_cur, k_act, v_act, kblk_mean, st);
   } else {
-    if (s.d == 128) launch_gather<float, 128>(s, pk, pv, n_pages, sel_pages, k_act, v_act, kblk_mean, st);
-    else launch_gather<float, 64>(s, pk, pv, n_pages, sel_pages, k_act, v_act, kblk_mean, st);
+    if (s.d == 128) launch_gather<float, 128>(s, pk, pv, n_pages, sel_pages, k_cur, v_cur, k_act, v_act, kblk_mean, st);
+    else launch_gather<float, 64>(s, pk, pv, n_pages, sel_pages, k_cur, v_cur, k_act, v_act, kblk_mean, st);
   }
   return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
+}
+
+extern "C" hsa_rc hsa_gather_pages(const hsa_geom* geom, const void* const* page_k, const void* const* page_v,
+                                   int32_t n_pages, const int32_t* sel_pages, void* k_act, void* v_act,
+                                   float* kblk_mean, hsa_stream stream) {
+  if (geom && geom->intra_split != 0) return HSA_ERR_BAD_PARAM;
+  return hsa_gather_active(geom, page_k, page_v, n_pages, sel_pages, nullptr, nullptr, k_act, v_act, kblk_mean,
+                           stream);
 }

@@ -24,20 +24,27 @@ hsa_rc derive(const hsa_geom* g, Dims* o) {
     return HSA_ERR_BAD_SHAPE;
   const long long B = 1LL * g->tile_t * g->tile_h * g->tile_w;
   if (B % 16 || B > 192) return HSA_ERR_BAD_SHAPE;
+  const int split = g->intra_split;
+  if (split < 0 || split > HSA_MAX_INTRA_SPLIT) return HSA_ERR_BAD_PARAM;
+  const long long Bk = split ? B / split : B;
+  if (split && (B % split || Bk % 16)) return HSA_ERR_BAD_SHAPE;
   const long long tpf = 1LL * g->frame_h * g->frame_w;
   const long long Lp = tpf * g->frames_per_page, Lq = tpf * g->query_frames;
-  const long long L = Lp * g->n_sel_pages;
+  const long long Lh = Lp * g->n_sel_pages;
+  const long long L = Lh + (split ? Lq : 0);
   const long long D = 1LL * g->n_heads * g->head_dim;
   // every buffer index must fit comfortably in 32-bit element offsets per head
   if (Lp > (1LL << 24) || Lq > (1LL << 24) || L > (1LL << 24) || L * D > (1LL << 31) ||
       Lq * D > (1LL << 31) || Lp * D > (1LL << 31))
     return HSA_ERR_BAD_SHAPE;
-  if (L / B > HSA_MAX_KBLOCKS) return HSA_ERR_BAD_SHAPE;
+  if (L / Bk > HSA_MAX_KBLOCKS) return HSA_ERR_BAD_SHAPE;
   if (1LL * g->n_heads * (Lq / B) > HSA_MAX_ROWS) return HSA_ERR_BAD_SHAPE;
   Dims s;
   s.H = g->n_heads; s.d = g->head_dim; s.D = (int)D;
   s.Lp = (int)Lp; s.Lq = (int)Lq; s.B = (int)B; s.Kp = g->n_sel_pages; s.L = (int)L;
-  s.nKB = (int)(L / B); s.nQB = (int)(Lq / B); s.r = g->rank;
+  s.nKB = (int)(L / Bk); s.nQB = (int)(Lq / B); s.r = g->rank;
+  s.split = split; s.Bk = (int)Bk; s.Lh = (int)Lh; s.nKBh = (int)(Lh / B);
+  s.nC = split ? s.nKBh + (int)(Lq / Bk) : s.nKB;
   s.bf16 = g->dtype == HSA_BF16; s.esize = s.bf16 ? 2 : 4;
   s.rows = s.H * s.nQB;
   if (o) *o = s;
@@ -83,10 +90,15 @@ AttendPlan attend_plan(const Dims& s) {
 
 SparsePlan sparse_plan(const Dims& s) {
   SparsePlan p;
-  p.granules_per_block = s.B / 16;
+  p.granules_per_block = s.Bk / 16;
+  // segments of about 32 query-tile-sized blocks' worth of granules (even, so
+  // two-granule steps never straddle segments), and short enough that one
+  // spans at most 64 key blocks: the kernel keeps a segment's block ids one
+  // per lane
   const int seg_blocks = 32;
-  int sg = seg_blocks * p.granules_per_block;
+  int sg = seg_blocks * (s.B / 16);
   if (sg & 1) sg += 1;
+  while ((sg - 1) / p.granules_per_block + 2 > 64) sg -= 2;
   p.seg_granules = sg;
   p.max_segs = cdiv(s.nKB * p.granules_per_block, sg);
   p.max_items = s.rows * p.max_segs;

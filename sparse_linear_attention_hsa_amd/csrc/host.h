@@ -12,6 +12,11 @@ namespace hsa {
 // Sizes derived from an hsa_geom.
 struct Dims {
   int H, d, D, Lp, Lq, B, Kp, L, nKB, nQB, r;
+  int split;  // intra_split: 0, or the chunk's own keys follow the history in B/split-token blocks
+  int Bk;     // tokens per key block (B, or B / split)
+  int Lh;     // keys of the retrieved pages (L = Lh, or Lh + Lq with intra-chunk keys)
+  int nKBh;   // B-token history tiles, Lh / B
+  int nC;     // selection candidates: nKB, or nKBh + Lq / Bk
   int bf16;  // 1 if dtype == HSA_BF16
   int esize; // bytes per element
   int rows;  // H * nQB selection rows
@@ -51,7 +56,7 @@ AttendPlan attend_plan(const Dims& s);
 
 // Sparse-branch segmentation of the selected-block rows.
 struct SparsePlan {
-  int granules_per_block;  // B / 16
+  int granules_per_block;  // Bk / 16
   int seg_granules;        // target granules per work item
   int max_segs;            // per row
   int max_items;           // rows * max_segs

@@ -165,7 +165,7 @@ template <typename T, int D, int NW, int QPW, int WPE, int RING, bool FULL>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void sparse_attn_kernel(
     const T* __restrict__ q, const T* __restrict__ k_act, const T* __restrict__ v_act,
     const int32_t* __restrict__ blk_idx, const int4* __restrict__ items, const int* __restrict__ meta,
-    int H, int B, int L, int nKB, int nQB, float scale_log2,
+    int H, int B, int Bk, int L, int nKB, int nQB, float scale_log2,
     float* __restrict__ o_sp, float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int E = Vec<T>::N;          // elements per 16-byte chunk
   constexpr int KS = Mma<T>::K;         // keys per step
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
   const int4 it = items[item];
   const int row = it.x, g0 = it.y, gcount = it.z, slot = it.w;
   const int h = row / nQB, qb = row % nQB;
-  const int gpb = B / 16;
+  const int gpb = Bk / 16;  // granules per key block (query tiles are B rows)
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave index, kept in a scalar register
@@ -201,7 +201,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
   const int QT = B / 16;
   const int ntile = FULL ? QPW : min(QPW, QT - w * QPW);  // wave-uniform
 
-  // The segment's block ids, one per lane (a segment spans at most 33 blocks).
+  // The segment's block ids, one per lane (the plan keeps a segment within
+  // 64 blocks).
   const int b0 = g0 / gpb;
   const int nblk = gcount > 0 ? (g0 + gcount - 1) / gpb - b0 + 1 : 0;
   const int blk_lane = lane < nblk ? blk_idx[(size_t)row * nKB + b0 + lane] : -1;
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
       int key = -1;
       if (issued < gcount) {
         const int blk = __builtin_amdgcn_readlane(blk_lane, cur_blk);
-        if (blk >= 0 && blk < nKB) key = blk * B + cur_gran * 16;
+        if (blk >= 0 && blk < nKB) key = blk * Bk + cur_gran * 16;
       }
       // a masked granule (past the segment or an invalid block id) loads the
       // head's first granule: its scores are set to -inf, so it adds nothing
@@ -589,12 +590,12 @@ void launch_attn(const Dims& s, const SparsePlan& pl, const void* q, const void*
   if (s.B == 16 * NW * QPW)
     hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE, RING, true>), dim3(pl.grid), dim3(NW * kWave), 0, st,
                        reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act),
-                       reinterpret_cast<const T*>(v_act), idx, items, meta, s.H, s.B, s.L, s.nKB, s.nQB,
+                       reinterpret_cast<const T*>(v_act), idx, items, meta, s.H, s.B, s.Bk, s.L, s.nKB, s.nQB,
                        scale_log2, o_sp, po, pml);
   else
   hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE, RING, false>), dim3(pl.grid), dim3(NW * kWave), 0, st,
                      reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act),
-                     reinterpret_cast<const T*>(v_act), idx, items, meta, s.H, s.B, s.L, s.nKB, s.nQB,
+                     reinterpret_cast<const T*>(v_act), idx, items, meta, s.H, s.B, s.Bk, s.L, s.nKB, s.nQB,
                      scale_log2, o_sp, po, pml);
 }
 
@@ -631,6 +632,7 @@ extern "C" hsa_rc hsa_sparse_attn_timed(const hsa_geom* geom, const void* q, con
   const WsLayout w = ws_layout(s, 1);
   if (!ws || ws_bytes < w.sp_end) return HSA_ERR_WORKSPACE;
   const SparsePlan pl = sparse_plan(s);
+  if (pl.max_segs > kMaxPlanSegs) return HSA_ERR_BAD_SHAPE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* wsb = static_cast<char*>(ws);
   int4* items = reinterpret_cast<int4*>(wsb + w.sp_items);

@@ -18,10 +18,10 @@ _DTYPES = {torch.float32: HSA_F32, torch.bfloat16: HSA_BF16}
 
 
 def make_geom(n_heads, head_dim, frame_h, frame_w, frames_per_page, query_frames, tile,
-              n_sel_pages, rank, dtype) -> Geom:
+              n_sel_pages, rank, dtype, intra_split: int = 0) -> Geom:
     dt = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else {"f32": HSA_F32, "bf16": HSA_BF16}[dtype]
     return Geom(n_heads, head_dim, frame_h, frame_w, frames_per_page, query_frames,
-                tile[0], tile[1], tile[2], n_sel_pages, rank, dt)
+                tile[0], tile[1], tile[2], n_sel_pages, rank, dt, intra_split)
 
 
 @dataclass(frozen=True)
@@ -38,15 +38,25 @@ class Dims:
     nQB: int
     r: int
     dtype: torch.dtype
+    split: int = 0   # intra_split
+    Bk: int = 0      # tokens per key block
+    Lh: int = 0      # keys of the retrieved pages
+    nKBh: int = 0    # B-token history tiles
+    nC: int = 0      # selection candidates (row length of blk_mass)
 
     @staticmethod
     def of(g: Geom) -> "Dims":
         tpf = g.frame_h * g.frame_w
         B = g.tile_t * g.tile_h * g.tile_w
         Lp, Lq = tpf * g.frames_per_page, tpf * g.query_frames
-        L = Lp * g.n_sel_pages
-        return Dims(g.n_heads, g.head_dim, Lp, Lq, B, g.n_sel_pages, L, L // B, Lq // B, g.rank,
-                    torch.bfloat16 if g.dtype == HSA_BF16 else torch.float32)
+        s = int(g.intra_split)
+        Bk = B // s if s else B
+        Lh = Lp * g.n_sel_pages
+        L = Lh + (Lq if s else 0)
+        nKB = L // Bk
+        nC = Lh // B + Lq // Bk if s else nKB
+        return Dims(g.n_heads, g.head_dim, Lp, Lq, B, g.n_sel_pages, L, nKB, Lq // B, g.rank,
+                    torch.bfloat16 if g.dtype == HSA_BF16 else torch.float32, s, Bk, Lh, Lh // B, nC)
 
 
 def _p(t: Optional[torch.Tensor]):
@@ -107,6 +117,15 @@ def hsa_gather_pages(geom, pages_k, pages_v, sel_pages, k_act, v_act, kblk_mean=
     check("hsa_gather_pages", lib().hsa_gather_pages(
         ctypes.byref(geom), _table(pages_k), _table(pages_v), len(pages_k), _p(sel_pages), _p(k_act), _p(v_act),
         _p(kblk_mean), _s(stream)))
+
+
+def hsa_gather_active(geom, pages_k, pages_v, sel_pages, k_cur, v_cur, k_act, v_act, kblk_mean=None,
+                      stream=None):
+    """k_cur / v_cur: the chunk's own [Lq][H][d] keys and values (None
+    without intra-chunk keys)."""
+    check("hsa_gather_active", lib().hsa_gather_active(
+        ctypes.byref(geom), _table(pages_k), _table(pages_v), len(pages_k), _p(sel_pages), _p(k_cur), _p(v_cur),
+        _p(k_act), _p(v_act), _p(kblk_mean), _s(stream)))
 
 
 def hsa_linear_branch(geom, q, k_act, v_act, e_k, e_v, k_proj, v_proj, o_lin, flags, ws, stream=None):

@@ -46,7 +46,7 @@ class HsaStep:
         self.o_lin = torch.empty(s.Lq, s.H, s.d, dtype=f32, device=dev)
         self.blk_count = torch.empty(s.H, s.nQB, dtype=i32, device=dev)
         self.blk_idx = torch.empty(s.H, s.nQB, s.nKB, dtype=i32, device=dev)
-        self.blk_mass = torch.empty(s.H, s.nQB, s.nKB, dtype=f32, device=dev)
+        self.blk_mass = torch.empty(s.H, s.nQB, s.nC, dtype=f32, device=dev)
         self.o_sp = torch.empty(s.Lq, s.H, s.d, dtype=f32, device=dev)
         self.out = torch.empty(s.Lq, s.H, s.d, dtype=dt, device=dev)
         nbytes = ops.hsa_workspace_bytes(geom, n_pages)
@@ -88,9 +88,15 @@ class HsaStep:
         when a page is written.  Runs one scoring call over the pages."""
         ops.hsa_score_pages(self.geom, q, pages_k, self.page_kmean, self.scores, self.sel_pages, self.ws, stream)
 
-    def gather(self, pages_k, pages_v, stream=None):
-        ops.hsa_gather_pages(self.geom, pages_k, pages_v, self.sel_pages, self.k_act, self.v_act, self.kblk_mean,
-                             stream)
+    def gather(self, pages_k, pages_v, stream=None, k_cur=None, v_cur=None):
+        """k_cur / v_cur: the chunk's own keys and values [Lq][H][d], which
+        follow the pages when the geometry has intra-chunk keys."""
+        if self.geom.intra_split:
+            ops.hsa_gather_active(self.geom, pages_k, pages_v, self.sel_pages, k_cur, v_cur, self.k_act, self.v_act,
+                                  self.kblk_mean, stream)
+        else:
+            ops.hsa_gather_pages(self.geom, pages_k, pages_v, self.sel_pages, self.k_act, self.v_act,
+                                 self.kblk_mean, stream)
 
     def linear(self, q, e_k, e_v, flags: int = 0, stream=None, ws=None):
         ws = self.ws if ws is None else ws
@@ -118,17 +124,19 @@ class HsaStep:
 
     # the whole step -----------------------------------------------------
     def run(self, q, pages_k, pages_v, e_k, e_v, w_g, x, tau, stream=None, concurrent: bool = True,
-            indexed: bool = False, chunks=None):
+            indexed: bool = False, chunks=None, k_cur=None, v_cur=None):
         """indexed: score from the page index (index_pages ran before) rather
         than from the pages' keys; the gather still copies the pages.
         chunks: run prompt-level retrieval first and score only the pages of
-        the retrieved chunks (see retrieve)."""
+        the retrieved chunks (see retrieve).
+        k_cur, v_cur: the chunk's own keys and values (geometries with
+        intra-chunk keys)."""
         main = torch.cuda.current_stream() if stream is None else stream
         if chunks is not None:
             self.retrieve(q, [None] * self.n_pages if indexed else pages_k, chunks, main)
         else:
             self.score(q, pages_k, main, use_cache=indexed)
-        self.gather(pages_k, pages_v, main)
+        self.gather(pages_k, pages_v, main, k_cur, v_cur)
         if concurrent:
             gathered = torch.cuda.Event()
             gathered.record(main)

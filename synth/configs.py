@@ -41,6 +41,7 @@ class Config:
     layers: int = 1
     steps: int = 1
     host_page_frac: float = 0.0     # stack config: share of selected pages that live in host memory
+    intra_split: int = 0            # 0, or the chunk's own keys join the history in B/s-token blocks
     seed: int = 1000
 
     # ---- derived geometry -------------------------------------------------
@@ -62,12 +63,28 @@ class Config:
         return t * h * w
 
     @property
-    def active_tokens(self) -> int:      # L
+    def history_tokens(self) -> int:     # Lh: keys of the retrieved pages
         return self.n_sel_pages * self.page_tokens
 
     @property
-    def n_kblocks(self) -> int:          # nKB
-        return self.active_tokens // self.block
+    def active_tokens(self) -> int:      # L: history, then the chunk's own tokens with intra_split
+        return self.history_tokens + (self.query_tokens if self.intra_split else 0)
+
+    @property
+    def n_kblocks(self) -> int:          # B-token history tiles
+        return self.history_tokens // self.block
+
+    @property
+    def key_block(self) -> int:          # Bk: tokens per key block
+        return self.block // self.intra_split if self.intra_split else self.block
+
+    @property
+    def n_key_blocks(self) -> int:       # nKB: key blocks of the active buffer
+        return self.active_tokens // self.key_block
+
+    @property
+    def n_candidates(self) -> int:       # nC: selection candidates
+        return self.n_kblocks + (self.query_tokens // self.key_block if self.intra_split else 0)
 
     @property
     def n_qblocks(self) -> int:          # nQB
@@ -88,6 +105,8 @@ class Config:
         assert self.block % 16 == 0, "block must be a multiple of 16 tokens"
         assert 1 <= self.n_sel_pages <= self.n_pages
         assert self.dtype in ("f32", "bf16")
+        if self.intra_split:
+            assert self.block % self.intra_split == 0 and self.key_block % 16 == 0, "B/s must be a multiple of 16"
 
 
 def _c1(**kw) -> Config:

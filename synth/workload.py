@@ -36,7 +36,8 @@ import numpy as np
 
 from .configs import Config
 
-TID = dict(q=1, k=2, v=3, x=4, ek=5, ev=6, wg=7, mu=8, struct=9, tau=10, hot=11, host=12, prompt=13)
+TID = dict(q=1, k=2, v=3, x=4, ek=5, ev=6, wg=7, mu=8, struct=9, tau=10, hot=11, host=12, prompt=13,
+           kcur=14, vcur=15)
 
 
 def round_bf16(a: np.ndarray) -> np.ndarray:
@@ -189,6 +190,30 @@ class Workload:
         v = self.rng("v", page=j).standard_normal((c.page_tokens, c.n_heads, c.head_dim), dtype=np.float32)
         return self._finish(v)
 
+    def k_cur(self, step: int = 0) -> np.ndarray:
+        """The chunk's own keys [Lq][H][d] (joined to the history with
+        intra_split): N(0, 1), plus the planted direction at mu_norm on the
+        structured heads (the chunk is its own most relevant context), plus,
+        for the rank-8 structure, the rank-8 code of the query tile each token
+        belongs to (a query block finds its own tile's keys)."""
+        c = self.cfg
+        k = self.rng("kcur", step=step).standard_normal((c.query_tokens, c.n_heads, c.head_dim), dtype=np.float32)
+        heads = self._structured_heads()
+        k[:, heads, :] += (c.mu_norm * self.plant.w[heads]).astype(np.float32)
+        if c.structure == "rank8":
+            rs = self.rng("struct", page=10_000, step=step)  # the queries' coefficients
+            coef = rs.normal(0.0, c.struct_scale, size=(c.n_heads, c.n_qblocks, 8))
+            coef -= coef.mean(axis=1, keepdims=True)
+            add = np.einsum("hdk,hik->ihd", self.plant.U, coef)          # [nQB][H][d]
+            k.reshape(c.n_qblocks, c.block, c.n_heads, c.head_dim)[...] += add.astype(np.float32)[:, None]
+        return self._finish(k)
+
+    def v_cur(self, step: int = 0) -> np.ndarray:
+        """The chunk's own values [Lq][H][d], N(0, 1)."""
+        c = self.cfg
+        v = self.rng("vcur", step=step).standard_normal((c.query_tokens, c.n_heads, c.head_dim), dtype=np.float32)
+        return self._finish(v)
+
     def x(self, step: int = 0) -> np.ndarray:
         """Gate input [Lq][D] (the layer's hidden states of the current chunk)."""
         c = self.cfg
@@ -230,8 +255,11 @@ class Workload:
 
     # ------------------------------------------------------------ bundles
     def small_inputs(self, step: int = 0) -> Dict[str, np.ndarray]:
-        return dict(q=self.q(step), x=self.x(step), e_k=self.e_k(), e_v=self.e_v(),
-                    w_g=self.w_g(), tau=self.tau())
+        d = dict(q=self.q(step), x=self.x(step), e_k=self.e_k(), e_v=self.e_v(),
+                 w_g=self.w_g(), tau=self.tau())
+        if self.cfg.intra_split:
+            d.update(k_cur=self.k_cur(step), v_cur=self.v_cur(step))
+        return d
 
     def pages(self):
         return [self.page_k(j) for j in range(self.cfg.n_pages)], [self.page_v(j) for j in range(self.cfg.n_pages)]

@@ -22,7 +22,7 @@ TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-4, 1e-5)}
 
 def geom_of(cfg: Config):
     return make_geom(cfg.n_heads, cfg.head_dim, cfg.frame_h, cfg.frame_w, cfg.frames_per_page,
-                     cfg.query_frames, cfg.tile, cfg.n_sel_pages, cfg.rank, cfg.dtype)
+                     cfg.query_frames, cfg.tile, cfg.n_sel_pages, cfg.rank, cfg.dtype, cfg.intra_split)
 
 
 def torch_dtype(cfg: Config):
@@ -78,19 +78,25 @@ class Run:
         self.tau = torch.from_numpy(self.np["tau"]).cuda()
         self.pk = [dev(p, cfg) for p in self.pk_np]
         self.pv = [dev(p, cfg) for p in self.pv_np]
+        self.k_cur = dev(s["k_cur"], cfg) if cfg.intra_split else None
+        self.v_cur = dev(s["v_cur"], cfg) if cfg.intra_split else None
         self.geom = geom_of(cfg)
         self.step = HsaStep(self.geom, cfg.n_pages)
 
     def run(self, concurrent: bool = True, indexed: bool = False):
         self.step.run(self.q, self.pk, self.pv, self.e_k, self.e_v, self.w_g, self.x, self.tau,
-                      concurrent=concurrent, indexed=indexed)
+                      concurrent=concurrent, indexed=indexed, k_cur=self.k_cur, v_cur=self.v_cur)
         torch.cuda.synchronize()
         return self.step
 
     def oracle(self, sel_pages=None, block_sel=None):
         s = self.np
+        intra = {}
+        if self.cfg.intra_split:
+            intra = dict(k_cur=s["k_cur"], v_cur=s["v_cur"], b_intra=self.cfg.key_block)
         return orc.hsa_step(s["q"], self.pk_np, self.pv_np, s["e_k"], s["e_v"], s["w_g"], s["x"], s["tau"],
-                            self.cfg.n_sel_pages, self.cfg.block, sel_pages=sel_pages, block_sel=block_sel)
+                            self.cfg.n_sel_pages, self.cfg.block, sel_pages=sel_pages, block_sel=block_sel,
+                            **intra)
 
 
 def gpu_block_lists(step: HsaStep):
@@ -115,3 +121,32 @@ def check_block_selection(ref_blocks, gpu_lists, tau):
             assert orc.valid_block_selection(ref_blocks["mass"][h, i], got, tau[h]), f"invalid selection at tie (h={h}, i={i})"
             differ += 1
     return differ
+
+
+def key_blocks_of(cands, n_tiles: int, grp: int) -> np.ndarray:
+    """Candidate ids (history tiles j < n_tiles, then the chunk's blocks) ->
+    the key-block ids the library lists: tile j is key blocks grp*j ..
+    grp*j+grp-1, chunk candidate j is key block grp*n_tiles + j - n_tiles."""
+    out = []
+    for j in cands:
+        j = int(j)
+        out.extend(range(grp * j, grp * j + grp) if j < n_tiles else [grp * n_tiles + j - n_tiles])
+    return np.asarray(out, dtype=np.int64)
+
+
+def candidates_of(blocks, n_tiles: int, grp: int):
+    """Inverse of key_blocks_of; None unless every history tile is complete."""
+    blocks = [int(b) for b in blocks]
+    cands, i = [], 0
+    while i < len(blocks):
+        b = blocks[i]
+        if b < grp * n_tiles:
+            j = b // grp
+            if b != grp * j or blocks[i:i + grp] != list(range(grp * j, grp * j + grp)):
+                return None
+            cands.append(j)
+            i += grp
+        else:
+            cands.append(n_tiles + b - grp * n_tiles)
+            i += 1
+    return np.asarray(cands, dtype=np.int64)

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(_lib.SIGNATURES), names
     for n in names:
         assert hasattr(lib, n)
-    assert lib.hsa_abi_version() == 1
+    assert lib.hsa_abi_version() == 2
 
 
 def test_geometry_validation(lib):
@@ -63,6 +63,36 @@ def test_geometry_validation(lib):
         g = c1_geom(**kw)
         assert lib.hsa_geom_check(ctypes.byref(g)) == rc, name
         assert lib.hsa_workspace_bytes(ctypes.byref(g), 16) == 0, name
+
+
+def test_intra_chunk_geometry(lib):
+    # B = 96: splits 1, 2 and 3 give 96-, 48- and 32-token key blocks
+    for sp in (1, 2, 3):
+        g = c1_geom(intra_split=sp)
+        assert lib.hsa_geom_check(ctypes.byref(g)) == 0, sp
+        assert lib.hsa_workspace_bytes(ctypes.byref(g), 16) > lib.hsa_workspace_bytes(ctypes.byref(c1_geom()), 16)
+    bad = {
+        "negative": (dict(intra_split=-1), 4),
+        "above_max": (dict(intra_split=_lib.HSA_MAX_INTRA_SPLIT + 1), 4),
+        "key_block_not_16": (dict(intra_split=4), 2),                # 96 / 4 = 24
+        "not_dividing": (dict(tile_t=4, tile_h=2, tile_w=4, intra_split=3), 2),  # 32 / 3
+        "too_many_key_blocks": (dict(intra_split=3, n_sel_pages=5), 2),          # (62400 + 6240) / 32 > 2048
+    }
+    for name, (kw, rc) in bad.items():
+        g = c1_geom(**kw)
+        assert lib.hsa_geom_check(ctypes.byref(g)) == rc, name
+        assert lib.hsa_workspace_bytes(ctypes.byref(g), 16) == 0, name
+    fake = ctypes.c_void_p(0x1000)
+    pages = (ctypes.c_void_p * 16)(*([0x1000] * 16))
+    intra, plain = c1_geom(intra_split=2), c1_geom()
+    ga = lib.hsa_gather_active
+    # the chunk's keys and values: required with intra keys, refused without
+    assert ga(ctypes.byref(intra), pages, pages, 16, fake, None, fake, fake, fake, None, None) == 1
+    assert ga(ctypes.byref(intra), pages, pages, 16, fake, fake, None, fake, fake, None, None) == 1
+    assert ga(ctypes.byref(plain), pages, pages, 16, fake, fake, fake, fake, fake, None, None) == 4
+    assert ga(ctypes.byref(intra), pages, pages, 200, fake, fake, fake, fake, fake, None, None) == 4
+    # the plain gather does not take a geometry with intra keys
+    assert lib.hsa_gather_pages(ctypes.byref(intra), pages, pages, 16, fake, fake, fake, None, None) == 4
 
 
 def test_workspace_sizes(lib):

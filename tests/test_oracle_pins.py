@@ -275,6 +275,87 @@ def test_sparse_single_block_and_order_invariance():
     np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
 
 
+# ------------------------------------------------------ intra-chunk keys
+def test_intra_blocks_hand_example(golden):
+    g = golden("hw9_intra_blocks.json")
+    k = np.array(g["keys_hist"] + g["keys_chunk"], dtype=np.float64).reshape(1, -1, 1)
+    v = np.array(g["vals_hist"] + g["vals_chunk"], dtype=np.float64).reshape(1, -1, 1)
+    q = np.array(g["q"], dtype=np.float64).reshape(-1, 1, 1)
+    parts = orc.key_parts(len(g["keys_hist"]), g["b_hist"], len(g["keys_chunk"]), g["b_intra"])
+    assert parts == [(0, 2), (2, 2), (4, 1), (5, 1)]
+    for case in g["cases"]:
+        bs = orc.block_selection_parts(q, k, [case["tau"]], g["b_hist"], parts)
+        np.testing.assert_allclose(bs["mass"][0, 0], g["mass"], atol=1e-9)
+        assert bs["sel"][0][0].tolist() == case["sel"]
+        out = orc.sparse_attention_parts(q, k, v, bs["sel"], g["b_hist"], parts)
+        np.testing.assert_allclose(out[:, 0, 0], [case["out"]] * 2, rtol=1e-12)
+
+
+def test_intra_parts_at_the_history_size_reduce_to_uniform_blocks():
+    # b_intra == B: the candidates are the uniform B-token blocks of the joined
+    # sequence, so selection and attention are the uniform-block ones
+    rng = np.random.default_rng(21)
+    H, B, d, lh, lq = 2, 8, 16, 40, 16
+    q = rng.standard_normal((lq, H, d))
+    k = rng.standard_normal((H, lh + lq, d))
+    v = rng.standard_normal((H, lh + lq, d))
+    tau = [0.7, 0.9]
+    parts = orc.key_parts(lh, B, lq, B)
+    a = orc.block_selection_parts(q, k, tau, B, parts)
+    b = orc.block_selection(q, k, tau, B)
+    np.testing.assert_allclose(a["mass"], b["mass"], rtol=1e-12, atol=1e-15)
+    for h in range(H):
+        for i in range(lq // B):
+            assert a["sel"][h][i].tolist() == b["sel"][h][i].tolist()
+    np.testing.assert_allclose(orc.sparse_attention_parts(q, k, v, a["sel"], B, parts),
+                               orc.sparse_attention(q, k, v, b["sel"], B), rtol=1e-12, atol=1e-14)
+
+
+def test_intra_parts_all_selected_is_dense_attention_and_means_nest():
+    rng = np.random.default_rng(22)
+    H, B, bi, d, lh, lq = 2, 8, 4, 16, 24, 16
+    q = rng.standard_normal((lq, H, d))
+    k = rng.standard_normal((H, lh + lq, d))
+    v = rng.standard_normal((H, lh + lq, d))
+    parts = orc.key_parts(lh, B, lq, bi)
+    assert len(parts) == lh // B + lq // bi
+    bs = orc.block_selection_parts(q, k, [1.0, 1.0], B, parts)
+    assert all(len(s) == len(parts) for r in bs["sel"] for s in r)
+    out = orc.sparse_attention_parts(q, k, v, bs["sel"], B, parts)
+    for h in range(H):
+        np.testing.assert_allclose(out[:, h, :], sdpa(q[:, h, :], k[h], v[h]), rtol=1e-10, atol=1e-12)
+    # a history tile's mean is the mean of its two b_intra halves; a chunk
+    # block's mean is the plain mean of its own tokens
+    fine = orc.block_means(k, bi)
+    pm = orc.part_means(k, parts)
+    np.testing.assert_allclose(pm[:, :lh // B], 0.5 * (fine[:, 0:lh // bi:2] + fine[:, 1:lh // bi:2]), rtol=1e-12)
+    np.testing.assert_allclose(pm[:, lh // B:], fine[:, lh // bi:], rtol=1e-12)
+
+
+def test_intra_step_tau_one_is_dense_over_history_and_chunk():
+    rng = np.random.default_rng(23)
+    H, d, Lp, B, bi, lq, r = 2, 8, 16, 8, 4, 8, 4
+    pages_k = [rng.standard_normal((Lp, H, d)) for _ in range(3)]
+    pages_v = [rng.standard_normal((Lp, H, d)) for _ in range(3)]
+    q = rng.standard_normal((lq, H, d))
+    kc = rng.standard_normal((lq, H, d))
+    vc = rng.standard_normal((lq, H, d))
+    L = 2 * Lp + lq
+    e_k = rng.standard_normal((r, L))
+    e_v = rng.standard_normal((r, L))
+    x = rng.standard_normal((lq, H * d))
+    w_g = rng.standard_normal((2 * H, H * d)) * 0.1
+    res = orc.hsa_step(q, pages_k, pages_v, e_k, e_v, w_g, x, [1.0, 1.0], 2, B, k_cur=kc, v_cur=vc, b_intra=bi)
+    sp = res["sel_pages"]
+    for h in range(H):
+        keys = np.concatenate([pages_k[sp[0]][:, h], pages_k[sp[1]][:, h], kc[:, h]])
+        vals = np.concatenate([pages_v[sp[0]][:, h], pages_v[sp[1]][:, h], vc[:, h]])
+        np.testing.assert_allclose(res["o_sp"][:, h], sdpa(q[:, h], keys, vals), rtol=1e-10, atol=1e-12)
+        # the linear branch projects the joined sequence
+        np.testing.assert_allclose(res["lin"]["o_lin"][:, h], sdpa(q[:, h], e_k @ keys, e_v @ vals),
+                                   rtol=1e-10, atol=1e-12)
+
+
 # ------------------------------------------------------------------ S6 fuse
 def test_gate_hand_example(golden):
     g = golden("hw4_gate.json")
