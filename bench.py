@@ -17,6 +17,8 @@ Variants (each reports its own line; the default is the headline workload):
                            only their pages (--pages-per-chunk, default 8)
   --tiers N                N generated chunks over a history in page tiers,
                            fetched on demand vs predicted and prefetched
+  --intra S                the chunk's own tokens join the retrieved history in
+                           key blocks of B/S tokens (intra-chunk keys)
   --graph                  the step replayed as one HIP graph
 """
 from __future__ import annotations
@@ -49,14 +51,15 @@ def stage_model(cfg, n_sel_total: int, indexed: bool = False, scored_pages=None)
                                 cfg.active_tokens, cfg.block, cfg.rank,
                                 cfg.n_pages if scored_pages is None else scored_pages)
     D = H * d
+    Bk, nC = cfg.key_block, cfg.n_candidates  # key-block size; selection candidates per row
     return {
         "score": dict(bound="hbm", bytes=(P * D * 4 if indexed else P * Lp * D * es) + Lq * D * es),
         "gather": dict(bound="hbm", bytes=2 * (2 * L * D * es)),
         "linear": dict(bound="mfma", flops=2 * 2 * H * r * L * d + 2 * 2 * H * Lq * r * d,
                        bytes=2 * L * D * es + 2 * r * L * es + Lq * D * es + Lq * D * 4),
-        "select": dict(bound="hbm", bytes=Lq * D * es + H * (L // B) * d * 4,
-                       flops=2 * H * (Lq // B) * (L // B) * d),
-        "sparse": dict(bound="mfma", flops=4 * B * B * d * n_sel_total),
+        "select": dict(bound="hbm", bytes=Lq * D * es + H * (L // Bk) * d * 4,
+                       flops=2 * H * (Lq // B) * nC * d),
+        "sparse": dict(bound="mfma", flops=4 * B * Bk * d * n_sel_total),
         "fuse": dict(bound="hbm", bytes=Lq * D * es + 2 * Lq * D * 4 + Lq * D * es, flops=2 * Lq * D * 2 * H),
     }
 
@@ -133,6 +136,7 @@ def cpu_baseline(cfg, w, arrays):
     s, pk, pv = arrays
     H, B = cfg.n_heads, cfg.block
     nh = min(3, H)
+    intra = bool(cfg.intra_split)
     t = {}
     t0 = time.perf_counter()
     sc = orc.score_and_select(s["q"], pk, cfg.n_sel_pages)
@@ -141,16 +145,23 @@ def cpu_baseline(cfg, w, arrays):
     t0 = time.perf_counter()
     cat_k = orc.gather_active(pk, sel)
     cat_v = orc.gather_active(pv, sel)
+    if intra:  # the chunk's own keys follow the pages
+        cat_k = np.concatenate([cat_k, np.asarray(s["k_cur"], np.float64).transpose(1, 0, 2)], axis=1)
+        cat_v = np.concatenate([cat_v, np.asarray(s["v_cur"], np.float64).transpose(1, 0, 2)], axis=1)
+        parts = orc.key_parts(cfg.history_tokens, B, cfg.query_tokens, cfg.key_block)
     t["gather"] = time.perf_counter() - t0
     q = np.asarray(s["q"], dtype=np.float64)
     t0 = time.perf_counter()
     lin = orc.linear_branch(q, cat_k, cat_v, s["e_k"], s["e_v"])
     t["linear"] = time.perf_counter() - t0
     t0 = time.perf_counter()
-    bs = orc.block_selection(q, cat_k, s["tau"], B)
+    bs = orc.block_selection_parts(q, cat_k, s["tau"], B, parts) if intra else orc.block_selection(q, cat_k, s["tau"], B)
     t["select"] = time.perf_counter() - t0
     t0 = time.perf_counter()
-    o_sp = orc.sparse_attention(q[:, :nh], cat_k[:nh], cat_v[:nh], bs["sel"][:nh], B)
+    if intra:
+        o_sp = orc.sparse_attention_parts(q[:, :nh], cat_k[:nh], cat_v[:nh], bs["sel"][:nh], B, parts)
+    else:
+        o_sp = orc.sparse_attention(q[:, :nh], cat_k[:nh], cat_v[:nh], bs["sel"][:nh], B)
     t["sparse"] = (time.perf_counter() - t0) * H / nh
     o_full = np.zeros((cfg.query_tokens, H, cfg.head_dim))
     o_full[:, :nh] = o_sp
@@ -264,6 +275,7 @@ def run_tiers(args, cfg):
     s = w.small_inputs()
     up = lambda a: torch.from_numpy(a).to(tdt).cuda()
     q, x, e_k, e_v, w_g = (up(s[k]) for k in ("q", "x", "e_k", "e_v", "w_g"))
+    k_cur, v_cur = (up(s["k_cur"]), up(s["v_cur"])) if cfg.intra_split else (None, None)
     tau = torch.from_numpy(s["tau"]).cuda()
     pk_np, pv_np = w.pages()
     geom = make_geom(cfg.n_heads, cfg.head_dim, cfg.frame_h, cfg.frame_w, cfg.frames_per_page,
@@ -350,6 +362,9 @@ def main():
     ap.add_argument("--page-index", action="store_true",
                     help="score from a page index of mean keys built once before the timed steps "
                          "(as when pages are written) instead of reading every page's keys")
+    ap.add_argument("--intra", type=int, default=0,
+                    help="intra-chunk keys: the chunk's own tokens follow the retrieved pages in key blocks of "
+                         "B/S tokens (S = 2: 48-token blocks beside the 96-token history tiles)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run three device-to-device copies of 1 GiB (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -374,6 +389,13 @@ def main():
     from sparse_linear_attention_hsa_amd.step import HsaStep
 
     cfg = CONFIGS[args.config]
+    if args.intra:
+        from dataclasses import replace
+        if args.tiers or args.chunks or cfg.layers > 1 or cfg.steps > 1:
+            print("bench.py: --intra runs the single-step workloads without --tiers / --chunks", file=sys.stderr)
+            sys.exit(2)
+        cfg = replace(cfg, name=f"{cfg.name}_intra{args.intra}", intra_split=args.intra)
+        cfg.check()
     if args.tiers:
         return run_tiers(args, cfg)
     if cfg.layers > 1 or cfg.steps > 1:
@@ -383,6 +405,7 @@ def main():
     s = w.small_inputs()
     up = lambda a: torch.from_numpy(a).to(tdt).cuda()
     q, x, e_k, e_v, w_g = (up(s[k]) for k in ("q", "x", "e_k", "e_v", "w_g"))
+    k_cur, v_cur = (up(s["k_cur"]), up(s["v_cur"])) if cfg.intra_split else (None, None)
     tau = torch.from_numpy(s["tau"]).cuda()
     keep_host = not args.no_cpu_baseline  # the oracle's scoring reads every page
     pk_np, pv_np, pk, pv = [], [], [], []
@@ -396,7 +419,7 @@ def main():
         if (j + 1) % 8 == 0 or j + 1 == cfg.n_pages:
             print(f"bench: generated {j + 1}/{cfg.n_pages} pages", file=sys.stderr, flush=True)
     geom = make_geom(cfg.n_heads, cfg.head_dim, cfg.frame_h, cfg.frame_w, cfg.frames_per_page,
-                     cfg.query_frames, cfg.tile, cfg.n_sel_pages, cfg.rank, cfg.dtype)
+                     cfg.query_frames, cfg.tile, cfg.n_sel_pages, cfg.rank, cfg.dtype, cfg.intra_split)
     st = HsaStep(geom, cfg.n_pages)
     stream = torch.cuda.current_stream()
 
@@ -421,11 +444,11 @@ def main():
         # the step's own schedule: the linear branch on a side stream beside
         # block selection and the sparse branch, joined before the fusion
         # (on the current stream, which is the capture stream under --graph)
-        st.run(q, pk, pv, e_k, e_v, w_g, x, tau, indexed=indexed, chunks=chunks)
+        st.run(q, pk, pv, e_k, e_v, w_g, x, tau, indexed=indexed, chunks=chunks, k_cur=k_cur, v_cur=v_cur)
 
     def one_step_staged(ev, kev):
         # the same six calls in order on one stream, with events between them
-        calls = (score_stage, lambda: st.gather(pk, pv),
+        calls = (score_stage, lambda: st.gather(pk, pv, k_cur=k_cur, v_cur=v_cur),
                  lambda: st.linear(q, e_k, e_v),
                  lambda: st.select(q, tau), lambda: st.sparse(q, kernel_events=kev), lambda: st.fuse(x, w_g))
         for i, fn in enumerate(calls):
@@ -490,8 +513,9 @@ def main():
     peak_tf = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
 
     # Roofline of the dominant kernel: the block-sparse attention kernel
-    # (algorithmic flops 4*B*B*d per selected (query block, key block) pair,
-    # all pairs of the step in one launch) over its own event-timed duration.
+    # (algorithmic flops 4*B*Bk*d per selected (query block, key block) pair,
+    # Bk = B without intra-chunk keys; all pairs of the step in one launch)
+    # over its own event-timed duration.
     ach = model["sparse"]["flops"] / (attn_kernel_ms * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak_tf, "unit": "TFLOP/s",
             "frac": round(ach / peak_tf, 4), "traffic": measured_traffic(cfg.name),
@@ -502,8 +526,9 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "heads": cfg.n_heads, "head_dim": cfg.head_dim,
-                   "retrieved_tokens": cfg.active_tokens, "query_tokens": cfg.query_tokens,
+                   "retrieved_tokens": cfg.history_tokens, "query_tokens": cfg.query_tokens,
                    "history_pages": cfg.n_pages, "block": cfg.block, "rank": cfg.rank,
+                   "intra_split": cfg.intra_split, "key_block": cfg.key_block, "active_tokens": cfg.active_tokens,
                    "graph": bool(args.graph), "page_index": indexed, "chunks": args.chunks,
                    "pages_per_chunk": args.pages_per_chunk if args.chunks else None},
         "ms_per_step_stats": {"median": round(float(np.median(per_step)), 4),
@@ -513,7 +538,7 @@ def main():
         "attended_tflops": round(sparse_tf, 1), "mfma_frac_sparse": round(sparse_tf / peak_tf, 4),
         "peaks_measured": peaks,
         "mfma_frac_sparse_of_measured": round(sparse_tf / peaks["mfma_bf16_tflops"], 4),
-        "selected_block_frac": round(n_sel_total / (cfg.n_heads * cfg.n_qblocks * cfg.n_kblocks), 4),
+        "selected_block_frac": round(n_sel_total / (cfg.n_heads * cfg.n_qblocks * cfg.n_key_blocks), 4),
         "linear_tflops": round(lin_tf, 1),
         "score_gbs": round(model["score"]["bytes"] / (stage_ms["score"] * 1e-3) / 1e9, 1),
         "gather_gbs": round(model["gather"]["bytes"] / (stage_ms["gather"] * 1e-3) / 1e9, 1),

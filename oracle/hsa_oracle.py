@@ -433,15 +433,20 @@ def block_selection_parts(q: np.ndarray, k_act: np.ndarray, tau: Sequence[float]
     return dict(qbar=qb, kbar=kb, mass=mass, sel=sel, counts=counts, flags=flags)
 
 
+def sparse_row_parts(q_i, k_h, v_h, cands: Sequence[int], parts) -> np.ndarray:
+    """One query block over exactly the tokens of its selected candidates."""
+    idx = np.concatenate([np.arange(parts[j][0], parts[j][0] + parts[j][1]) for j in cands])
+    return attention(q_i, k_h[idx], v_h[idx])
+
+
 def sparse_attention_parts(q, k_act, v_act, sel, b, parts):
-    """q [Lq][H][d]; sel[h][i] candidate ids -> O_sp [Lq][H][d]: attention of
-    query block i over exactly the tokens of its selected candidates."""
+    """q [Lq][H][d]; sel[h][i] candidate ids -> O_sp [Lq][H][d]."""
     Lq, H, d = q.shape
     out = np.empty((Lq, H, d))
     for h in range(H):
         for i in range(Lq // b):
-            idx = np.concatenate([np.arange(parts[j][0], parts[j][0] + parts[j][1]) for j in sel[h][i]])
-            out[i * b:(i + 1) * b, h, :] = attention(q[i * b:(i + 1) * b, h, :], k_act[h][idx], v_act[h][idx])
+            out[i * b:(i + 1) * b, h, :] = sparse_row_parts(q[i * b:(i + 1) * b, h, :], k_act[h], v_act[h],
+                                                            sel[h][i], parts)
     return out
 
 
