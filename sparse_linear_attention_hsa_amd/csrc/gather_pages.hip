@@ -23,8 +23,8 @@ namespace {
 constexpr int kGatherThreads = 256;
 constexpr int kBatch = 6;  // passes whose loads are in flight together
 
-// NSUB: the largest number of key blocks per B-token block (1 without
-// intra-chunk keys, where key blocks are B tokens).
+// NSUB: key blocks per B-token block (1 without intra-chunk keys, where key
+// blocks are B tokens).
 template <typename T, int D, int NSUB>
 __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
     PageTable pk, PageTable pv, int n_pages, const int32_t* __restrict__ sel, const T* __restrict__ k_cur,
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
   constexpr int VS = D + VPAD;                     // LDS row stride (elements)
   extern __shared__ __align__(16) unsigned char smem[];
   T* vs = reinterpret_cast<T*>(smem);                              // [B][VS]
-  float* red = reinterpret_cast<float*>(smem + (size_t)B * VS * sizeof(T));  // [nsub][256][E]
+  float* red = reinterpret_cast<float*>(smem + (size_t)B * VS * sizeof(T));  // [256][E]
 
   const int bpp = Lp / B;
   const int h = blockIdx.y;
@@ -97,11 +97,10 @@ __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
       }
     }
   }
+  if (NSUB == 1) {
 #pragma unroll
-  for (int su = 0; su < NSUB; ++su)
-    if (su < nsub)
-#pragma unroll
-      for (int e = 0; e < E; ++e) red[(su * kGatherThreads + t) * E + e] = acc[su][e];
+    for (int e = 0; e < E; ++e) red[t * E + e] = acc[0][e];
+  }
   __syncthreads();
 
   // values: [16 tokens][D] granules in LDS -> [D][16] granules in memory
@@ -118,21 +117,33 @@ __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
     st16(v_act + (((size_t)h * (L / 16) + g0 + gr) * D + drow) * 16 + part * E, pack16<T>(f));
   }
 
-  // key-block means (fixed-order sum over the row phases)
-  if (kblk_mean != nullptr && t < CPR * nsub) {
-    const int su = t / CPR, c = t % CPR;
-    float s[E];
+  // key-block means (fixed-order sum over the row phases), one key block at
+  // a time through the same LDS area (its first one is already there when
+  // a block holds one key block)
+  if (kblk_mean == nullptr) return;
 #pragma unroll
-    for (int e = 0; e < E; ++e) s[e] = 0.f;
-    for (int ph = 0; ph < RPP; ++ph) {
+  for (int su = 0; su < NSUB; ++su) {
+    if (su >= nsub) break;  // block-uniform
+    if (NSUB > 1) {
+      if (su > 0) __syncthreads();  // the previous key block's sums are read
 #pragma unroll
-      for (int e = 0; e < E; ++e) s[e] += red[(su * kGatherThreads + ph * CPR + c) * E + e];
+      for (int e = 0; e < E; ++e) red[t * E + e] = acc[su][e];
+      __syncthreads();
     }
-    const float inv = 1.f / (float)Bk;
-    const int j = (int)(act0 / Bk) + su;
-    float* dst = kblk_mean + ((size_t)h * nKB + j) * D + c * E;
+    if (t < CPR) {
+      float s[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) dst[e] = s[e] * inv;
+      for (int e = 0; e < E; ++e) s[e] = 0.f;
+      for (int ph = 0; ph < RPP; ++ph) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[e] += red[(ph * CPR + t) * E + e];
+      }
+      const float inv = 1.f / (float)Bk;
+      const int j = (int)(act0 / Bk) + su;
+      float* dst = kblk_mean + ((size_t)h * nKB + j) * D + t * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) dst[e] = s[e] * inv;
+    }
   }
 }
 
@@ -142,9 +153,13 @@ void launch_gather(const Dims& s, const PageTable& pk, const PageTable& pv, int 
                    hipStream_t st) {
   constexpr int E = Vec<T>::N;
   const int nsub = s.B / s.Bk;
-  const size_t smem = (size_t)s.B * (D + E) * sizeof(T) + (size_t)nsub * kGatherThreads * E * sizeof(float);
+  const size_t smem = (size_t)s.B * (D + E) * sizeof(T) + (size_t)kGatherThreads * E * sizeof(float);
   dim3 grid(s.Kp * (s.Lp / s.B) + (s.split ? s.Lq / s.B : 0), s.H);
-  auto kern = nsub == 1 ? gather_block_kernel<T, D, 1> : gather_block_kernel<T, D, HSA_MAX_INTRA_SPLIT>;
+  static_assert(HSA_MAX_INTRA_SPLIT == 4, "one instantiation per key blocks per block");
+  auto kern = nsub == 1   ? gather_block_kernel<T, D, 1>
+              : nsub == 2 ? gather_block_kernel<T, D, 2>
+              : nsub == 3 ? gather_block_kernel<T, D, 3>
+                          : gather_block_kernel<T, D, 4>;
   if (smem > 65536)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)smem);
