@@ -328,6 +328,55 @@ hsa_rc hsa_sparse_attn_timed(const hsa_geom* geom, const void* q, const void* k_
 hsa_rc hsa_fuse(const hsa_geom* geom, const void* x, const void* w_g, const float* gate_override,
                 const float* o_lin, const float* o_sp, void* out, hsa_stream stream);
 
+/* ---------------------------------------------------------------------------
+ * Pages read in place (no active-buffer copy).  Paper section 3.2 (the
+ * retrieved pages are what the attention reads; the page index is built from
+ * the keys when pages are written) and the copy into the active buffer that
+ * the pages' own profile names as the largest cost of the step.  A page is
+ * laid out once, when it is written, in the layouts the kernels read: K as
+ * [H][Lp][d] and V as [H][Lp/16][d][16] (the active buffer's layouts over
+ * one page), with the mean of every B-token block [H][Lp/B][d] float32.  A
+ * step then scores from the page index (hsa_score_pages with NULL page
+ * pointers and page_kmean), takes the selected pages' block means
+ * (hsa_gather_block_means, for hsa_block_select with k_act = NULL), and runs
+ * the linear and sparse branches straight from the laid-out pages: active key
+ * t is token t % Lp of page sel_pages[t / Lp], so every result is the one the
+ * active-buffer path computes.  Requires intra_split = 0 (HSA_ERR_BAD_PARAM).
+ * ------------------------------------------------------------------------- */
+
+/* Lay out one page: k_page, v_page [Lp][H][d] dtype (as the model writes
+ * them) -> k_out [H][Lp][d], v_out [H][Lp/16][d][16] dtype, blk_mean
+ * [H][Lp/B][d] float32 (or NULL).  The output buffers are the caller's and
+ * must not overlap the inputs.  Errors: HSA_ERR_NULL_ARG, geometry errors. */
+hsa_rc hsa_page_prepare(const hsa_geom* geom, const void* k_page, const void* v_page, void* k_out, void* v_out,
+                        float* blk_mean, hsa_stream stream);
+
+/* kblk_mean [H][nKB][d] float32 out: the block means of the selected pages,
+ * from page_blk_mean, a HOST array of n_pages device pointers, each a page's
+ * blk_mean from hsa_page_prepare.  sel_pages [K_p] int32 device, as
+ * hsa_gather_pages (out-of-range ids are clamped).  Errors: HSA_ERR_NULL_ARG
+ * (any entry NULL), HSA_ERR_BAD_PARAM (n_pages). */
+hsa_rc hsa_gather_block_means(const hsa_geom* geom, const float* const* page_blk_mean, int32_t n_pages,
+                              const int32_t* sel_pages, float* kblk_mean, hsa_stream stream);
+
+/* hsa_linear_branch over laid-out pages: page_k, page_v are HOST arrays of
+ * n_pages device pointers, each a page's k_out / v_out from hsa_page_prepare;
+ * sel_pages as above.  Other arguments, flags, workspace and errors as
+ * hsa_linear_branch; with HSA_LIN_REUSE_PROJ the pages may be NULL.
+ * HSA_ERR_BAD_SHAPE if a page holds fewer than 32 tokens. */
+hsa_rc hsa_linear_branch_paged(const hsa_geom* geom, const void* q, const void* const* page_k,
+                               const void* const* page_v, int32_t n_pages, const int32_t* sel_pages,
+                               const void* e_k, const void* e_v, void* k_proj, void* v_proj, float* o_lin,
+                               int32_t flags, void* ws, size_t ws_bytes, hsa_stream stream);
+
+/* hsa_sparse_attn_timed over laid-out pages (page_k, page_v, n_pages,
+ * sel_pages as hsa_linear_branch_paged); the events may be NULL.  Errors as
+ * hsa_sparse_attn, plus HSA_ERR_BAD_PARAM for n_pages. */
+hsa_rc hsa_sparse_attn_paged(const hsa_geom* geom, const void* q, const void* const* page_k,
+                             const void* const* page_v, int32_t n_pages, const int32_t* sel_pages,
+                             const int32_t* blk_count, const int32_t* blk_idx, float* o_sp, void* ws,
+                             size_t ws_bytes, hsa_stream stream, hsa_event ev_begin, hsa_event ev_end);
+
 /* Bytes of workspace every call above needs for this geometry (0 if the
  * geometry is invalid).  One workspace serves all calls on one stream. */
 size_t hsa_workspace_bytes(const hsa_geom* geom, int32_t n_pages);

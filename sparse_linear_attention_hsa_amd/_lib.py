@@ -47,6 +47,12 @@ SIGNATURES = {
     "hsa_gather_active": (_i32, [_GP, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _vp]),
     "hsa_linear_branch": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
+    "hsa_page_prepare": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "hsa_gather_block_means": (_i32, [_GP, ctypes.POINTER(_vp), _i32, _vp, _vp, _vp]),
+    "hsa_linear_branch_paged": (_i32, [_GP, _vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp,
+                                       _vp, _vp, _i32, _vp, _sz, _vp]),
+    "hsa_sparse_attn_paged": (_i32, [_GP, _vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp,
+                                     _vp, _sz, _vp, _vp, _vp]),
     "hsa_block_select": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "hsa_sparse_attn": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "hsa_sparse_attn_timed": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),

@@ -25,6 +25,19 @@ struct PageTable {
   const void* p[kMaxPages];
 };
 
+// Keys and values read in place from laid-out pages (PAGED kernels): page j
+// holds K as [H][Lp][d] and V as [H][Lp/16][d][16] (the active buffer's
+// layouts over one page), and active key t is token t % Lp of page
+// sel[t / Lp].  The unpaged form carries nothing.
+template <bool PAGED> struct PagedKV {
+  static constexpr int Lp = 0;
+};
+template <> struct PagedKV<true> {
+  PageTable pk, pv;
+  const int32_t* sel;
+  int n_pages, Lp;
+};
+
 __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
   size_t tok0, act0;  // first token of the block in its source, and in the active buffer
   if ((int)blockIdx.x < Kp * bpp) {
     const int p = blockIdx.x / bpp, blk = blockIdx.x % bpp;
-    int page = sel[p];
+    int page = sel ? sel[p] : p;  // no selection: the pages in table order
     page = page < 0 ? 0 : (page >= n_pages ? n_pages - 1 : page);
     ksrc = reinterpret_cast<const T*>(pk.p[page]);
     vsrc = reinterpret_cast<const T*>(pv.p[page]);
@@ -168,8 +168,75 @@ void launch_gather(const Dims& s, const PageTable& pk, const PageTable& pv, int 
                      s.Bk, s.L, s.nKB, reinterpret_cast<T*>(k_act), reinterpret_cast<T*>(v_act), kblk_mean);
 }
 
+// Key-block means of the selected pages from each page's own block means
+// [H][Lp/B][d] (written when the page was laid out): one thread per element
+// of kblk_mean [H][nKB][d].
+__global__ __launch_bounds__(256) void gather_block_means_kernel(PageTable pm, int n_pages,
+                                                                const int32_t* __restrict__ sel, int H, int D,
+                                                                int bpp, int nKB, float* __restrict__ kblk_mean) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)H * nKB * D) return;
+  const int e = (int)(i % D);
+  const int j = (int)((i / D) % nKB);
+  const int h = (int)(i / ((size_t)D * nKB));
+  const int p = j / bpp, lb = j % bpp;
+  int page = sel[p];
+  page = page < 0 ? 0 : (page >= n_pages ? n_pages - 1 : page);
+  kblk_mean[i] = reinterpret_cast<const float*>(pm.p[page])[((size_t)h * bpp + lb) * D + e];
+}
+
 }  // namespace
 }  // namespace hsa
+
+extern "C" hsa_rc hsa_page_prepare(const hsa_geom* geom, const void* k_page, const void* v_page, void* k_out,
+                                   void* v_out, float* blk_mean, hsa_stream stream) {
+  using namespace hsa;
+  Dims s;
+  hsa_rc rc = derive(geom, &s);
+  if (rc != HSA_OK) return rc;
+  if (s.split) return HSA_ERR_BAD_PARAM;
+  if (!k_page || !v_page || !k_out || !v_out) return HSA_ERR_NULL_ARG;
+  // the active-buffer gather over one page, in table order
+  Dims one = s;
+  one.Kp = 1;
+  one.L = one.Lh = s.Lp;
+  one.nKB = one.nKBh = one.nC = s.Lp / s.B;
+  PageTable pk, pv;
+  for (int j = 0; j < kMaxPages; ++j) pk.p[j] = pv.p[j] = nullptr;
+  pk.p[0] = k_page;
+  pv.p[0] = v_page;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (s.bf16) {
+    if (s.d == 128) launch_gather<bf16_t, 128>(one, pk, pv, 1, nullptr, nullptr, nullptr, k_out, v_out, blk_mean, st);
+    else launch_gather<bf16_t, 64>(one, pk, pv, 1, nullptr, nullptr, nullptr, k_out, v_out, blk_mean, st);
+  } else {
+    if (s.d == 128) launch_gather<float, 128>(one, pk, pv, 1, nullptr, nullptr, nullptr, k_out, v_out, blk_mean, st);
+    else launch_gather<float, 64>(one, pk, pv, 1, nullptr, nullptr, nullptr, k_out, v_out, blk_mean, st);
+  }
+  return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
+}
+
+extern "C" hsa_rc hsa_gather_block_means(const hsa_geom* geom, const float* const* page_blk_mean, int32_t n_pages,
+                                         const int32_t* sel_pages, float* kblk_mean, hsa_stream stream) {
+  using namespace hsa;
+  Dims s;
+  hsa_rc rc = derive(geom, &s);
+  if (rc != HSA_OK) return rc;
+  if (s.split) return HSA_ERR_BAD_PARAM;
+  if (!page_blk_mean || !sel_pages || !kblk_mean) return HSA_ERR_NULL_ARG;
+  if (n_pages < 1 || n_pages > HSA_MAX_PAGES || s.Kp > n_pages) return HSA_ERR_BAD_PARAM;
+  PageTable pm;
+  for (int j = 0; j < kMaxPages; ++j) pm.p[j] = nullptr;
+  for (int j = 0; j < n_pages; ++j) {
+    if (!page_blk_mean[j]) return HSA_ERR_NULL_ARG;
+    pm.p[j] = page_blk_mean[j];
+  }
+  const size_t n = (size_t)s.H * s.nKB * s.d;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(gather_block_means_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, pm, n_pages,
+                     sel_pages, s.H, s.d, s.Lp / s.B, s.nKB, kblk_mean);
+  return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
+}
 
 extern "C" hsa_rc hsa_gather_active(const hsa_geom* geom, const void* const* page_k, const void* const* page_v,
                                     int32_t n_pages, const int32_t* sel_pages, const void* k_cur,

@@ -80,10 +80,10 @@ constexpr int kProjThreads = 512;  // 8 waves
 constexpr int kProjHeads = 2;
 constexpr int kProjRing = 4;
 
-template <typename T, int D>
+template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lin_project_kernel(
     const T* __restrict__ k_act, const T* __restrict__ v_act, const T* __restrict__ e_k,
-    const T* __restrict__ e_v, int H, int L, int r, int splits, float* __restrict__ partial) {
+    const T* __restrict__ e_v, int H, int L, int r, int splits, float* __restrict__ partial, PagedKV<PAGED> pg) {
   constexpr int E = Vec<T>::N;
   constexpr int KS = Mma<T>::K;                      // tokens per stage (one contraction step)
   constexpr int DT = D / 16;
@@ -147,6 +147,24 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2,
   // exactly PER loads per wave (tails read the zero page), so the waits can count them
   auto issue = [&](int stg, unsigned char* le, unsigned char* lx) {
     const int tok0 = stg * KS;
+    // paged: the stage's KS tokens lie in at most two pages (16-token
+    // granules never straddle one); tokens from bnd on are in the second
+    int bnd = 0, first = 0;
+    const T* kpage[2] = {nullptr, nullptr};
+    const T* vpage[2] = {nullptr, nullptr};
+    if constexpr (PAGED) {
+      const int kp = L / pg.Lp;
+      const int p0 = tok0 / pg.Lp, p1 = min(p0 + 1, kp - 1);
+      first = p0 * pg.Lp;
+      bnd = first + pg.Lp;
+      int pa = pg.sel[p0], pb = pg.sel[p1];
+      pa = pa < 0 ? 0 : (pa >= pg.n_pages ? pg.n_pages - 1 : pa);
+      pb = pb < 0 ? 0 : (pb >= pg.n_pages ? pg.n_pages - 1 : pb);
+      kpage[0] = reinterpret_cast<const T*>(pg.pk.p[pa]);
+      kpage[1] = reinterpret_cast<const T*>(pg.pk.p[pb]);
+      vpage[0] = reinterpret_cast<const T*>(pg.pv.p[pa]);
+      vpage[1] = reinterpret_cast<const T*>(pg.pv.p[pb]);
+    }
 #pragma unroll
     for (int ii = 0; ii < EINST / NW; ++ii) {
       const int i = ii * NW + w;
@@ -169,14 +187,32 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2,
         const int rowv = (j % (D / 64)) * 64 + lane;
         const int gr = region / PV, part = region % PV;
         const int tk = tok0 + gr * 16;
-        src = (hh < H && tk < L)
-                  ? (const void*)(v_act + (((size_t)hh * (L / 16) + tk / 16) * D + rowv) * 16 + part * E)
-                  : (const void*)(kZeroPage + lane);
+        if constexpr (PAGED) {
+          const bool second = tk >= bnd;
+          const int lt = tk - (second ? bnd : first);
+          src = (hh < H && tk < L)
+                    ? (const void*)((second ? vpage[1] : vpage[0]) +
+                                    (((size_t)hh * (pg.Lp / 16) + lt / 16) * D + rowv) * 16 + part * E)
+                    : (const void*)(kZeroPage + lane);
+        } else {
+          src = (hh < H && tk < L)
+                    ? (const void*)(v_act + (((size_t)hh * (L / 16) + tk / 16) * D + rowv) * 16 + part * E)
+                    : (const void*)(kZeroPage + lane);
+        }
       } else {
         const int tr = j * KROWS + lane / (D / E);
         const int chunk = (lane % (D / E)) ^ kslot(tr);
-        src = (hh < H && tok0 + tr < L) ? (const void*)(k_act + ((size_t)hh * L + tok0 + tr) * D + chunk * E)
-                                        : (const void*)(kZeroPage + lane);
+        if constexpr (PAGED) {
+          const int tk = tok0 + tr;
+          const bool second = tk >= bnd;
+          const int lt = tk - (second ? bnd : first);
+          src = (hh < H && tk < L)
+                    ? (const void*)((second ? kpage[1] : kpage[0]) + ((size_t)hh * pg.Lp + lt) * D + chunk * E)
+                    : (const void*)(kZeroPage + lane);
+        } else {
+          src = (hh < H && tok0 + tr < L) ? (const void*)(k_act + ((size_t)hh * L + tok0 + tr) * D + chunk * E)
+                                          : (const void*)(kZeroPage + lane);
+        }
       }
       __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(lx + hsl * XBYTES + j * 1024), 16, 0, 0);
     }
@@ -526,18 +562,18 @@ __global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(2, 
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool PAGED>
 void launch_linear(const Dims& s, const void* q, const void* k_act, const void* v_act, const void* e_k,
                    const void* e_v, void* k_proj, void* v_proj, float* o_lin, int flags, char* ws,
-                   const WsLayout& w, hipStream_t st) {
+                   const WsLayout& w, const PagedKV<PAGED>& pg, hipStream_t st) {
   const ProjPlan pp = proj_plan(s);
   float* partial = reinterpret_cast<float*>(ws + w.lin_partial);
   if (!(flags & HSA_LIN_REUSE_PROJ)) {
     const int n_items = pp.splits * 2 * ((s.H + 1) / 2);
-    hipLaunchKernelGGL((lin_project_kernel<T, D>), dim3((n_items + 7) / 8 * 8), dim3(kProjThreads), 0, st,
+    hipLaunchKernelGGL((lin_project_kernel<T, D, PAGED>), dim3((n_items + 7) / 8 * 8), dim3(kProjThreads), 0, st,
                        reinterpret_cast<const T*>(k_act), reinterpret_cast<const T*>(v_act),
                        reinterpret_cast<const T*>(e_k), reinterpret_cast<const T*>(e_v), s.H, s.L, s.r, pp.splits,
-                       partial);
+                       partial, pg);
     hipLaunchKernelGGL(lin_reduce_kernel, dim3(2 * s.H, (s.r * D / 4 + 255) / 256), dim3(256), 0, st, partial, s.H, D, s.r, pp.splits,
                        reinterpret_cast<float*>(k_proj), reinterpret_cast<float*>(v_proj));
   }
@@ -559,6 +595,35 @@ void launch_linear(const Dims& s, const void* q, const void* k_act, const void* 
 }  // namespace
 }  // namespace hsa
 
+namespace hsa {
+namespace {
+
+template <bool PAGED>
+hsa_rc linear_entry(const Dims& s, const void* q, const void* k_act, const void* v_act, const void* e_k,
+                    const void* e_v, void* k_proj, void* v_proj, float* o_lin, int32_t flags, void* ws,
+                    size_t ws_bytes, hsa_stream stream, const PagedKV<PAGED>& pg) {
+  if (flags & ~(HSA_LIN_REUSE_PROJ | HSA_LIN_PROJ_ONLY)) return HSA_ERR_BAD_PARAM;
+  if ((flags & HSA_LIN_REUSE_PROJ) && (flags & HSA_LIN_PROJ_ONLY)) return HSA_ERR_BAD_PARAM;
+  if (!k_proj || !v_proj) return HSA_ERR_NULL_ARG;
+  if (!(flags & HSA_LIN_REUSE_PROJ) && ((!PAGED && (!k_act || !v_act)) || !e_k || !e_v)) return HSA_ERR_NULL_ARG;
+  if (!(flags & HSA_LIN_PROJ_ONLY) && (!q || !o_lin)) return HSA_ERR_NULL_ARG;
+  const WsLayout w = ws_layout(s, 1);
+  if (!ws || ws_bytes < w.lin_end) return HSA_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(ws);
+  if (s.bf16) {
+    if (s.d == 128) launch_linear<bf16_t, 128, PAGED>(s, q, k_act, v_act, e_k, e_v, k_proj, v_proj, o_lin, flags, wsb, w, pg, st);
+    else launch_linear<bf16_t, 64, PAGED>(s, q, k_act, v_act, e_k, e_v, k_proj, v_proj, o_lin, flags, wsb, w, pg, st);
+  } else {
+    if (s.d == 128) launch_linear<float, 128, PAGED>(s, q, k_act, v_act, e_k, e_v, k_proj, v_proj, o_lin, flags, wsb, w, pg, st);
+    else launch_linear<float, 64, PAGED>(s, q, k_act, v_act, e_k, e_v, k_proj, v_proj, o_lin, flags, wsb, w, pg, st);
+  }
+  return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace hsa
+
 extern "C" hsa_rc hsa_linear_branch(const hsa_geom* geom, const void* q, const void* k_act, const void* v_act,
                                     const void* e_k, const void* e_v, void* k_proj, void* v_proj, float* o_lin,
                                     int32_t flags, void* ws, size_t ws_bytes, hsa_stream stream) {
@@ -566,21 +631,36 @@ extern "C" hsa_rc hsa_linear_branch(const hsa_geom* geom, const void* q, const v
   Dims s;
   hsa_rc rc = derive(geom, &s);
   if (rc != HSA_OK) return rc;
-  if (flags & ~(HSA_LIN_REUSE_PROJ | HSA_LIN_PROJ_ONLY)) return HSA_ERR_BAD_PARAM;
-  if ((flags & HSA_LIN_REUSE_PROJ) && (flags & HSA_LIN_PROJ_ONLY)) return HSA_ERR_BAD_PARAM;
-  if (!k_proj || !v_proj) return HSA_ERR_NULL_ARG;
-  if (!(flags & HSA_LIN_REUSE_PROJ) && (!k_act || !v_act || !e_k || !e_v)) return HSA_ERR_NULL_ARG;
-  if (!(flags & HSA_LIN_PROJ_ONLY) && (!q || !o_lin)) return HSA_ERR_NULL_ARG;
-  const WsLayout w = ws_layout(s, 1);
-  if (!ws || ws_bytes < w.lin_end) return HSA_ERR_WORKSPACE;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  char* wsb = static_cast<char*>(ws);
-  if (s.bf16) {
-    if (s.d == 128) launch_linear<bf16_t, 128>(s, q, k_act, v_act, e_k, e_v, k_proj, v_proj, o_lin, flags, wsb, w, st);
-    else launch_linear<bf16_t, 64>(s, q, k_act, v_act, e_k, e_v, k_proj, v_proj, o_lin, flags, wsb, w, st);
-  } else {
-    if (s.d == 128) launch_linear<float, 128>(s, q, k_act, v_act, e_k, e_v, k_proj, v_proj, o_lin, flags, wsb, w, st);
-    else launch_linear<float, 64>(s, q, k_act, v_act, e_k, e_v, k_proj, v_proj, o_lin, flags, wsb, w, st);
+  return linear_entry<false>(s, q, k_act, v_act, e_k, e_v, k_proj, v_proj, o_lin, flags, ws, ws_bytes, stream,
+                             PagedKV<false>{});
+}
+
+extern "C" hsa_rc hsa_linear_branch_paged(const hsa_geom* geom, const void* q, const void* const* page_k,
+                                          const void* const* page_v, int32_t n_pages, const int32_t* sel_pages,
+                                          const void* e_k, const void* e_v, void* k_proj, void* v_proj,
+                                          float* o_lin, int32_t flags, void* ws, size_t ws_bytes,
+                                          hsa_stream stream) {
+  using namespace hsa;
+  Dims s;
+  hsa_rc rc = derive(geom, &s);
+  if (rc != HSA_OK) return rc;
+  if (s.split) return HSA_ERR_BAD_PARAM;
+  // a contraction step (at most 32 tokens) must span at most two pages
+  if (s.Lp < 32) return HSA_ERR_BAD_SHAPE;
+  PagedKV<true> pg;
+  for (int j = 0; j < kMaxPages; ++j) pg.pk.p[j] = pg.pv.p[j] = nullptr;
+  if (!(flags & HSA_LIN_REUSE_PROJ)) {
+    if (!page_k || !page_v || !sel_pages) return HSA_ERR_NULL_ARG;
+    if (n_pages < 1 || n_pages > HSA_MAX_PAGES || s.Kp > n_pages) return HSA_ERR_BAD_PARAM;
+    for (int j = 0; j < n_pages; ++j) {
+      if (!page_k[j] || !page_v[j]) return HSA_ERR_NULL_ARG;
+      pg.pk.p[j] = page_k[j];
+      pg.pv.p[j] = page_v[j];
+    }
   }
-  return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
+  pg.sel = sel_pages;
+  pg.n_pages = n_pages;
+  pg.Lp = s.Lp;
+  return linear_entry<true>(s, q, nullptr, nullptr, e_k, e_v, k_proj, v_proj, o_lin, flags, ws, ws_bytes, stream,
+                            pg);
 }

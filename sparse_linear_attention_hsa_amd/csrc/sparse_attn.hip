@@ -161,12 +161,12 @@ __global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
 
 // FULL: every wave owns exactly QPW query tiles (B == 16*NW*QPW), so the tile
 // loops carry no run-time guards and the matrix-core chains stay branch-free.
-template <typename T, int D, int NW, int QPW, int WPE, int RING, bool FULL>
+template <typename T, int D, int NW, int QPW, int WPE, int RING, bool FULL, bool PAGED>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void sparse_attn_kernel(
     const T* __restrict__ q, const T* __restrict__ k_act, const T* __restrict__ v_act,
     const int32_t* __restrict__ blk_idx, const int4* __restrict__ items, const int* __restrict__ meta,
     int H, int B, int Bk, int L, int nKB, int nQB, float scale_log2,
-    float* __restrict__ o_sp, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    float* __restrict__ o_sp, float* __restrict__ part_o, float* __restrict__ part_ml, PagedKV<PAGED> pg) {
   constexpr int E = Vec<T>::N;          // elements per 16-byte chunk
   constexpr int KS = Mma<T>::K;         // keys per step
   constexpr int GPS = KS / 16;          // granules per step
@@ -206,6 +206,17 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
   const int b0 = g0 / gpb;
   const int nblk = gcount > 0 ? (g0 + gcount - 1) / gpb - b0 + 1 : 0;
   const int blk_lane = lane < nblk ? blk_idx[(size_t)row * nKB + b0 + lane] : -1;
+  // paged: each lane's block as (block within its page, that page's id); an
+  // invalid id takes the first selected page
+  int lblk_lane = 0, page_lane = 0;
+  if constexpr (PAGED) {
+    const int bpp = pg.Lp / Bk;
+    const bool valid = blk_lane >= 0 && blk_lane < nKB;
+    const int ps = valid ? blk_lane / bpp : 0;
+    lblk_lane = valid ? blk_lane - ps * bpp : 0;
+    const int page = pg.sel[ps];
+    page_lane = page < 0 ? 0 : (page >= pg.n_pages ? pg.n_pages - 1 : page);
+  }
 
   // Q^T operand: lane (g, c) holds Q[row c of tile][chunk 4s+g] for step s.
   uint4 qreg[QPW][DSTEPS];
@@ -247,6 +258,9 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
   // active K/V is at most HSA_MAX_KBLOCKS * 192 * 128 * 4 bytes, well within
   // 32 bits.
   const int head_bytes = (int)((size_t)L * D * sizeof(T));
+  // paged: one head of one page, K [Lp][d] or V [Lp/16][d][16]
+  const int page_head_bytes = PAGED ? (int)((size_t)pg.Lp * D * sizeof(T)) : 0;
+  const size_t page_head_elems = PAGED ? (size_t)h * pg.Lp * D : 0;
 
   // per-lane parts of the direct-load addresses (element offsets from the
   // start of the granule); only the granule's key offset changes per step
@@ -277,16 +291,21 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
   // Stage the next GPS granules into (lk, lv); returns their validity bits.
   auto issue = [&](unsigned char* lk, unsigned char* lv) -> unsigned {
     int kofs[GPS];
+    int pgid[GPS];  // paged: the granule's page
     unsigned mask = 0;
 #pragma unroll
     for (int j = 0; j < GPS; ++j) {
       int key = -1;
+      const int src = issued < gcount ? cur_blk : 0;  // lane of the granule's block
       if (issued < gcount) {
         const int blk = __builtin_amdgcn_readlane(blk_lane, cur_blk);
-        if (blk >= 0 && blk < nKB) key = blk * Bk + cur_gran * 16;
+        const int kb = PAGED ? __builtin_amdgcn_readlane(lblk_lane, cur_blk) : blk;
+        if (blk >= 0 && blk < nKB) key = kb * Bk + cur_gran * 16;
       }
+      if constexpr (PAGED) pgid[j] = __builtin_amdgcn_readlane(page_lane, src);
       // a masked granule (past the segment or an invalid block id) loads the
-      // head's first granule: its scores are set to -inf, so it adds nothing
+      // head's first granule (paged: of its page or the first selected one):
+      // its scores are set to -inf, so it adds nothing
       kofs[j] = key >= 0 ? key : 0;
       mask |= (key >= 0 ? 1u : 0u) << j;
       ++issued;
@@ -300,14 +319,26 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
       const int i = ii * NW + w;
       if (KINST % NW != 0 && i >= KINST) break;
       const int kg = kofs[kgran[ii]];
-      buffer_load_lds16(kh, head_bytes, lk + i * 1024, koff[ii] * (int)sizeof(T), kg * D * (int)sizeof(T));
+      if constexpr (PAGED) {
+        const int pid = __builtin_amdgcn_readfirstlane(pgid[kgran[ii]]);
+        buffer_load_lds16(reinterpret_cast<const T*>(pg.pk.p[pid]) + page_head_elems, page_head_bytes,
+                          lk + i * 1024, koff[ii] * (int)sizeof(T), kg * D * (int)sizeof(T));
+      } else {
+        buffer_load_lds16(kh, head_bytes, lk + i * 1024, koff[ii] * (int)sizeof(T), kg * D * (int)sizeof(T));
+      }
     }
 #pragma unroll
     for (int ii = 0; ii < VPW; ++ii) {
       const int i = ii * NW + w;
       if (VINST % NW != 0 && i >= VINST) break;
       const int kg = kofs[vgran[ii]];
-      buffer_load_lds16(vh, head_bytes, lv + i * 1024, voff[ii] * (int)sizeof(T), kg * D * (int)sizeof(T));
+      if constexpr (PAGED) {
+        const int pid = __builtin_amdgcn_readfirstlane(pgid[vgran[ii]]);
+        buffer_load_lds16(reinterpret_cast<const T*>(pg.pv.p[pid]) + page_head_elems, page_head_bytes,
+                          lv + i * 1024, voff[ii] * (int)sizeof(T), kg * D * (int)sizeof(T));
+      } else {
+        buffer_load_lds16(vh, head_bytes, lv + i * 1024, voff[ii] * (int)sizeof(T), kg * D * (int)sizeof(T));
+      }
     }
     return mask;
   };
@@ -577,10 +608,10 @@ __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
   }
 }
 
-template <typename T, int D, int NW, int QPW>
+template <typename T, int D, int NW, int QPW, bool PAGED>
 void launch_attn(const Dims& s, const SparsePlan& pl, const void* q, const void* k_act, const void* v_act,
                  const int32_t* idx, const int4* items, const int* meta, float* o_sp,
-                 float* po, float* pml, hipStream_t st) {
+                 float* po, float* pml, const PagedKV<PAGED>& pg, hipStream_t st) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
   // bf16: two query tiles per wave fit 168 registers, three waves per SIMD
   constexpr int WPE = sizeof(T) == 2 ? (QPW <= 2 ? 3 : 2) : 1;
@@ -588,26 +619,26 @@ void launch_attn(const Dims& s, const SparsePlan& pl, const void* q, const void*
   constexpr int STAGE = 2 * Mma<T>::K * D * (int)sizeof(T);
   constexpr int RING = 3 * STAGE <= 24576 ? 3 : 2;
   if (s.B == 16 * NW * QPW)
-    hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE, RING, true>), dim3(pl.grid), dim3(NW * kWave), 0, st,
-                       reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act),
+    hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE, RING, true, PAGED>), dim3(pl.grid), dim3(NW * kWave),
+                       0, st, reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act),
                        reinterpret_cast<const T*>(v_act), idx, items, meta, s.H, s.B, s.Bk, s.L, s.nKB, s.nQB,
-                       scale_log2, o_sp, po, pml);
+                       scale_log2, o_sp, po, pml, pg);
   else
-  hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE, RING, false>), dim3(pl.grid), dim3(NW * kWave), 0, st,
-                     reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act),
+  hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE, RING, false, PAGED>), dim3(pl.grid), dim3(NW * kWave),
+                     0, st, reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act),
                      reinterpret_cast<const T*>(v_act), idx, items, meta, s.H, s.B, s.Bk, s.L, s.nKB, s.nQB,
-                     scale_log2, o_sp, po, pml);
+                     scale_log2, o_sp, po, pml, pg);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool PAGED>
 void dispatch_attn(const Dims& s, const SparsePlan& pl, const void* q, const void* k_act, const void* v_act,
                    const int32_t* idx, const int4* items, const int* meta, float* o_sp,
-                   float* po, float* pml, hipStream_t st) {
+                   float* po, float* pml, const PagedKV<PAGED>& pg, hipStream_t st) {
   const int QT = s.B / 16;
   const int nw = (QT + 1) / 2;  // at most two 16-row query tiles per wave
   const int qpw = (QT + nw - 1) / nw;
 #define HSA_ATTN_CASE(NW_, QPW_) \
-  if (nw == NW_ && qpw == QPW_) return launch_attn<T, D, NW_, QPW_>(s, pl, q, k_act, v_act, idx, items, meta, o_sp, po, pml, st);
+  if (nw == NW_ && qpw == QPW_) return launch_attn<T, D, NW_, QPW_, PAGED>(s, pl, q, k_act, v_act, idx, items, meta, o_sp, po, pml, pg, st);
   HSA_ATTN_CASE(1, 1)
   HSA_ATTN_CASE(1, 2)
   HSA_ATTN_CASE(2, 2)
@@ -621,14 +652,13 @@ void dispatch_attn(const Dims& s, const SparsePlan& pl, const void* q, const voi
 }  // namespace
 }  // namespace hsa
 
-extern "C" hsa_rc hsa_sparse_attn_timed(const hsa_geom* geom, const void* q, const void* k_act, const void* v_act,
-                                        const int32_t* blk_count, const int32_t* blk_idx, float* o_sp, void* ws,
-                                        size_t ws_bytes, hsa_stream stream, hsa_event ev_begin, hsa_event ev_end) {
-  using namespace hsa;
-  Dims s;
-  hsa_rc rc = derive(geom, &s);
-  if (rc != HSA_OK) return rc;
-  if (!q || !k_act || !v_act || !blk_count || !blk_idx || !o_sp) return HSA_ERR_NULL_ARG;
+namespace hsa {
+namespace {
+
+template <bool PAGED>
+hsa_rc sparse_entry(const Dims& s, const void* q, const void* k_act, const void* v_act, const int32_t* blk_count,
+                    const int32_t* blk_idx, float* o_sp, void* ws, size_t ws_bytes, hsa_stream stream,
+                    hsa_event ev_begin, hsa_event ev_end, const PagedKV<PAGED>& pg) {
   const WsLayout w = ws_layout(s, 1);
   if (!ws || ws_bytes < w.sp_end) return HSA_ERR_WORKSPACE;
   const SparsePlan pl = sparse_plan(s);
@@ -645,11 +675,11 @@ extern "C" hsa_rc hsa_sparse_attn_timed(const hsa_geom* geom, const void* q, con
                      pl.granules_per_block, gps, pl.seg_granules, pl.max_segs, items, rowinfo, meta);
   if (ev_begin && hipEventRecord(reinterpret_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return HSA_ERR_HIP;
   if (s.bf16) {
-    if (s.d == 128) dispatch_attn<bf16_t, 128>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
-    else dispatch_attn<bf16_t, 64>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
+    if (s.d == 128) dispatch_attn<bf16_t, 128, PAGED>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, pg, st);
+    else dispatch_attn<bf16_t, 64, PAGED>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, pg, st);
   } else {
-    if (s.d == 128) dispatch_attn<float, 128>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
-    else dispatch_attn<float, 64>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, st);
+    if (s.d == 128) dispatch_attn<float, 128, PAGED>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, pg, st);
+    else dispatch_attn<float, 64, PAGED>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, pg, st);
   }
   if (ev_end && hipEventRecord(reinterpret_cast<hipEvent_t>(ev_end), st) != hipSuccess) return HSA_ERR_HIP;
   const size_t comb_lds = (size_t)pl.max_segs * s.B * sizeof(float2);
@@ -661,6 +691,46 @@ extern "C" hsa_rc hsa_sparse_attn_timed(const hsa_geom* geom, const void* q, con
   hipLaunchKernelGGL(comb, dim3(s.rows * kCombParts), dim3(kCombThreads), comb_lds, st, rowinfo, po, pml, s.H, s.B,
                      s.nQB, o_sp);
   return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace hsa
+
+extern "C" hsa_rc hsa_sparse_attn_timed(const hsa_geom* geom, const void* q, const void* k_act, const void* v_act,
+                                        const int32_t* blk_count, const int32_t* blk_idx, float* o_sp, void* ws,
+                                        size_t ws_bytes, hsa_stream stream, hsa_event ev_begin, hsa_event ev_end) {
+  using namespace hsa;
+  Dims s;
+  hsa_rc rc = derive(geom, &s);
+  if (rc != HSA_OK) return rc;
+  if (!q || !k_act || !v_act || !blk_count || !blk_idx || !o_sp) return HSA_ERR_NULL_ARG;
+  return sparse_entry<false>(s, q, k_act, v_act, blk_count, blk_idx, o_sp, ws, ws_bytes, stream, ev_begin, ev_end,
+                             PagedKV<false>{});
+}
+
+extern "C" hsa_rc hsa_sparse_attn_paged(const hsa_geom* geom, const void* q, const void* const* page_k,
+                                        const void* const* page_v, int32_t n_pages, const int32_t* sel_pages,
+                                        const int32_t* blk_count, const int32_t* blk_idx, float* o_sp, void* ws,
+                                        size_t ws_bytes, hsa_stream stream, hsa_event ev_begin, hsa_event ev_end) {
+  using namespace hsa;
+  Dims s;
+  hsa_rc rc = derive(geom, &s);
+  if (rc != HSA_OK) return rc;
+  if (s.split) return HSA_ERR_BAD_PARAM;
+  if (!q || !page_k || !page_v || !sel_pages || !blk_count || !blk_idx || !o_sp) return HSA_ERR_NULL_ARG;
+  if (n_pages < 1 || n_pages > HSA_MAX_PAGES || s.Kp > n_pages) return HSA_ERR_BAD_PARAM;
+  PagedKV<true> pg;
+  for (int j = 0; j < kMaxPages; ++j) pg.pk.p[j] = pg.pv.p[j] = nullptr;
+  for (int j = 0; j < n_pages; ++j) {
+    if (!page_k[j] || !page_v[j]) return HSA_ERR_NULL_ARG;
+    pg.pk.p[j] = page_k[j];
+    pg.pv.p[j] = page_v[j];
+  }
+  pg.sel = sel_pages;
+  pg.n_pages = n_pages;
+  pg.Lp = s.Lp;
+  return sparse_entry<true>(s, q, nullptr, nullptr, blk_count, blk_idx, o_sp, ws, ws_bytes, stream, ev_begin, ev_end,
+                            pg);
 }
 
 extern "C" hsa_rc hsa_sparse_attn(const hsa_geom* geom, const void* q, const void* k_act, const void* v_act,

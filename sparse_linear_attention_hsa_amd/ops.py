@@ -134,6 +134,34 @@ def hsa_linear_branch(geom, q, k_act, v_act, e_k, e_v, k_proj, v_proj, o_lin, fl
         flags, _p(ws), 0 if ws is None else ws.numel() * ws.element_size(), _s(stream)))
 
 
+def hsa_page_prepare(geom, k_page, v_page, k_out, v_out, blk_mean=None, stream=None):
+    check("hsa_page_prepare", lib().hsa_page_prepare(
+        ctypes.byref(geom), _p(k_page), _p(v_page), _p(k_out), _p(v_out), _p(blk_mean), _s(stream)))
+
+
+def hsa_gather_block_means(geom, page_blk_mean, sel_pages, kblk_mean, stream=None):
+    check("hsa_gather_block_means", lib().hsa_gather_block_means(
+        ctypes.byref(geom), _table(page_blk_mean), len(page_blk_mean), _p(sel_pages), _p(kblk_mean), _s(stream)))
+
+
+def hsa_linear_branch_paged(geom, q, pages_k, pages_v, sel_pages, e_k, e_v, k_proj, v_proj, o_lin, flags, ws,
+                            stream=None):
+    check("hsa_linear_branch_paged", lib().hsa_linear_branch_paged(
+        ctypes.byref(geom), _p(q), _table(pages_k), _table(pages_v), len(pages_k), _p(sel_pages), _p(e_k), _p(e_v),
+        _p(k_proj), _p(v_proj), _p(o_lin), flags, _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+        _s(stream)))
+
+
+def hsa_sparse_attn_paged(geom, q, pages_k, pages_v, sel_pages, blk_count, blk_idx, o_sp, ws, events=None,
+                          stream=None):
+    """events: optional (begin, end) torch.cuda.Event pair (enable_timing=True)
+    recorded around the attention kernel alone."""
+    handles = _event_handles(events, stream) if events is not None else (None, None)
+    check("hsa_sparse_attn_paged", lib().hsa_sparse_attn_paged(
+        ctypes.byref(geom), _p(q), _table(pages_k), _table(pages_v), len(pages_k), _p(sel_pages), _p(blk_count),
+        _p(blk_idx), _p(o_sp), _p(ws), ws.numel() * ws.element_size(), _s(stream), handles[0], handles[1]))
+
+
 def hsa_block_select(geom, q, k_act, kblk_mean, tau, blk_count, blk_idx, blk_mass, ws, stream=None):
     check("hsa_block_select", lib().hsa_block_select(
         ctypes.byref(geom), _p(q), _p(k_act), _p(kblk_mean), _p(tau), _p(blk_count), _p(blk_idx), _p(blk_mass),

@@ -122,6 +122,52 @@ class HsaStep:
     def fuse(self, x, w_g, stream=None):
         ops.hsa_fuse(self.geom, x, w_g, None, self.o_lin, self.o_sp, self.out, stream)
 
+    # pages read in place ------------------------------------------------
+    def prepare_pages(self, pages_k, pages_v, stream=None):
+        """Lay out every page once, as when it is written: K [H][Lp][d], V
+        [H][Lp/16][d][16] and the block means [H][Lp/B][d] (the layouts the
+        kernels read, over one page).  Returns (k_pages, v_pages, blk_means)."""
+        s, dev = self.s, self.k_act.device
+        ks, vs, ms = [], [], []
+        for pk, pv in zip(pages_k, pages_v):
+            ko = torch.empty(s.H, s.Lp, s.d, dtype=s.dtype, device=dev)
+            vo = torch.empty(s.H, s.Lp // 16, s.d, 16, dtype=s.dtype, device=dev)
+            mo = torch.empty(s.H, s.Lp // s.B, s.d, dtype=torch.float32, device=dev)
+            ops.hsa_page_prepare(self.geom, pk, pv, ko, vo, mo, stream)
+            ks.append(ko)
+            vs.append(vo)
+            ms.append(mo)
+        return ks, vs, ms
+
+    def run_paged(self, q, prepared, e_k, e_v, w_g, x, tau, stream=None, concurrent: bool = True,
+                  kernel_events=None):
+        """The step over laid-out pages, with no active-buffer copy: scoring
+        from the page index (index_pages ran before), the selected pages' block
+        means, the linear branch (side stream) and the sparse branch reading
+        the pages in place, then the fusion."""
+        kp, vp, bm = prepared
+        main = torch.cuda.current_stream() if stream is None else stream
+        self.score(q, [None] * self.n_pages, main, use_cache=True)
+        ops.hsa_gather_block_means(self.geom, bm, self.sel_pages, self.kblk_mean, main)
+        side = self.side if concurrent else main
+        if concurrent:
+            scored = torch.cuda.Event()
+            scored.record(main)
+            self.side.wait_event(scored)
+        ops.hsa_linear_branch_paged(self.geom, q, kp, vp, self.sel_pages, e_k, e_v, self.k_proj, self.v_proj,
+                                    self.o_lin, 0, self.ws_lin if concurrent else self.ws, side)
+        if concurrent:
+            linear_done = torch.cuda.Event()
+            linear_done.record(side)
+        ops.hsa_block_select(self.geom, q, None, self.kblk_mean, tau, self.blk_count, self.blk_idx, self.blk_mass,
+                             self.ws, main)
+        ops.hsa_sparse_attn_paged(self.geom, q, kp, vp, self.sel_pages, self.blk_count, self.blk_idx, self.o_sp,
+                                  self.ws, kernel_events, main)
+        if concurrent:
+            main.wait_event(linear_done)
+        self.fuse(x, w_g, main)
+        return self.out
+
     # the whole step -----------------------------------------------------
     def run(self, q, pages_k, pages_v, e_k, e_v, w_g, x, tau, stream=None, concurrent: bool = True,
             indexed: bool = False, chunks=None, k_cur=None, v_cur=None):

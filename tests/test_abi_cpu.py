@@ -95,6 +95,40 @@ def test_intra_chunk_geometry(lib):
     assert lib.hsa_gather_pages(ctypes.byref(intra), pages, pages, 16, fake, fake, fake, None, None) == 4
 
 
+def test_paged_entry_points_reject_bad_arguments(lib):
+    g, intra = c1_geom(), c1_geom(intra_split=2)
+    fake = ctypes.c_void_p(0x1000)
+    pages = (ctypes.c_void_p * 16)(*([0x1000] * 16))
+    null_pages = (ctypes.c_void_p * 16)()
+    big = 1 << 40
+    # page layout: NULL buffers; no intra-chunk keys
+    assert lib.hsa_page_prepare(ctypes.byref(g), None, fake, fake, fake, None, None) == 1
+    assert lib.hsa_page_prepare(ctypes.byref(g), fake, fake, fake, None, None, None) == 1
+    assert lib.hsa_page_prepare(ctypes.byref(intra), fake, fake, fake, fake, None, None) == 4
+    # block means of the selected pages: NULL entries, page counts
+    gm = lib.hsa_gather_block_means
+    assert gm(ctypes.byref(g), null_pages, 16, fake, fake, None) == 1
+    assert gm(ctypes.byref(g), pages, 16, None, fake, None) == 1
+    assert gm(ctypes.byref(g), pages, 3, fake, fake, None) == 4
+    assert gm(ctypes.byref(g), pages, 200, fake, fake, None) == 4
+    assert gm(ctypes.byref(intra), pages, 16, fake, fake, None) == 4
+    # linear branch over pages: NULL pages (unless the projection is reused), counts, flags, workspace
+    lp = lib.hsa_linear_branch_paged
+    assert lp(ctypes.byref(g), fake, null_pages, pages, 16, fake, fake, fake, fake, fake, fake, 0, fake, big, None) == 1
+    assert lp(ctypes.byref(g), fake, pages, pages, 16, None, fake, fake, fake, fake, fake, 0, fake, big, None) == 1
+    assert lp(ctypes.byref(g), fake, pages, pages, 3, fake, fake, fake, fake, fake, fake, 0, fake, big, None) == 4
+    assert lp(ctypes.byref(g), fake, pages, pages, 16, fake, fake, fake, fake, fake, fake, 3, fake, big, None) == 4
+    assert lp(ctypes.byref(g), fake, pages, pages, 16, fake, fake, fake, fake, fake, fake, 0, fake, 16, None) == 5
+    assert lp(ctypes.byref(intra), fake, pages, pages, 16, fake, fake, fake, fake, fake, fake, 0, fake, big, None) == 4
+    # sparse branch over pages
+    sp = lib.hsa_sparse_attn_paged
+    assert sp(ctypes.byref(g), fake, pages, null_pages, 16, fake, fake, fake, fake, fake, big, None, None, None) == 1
+    assert sp(ctypes.byref(g), fake, pages, pages, 16, None, fake, fake, fake, fake, big, None, None, None) == 1
+    assert sp(ctypes.byref(g), fake, pages, pages, 2, fake, fake, fake, fake, fake, big, None, None, None) == 4
+    assert sp(ctypes.byref(g), fake, pages, pages, 16, fake, fake, fake, fake, fake, 16, None, None, None) == 5
+    assert sp(ctypes.byref(intra), fake, pages, pages, 16, fake, fake, fake, fake, fake, big, None, None, None) == 4
+
+
 def test_workspace_sizes(lib):
     g = c1_geom()
     a = lib.hsa_workspace_bytes(ctypes.byref(g), 16)
