@@ -17,6 +17,9 @@ Variants (each reports its own line; the default is the headline workload):
                            only their pages (--pages-per-chunk, default 8)
   --tiers N                N generated chunks over a history in page tiers,
                            fetched on demand vs predicted and prefetched
+  --paged                  pages laid out once when written; the step scores from
+                           the page index and reads the selected pages in place
+                           (no active-buffer copy)
   --intra S                the chunk's own tokens join the retrieved history in
                            key blocks of B/S tokens (intra-chunk keys)
   --graph                  the step replayed as one HIP graph
@@ -42,7 +45,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 STAGES = ("score", "gather", "linear", "select", "sparse", "fuse")
 
 
-def stage_model(cfg, n_sel_total: int, indexed: bool = False, scored_pages=None):
+def stage_model(cfg, n_sel_total: int, indexed: bool = False, scored_pages=None, paged: bool = False):
     """Algorithmic work of one call of each stage (bytes moved or flops).
     With the page index, scoring reads the pages' fp32 mean keys instead of
     their keys; with prompt-level retrieval it reads only scored_pages."""
@@ -54,7 +57,8 @@ def stage_model(cfg, n_sel_total: int, indexed: bool = False, scored_pages=None)
     Bk, nC = cfg.key_block, cfg.n_candidates  # key-block size; selection candidates per row
     return {
         "score": dict(bound="hbm", bytes=(P * D * 4 if indexed else P * Lp * D * es) + Lq * D * es),
-        "gather": dict(bound="hbm", bytes=2 * (2 * L * D * es)),
+        # paged: the gather stage only moves the selected pages' block means
+        "gather": dict(bound="hbm", bytes=2 * H * (L // Bk) * d * 4 if paged else 2 * (2 * L * D * es)),
         "linear": dict(bound="mfma", flops=2 * 2 * H * r * L * d + 2 * 2 * H * Lq * r * d,
                        bytes=2 * L * D * es + 2 * r * L * es + Lq * D * es + Lq * D * 4),
         "select": dict(bound="hbm", bytes=Lq * D * es + H * (L // Bk) * d * 4,
@@ -362,6 +366,9 @@ def main():
     ap.add_argument("--page-index", action="store_true",
                     help="score from a page index of mean keys built once before the timed steps "
                          "(as when pages are written) instead of reading every page's keys")
+    ap.add_argument("--paged", action="store_true",
+                    help="lay the pages out once (as when written) and run the step reading them in place: scoring "
+                         "from the page index, no active-buffer copy")
     ap.add_argument("--intra", type=int, default=0,
                     help="intra-chunk keys: the chunk's own tokens follow the retrieved pages in key blocks of "
                          "B/S tokens (S = 2: 48-token blocks beside the 96-token history tiles)")
@@ -385,10 +392,18 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
         return
     from synth import CONFIGS, Workload
+    from sparse_linear_attention_hsa_amd import ops
     from sparse_linear_attention_hsa_amd.ops import make_geom
     from sparse_linear_attention_hsa_amd.step import HsaStep
 
     cfg = CONFIGS[args.config]
+    if args.paged and (args.intra or args.chunks or args.tiers or cfg.layers > 1 or cfg.steps > 1):
+        print("bench.py: --paged runs the single-step workloads without --intra / --chunks / --tiers",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.paged:
+        from dataclasses import replace
+        cfg = replace(cfg, name=f"{cfg.name}_paged")
     if args.intra:
         from dataclasses import replace
         if args.tiers or args.chunks or cfg.layers > 1 or cfg.steps > 1:
@@ -423,9 +438,14 @@ def main():
     st = HsaStep(geom, cfg.n_pages)
     stream = torch.cuda.current_stream()
 
-    indexed = bool(args.page_index)
+    paged = bool(args.paged)
+    indexed = bool(args.page_index) or paged
     if indexed:
         st.index_pages(q, pk)  # the page index, built once (outside the timed steps)
+        torch.cuda.synchronize()
+    prepared = None
+    if paged:  # every page laid out once, as when it is written (outside the timed steps)
+        prepared = st.prepare_pages(pk, pv)
         torch.cuda.synchronize()
     chunks = None
     if args.chunks:
@@ -444,13 +464,27 @@ def main():
         # the step's own schedule: the linear branch on a side stream beside
         # block selection and the sparse branch, joined before the fusion
         # (on the current stream, which is the capture stream under --graph)
-        st.run(q, pk, pv, e_k, e_v, w_g, x, tau, indexed=indexed, chunks=chunks, k_cur=k_cur, v_cur=v_cur)
+        if paged:
+            st.run_paged(q, prepared, e_k, e_v, w_g, x, tau)
+        else:
+            st.run(q, pk, pv, e_k, e_v, w_g, x, tau, indexed=indexed, chunks=chunks, k_cur=k_cur, v_cur=v_cur)
 
     def one_step_staged(ev, kev):
         # the same six calls in order on one stream, with events between them
         calls = (score_stage, lambda: st.gather(pk, pv, k_cur=k_cur, v_cur=v_cur),
                  lambda: st.linear(q, e_k, e_v),
                  lambda: st.select(q, tau), lambda: st.sparse(q, kernel_events=kev), lambda: st.fuse(x, w_g))
+        if paged:  # the same stages reading the laid-out pages
+            kp_, vp_, bm_ = prepared
+            calls = (score_stage,
+                     lambda: ops.hsa_gather_block_means(geom, bm_, st.sel_pages, st.kblk_mean),
+                     lambda: ops.hsa_linear_branch_paged(geom, q, kp_, vp_, st.sel_pages, e_k, e_v, st.k_proj,
+                                                         st.v_proj, st.o_lin, 0, st.ws),
+                     lambda: ops.hsa_block_select(geom, q, None, st.kblk_mean, tau, st.blk_count, st.blk_idx,
+                                                  st.blk_mass, st.ws),
+                     lambda: ops.hsa_sparse_attn_paged(geom, q, kp_, vp_, st.sel_pages, st.blk_count, st.blk_idx,
+                                                       st.o_sp, st.ws, kev),
+                     lambda: st.fuse(x, w_g))
         for i, fn in enumerate(calls):
             ev[i][0].record(stream)
             fn()
@@ -507,7 +541,7 @@ def main():
     if chunks is not None:  # only the retrieved chunks' pages are read
         pc = chunks[2].cpu().numpy()
         scored_pages = int(np.isin(pc, st.sel_chunks.cpu().numpy()).sum())
-    model = stage_model(cfg, n_sel_total, indexed, scored_pages)
+    model = stage_model(cfg, n_sel_total, indexed, scored_pages, paged)
     sparse_tf = model["sparse"]["flops"] / (stage_ms["sparse"] * 1e-3) / 1e12
     lin_tf = model["linear"]["flops"] / (stage_ms["linear"] * 1e-3) / 1e12
     peak_tf = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -529,7 +563,7 @@ def main():
                    "retrieved_tokens": cfg.history_tokens, "query_tokens": cfg.query_tokens,
                    "history_pages": cfg.n_pages, "block": cfg.block, "rank": cfg.rank,
                    "intra_split": cfg.intra_split, "key_block": cfg.key_block, "active_tokens": cfg.active_tokens,
-                   "graph": bool(args.graph), "page_index": indexed, "chunks": args.chunks,
+                   "graph": bool(args.graph), "page_index": indexed, "paged": paged, "chunks": args.chunks,
                    "pages_per_chunk": args.pages_per_chunk if args.chunks else None},
         "ms_per_step_stats": {"median": round(float(np.median(per_step)), 4),
                               "min": round(float(per_step.min()), 4),
