@@ -66,3 +66,21 @@ def test_paged_full_size_equals_gathered():
         assert torch.equal(getattr(st, k), want[k]), k
     del r, st, prepared
     torch.cuda.empty_cache()
+
+
+def test_paged_graph_replays_match_eager():
+    """The paged step captured into a HIP graph: every replay, with eager
+    paged steps between replays, equals the eager step bit for bit."""
+    r, st, prepared, want = _both(M1)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.run_paged(r.q, prepared, r.e_k, r.e_v, r.w_g, r.x, r.tau)
+    for rep in range(3):
+        for k in NAMES:
+            getattr(st, k).zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in NAMES:
+            assert torch.equal(getattr(st, k), want[k]), f"replay {rep}: {k}"
+        st.run_paged(r.q, prepared, r.e_k, r.e_v, r.w_g, r.x, r.tau)  # eager work between replays
+        torch.cuda.synchronize()
