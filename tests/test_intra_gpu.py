@@ -116,3 +116,25 @@ def test_tau_one_is_dense_over_history_and_chunk():
     assert np.all(st.blk_count.cpu().numpy() == cfg.n_key_blocks)
     ref = r.oracle(sel_pages=st.sel_pages.cpu().numpy())
     assert_close("o_sp", host(st.o_sp), ref["o_sp"], cfg)
+
+
+def test_intra_graph_replays_match_eager():
+    """The step with intra-chunk keys captured into a HIP graph: every replay,
+    with eager steps between replays, equals the eager step bit for bit."""
+    cfg = INTRA[0]
+    r = Run(cfg)
+    st = r.run()
+    names = ("out", "o_sp", "o_lin", "blk_count", "blk_idx", "k_act", "kblk_mean")
+    ref = {k: getattr(st, k).clone() for k in names}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.run(r.q, r.pk, r.pv, r.e_k, r.e_v, r.w_g, r.x, r.tau, k_cur=r.k_cur, v_cur=r.v_cur)
+    for rep in range(3):
+        for k in names:
+            getattr(st, k).zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in names:
+            assert torch.equal(getattr(st, k), ref[k]), f"replay {rep}: {k}"
+        r.run()
+        torch.cuda.synchronize()
