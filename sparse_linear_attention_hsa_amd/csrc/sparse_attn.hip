@@ -206,17 +206,29 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
   const int b0 = g0 / gpb;
   const int nblk = gcount > 0 ? (g0 + gcount - 1) / gpb - b0 + 1 : 0;
   const int blk_lane = lane < nblk ? blk_idx[(size_t)row * nKB + b0 + lane] : -1;
-  // paged: each lane's block as (block within its page, that page's id); an
-  // invalid id takes the first selected page
-  int lblk_lane = 0, page_lane = 0;
+  // paged: each lane's block as its block within its page (-1 for an invalid
+  // id) and that page's K and V base pointers, held in registers so that a
+  // granule's page costs register reads, not a memory wait; an invalid id
+  // takes the first selected page
+  int lblk_lane = -1;
+  uint32_t kp_lo = 0, kp_hi = 0, vp_lo = 0, vp_hi = 0;
   if constexpr (PAGED) {
     const int bpp = pg.Lp / Bk;
     const bool valid = blk_lane >= 0 && blk_lane < nKB;
     const int ps = valid ? blk_lane / bpp : 0;
-    lblk_lane = valid ? blk_lane - ps * bpp : 0;
-    const int page = pg.sel[ps];
-    page_lane = page < 0 ? 0 : (page >= pg.n_pages ? pg.n_pages - 1 : page);
+    lblk_lane = valid ? blk_lane - ps * bpp : -1;
+    int page = pg.sel[ps];
+    page = page < 0 ? 0 : (page >= pg.n_pages ? pg.n_pages - 1 : page);
+    const uint64_t kp = reinterpret_cast<uint64_t>(pg.pk.p[page]);
+    const uint64_t vp = reinterpret_cast<uint64_t>(pg.pv.p[page]);
+    kp_lo = (uint32_t)kp;
+    kp_hi = (uint32_t)(kp >> 32);
+    vp_lo = (uint32_t)vp;
+    vp_hi = (uint32_t)(vp >> 32);
   }
+  auto ptr_of = [](uint32_t lo, uint32_t hi) {
+    return reinterpret_cast<const T*>((uint64_t)lo | ((uint64_t)hi << 32));
+  };
 
   // Q^T operand: lane (g, c) holds Q[row c of tile][chunk 4s+g] for step s.
   uint4 qreg[QPW][DSTEPS];
@@ -291,18 +303,27 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
   // Stage the next GPS granules into (lk, lv); returns their validity bits.
   auto issue = [&](unsigned char* lk, unsigned char* lv) -> unsigned {
     int kofs[GPS];
-    int pgid[GPS];  // paged: the granule's page
+    uint32_t kb_lo[GPS], kb_hi[GPS], vb_lo[GPS], vb_hi[GPS];  // paged: the granule's page
     unsigned mask = 0;
 #pragma unroll
     for (int j = 0; j < GPS; ++j) {
       int key = -1;
       const int src = issued < gcount ? cur_blk : 0;  // lane of the granule's block
       if (issued < gcount) {
-        const int blk = __builtin_amdgcn_readlane(blk_lane, cur_blk);
-        const int kb = PAGED ? __builtin_amdgcn_readlane(lblk_lane, cur_blk) : blk;
-        if (blk >= 0 && blk < nKB) key = kb * Bk + cur_gran * 16;
+        if constexpr (PAGED) {
+          const int lb = __builtin_amdgcn_readlane(lblk_lane, cur_blk);
+          if (lb >= 0) key = lb * Bk + cur_gran * 16;
+        } else {
+          const int blk = __builtin_amdgcn_readlane(blk_lane, cur_blk);
+          if (blk >= 0 && blk < nKB) key = blk * Bk + cur_gran * 16;
+        }
       }
-      if constexpr (PAGED) pgid[j] = __builtin_amdgcn_readlane(page_lane, src);
+      if constexpr (PAGED) {
+        kb_lo[j] = __builtin_amdgcn_readlane(kp_lo, src);
+        kb_hi[j] = __builtin_amdgcn_readlane(kp_hi, src);
+        vb_lo[j] = __builtin_amdgcn_readlane(vp_lo, src);
+        vb_hi[j] = __builtin_amdgcn_readlane(vp_hi, src);
+      }
       // a masked granule (past the segment or an invalid block id) loads the
       // head's first granule (paged: of its page or the first selected one):
       // its scores are set to -inf, so it adds nothing
@@ -320,9 +341,10 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
       if (KINST % NW != 0 && i >= KINST) break;
       const int kg = kofs[kgran[ii]];
       if constexpr (PAGED) {
-        const int pid = __builtin_amdgcn_readfirstlane(pgid[kgran[ii]]);
-        buffer_load_lds16(reinterpret_cast<const T*>(pg.pk.p[pid]) + page_head_elems, page_head_bytes,
-                          lk + i * 1024, koff[ii] * (int)sizeof(T), kg * D * (int)sizeof(T));
+        const uint32_t lo = __builtin_amdgcn_readfirstlane(kb_lo[kgran[ii]]);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane(kb_hi[kgran[ii]]);
+        buffer_load_lds16(ptr_of(lo, hi) + page_head_elems, page_head_bytes, lk + i * 1024,
+                          koff[ii] * (int)sizeof(T), kg * D * (int)sizeof(T));
       } else {
         buffer_load_lds16(kh, head_bytes, lk + i * 1024, koff[ii] * (int)sizeof(T), kg * D * (int)sizeof(T));
       }
@@ -333,9 +355,10 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
       if (VINST % NW != 0 && i >= VINST) break;
       const int kg = kofs[vgran[ii]];
       if constexpr (PAGED) {
-        const int pid = __builtin_amdgcn_readfirstlane(pgid[vgran[ii]]);
-        buffer_load_lds16(reinterpret_cast<const T*>(pg.pv.p[pid]) + page_head_elems, page_head_bytes,
-                          lv + i * 1024, voff[ii] * (int)sizeof(T), kg * D * (int)sizeof(T));
+        const uint32_t lo = __builtin_amdgcn_readfirstlane(vb_lo[vgran[ii]]);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane(vb_hi[vgran[ii]]);
+        buffer_load_lds16(ptr_of(lo, hi) + page_head_elems, page_head_bytes, lv + i * 1024,
+                          voff[ii] * (int)sizeof(T), kg * D * (int)sizeof(T));
       } else {
         buffer_load_lds16(vh, head_bytes, lv + i * 1024, voff[ii] * (int)sizeof(T), kg * D * (int)sizeof(T));
       }
