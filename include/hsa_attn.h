@@ -371,7 +371,8 @@ hsa_rc hsa_linear_branch_paged(const hsa_geom* geom, const void* q, const void* 
 
 /* hsa_sparse_attn_timed over laid-out pages (page_k, page_v, n_pages,
  * sel_pages as hsa_linear_branch_paged); the events may be NULL.  Errors as
- * hsa_sparse_attn, plus HSA_ERR_BAD_PARAM for n_pages. */
+ * hsa_sparse_attn, plus HSA_ERR_BAD_PARAM for n_pages (a valid geometry keeps
+ * one head of one page within the 32-bit offsets the kernel uses). */
 hsa_rc hsa_sparse_attn_paged(const hsa_geom* geom, const void* q, const void* const* page_k,
                              const void* const* page_v, int32_t n_pages, const int32_t* sel_pages,
                              const int32_t* blk_count, const int32_t* blk_idx, float* o_sp, void* ws,

@@ -58,8 +58,9 @@ def test_paged_step_in_order_and_repeated():
         assert torch.equal(getattr(st, k), want[k]), k
 
 
-def test_paged_full_size_equals_gathered():
-    cfg = CONFIGS["c1_full"]
+@pytest.mark.parametrize("name", ["c1_full", "c3_head_imbalance"])
+def test_paged_full_size_equals_gathered(name):
+    cfg = CONFIGS[name]
     print(f"\n[paged full size] {cfg.name}", flush=True)
     r, st, prepared, want = _both(cfg)
     for k in NAMES:
