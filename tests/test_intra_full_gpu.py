@@ -1,6 +1,7 @@
 """Intra-chunk keys at full size, in the launch configuration the benchmark
-times (bench.py --intra 2): the 12-head, d = 128 workload with 49,920
-retrieved keys and the chunk's own 6,240 tokens in 48-token key blocks
+times (bench.py --intra 2): the 12-head, d = 128 workloads (plain and with
+imbalanced heads) with 49,920 retrieved keys and the chunk's own 6,240 tokens
+in 48-token key blocks
 beside the 96-token history tiles (WorldAttention paper, section 3.3,
 inter- and intra-chunk sparse granularity).  Checked against the float64
 oracle: the active K/V bit-exact and the key-block means, the projections
@@ -24,8 +25,9 @@ pytestmark = pytest.mark.gpu
 PROJ_TOL = (2e-4, 1e-5)
 
 
-def test_full_size_intra_step():
-    cfg = replace(CONFIGS["c1_full"], name="c1_full_intra2", intra_split=2)
+@pytest.mark.parametrize("name", ["c1_full", "c3_head_imbalance"])
+def test_full_size_intra_step(name):
+    cfg = replace(CONFIGS[name], name=f"{name}_intra2", intra_split=2)
     print(f"\n[full-size intra parity] Lh={cfg.history_tokens} Lq={cfg.query_tokens} B={cfg.block} "
           f"Bk={cfg.key_block} nKB={cfg.n_key_blocks} nC={cfg.n_candidates}", flush=True)
     r = Run(cfg)
