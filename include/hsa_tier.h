@@ -60,8 +60,10 @@ hsa_rc hsa_tier_seed(hsa_tier* t, const int32_t* pages, int32_t n, int32_t tier,
  * this order.  l1_slot[i] receives page i's device slot; moves[0..*n_moves)
  * receives the copies to run, in order, before those slots are read: for a
  * miss, the least recently used L1 page outside the request is evicted
- * (copied to L2 first if L2 lacks it, taking L2's least recently used slot)
- * and the page is loaded from L2 if there, else from L3.  At most 2n moves;
+ * (copied to L2 first if L2 lacks it, taking L2's least recently used slot
+ * that holds no page of the request; with no such slot it is not copied and
+ * L3 keeps it) and the page is loaded from L2 if there, else from L3.  At
+ * most 2n moves;
  * max_moves must be >= 2n.  On error nothing changes: HSA_ERR_NULL_ARG,
  * HSA_ERR_BAD_PARAM (ids, n, max_moves). */
 hsa_rc hsa_tier_request(hsa_tier* t, const int32_t* pages, int32_t n, int32_t* l1_slot, hsa_tier_move* moves,

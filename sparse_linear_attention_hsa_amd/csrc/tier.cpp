@@ -19,15 +19,15 @@ struct hsa_tier {
 
 namespace {
 
-// A free slot, else the least recently used one whose page is neither
-// pinned nor `keep`; -1 if there is none.
+// A free slot, else the least recently used one whose page is not pinned;
+// -1 if there is none.
 int32_t pick_slot(const std::vector<int32_t>& page_of_slot, const std::vector<int64_t>& used,
-                  const std::vector<char>* pinned, int32_t keep = -1) {
+                  const std::vector<char>* pinned) {
   int32_t best = -1;
   for (int32_t s = 0; s < (int32_t)page_of_slot.size(); ++s) {
     const int32_t p = page_of_slot[s];
     if (p < 0) return s;
-    if ((pinned && (*pinned)[p]) || p == keep) continue;
+    if (pinned && (*pinned)[p]) continue;
     if (best < 0 || used[s] < used[best]) best = s;
   }
   return best;
@@ -111,9 +111,10 @@ hsa_rc hsa_tier_request(hsa_tier* t, const int32_t* pages, int32_t n, int32_t* l
       const int32_t victim = t->l1_page[s];
       if (victim >= 0) {
         ++t->stats[4];
-        // the page sinks to L2, where the least recently used page other than
-        // the one about to be loaded from it leaves (L3 still holds it)
-        const int32_t s2 = t->l2_of[victim] < 0 ? pick_slot(t->l2_page, t->l2_used, nullptr, p) : -1;
+        // the page sinks to L2, where the least recently used page outside
+        // this request leaves (L3 still holds it); if every L2 slot holds a
+        // page of this request, the victim does not sink (L3 keeps it)
+        const int32_t s2 = t->l2_of[victim] < 0 ? pick_slot(t->l2_page, t->l2_used, &pinned) : -1;
         if (s2 >= 0) {
           const int32_t gone = t->l2_page[s2];
           if (gone >= 0) t->l2_of[gone] = -1;

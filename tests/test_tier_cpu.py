@@ -43,6 +43,30 @@ def test_hand_trace():
     assert t.stats() == dict(requested=7, l1_hits=1, from_l2=2, from_l3=4, l1_evictions=4, l1_to_l2=3)
 
 
+def test_sinking_page_never_displaces_a_page_of_the_request():
+    """Six pages, two device slots, two host slots; L1 holds {0, 1}, L2 holds
+    {3, 2} (slots 0, 1).  Worked by hand for the request [2, 3]:
+    - page 2 misses L1; the victim is page 0 (least recent, not requested).
+      Both L2 slots hold pages of this request, so page 0 does not sink (L3
+      keeps it); page 2 comes from L2 slot 1 into device slot 0.
+    - page 3 misses L1; the victim is page 1, which does not sink either; page 3
+      comes from L2 slot 0 into device slot 1.
+    Both pages come from L2 and nothing is fetched from L3."""
+    t = TierPolicy(6, 2, 2)
+    assert t.seed([0, 1], 1) == [0, 1]
+    assert t.seed([3, 2], 2) == [0, 1]
+    slots, moves = t.request([2, 3])
+    assert slots == [0, 1]
+    assert moves == [(L2_TO_L1, 2, 1, 0), (L2_TO_L1, 3, 0, 1)]
+    st = t.stats()
+    assert st["from_l2"] == 2 and st["from_l3"] == 0 and st["l1_to_l2"] == 0 and st["l1_evictions"] == 2
+    assert [t.locate(j) for j in range(6)] == [(-1, -1), (-1, -1), (0, 1), (1, 0), (-1, -1), (-1, -1)]
+    # a later request with room in L2 lets a victim sink again: page 4 evicts
+    # page 2 (least recent), whose L2 copy is still there, so no copy down
+    slots, moves = t.request([4])
+    assert slots == [0] and moves == [(L3_TO_L1, 4, -1, 0)]
+
+
 def test_without_l2_pages_come_back_from_l3():
     t = TierPolicy(4, 2, 0)
     t.request([0, 1])
