@@ -114,10 +114,17 @@ def page_scores(qbar: np.ndarray, kbars: np.ndarray) -> np.ndarray:
     return dots.mean(axis=1) / math.sqrt(d)
 
 
+def nan_as_neginf(vals) -> np.ndarray:
+    v = np.asarray(vals, dtype=np.float64)
+    return np.where(np.isnan(v), -np.inf, v)
+
+
 def top_k_lower_index(vals: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Order by (value descending, index ascending); return (order, top-k ascending)."""
-    idx = np.arange(len(vals))
-    order = np.lexsort((idx, -np.asarray(vals, dtype=np.float64)))
+    """Order by (value descending, index ascending); return (order, top-k ascending).
+    Reading: a NaN value ranks as -inf (below every number, equal values by index)."""
+    v = nan_as_neginf(vals)
+    idx = np.arange(len(v))
+    order = np.lexsort((idx, -v))
     return order, np.sort(order[:k])
 
 
@@ -205,7 +212,7 @@ def select_pages_in_chunks(alpha: np.ndarray, page_chunk: Sequence[int], sel_chu
             tie = True
     # tiers: within a chunk's share, other pages of the chosen chunks, the rest
     tier = np.where(in_share, 0, np.where(cand, 1, 2))
-    key_alpha = np.where(cand, alpha, -np.inf)
+    key_alpha = np.where(cand, nan_as_neginf(alpha), -np.inf)
     order = sorted(range(P), key=lambda j: (tier[j], -key_alpha[j], j))
     sel = np.sort(np.array(order[:k_p], dtype=np.int64))
     n_in = int(in_share.sum())
@@ -246,8 +253,10 @@ def gather_active(pages: Sequence[np.ndarray], sel: Sequence[int]) -> np.ndarray
 
 
 def project(e: np.ndarray, act: np.ndarray) -> np.ndarray:
-    """e [r][L], act [H][L][d] -> [H][r][d]: the sequence-axis projection per head."""
-    return np.einsum("rl,hld->hrd", e.astype(np.float64), act.astype(np.float64))
+    """e [r][L], act [H][L][d] -> [H][r][d]: the sequence-axis projection per head
+    (one matrix product E @ act_h per head)."""
+    e = np.asarray(e, dtype=np.float64)
+    return np.stack([e @ np.asarray(a, dtype=np.float64) for a in act])
 
 
 def softmax_rows(s: np.ndarray) -> np.ndarray:

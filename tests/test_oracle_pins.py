@@ -110,13 +110,39 @@ def test_prompt_retrieval_invariances():
     assert r["sel"].tolist() == [4] and abs(r["sims"][4] - 1.0) < 1e-12
 
 
+def test_ranking_readings_equal_values_nan_and_zero_embeddings():
+    """Readings where the pages say nothing: equal values go to the lower id,
+    a NaN ranks as -inf (so with -inf the lower id wins), a zero prompt
+    embedding has similarity 0 with every chunk.  Values worked by hand."""
+    nan, inf = float("nan"), float("inf")
+    assert orc.top_k_lower_index(np.array([0.2, 0.2, 0.2]), 2)[1].tolist() == [0, 1]
+    assert orc.top_k_lower_index(np.array([0.3, nan, 0.5, nan, 0.1]), 3)[1].tolist() == [0, 2, 4]
+    assert orc.top_k_lower_index(np.array([0.3, nan, 0.5, nan, 0.1]), 4)[1].tolist() == [0, 1, 2, 4]
+    assert orc.top_k_lower_index(np.array([nan, -inf, 0.2]), 2)[1].tolist() == [0, 2]
+    assert orc.top_k_lower_index(np.array([-inf, nan, 0.2]), 2)[1].tolist() == [0, 2]
+    sel, tie = orc.select_pages(np.array([0.1, 0.4, 0.4, 0.2]), 2)
+    assert sel.tolist() == [1, 2] and not tie
+    sel, tie = orc.select_pages(np.array([0.1, 0.4, 0.2, 0.2]), 2)
+    assert sel.tolist() == [1, 2] and tie
+    # uniform mass over 12 blocks: 7/12 < 0.6 <= 8/12, the eight lowest ids
+    sel, flag = orc.select_blocks(np.full(12, 1.0 / 12.0), 0.6)
+    assert sel.tolist() == list(range(8)) and flag
+    # a NaN embedding ranks last; a zero one has similarity 0; a zero prompt ties every chunk at 0
+    e_past = np.array([[nan, 1.0, 0.0], [0.0, 0.0, 0.0], [-1.0, 0.0, 0.0], [1.0, 1.0, 0.0]])
+    r = orc.prompt_retrieval(np.array([1.0, 0.0, 0.0]), e_past, 3)
+    assert np.isnan(r["sims"][0]) and r["sims"][1] == 0.0 and r["sims"][2] == -1.0
+    assert abs(r["sims"][3] - 1.0 / np.sqrt(2.0)) < 1e-15 and r["sel"].tolist() == [1, 2, 3]
+    r = orc.prompt_retrieval(np.zeros(3), e_past, 2)
+    assert r["sims"].tolist() == [0.0] * 4 and r["sel"].tolist() == [0, 1] and r["tie"]
+
+
 def test_chunk_pages_hand_examples(golden):
     g = golden("hw8_chunk_pages.json")
     for case in g["cases"]:
         sel, tie = orc.select_pages_in_chunks(np.array(case["alpha"]), case["page_chunk"], case["chunks"],
                                               case["k_p"])
         assert sel.tolist() == case["sel"], case
-        assert not tie
+        assert tie == case["tie"], case
 
 
 def test_chunk_pages_special_cases():
