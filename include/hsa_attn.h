@@ -123,7 +123,9 @@ typedef struct ihipEvent_t* hsa_event;    /* a hipEvent_t  */
  *              key is written here (a reusable page index); for NULL pages it
  *              is read.
  *  n_pages     1 <= P <= HSA_MAX_PAGES, K_p <= P.
- *  scores      [P] float32 out: alpha_j.
+ *  scores      [P] float32 out: alpha_j.  A score that comes out NaN (NaN or
+ *              Inf in q or a page) is reported and ranked as -inf, so the
+ *              order stays total and exactly K_p pages are retrieved.
  *  sel_pages   [K_p] int32 out: the retrieved page ids, ascending.
  *  ws          workspace of ws_bytes >= hsa_workspace_bytes(geom, n_pages).
  * ------------------------------------------------------------------------- */
@@ -144,7 +146,8 @@ hsa_rc hsa_score_pages(const hsa_geom* geom, const void* q, const void* const* p
  *  emb_dim        1 <= E <= HSA_MAX_EMBED.
  *  k_chunks       1 <= k <= C.
  *  sims           [C] float32 out: cosine similarities, fp32 sums; 0 where
- *                 either embedding is all zeros.
+ *                 either embedding is all zeros; -inf (ranked last) where
+ *                 the similarity comes out NaN (NaN or Inf inputs).
  *  sel_chunks     [k] int32 out: the k most similar chunks (ties to the
  *                 lower id), ascending.
  * Errors: HSA_ERR_NULL_ARG, HSA_ERR_BAD_PARAM (sizes), HSA_ERR_HIP.

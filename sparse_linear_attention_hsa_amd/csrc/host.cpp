@@ -122,7 +122,8 @@ WsLayout ws_layout(const Dims& s, int n_pages) {
   w.lin_khi = align256((size_t)pp.splits * 2 * s.H * pp.rtiles * 16 * s.d * 4);
   w.lin_klo = align256(w.lin_khi + kbytes);
   w.lin_vt = align256(w.lin_klo + kbytes);
-  w.lin_end = align256(w.lin_vt + kbytes);
+  w.lin_vlo = align256(w.lin_vt + kbytes);
+  w.lin_end = align256(w.lin_vlo + kbytes);
   // select
   w.sel_qbar = 0;
   w.sel_kbar = align256((size_t)s.H * s.nQB * s.d * 4);

@@ -70,7 +70,7 @@ struct WsLayout {
   // score
   size_t score_partial, score_qbar, score_kbar, score_end;
   // linear
-  size_t lin_partial, lin_khi, lin_klo, lin_vt, lin_end;
+  size_t lin_partial, lin_khi, lin_klo, lin_vt, lin_vlo, lin_end;
   // select
   size_t sel_qbar, sel_kbar, sel_logit, sel_end;
   // sparse

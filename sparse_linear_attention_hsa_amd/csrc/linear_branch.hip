@@ -366,14 +366,16 @@ __global__ __launch_bounds__(256) void lin_reduce_kernel(const float* __restrict
 }
 
 // Operands of the attention over the rank axis, prepared once per call from
-// the float32 projections: Ktil as element-type rows [H][rpad][D] (for bf16 a
-// high part plus the bf16 rounding of the remainder, so the two products
-// together keep float32-like logits) and Vtil^T as [H][D][rpad]; rows and
-// columns past r are zero.  grid (ceil(rpad*D/256), H, 2): z = 0 Ktil, 1 Vtil^T.
+// the float32 projections: Ktil as element-type rows [H][rpad][D] and Vtil^T
+// as [H][D][rpad], for bf16 each as a high part plus the bf16 rounding of the
+// remainder, so the paired products keep float32-like logits and values;
+// rows and columns past r are zero.  grid (ceil(rpad*D/256), H, 2): z = 0
+// Ktil, 1 Vtil^T.
 template <typename T>
 __global__ __launch_bounds__(256) void lin_prep_kernel(const float* __restrict__ k_proj,
                                                        const float* __restrict__ v_proj, int D, int r, int rpad,
-                                                       T* __restrict__ khi, T* __restrict__ klo, T* __restrict__ vt) {
+                                                       T* __restrict__ khi, T* __restrict__ klo, T* __restrict__ vt,
+                                                       T* __restrict__ vlo) {
   const int h = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= rpad * D) return;
@@ -386,7 +388,9 @@ __global__ __launch_bounds__(256) void lin_prep_kernel(const float* __restrict__
   } else {
     const int col = e / rpad, rr = e % rpad;
     const float v = rr < r ? v_proj[((size_t)h * D + col) * r + rr] : 0.f;
-    vt[(size_t)h * D * rpad + e] = from_f32<T>(v);
+    const T hi = from_f32<T>(v);
+    vt[(size_t)h * D * rpad + e] = hi;
+    if (sizeof(T) == 2) vlo[(size_t)h * D * rpad + e] = from_f32<T>(v - to_f32<T>(hi));
   }
 }
 
@@ -396,8 +400,12 @@ __global__ __launch_bounds__(256) void lin_prep_kernel(const float* __restrict__
 // single barrier; then every wave walks its units independently: S^T =
 // Ktil Q^T chunk by chunk over the rank axis (keys on the rows, one query
 // per accumulator column), an online softmax, and O^T += Vtil^T P^T with the
-// Vtil^T operand read straight from memory (a head's Vtil^T is 64 KB and
-// stays in L2), one chunk ahead.  Chunk rows past r are masked.
+// Vtil^T operand (for bf16 its high and low parts) read straight from memory
+// at the start of the chunk (a head's Vtil^T is 64 KB per part and stays in
+// L2).  For bf16 the weights are rounded to bf16 for the product, and the
+// denominator is summed from the same rounded weights (an all-ones tile), so
+// numerator and denominator use identical weights.  Chunk rows past r are
+// masked.
 constexpr int kAttWaves = 8;
 constexpr int kAttThreads = kAttWaves * kWave;
 constexpr int kAttMaxRank = 256;
@@ -405,8 +413,9 @@ constexpr int kAttUnit = 32;  // queries per unit: two 16-row tiles share every 
 
 template <typename T, int D>
 __global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lin_attend_kernel(
-    const T* __restrict__ q, const T* __restrict__ khi, const T* __restrict__ klo, const T* __restrict__ vt, int H,
-    int Lq, int r, int rpad, int units_per_wg, float scale_log2, float* __restrict__ o_lin) {
+    const T* __restrict__ q, const T* __restrict__ khi, const T* __restrict__ klo, const T* __restrict__ vt,
+    const T* __restrict__ vlo, int H, int Lq, int r, int rpad, int units_per_wg, float scale_log2,
+    float* __restrict__ o_lin) {
   constexpr int E = Vec<T>::N;
   constexpr int KS = Mma<T>::K;        // rank rows per chunk (= one PV contraction step)
   constexpr int GPS = KS / 16;         // 16-row tiles per chunk
@@ -418,7 +427,6 @@ __global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int ROWB = D * (int)sizeof(T);
   constexpr int RPI = 1024 / ROWB;     // Ktil rows per direct-load instruction
   constexpr int PART = kAttMaxRank * ROWB;
-  constexpr bool PREFETCH_V = SPLIT;   // the float32 variant has no registers to spare
   __shared__ __align__(1024) unsigned char lds_k[SPLIT ? 2 * PART : PART];
 
   const int tid = threadIdx.x, lane = tid % kWave;
@@ -445,6 +453,11 @@ __global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int u_begin = blockIdx.x * units_per_wg;
   const int u_end = min(units, u_begin + units_per_wg);
   const T* vh = vt + (size_t)h * D * rpad;
+  const T* vl = vlo + (size_t)h * D * rpad;  // bf16 only
+  // all-ones A operand (bf16 1.0 pairs): its product with P^T holds in every
+  // row the column sums of the rounded weights, the denominator that matches
+  // the numerator's weights exactly
+  const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
   for (int u = u_begin + w; u < u_end; u += kAttWaves) {
     const int qbase = u * kAttUnit;
     uint4 qreg[QT][DSTEPS];
@@ -456,23 +469,25 @@ __global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(2, 
         qreg[t][s] = ld16_masked(q + ((size_t)min(qrow, Lq - 1) * H + h) * D + (4 * s + g) * E, qrow < Lq);
     }
     f32x4 o[QT][DT];
+    f32x4 lacc[QT];  // bf16: denominators from the ones tile
     float m_run[QT], l_run[QT];
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       m_run[t] = -INFINITY;
       l_run[t] = 0.f;
+      lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // Vtil^T operand of chunk ch: lane (g, c) holds row 16*dt + c, ranks ch*KS + g*E ...
-    uint4 vop[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vop[dt] = ld16(vh + (size_t)(16 * dt + c) * rpad + g * E);
     for (int ch = 0; ch < nchunk; ++ch) {
-      uint4 vnext[DT];
-      if (PREFETCH_V && ch + 1 < nchunk) {
+      // this chunk's Vtil^T operands, lane (g, c) holding row 16*dt + c,
+      // ranks ch*KS + g*E ...; their latency hides behind S and the softmax
+      uint4 vop[DT], vop_lo[DT];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vnext[dt] = ld16(vh + (size_t)(16 * dt + c) * rpad + (ch + 1) * KS + g * E);
+      for (int dt = 0; dt < DT; ++dt) {
+        const size_t off = (size_t)(16 * dt + c) * rpad + ch * KS + g * E;
+        vop[dt] = ld16(vh + off);
+        if (SPLIT) vop_lo[dt] = ld16(vl + off);
       }
       f32x4 sacc[QT][GPS];
 #pragma unroll
@@ -526,32 +541,36 @@ __global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(2, 
           for (int i = 0; i < 4; ++i) {
             const float e = fast_exp2(fmaf(sacc[t][kt][i], scale_log2, -m_run[t]));
             p[kt][i] = e;
-            ls += e;
+            if (!SPLIT) ls += e;
           }
-        l_run[t] = l_run[t] * alpha[t] + ls;
+        if (!SPLIT) l_run[t] = l_run[t] * alpha[t] + ls;
         pk[t] = pack_p<T>(p);
       }
       if (__any(need_any)) {
 #pragma unroll
-        for (int t = 0; t < QT; ++t)
+        for (int t = 0; t < QT; ++t) {
+          if (SPLIT) lacc[t] *= alpha[t];
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha[t];
+        }
       }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int t = 0; t < QT; ++t) Mma<T>::run(o[t][dt], vop[dt], pk[t]);
-      if (ch + 1 < nchunk) {
+        for (int t = 0; t < QT; ++t) {
+          Mma<T>::run(o[t][dt], vop[dt], pk[t]);
+          if (SPLIT) Mma<T>::run(o[t][dt], vop_lo[dt], pk[t]);
+        }
+      if (SPLIT) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          vop[dt] = PREFETCH_V ? vnext[dt] : ld16(vh + (size_t)(16 * dt + c) * rpad + (ch + 1) * KS + g * E);
+        for (int t = 0; t < QT; ++t) Mma<T>::run(lacc[t], ones, pk[t]);
       }
     }
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       const int qrow = qbase + 16 * t + c;
       if (qrow < Lq) {
-        const float inv = 1.f / sum4g(l_run[t]);
+        const float inv = 1.f / (SPLIT ? lacc[t][0] : sum4g(l_run[t]));
         float* dst = o_lin + ((size_t)qrow * H + h) * D + 4 * g;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -582,13 +601,14 @@ void launch_linear(const Dims& s, const void* q, const void* k_act, const void* 
   T* khi = reinterpret_cast<T*>(ws + w.lin_khi);
   T* klo = reinterpret_cast<T*>(ws + w.lin_klo);
   T* vt = reinterpret_cast<T*>(ws + w.lin_vt);
+  T* vlo = reinterpret_cast<T*>(ws + w.lin_vlo);
   hipLaunchKernelGGL((lin_prep_kernel<T>), dim3((pp.rpad * D + 255) / 256, s.H, 2), dim3(256), 0, st,
                      reinterpret_cast<const float*>(k_proj), reinterpret_cast<const float*>(v_proj), D, s.r, pp.rpad,
-                     khi, klo, vt);
+                     khi, klo, vt, vlo);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
   const AttendPlan ap = attend_plan(s);
   hipLaunchKernelGGL((lin_attend_kernel<T, D>), dim3(ap.wg_per_head, s.H), dim3(kAttThreads), 0, st,
-                     reinterpret_cast<const T*>(q), khi, klo, vt, s.H, s.Lq, s.r, pp.rpad, ap.units_per_wg,
+                     reinterpret_cast<const T*>(q), khi, klo, vt, vlo, s.H, s.Lq, s.r, pp.rpad, ap.units_per_wg,
                      scale_log2, o_lin);
 }
 

@@ -203,7 +203,10 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
       for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
     }
     if (lane == 0) {
-      alpha[j] = cand ? s * scale : -INFINITY;
+      // a NaN score (NaN or Inf in the inputs) ranks as -inf, so the order
+      // stays total and exactly K_p pages are chosen
+      const float a = s * scale;
+      alpha[j] = cand && !__builtin_isnan(a) ? a : -INFINITY;
       tier[j] = cand ? 1 : 2;
       chunk_of[j] = filt.page_chunk ? filt.page_chunk[j] : 0;
     }
@@ -273,7 +276,12 @@ __global__ __launch_bounds__(kRetrThreads) void retrieve_chunks_kernel(
       dot += __shfl_xor(dot, o);
       n += __shfl_xor(n, o);
     }
-    if (lane == 0) sim_s[c] = (ncur > 0.f && n > 0.f) ? dot / (sqrtf(ncur) * sqrtf(n)) : 0.f;
+    if (lane == 0) {
+      // a zero embedding has similarity 0 with every embedding; otherwise a
+      // NaN (from NaN or Inf inputs) ranks as -inf, so the order stays total
+      const float c_sim = (ncur == 0.f || n == 0.f) ? 0.f : dot / (sqrtf(ncur) * sqrtf(n));
+      sim_s[c] = __builtin_isnan(c_sim) ? -INFINITY : c_sim;
+    }
   }
   __syncthreads();
   for (int c = threadIdx.x; c < n_chunks; c += kRetrThreads) {

@@ -71,8 +71,8 @@ def _run(cfg, geom, host_ids, inputs, pairs, n_slots=4, concurrent=True):
     return res, sel
 
 
-def _check_layer_step(cfg, a, s, gpu_sel, r, rows=None):
-    """Oracle for one (layer, step) with the first step's pages; rows = sampled (h, query block) or all."""
+def _check_layer_step(cfg, a, s, gpu_sel, r):
+    """Oracle for one (layer, step) with the first step's pages, over every row."""
     B, H = cfg.block, cfg.n_heads
     sc = orc.score_and_select(a["q"][0], a["pages_k"], cfg.n_sel_pages)
     if not np.array_equal(gpu_sel, sc["sel"]):
@@ -84,18 +84,12 @@ def _check_layer_step(cfg, a, s, gpu_sel, r, rows=None):
     gl = [[r["idx"][h, i, :r["cnt"][h, i]].astype(np.int64) for i in range(cfg.n_qblocks)] for h in range(H)]
     check_block_selection(bs, gl, a["tau"])
     ktil, vtil = orc.project(a["e_k"], k_act), orc.project(a["e_v"], v_act)
-    qblocks = range(cfg.n_qblocks) if rows is None else sorted({i for _, i in rows})
-    tok = np.concatenate([np.arange(i * B, (i + 1) * B) for i in qblocks])
-    o_lin_ref = orc.linear_attention(q[tok], ktil, vtil)
-    o_sp_ref = np.empty((len(tok), H, cfg.head_dim))
-    for h in range(H):
-        for n, i in enumerate(qblocks):
-            o_sp_ref[n * B:(n + 1) * B, h, :] = orc.sparse_row(q[i * B:(i + 1) * B, h, :], k_act[h], v_act[h],
-                                                               gl[h][i], B)
-    out_ref = orc.fuse(x[tok], a["w_g"], o_lin_ref, o_sp_ref)
-    assert_close("o_lin", r["o_lin"][tok], o_lin_ref, cfg)
-    assert_close("o_sp", r["o_sp"][tok], o_sp_ref, cfg)
-    assert_close("out", r["out"][tok], out_ref, cfg)
+    o_lin_ref = orc.linear_attention(q, ktil, vtil)
+    o_sp_ref = orc.sparse_attention(q, k_act, v_act, gl, B)
+    out_ref = orc.fuse(x, a["w_g"], o_lin_ref, o_sp_ref)
+    assert_close("o_lin", r["o_lin"], o_lin_ref, cfg)
+    assert_close("o_sp", r["o_sp"], o_sp_ref, cfg)
+    assert_close("out", r["out"], out_ref, cfg)
 
 
 @pytest.mark.parametrize("n_slots", [2, 4])
@@ -117,7 +111,8 @@ def test_stack_small_every_layer_step(n_slots):
             _check_layer_step(cfg, keep[l], s, sel[l], got[(l, s)])
 
 
-def test_stack_c4_sampled():
+def test_stack_c4_four_layer_steps():
+    """The first and last layer, first and last step: every row of the four."""
     cfg = CONFIGS["c4_stack"]
     last = cfg.layers - 1
     print(f"\n[stack] {cfg.name}: {cfg.layers} layers x {cfg.steps} steps, "
@@ -125,12 +120,7 @@ def test_stack_c4_sampled():
     geom, host_ids, streamed, _, keep = _build(cfg, layers_needed_host=(0, last))
     pairs = [(0, 0), (0, cfg.steps - 1), (last, 0), (last, cfg.steps - 1)]
     got, sel = _run(cfg, geom, host_ids, streamed, pairs)
-    rng = np.random.default_rng(11)
     for (l, s) in pairs:
-        cnt = got[(l, s)]["cnt"]
-        flat = cnt.reshape(-1)
-        pick = {int(np.argmax(flat)), int(np.argmin(flat))} | set(int(i) for i in rng.choice(flat.size, 3, replace=False))
-        rows = [(i // cfg.n_qblocks, i % cfg.n_qblocks) for i in pick]
         print(f"  layer {l} step {s}: pages {sel[l].tolist()} (host {host_ids[l].tolist()}), "
-              f"selected pairs {int(flat.sum())}", flush=True)
-        _check_layer_step(cfg, keep[l], s, sel[l], got[(l, s)], rows=rows)
+              f"selected pairs {int(got[(l, s)]['cnt'].sum())}", flush=True)
+        _check_layer_step(cfg, keep[l], s, sel[l], got[(l, s)])
