@@ -12,10 +12,11 @@
  * ---------------------------------------
  *  - Every tensor argument is a DEVICE pointer owned by the caller, except
  *    the page pointer tables (`page_k`, `page_v`), which are HOST arrays of
- *    device pointers.  The library never allocates or frees memory and keeps
- *    no mutable global state; scratch memory is the caller's workspace
- *    (size from hsa_workspace_bytes).  Calls are re-entrant on different
- *    streams as long as they do not share a workspace.
+ *    device pointers.  The library never allocates or frees memory; scratch
+ *    memory is the caller's workspace (size from hsa_workspace_bytes).
+ *    Calls are re-entrant on different streams as long as they do not share
+ *    a workspace.  The one exception, hsa_block_select_noalloc, keeps its
+ *    scratch in a fixed device array of the library (see there).
  *  - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
  *    default stream) and returns; results are valid once the stream has
  *    reached that point.  No call synchronises with the host, so a sequence
@@ -285,6 +286,34 @@ hsa_rc hsa_linear_branch(const hsa_geom* geom, const void* q, const void* k_act,
 hsa_rc hsa_block_select(const hsa_geom* geom, const void* q, const void* k_act, const float* kblk_mean,
                         const float* tau, int32_t* blk_count, int32_t* blk_idx, float* blk_mass,
                         void* ws, size_t ws_bytes, hsa_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * hsa_block_select without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc).  Same arguments, kernels and results as
+ * hsa_block_select, bit for bit; the scratch (pooled query means, candidate
+ * means, pooled logits) lives in a device array of HSA_NOALLOC_SCRATCH_BYTES
+ * inside the library, which each GPU it runs on holds until the process
+ * ends.  The call allocates nothing (no hipMalloc, no hipFree, no allocating
+ * library routine); its first call on a device looks up that device's copy
+ * of the array (hipGetSymbolAddress).
+ *
+ *  Size limit: a geometry whose selection scratch (the block-selection part
+ *  of hsa_workspace_bytes: H*nQB*d + H*nKB*d + H*nQB*nKB floats, each part
+ *  rounded up to 256 bytes) exceeds HSA_NOALLOC_SCRATCH_BYTES is rejected
+ *  with HSA_ERR_WORKSPACE before anything is launched.  That covers 12 heads
+ *  of d = 128 with 49,920 retrieved keys in 96-token blocks and 6,240
+ *  queries, also with the chunk's own keys in 48-token blocks.
+ *  Concurrency: every call on one GPU shares that GPU's array, so calls that
+ *  overlap on one GPU (different streams, or different host threads without
+ *  ordering) race and give undefined results; calls ordered on one stream
+ *  are safe.  Nothing in the array needs to start at zero: each call writes
+ *  every scratch element it reads.
+ * ------------------------------------------------------------------------- */
+#define HSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+hsa_rc hsa_block_select_noalloc(const hsa_geom* geom, const void* q, const void* k_act, const float* kblk_mean,
+                                const float* tau, int32_t* blk_count, int32_t* blk_idx, float* blk_mass,
+                                hsa_stream stream);
 
 /* ---------------------------------------------------------------------------
  * S5 -- block-sparse attention.  Paper section 3.3, "Sparse branch" and

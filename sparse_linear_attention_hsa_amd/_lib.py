@@ -20,6 +20,7 @@ HSA_MAX_ROWS = 4096
 HSA_MAX_CHUNKS = 4096
 HSA_MAX_EMBED = 65536
 HSA_MAX_INTRA_SPLIT = 4
+HSA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 RC_NAMES = {0: "HSA_OK", 1: "HSA_ERR_NULL_ARG", 2: "HSA_ERR_BAD_SHAPE", 3: "HSA_ERR_BAD_DTYPE",
             4: "HSA_ERR_BAD_PARAM", 5: "HSA_ERR_WORKSPACE", 6: "HSA_ERR_HIP"}
@@ -54,6 +55,7 @@ SIGNATURES = {
     "hsa_sparse_attn_paged": (_i32, [_GP, _vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp,
                                      _vp, _sz, _vp, _vp, _vp]),
     "hsa_block_select": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "hsa_block_select_noalloc": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "hsa_sparse_attn": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "hsa_sparse_attn_timed": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),
     "hsa_fuse": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),

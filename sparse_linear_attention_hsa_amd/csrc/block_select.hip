@@ -16,6 +16,8 @@
 //            than a sort), and the selected ids in ascending order.
 // Everything is float32 and in a fixed order, so the selection is bitwise
 // reproducible; no atomics.
+#include <mutex>
+
 #include "common.h"
 #include "host.h"
 
@@ -359,8 +361,67 @@ void launch_select(const Dims& s, const void* q, const void* k_act, const float*
 #undef HSA_SEL_CASE
 }
 
+// Scratch of the no-allocation variant: the pooled query means, candidate
+// means and pooled logits of one call, in a file-scope device array that
+// every GPU the library runs on holds until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it is only a
+// stand-in); it passes the device address that hipGetSymbolAddress returns
+// for the current device, fetched once per device.
+static __device__ __align__(256) unsigned char scratch[HSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, or nullptr.
+char* scratch_on_current_device(hsa_rc* rc) {
+  static std::mutex mu;
+  static char* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *rc = HSA_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      *rc = HSA_ERR_HIP;
+      return nullptr;
+    }
+    addr[dev] = static_cast<char*>(p);
+  }
+  return addr[dev];
+}
+
+void launch_select_any(const Dims& s, const void* q, const void* k_act, const float* kblk_mean, const float* tau,
+                       int32_t* cnt, int32_t* idx, float* mass, char* ws, const WsLayout& w, hipStream_t st) {
+  if (s.bf16) {
+    if (s.d == 128) launch_select<bf16_t, 128>(s, q, k_act, kblk_mean, tau, cnt, idx, mass, ws, w, st);
+    else launch_select<bf16_t, 64>(s, q, k_act, kblk_mean, tau, cnt, idx, mass, ws, w, st);
+  } else {
+    if (s.d == 128) launch_select<float, 128>(s, q, k_act, kblk_mean, tau, cnt, idx, mass, ws, w, st);
+    else launch_select<float, 64>(s, q, k_act, kblk_mean, tau, cnt, idx, mass, ws, w, st);
+  }
+}
+
 }  // namespace
 }  // namespace hsa
+
+extern "C" hsa_rc hsa_block_select_noalloc(const hsa_geom* geom, const void* q, const void* k_act,
+                                           const float* kblk_mean, const float* tau, int32_t* blk_count,
+                                           int32_t* blk_idx, float* blk_mass, hsa_stream stream) {
+  using namespace hsa;
+  Dims s;
+  hsa_rc rc = derive(geom, &s);
+  if (rc != HSA_OK) return rc;
+  if (!q || !tau || !blk_count || !blk_idx || (!k_act && !kblk_mean)) return HSA_ERR_NULL_ARG;
+  const WsLayout w = ws_layout(s, 1);
+  if (w.sel_end > (size_t)HSA_NOALLOC_SCRATCH_BYTES) return HSA_ERR_WORKSPACE;
+  char* ws = scratch_on_current_device(&rc);
+  if (!ws) return rc;
+  launch_select_any(s, q, k_act, kblk_mean, tau, blk_count, blk_idx, blk_mass, ws, w,
+                    reinterpret_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
+}
 
 extern "C" hsa_rc hsa_block_select(const hsa_geom* geom, const void* q, const void* k_act, const float* kblk_mean,
                                    const float* tau, int32_t* blk_count, int32_t* blk_idx, float* blk_mass,
@@ -372,14 +433,7 @@ extern "C" hsa_rc hsa_block_select(const hsa_geom* geom, const void* q, const vo
   if (!q || !tau || !blk_count || !blk_idx || (!k_act && !kblk_mean)) return HSA_ERR_NULL_ARG;
   const WsLayout w = ws_layout(s, 1);
   if (!ws || ws_bytes < w.sel_end) return HSA_ERR_WORKSPACE;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  char* wsb = static_cast<char*>(ws);
-  if (s.bf16) {
-    if (s.d == 128) launch_select<bf16_t, 128>(s, q, k_act, kblk_mean, tau, blk_count, blk_idx, blk_mass, wsb, w, st);
-    else launch_select<bf16_t, 64>(s, q, k_act, kblk_mean, tau, blk_count, blk_idx, blk_mass, wsb, w, st);
-  } else {
-    if (s.d == 128) launch_select<float, 128>(s, q, k_act, kblk_mean, tau, blk_count, blk_idx, blk_mass, wsb, w, st);
-    else launch_select<float, 64>(s, q, k_act, kblk_mean, tau, blk_count, blk_idx, blk_mass, wsb, w, st);
-  }
+  launch_select_any(s, q, k_act, kblk_mean, tau, blk_count, blk_idx, blk_mass, static_cast<char*>(ws), w,
+                    reinterpret_cast<hipStream_t>(stream));
   return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
 }

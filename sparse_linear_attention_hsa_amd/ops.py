@@ -168,6 +168,13 @@ def hsa_block_select(geom, q, k_act, kblk_mean, tau, blk_count, blk_idx, blk_mas
         _p(ws), ws.numel() * ws.element_size(), _s(stream)))
 
 
+def hsa_block_select_noalloc(geom, q, k_act, kblk_mean, tau, blk_count, blk_idx, blk_mass, stream=None):
+    """hsa_block_select with the library's own device scratch instead of a workspace."""
+    check("hsa_block_select_noalloc", lib().hsa_block_select_noalloc(
+        ctypes.byref(geom), _p(q), _p(k_act), _p(kblk_mean), _p(tau), _p(blk_count), _p(blk_idx), _p(blk_mass),
+        _s(stream)))
+
+
 def hsa_sparse_attn(geom, q, k_act, v_act, blk_count, blk_idx, o_sp, ws, stream=None):
     check("hsa_sparse_attn", lib().hsa_sparse_attn(
         ctypes.byref(geom), _p(q), _p(k_act), _p(v_act), _p(blk_count), _p(blk_idx), _p(o_sp),

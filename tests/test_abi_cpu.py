@@ -214,3 +214,16 @@ def test_entry_points_reject_bad_arguments_before_launch(lib):
 def test_status_strings(lib):
     for rc, name in _lib.RC_NAMES.items():
         assert lib.hsa_rc_string(rc).decode().startswith(name)
+
+
+def test_noalloc_select_rejects_before_launching(lib):
+    """The workspace-free block selection checks its arguments and the size
+    of its fixed scratch on the host, before touching the device."""
+    big = c1_geom(n_heads=24, n_sel_pages=8)    # selection scratch about 20 MB
+    assert lib.hsa_geom_check(ctypes.byref(big)) == 0
+    p = ctypes.c_void_p(256)                    # never dereferenced: the call returns first
+    assert lib.hsa_block_select_noalloc(ctypes.byref(big), p, p, p, p, p, p, None, None) == 5
+    assert lib.hsa_block_select_noalloc(ctypes.byref(c1_geom()), None, p, p, p, p, p, None, None) == 1
+    assert lib.hsa_block_select_noalloc(ctypes.byref(c1_geom()), p, None, None, p, p, p, None, None) == 1
+    assert lib.hsa_block_select_noalloc(ctypes.byref(c1_geom(dtype=7)), p, p, p, p, p, p, None, None) == 3
+    assert _lib.HSA_NOALLOC_SCRATCH_BYTES == 16 << 20
