@@ -125,21 +125,11 @@ def measured_traffic(workload: str):
         return None
 
 
-def cpu_baseline(cfg, w, arrays):
-    """Time the float64 oracle on a bounded sample of the same workload and
-    scale it to one chunk: scoring, gather, linear branch, block selection
-    and fusion run whole; the sparse branch runs for the first three heads
-    on every query block (x H/3).  About 10 s of CPU work at C1."""
+def _oracle_pass(cfg, arrays, nh):
+    """One timed pass of the float64 oracle over the sample; per-stage seconds."""
     from oracle import hsa_oracle as orc
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        cores = max([i.get("num_threads", 1) for i in info] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
     s, pk, pv = arrays
     H, B = cfg.n_heads, cfg.block
-    nh = min(3, H)
     intra = bool(cfg.intra_split)
     t = {}
     t0 = time.perf_counter()
@@ -172,11 +162,36 @@ def cpu_baseline(cfg, w, arrays):
     t0 = time.perf_counter()
     orc.fuse(s["x"], s["w_g"], lin["o_lin"], o_full)
     t["fuse"] = time.perf_counter() - t0
-    total_ms = 1e3 * sum(t.values())
-    return {"value": round(total_ms, 1), "unit": "ms/chunk", "cores": int(cores), "kind": "oracle",
+    return t
+
+
+def cpu_baseline(cfg, w, arrays):
+    """Time the float64 oracle on a bounded sample of the same workload and
+    scale it to one chunk: scoring, gather, linear branch, block selection
+    and fusion run whole; the sparse branch runs for the first three heads
+    on every query block (x H/3).  The median of three passes with every
+    host core, then one pass on one thread (and the tiny workload's whole
+    oracle step on one thread)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from synth import C0, Workload
+    cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    nh = min(3, cfg.n_heads)
+    runs = [_oracle_pass(cfg, arrays, nh) for _ in range(3)]
+    totals = [1e3 * sum(t.values()) for t in runs]
+    med = int(np.argsort(totals)[1])
+    with threadpool_limits(limits=1):
+        one = 1e3 * sum(_oracle_pass(cfg, arrays, nh).values())
+        w0 = Workload(C0)
+        s0 = w0.small_inputs()
+        pk0, pv0 = w0.pages()
+        one_c0 = 1e3 * sum(_oracle_pass(C0, (s0, pk0, pv0), C0.n_heads).values())
+    return {"value": round(totals[med], 1), "unit": "ms/chunk", "cores": int(cores), "kind": "oracle",
             "sample": f"float64 NumPy oracle; scoring, gather, linear branch, block selection and fusion whole; "
-                      f"sparse branch on heads 0..{nh - 1} of {H}, every query block (x{H}/{nh})",
-            "stages_ms": {k: round(1e3 * v, 1) for k, v in t.items()}}
+                      f"sparse branch on heads 0..{nh - 1} of {cfg.n_heads}, every query block (x{cfg.n_heads}/{nh}); "
+                      f"median of 3 passes on {cores} threads",
+            "runs_ms": [round(v, 1) for v in totals],
+            "stages_ms": {k: round(1e3 * v, 1) for k, v in runs[med].items()},
+            "one_thread_ms": {cfg.name: round(one, 1), C0.name: round(one_c0, 3)}}
 
 
 def run_stack(args, cfg):
@@ -347,74 +362,18 @@ def run_tiers(args, cfg):
     }), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c1_full")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true", help="replay the step as one HIP graph")
-    ap.add_argument("--chunks", type=int, default=0,
-                    help="prompt-level retrieval first: keep the K most similar chunks and score only their pages "
-                         "(K_p/K pages from each)")
-    ap.add_argument("--pages-per-chunk", type=int, default=8, help="history pages per chunk for --chunks")
-    ap.add_argument("--tiers", type=int, default=0,
-                    help="run this many generated chunks with the pages in tiers, fetched on demand and prefetched")
-    ap.add_argument("--tiers-steps", type=int, default=120,
-                    help="per-step stages repeated per generated chunk under --tiers (30 layers x 4 steps)")
-    ap.add_argument("--page-index", action="store_true",
-                    help="score from a page index of mean keys built once before the timed steps "
-                         "(as when pages are written) instead of reading every page's keys")
-    ap.add_argument("--paged", action="store_true",
-                    help="lay the pages out once (as when written) and run the step reading them in place: scoring "
-                         "from the page index, no active-buffer copy")
-    ap.add_argument("--intra", type=int, default=0,
-                    help="intra-chunk keys: the chunk's own tokens follow the retrieved pages in key blocks of "
-                         "B/S tokens (S = 2: 48-token blocks beside the 96-token history tiles)")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="only run three device-to-device copies of 1 GiB (calibrates the HBM byte counters)")
-    args = ap.parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus > 1 or world > 1:
-        print("bench.py: this build measures one GPU; --gpus > 1 is not supported "
-              "(the HSA step shards by head, see the design notes, but no multi-GPU path is built)", file=sys.stderr)
-        sys.exit(2)
-
+def run_single(args, cfg, steps: int, warmup: int, with_cpu: bool, with_peaks: bool = True) -> dict:
+    """One layer, one denoising step of a single-step workload: W warm-up
+    steps, a per-stage pass of K steps (calls in order on one stream, events
+    between them), then K timed steps in the step's own schedule.  Returns
+    the benchmark line as a dict."""
     import torch
-    if args.copy_probe:
-        n = 1 << 30
-        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
-        return
-    from synth import CONFIGS, Workload
+    from concurrent.futures import ThreadPoolExecutor
+    from synth import Workload
     from sparse_linear_attention_hsa_amd import ops
     from sparse_linear_attention_hsa_amd.ops import make_geom
     from sparse_linear_attention_hsa_amd.step import HsaStep
 
-    cfg = CONFIGS[args.config]
-    if args.paged and (args.intra or args.chunks or args.tiers or cfg.layers > 1 or cfg.steps > 1):
-        print("bench.py: --paged runs the single-step workloads without --intra / --chunks / --tiers",
-              file=sys.stderr)
-        sys.exit(2)
-    if args.paged:
-        from dataclasses import replace
-        cfg = replace(cfg, name=f"{cfg.name}_paged")
-    if args.intra:
-        from dataclasses import replace
-        if args.tiers or args.chunks or cfg.layers > 1 or cfg.steps > 1:
-            print("bench.py: --intra runs the single-step workloads without --tiers / --chunks", file=sys.stderr)
-            sys.exit(2)
-        cfg = replace(cfg, name=f"{cfg.name}_intra{args.intra}", intra_split=args.intra)
-        cfg.check()
-    if args.tiers:
-        return run_tiers(args, cfg)
-    if cfg.layers > 1 or cfg.steps > 1:
-        return run_stack(args, cfg)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     w = Workload(cfg)
     s = w.small_inputs()
@@ -422,17 +381,17 @@ def main():
     q, x, e_k, e_v, w_g = (up(s[k]) for k in ("q", "x", "e_k", "e_v", "w_g"))
     k_cur, v_cur = (up(s["k_cur"]), up(s["v_cur"])) if cfg.intra_split else (None, None)
     tau = torch.from_numpy(s["tau"]).cuda()
-    keep_host = not args.no_cpu_baseline  # the oracle's scoring reads every page
+    keep_host = with_cpu  # the oracle's scoring reads every page
     pk_np, pv_np, pk, pv = [], [], [], []
-    for j in range(cfg.n_pages):
-        kj, vj = w.page_k(j), w.page_v(j)
-        pk.append(up(kj))
-        pv.append(up(vj))
-        if keep_host:
-            pk_np.append(kj)
-            pv_np.append(vj)
-        if (j + 1) % 8 == 0 or j + 1 == cfg.n_pages:
-            print(f"bench: generated {j + 1}/{cfg.n_pages} pages", file=sys.stderr, flush=True)
+    with ThreadPoolExecutor(16) as ex:  # pages generated on a thread pool, uploaded in order
+        for j, (kj, vj) in enumerate(ex.map(lambda i: (w.page_k(i), w.page_v(i)), range(cfg.n_pages))):
+            pk.append(up(kj))
+            pv.append(up(vj))
+            if keep_host:
+                pk_np.append(kj)
+                pv_np.append(vj)
+            if (j + 1) % 8 == 0 or j + 1 == cfg.n_pages:
+                print(f"bench: {cfg.name}: generated {j + 1}/{cfg.n_pages} pages", file=sys.stderr, flush=True)
     geom = make_geom(cfg.n_heads, cfg.head_dim, cfg.frame_h, cfg.frame_w, cfg.frames_per_page,
                      cfg.query_frames, cfg.tile, cfg.n_sel_pages, cfg.rank, cfg.dtype, cfg.intra_split)
     st = HsaStep(geom, cfg.n_pages)
@@ -490,7 +449,7 @@ def main():
             fn()
             ev[i][1].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         one_step()
     torch.cuda.synchronize()
 
@@ -509,29 +468,29 @@ def main():
     # stream).  This pass runs before the timed region, so the timed steps
     # find the GPU in its steady state.
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in STAGES]
-           for _ in range(args.steps)]
-    kevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+           for _ in range(steps)]
+    kevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
-    for k in range(args.steps):
+    for k in range(steps):
         one_step_staged(evs[k], kevs[k])
     torch.cuda.synchronize()
     # timed region: K whole steps in the step's own schedule (an event after
     # every step gives the per-step spread; events do not synchronise)
-    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     step_ev[0].record(stream)
-    for k in range(args.steps):
+    for k in range(steps):
         if graph is not None:
             graph.replay()
         else:
             one_step()
         step_ev[k + 1].record(stream)
     torch.cuda.synchronize()
-    ms = step_ev[0].elapsed_time(step_ev[-1]) / args.steps
-    per_step = np.array([step_ev[k].elapsed_time(step_ev[k + 1]) for k in range(args.steps)])
-    peaks = measured_peaks()
+    ms = step_ev[0].elapsed_time(step_ev[-1]) / steps
+    per_step = np.array([step_ev[k].elapsed_time(step_ev[k + 1]) for k in range(steps)])
+    peaks = measured_peaks() if with_peaks else None
 
-    stage_ms = {name: float(np.mean([evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(args.steps)]))
+    stage_ms = {name: float(np.mean([evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(steps)]))
                 for i, name in enumerate(STAGES)}
     attn_kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in kevs]))
 
@@ -556,8 +515,8 @@ def main():
             "kernel": "sparse_attn_kernel", "kernel_ms": round(attn_kernel_ms, 4)}
 
     out = {
-        "metric": METRIC, "value": round(ms, 4), "unit": "ms/chunk", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak",
+        "metric": METRIC, "value": round(ms, 4), "unit": "ms/chunk", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "heads": cfg.n_heads, "head_dim": cfg.head_dim,
                    "retrieved_tokens": cfg.history_tokens, "query_tokens": cfg.query_tokens,
@@ -571,20 +530,101 @@ def main():
         "step_tflops": round(sum(m.get("flops", 0) for m in model.values()) / (ms * 1e-3) / 1e12, 1),
         "attended_tflops": round(sparse_tf, 1), "mfma_frac_sparse": round(sparse_tf / peak_tf, 4),
         "peaks_measured": peaks,
-        "mfma_frac_sparse_of_measured": round(sparse_tf / peaks["mfma_bf16_tflops"], 4),
         "selected_block_frac": round(n_sel_total / (cfg.n_heads * cfg.n_qblocks * cfg.n_key_blocks), 4),
         "linear_tflops": round(lin_tf, 1),
         "score_gbs": round(model["score"]["bytes"] / (stage_ms["score"] * 1e-3) / 1e9, 1),
         "gather_gbs": round(model["gather"]["bytes"] / (stage_ms["gather"] * 1e-3) / 1e9, 1),
-        "hbm_frac": {k: {"of_8tbs": round(model[k]["bytes"] / (stage_ms[k] * 1e-3) / 8e12, 4),
-                         "of_measured_copy": round(model[k]["bytes"] / (stage_ms[k] * 1e-3) / 1e9
-                                                   / peaks["hbm_copy_gbs"], 4)}
-                     for k in ("score", "gather")},
+        "hbm_frac_of_8tbs": {k: round(model[k]["bytes"] / (stage_ms[k] * 1e-3) / 8e12, 4) for k in ("score", "gather")},
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    if with_cpu:
         out["cpu_baseline"] = cpu_baseline(cfg, w, (s, pk_np, pv_np))
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c1_full")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="time only the chosen workload (by default c1_full also times c3 and c2 as extra keys)")
+    ap.add_argument("--graph", action="store_true", help="replay the step as one HIP graph")
+    ap.add_argument("--chunks", type=int, default=0,
+                    help="prompt-level retrieval first: keep the K most similar chunks and score only their pages "
+                         "(K_p/K pages from each)")
+    ap.add_argument("--pages-per-chunk", type=int, default=8, help="history pages per chunk for --chunks")
+    ap.add_argument("--tiers", type=int, default=0,
+                    help="run this many generated chunks with the pages in tiers, fetched on demand and prefetched")
+    ap.add_argument("--tiers-steps", type=int, default=120,
+                    help="per-step stages repeated per generated chunk under --tiers (30 layers x 4 steps)")
+    ap.add_argument("--page-index", action="store_true",
+                    help="score from a page index of mean keys built once before the timed steps "
+                         "(as when pages are written) instead of reading every page's keys")
+    ap.add_argument("--paged", action="store_true",
+                    help="lay the pages out once (as when written) and run the step reading them in place: scoring "
+                         "from the page index, no active-buffer copy")
+    ap.add_argument("--intra", type=int, default=0,
+                    help="intra-chunk keys: the chunk's own tokens follow the retrieved pages in key blocks of "
+                         "B/S tokens (S = 2: 48-token blocks beside the 96-token history tiles)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run three device-to-device copies of 1 GiB (calibrates the HBM byte counters)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py: this build measures one GPU; --gpus > 1 is not supported "
+              "(the HSA step shards by head, see the design notes, but no multi-GPU path is built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_probe:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+        return
+    from synth import CONFIGS
+
+    cfg = CONFIGS[args.config]
+    if args.paged and (args.intra or args.chunks or args.tiers or cfg.layers > 1 or cfg.steps > 1):
+        print("bench.py: --paged runs the single-step workloads without --intra / --chunks / --tiers",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.paged:
+        from dataclasses import replace
+        cfg = replace(cfg, name=f"{cfg.name}_paged")
+    if args.intra:
+        from dataclasses import replace
+        if args.tiers or args.chunks or cfg.layers > 1 or cfg.steps > 1:
+            print("bench.py: --intra runs the single-step workloads without --tiers / --chunks", file=sys.stderr)
+            sys.exit(2)
+        cfg = replace(cfg, name=f"{cfg.name}_intra{args.intra}", intra_split=args.intra)
+        cfg.check()
+    if args.tiers:
+        return run_tiers(args, cfg)
+    if cfg.layers > 1 or cfg.steps > 1:
+        return run_stack(args, cfg)
+    out = run_single(args, cfg, args.steps, args.warmup, not args.no_cpu_baseline)
+    variant = args.graph or args.page_index or args.paged or args.chunks or args.intra
+    if args.config == "c1_full" and not variant and not args.no_extra_configs:
+        # the head-imbalance and long-history workloads, timed the same way
+        # (fewer steps), as extra keys of the same line
+        torch.cuda.empty_cache()
+        out["extra_configs"] = {}
+        for name in ("c3_head_imbalance", "c2_long_history"):
+            e = run_single(args, CONFIGS[name], min(args.steps, 20), min(args.warmup, 5), False, with_peaks=False)
+            out["extra_configs"][name] = {
+                "ms_per_chunk": e["value"], "ms_per_step_stats": e["ms_per_step_stats"],
+                "sparse_roofline_frac": e["roofline"]["frac"], "sparse_kernel_ms": e["roofline"]["kernel_ms"],
+                "attended_tflops": e["attended_tflops"], "selected_block_frac": e["selected_block_frac"],
+                "stages_ms": e["stages_ms"], "history_pages": CONFIGS[name].n_pages}
+            torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 

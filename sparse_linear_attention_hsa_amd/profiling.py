@@ -5,9 +5,21 @@
     python -m sparse_linear_attention_hsa_amd.profiling traffic --fetch <dir> --write <dir> \
         --copy-fetch <dir> --copy-write <dir> --copy-bytes N --kernel <regex> --workload <name> \
         --out <out.txt> --cmd "<command>"
+    python -m sparse_linear_attention_hsa_amd.profiling mfma <pmc_dir> <out.txt> --kernels <regex> ... \
+        --workload <name> --cmd "<command>"
 
 `stats` condenses a `rocprofv3 --kernel-trace --stats --output-format csv`
 run into a per-kernel table (calls, average / min / max duration, share).
+
+`mfma` turns one counter run (`--pmc SQ_VALU_MFMA_BUSY_CYCLES
+SQ_VALU_MFMA_COEXEC_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU
+GRBM_GUI_ACTIVE`, `--output-format csv`) into matrix-core utilisation per
+kernel.  Every counter is a whole-GPU sum per dispatch; GRBM_GUI_ACTIVE
+counts the dispatch's busy cycles once per XCD, so a dispatch lasts
+GRBM_GUI_ACTIVE / 8 cycles, and the matrix cores' capacity is 4 SIMDs x
+256 CUs of those cycles.  The MFMA probe kernel (a chain of back-to-back
+16x16x32 bf16 products on every SIMD) is listed beside them as the
+calibration: it should read close to 1.
 
 `traffic` turns two counter runs (`--pmc FETCH_SIZE`, then `--pmc
 WRITE_SIZE`, both `--output-format csv`) into HBM bytes per launch of one
@@ -159,6 +171,46 @@ def write_traffic(a) -> None:
         f.write(f"source_sha256: {source_digest()}\n")
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_MFMA",
+                 "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE")
+N_XCD, N_CU, SIMD_PER_CU = 8, 256, 4
+
+
+def source_digests() -> dict:
+    out = {}
+    for path in sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip"))):
+        with open(path, "rb") as f:
+            out[os.path.basename(path)] = hashlib.sha256(f.read()).hexdigest()[:16]
+    return out
+
+
+def write_mfma(a) -> None:
+    with open(a.out, "w") as f:
+        f.write(f"# matrix-core utilisation per dispatch, workload {a.workload}\n")
+        f.write(f"# command: {a.cmd}\n")
+        f.write("# cycles = GRBM_GUI_ACTIVE / 8 (counted once per XCD); mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+                "(4 SIMDs x 256 CUs x cycles);\n# coexec = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES "
+                "(share of matrix-core busy cycles with a VALU op issued beside it);\n"
+                "# busy_cu = SQ_BUSY_CU_CYCLES / (256 x cycles); valu_per_mfma = SQ_INSTS_VALU / SQ_INSTS_MFMA\n")
+        hdr = (f"{'kernel':<40} {'cycles':>10} {'mfma_insts':>12} {'busy/inst':>9} {'mfma_busy':>9} "
+               f"{'coexec':>7} {'busy_cu':>7} {'valu/mfma':>9}\n")
+        f.write(hdr)
+        for rx in a.kernels:
+            v = {c: counter_per_dispatch(a.pmc_dir, c, rx) for c in MFMA_COUNTERS}
+            cyc = v["GRBM_GUI_ACTIVE"] / N_XCD
+            busy = v["SQ_VALU_MFMA_BUSY_CYCLES"]
+            insts = v["SQ_INSTS_MFMA"]
+            f.write(f"{rx[:40]:<40} {cyc:>10.0f} {insts:>12.0f} {busy / max(insts, 1):>9.1f} "
+                    f"{busy / (SIMD_PER_CU * N_CU * cyc):>9.3f} {v['SQ_VALU_MFMA_COEXEC_CYCLES'] / max(busy, 1):>7.3f} "
+                    f"{v['SQ_BUSY_CU_CYCLES'] / (N_CU * cyc):>7.3f} {v['SQ_INSTS_VALU'] / max(insts, 1):>9.2f}\n")
+        f.write("# raw per-dispatch averages:\n")
+        for rx in a.kernels:
+            vals = " ".join(f"{c}={counter_per_dispatch(a.pmc_dir, c, rx):.4g}" for c in MFMA_COUNTERS)
+            f.write(f"#   {rx}: {vals}\n")
+        f.write("# source sha256 (first 16 hex digits): " +
+                " ".join(f"{k}={h}" for k, h in source_digests().items()) + "\n")
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -175,9 +227,17 @@ def main(argv=None) -> int:
     t.add_argument("--workload", required=True)
     t.add_argument("--out", required=True)
     t.add_argument("--cmd", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("pmc_dir")
+    m.add_argument("out")
+    m.add_argument("--kernels", nargs="+", required=True, help="one kernel-name regex per table row")
+    m.add_argument("--workload", required=True)
+    m.add_argument("--cmd", required=True)
     a = ap.parse_args(argv)
     if a.what == "stats":
         write_stats(a.stats_dir, a.out, a.cmd, a.bench_log)
+    elif a.what == "mfma":
+        write_mfma(a)
     else:
         write_traffic(a)
     return 0
