@@ -67,7 +67,8 @@ extern "C" {
 #endif
 
 #define HSA_ATTN_ABI_VERSION 2
-#define HSA_MAX_PAGES 128      /* pages per call (pointer tables travel as launch arguments) */
+#define HSA_MAX_PAGES 128      /* pages per call with HOST page tables (they travel as launch arguments) */
+#define HSA_MAX_BANK_PAGES 8192 /* pages per call with DEVICE page tables (the *_devtab calls) */
 #define HSA_MAX_KBLOCKS 2048   /* nKB limit of the block selection (one sort per row in LDS) */
 #define HSA_MAX_INTRA_SPLIT 4  /* largest intra_split */
 #define HSA_MAX_ROWS 4096      /* H * nQB limit (selection rows; the sparse branch plans them in LDS) */
@@ -129,6 +130,8 @@ typedef struct ihipEvent_t* hsa_event;    /* a hipEvent_t  */
  *              order stays total and exactly K_p pages are retrieved.
  *  sel_pages   [K_p] int32 out: the retrieved page ids, ascending.
  *  ws          workspace of ws_bytes >= hsa_workspace_bytes(geom, n_pages).
+ * Larger banks (up to HSA_MAX_BANK_PAGES pages) take a device page table:
+ * hsa_score_pages_devtab below.
  * ------------------------------------------------------------------------- */
 hsa_rc hsa_score_pages(const hsa_geom* geom, const void* q, const void* const* page_k,
                        float* page_kmean, int32_t n_pages, float* scores, int32_t* sel_pages,
@@ -163,7 +166,8 @@ hsa_rc hsa_retrieve_chunks(const float* prompt, const float* chunk_prompts, int3
  * chunk and Top-4 one page from each).
  *
  *  Arguments as hsa_score_pages, plus:
- *  page_chunk  [P] int32 device: the chunk of every page.
+ *  page_chunk  [P] int32 device: the chunk of every page, in
+ *              [0, HSA_MAX_CHUNKS).
  *  sel_chunks  [k_chunks] int32 device: distinct chosen chunk ids (the output
  *              of hsa_retrieve_chunks).
  *  k_chunks    1 <= k <= K_p and K_p % k == 0.
@@ -223,6 +227,42 @@ hsa_rc hsa_gather_pages(const hsa_geom* geom, const void* const* page_k, const v
 hsa_rc hsa_gather_active(const hsa_geom* geom, const void* const* page_k, const void* const* page_v,
                          int32_t n_pages, const int32_t* sel_pages, const void* k_cur, const void* v_cur,
                          void* k_act, void* v_act, float* kblk_mean, hsa_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * Page banks larger than HSA_MAX_PAGES: S1 and S2 with the page pointer
+ * tables in DEVICE memory.  Paper section 3.2 (the full history stays
+ * available and restorable, the page index is built from the keys); the
+ * calls are those above with the same results, for 1 <= n_pages <=
+ * HSA_MAX_BANK_PAGES.
+ *
+ *  page_k_table, page_v_table  DEVICE arrays of n_pages device pointers
+ *              (pointer j is page j, as the host tables above).  The host
+ *              does not read them, so their entries are not validated:
+ *              - scoring: a NULL entry is scored from page_kmean[j]; with
+ *                page_kmean NULL as well the page has no mean and scores
+ *                -inf (it is chosen only when fewer than K_p pages have a
+ *                score, lowest id first);
+ *              - gather: a NULL entry among the selected pages contributes
+ *                zeros to the active buffer.
+ *  ws          workspace of ws_bytes >= hsa_workspace_bytes(geom, n_pages),
+ *              which grows with n_pages (per-page partial sums and means).
+ * Ranking: all n_pages scores are sorted on one workgroup (a bitonic sort of
+ * 64-bit keys in LDS), so the selection is the same total order as the host
+ * table calls: higher score, then lower id; NaN as -inf.
+ * Errors: as the host-table calls, with HSA_MAX_BANK_PAGES for the page
+ * count.
+ * ------------------------------------------------------------------------- */
+hsa_rc hsa_score_pages_devtab(const hsa_geom* geom, const void* q, const void* const* page_k_table,
+                              float* page_kmean, int32_t n_pages, float* scores, int32_t* sel_pages,
+                              void* ws, size_t ws_bytes, hsa_stream stream);
+hsa_rc hsa_score_chunk_pages_devtab(const hsa_geom* geom, const void* q, const void* const* page_k_table,
+                                    float* page_kmean, int32_t n_pages, const int32_t* page_chunk,
+                                    const int32_t* sel_chunks, int32_t k_chunks, float* scores,
+                                    int32_t* sel_pages, void* ws, size_t ws_bytes, hsa_stream stream);
+hsa_rc hsa_gather_active_devtab(const hsa_geom* geom, const void* const* page_k_table,
+                                const void* const* page_v_table, int32_t n_pages, const int32_t* sel_pages,
+                                const void* k_cur, const void* v_cur, void* k_act, void* v_act,
+                                float* kblk_mean, hsa_stream stream);
 
 /* ---------------------------------------------------------------------------
  * S3 -- linear branch.  Paper section 3.3, "Linear branch" (output equation);
@@ -410,8 +450,9 @@ hsa_rc hsa_sparse_attn_paged(const hsa_geom* geom, const void* q, const void* co
                              const int32_t* blk_count, const int32_t* blk_idx, float* o_sp, void* ws,
                              size_t ws_bytes, hsa_stream stream, hsa_event ev_begin, hsa_event ev_end);
 
-/* Bytes of workspace every call above needs for this geometry (0 if the
- * geometry is invalid).  One workspace serves all calls on one stream. */
+/* Bytes of workspace every call above needs for this geometry and a bank of
+ * n_pages pages (0 if the geometry is invalid or n_pages exceeds
+ * HSA_MAX_BANK_PAGES).  One workspace serves all calls on one stream. */
 size_t hsa_workspace_bytes(const hsa_geom* geom, int32_t n_pages);
 
 /* Bytes of workspace hsa_linear_branch alone needs (0 if the geometry is

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libhsa_attn.so")
 HSA_F32, HSA_BF16 = 0, 1
 HSA_LIN_REUSE_PROJ, HSA_LIN_PROJ_ONLY = 1, 2
 HSA_MAX_PAGES = 128
+HSA_MAX_BANK_PAGES = 8192
 HSA_MAX_KBLOCKS = 2048
 HSA_MAX_ROWS = 4096
 HSA_MAX_CHUNKS = 4096
@@ -43,6 +44,9 @@ SIGNATURES = {
     "hsa_score_pages": (_i32, [_GP, _vp, ctypes.POINTER(_vp), _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "hsa_score_chunk_pages": (_i32, [_GP, _vp, ctypes.POINTER(_vp), _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _sz,
                                      _vp]),
+    "hsa_score_pages_devtab": (_i32, [_GP, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "hsa_score_chunk_pages_devtab": (_i32, [_GP, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "hsa_gather_active_devtab": (_i32, [_GP, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "hsa_retrieve_chunks": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "hsa_gather_pages": (_i32, [_GP, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp, _vp]),
     "hsa_gather_active": (_i32, [_GP, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp, _vp, _vp,

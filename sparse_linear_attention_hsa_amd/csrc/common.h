@@ -20,9 +20,16 @@ constexpr int kMaxPages = HSA_MAX_PAGES;
 // kZeroPage[lane]).
 __device__ const uint4 kZeroPage[64] = {};
 
-// Page pointer tables travel by value as launch arguments.
+// Page pointer tables: by value as launch arguments (up to HSA_MAX_PAGES
+// pages), or a device array of pointers (up to HSA_MAX_BANK_PAGES).  Kernels
+// take either through at(j).
 struct PageTable {
   const void* p[kMaxPages];
+  __device__ __forceinline__ const void* at(int j) const { return p[j]; }
+};
+struct DevPageTable {
+  const void* const* p;
+  __device__ __forceinline__ const void* at(int j) const { return p[j]; }
 };
 
 // Keys and values read in place from laid-out pages (PAGED kernels): page j

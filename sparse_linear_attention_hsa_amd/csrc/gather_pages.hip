@@ -25,9 +25,9 @@ constexpr int kBatch = 6;  // passes whose loads are in flight together
 
 // NSUB: key blocks per B-token block (1 without intra-chunk keys, where key
 // blocks are B tokens).
-template <typename T, int D, int NSUB>
+template <typename T, int D, int NSUB, typename Tab>
 __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
-    PageTable pk, PageTable pv, int n_pages, const int32_t* __restrict__ sel, const T* __restrict__ k_cur,
+    Tab pk, Tab pv, int n_pages, const int32_t* __restrict__ sel, const T* __restrict__ k_cur,
     const T* __restrict__ v_cur, int H, int Lp, int Kp, int B, int Bk, int L, int nKB,
     T* __restrict__ k_act, T* __restrict__ v_act, float* __restrict__ kblk_mean) {
   constexpr int E = Vec<T>::N;
@@ -48,8 +48,8 @@ __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
     const int p = blockIdx.x / bpp, blk = blockIdx.x % bpp;
     int page = sel ? sel[p] : p;  // no selection: the pages in table order
     page = page < 0 ? 0 : (page >= n_pages ? n_pages - 1 : page);
-    ksrc = reinterpret_cast<const T*>(pk.p[page]);
-    vsrc = reinterpret_cast<const T*>(pv.p[page]);
+    ksrc = reinterpret_cast<const T*>(pk.at(page));
+    vsrc = reinterpret_cast<const T*>(pv.at(page));
     tok0 = (size_t)blk * B;
     act0 = (size_t)p * Lp + tok0;
   } else {  // the chunk's own tokens, after the Kp pages
@@ -62,6 +62,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
   const int t = threadIdx.x;
   const int ch = t % CPR, r0 = t / CPR;
   const int nsub = B / Bk;
+  const bool present = ksrc != nullptr && vsrc != nullptr;  // uniform: a NULL page of a device table gathers zeros
 
   float acc[NSUB][E];
 #pragma unroll
@@ -76,8 +77,12 @@ __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
       const int row = (base + u) * RPP + r0;
       if (base + u < npass && row < B) {
         const size_t off = ((tok0 + row) * H + h) * D + ch * E;
-        kv[u] = ld16_nt(ksrc + off);  // pages are read once: streaming loads
-        vv[u] = ld16_nt(vsrc + off);
+        if (present) {
+          kv[u] = ld16_nt(ksrc + off);  // pages are read once: streaming loads
+          vv[u] = ld16_nt(vsrc + off);
+        } else {
+          kv[u] = vv[u] = make_uint4(0u, 0u, 0u, 0u);
+        }
       }
     }
 #pragma unroll
@@ -147,8 +152,8 @@ __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
   }
 }
 
-template <typename T, int D>
-void launch_gather(const Dims& s, const PageTable& pk, const PageTable& pv, int n_pages, const int32_t* sel,
+template <typename T, int D, typename Tab>
+void launch_gather(const Dims& s, const Tab& pk, const Tab& pv, int n_pages, const int32_t* sel,
                    const void* k_cur, const void* v_cur, void* k_act, void* v_act, float* kblk_mean,
                    hipStream_t st) {
   constexpr int E = Vec<T>::N;
@@ -156,10 +161,10 @@ void launch_gather(const Dims& s, const PageTable& pk, const PageTable& pv, int 
   const size_t smem = (size_t)s.B * (D + E) * sizeof(T) + (size_t)kGatherThreads * E * sizeof(float);
   dim3 grid(s.Kp * (s.Lp / s.B) + (s.split ? s.Lq / s.B : 0), s.H);
   static_assert(HSA_MAX_INTRA_SPLIT == 4, "one instantiation per key blocks per block");
-  auto kern = nsub == 1   ? gather_block_kernel<T, D, 1>
-              : nsub == 2 ? gather_block_kernel<T, D, 2>
-              : nsub == 3 ? gather_block_kernel<T, D, 3>
-                          : gather_block_kernel<T, D, 4>;
+  auto kern = nsub == 1   ? gather_block_kernel<T, D, 1, Tab>
+              : nsub == 2 ? gather_block_kernel<T, D, 2, Tab>
+              : nsub == 3 ? gather_block_kernel<T, D, 3, Tab>
+                          : gather_block_kernel<T, D, 4, Tab>;
   if (smem > 65536)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)smem);
@@ -182,7 +187,7 @@ __global__ __launch_bounds__(256) void gather_block_means_kernel(PageTable pm, i
   const int p = j / bpp, lb = j % bpp;
   int page = sel[p];
   page = page < 0 ? 0 : (page >= n_pages ? n_pages - 1 : page);
-  kblk_mean[i] = reinterpret_cast<const float*>(pm.p[page])[((size_t)h * bpp + lb) * D + e];
+  kblk_mean[i] = reinterpret_cast<const float*>(pm.at(page))[((size_t)h * bpp + lb) * D + e];
 }
 
 }  // namespace
@@ -238,18 +243,44 @@ extern "C" hsa_rc hsa_gather_block_means(const hsa_geom* geom, const float* cons
   return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
 }
 
+namespace hsa {
+namespace {
+
+template <typename Tab>
+void gather_any(const Dims& s, const Tab& pk, const Tab& pv, int n_pages, const int32_t* sel, const void* k_cur,
+                const void* v_cur, void* k_act, void* v_act, float* kblk_mean, hipStream_t st) {
+  if (s.bf16) {
+    if (s.d == 128) launch_gather<bf16_t, 128>(s, pk, pv, n_pages, sel, k_cur, v_cur, k_act, v_act, kblk_mean, st);
+    else launch_gather<bf16_t, 64>(s, pk, pv, n_pages, sel, k_cur, v_cur, k_act, v_act, kblk_mean, st);
+  } else {
+    if (s.d == 128) launch_gather<float, 128>(s, pk, pv, n_pages, sel, k_cur, v_cur, k_act, v_act, kblk_mean, st);
+    else launch_gather<float, 64>(s, pk, pv, n_pages, sel, k_cur, v_cur, k_act, v_act, kblk_mean, st);
+  }
+}
+
+hsa_rc gather_checks(const hsa_geom* geom, Dims* s, const void* page_k, const void* page_v, int32_t n_pages,
+                     int32_t max_pages, const int32_t* sel_pages, const void* k_cur, const void* v_cur, void* k_act,
+                     void* v_act) {
+  hsa_rc rc = derive(geom, s);
+  if (rc != HSA_OK) return rc;
+  if (!page_k || !page_v || !sel_pages || !k_act || !v_act) return HSA_ERR_NULL_ARG;
+  if (s->split && (!k_cur || !v_cur)) return HSA_ERR_NULL_ARG;
+  if (!s->split && (k_cur || v_cur)) return HSA_ERR_BAD_PARAM;
+  if (n_pages < 1 || n_pages > max_pages || s->Kp > n_pages) return HSA_ERR_BAD_PARAM;
+  return HSA_OK;
+}
+
+}  // namespace
+}  // namespace hsa
+
 extern "C" hsa_rc hsa_gather_active(const hsa_geom* geom, const void* const* page_k, const void* const* page_v,
                                     int32_t n_pages, const int32_t* sel_pages, const void* k_cur,
                                     const void* v_cur, void* k_act, void* v_act, float* kblk_mean,
                                     hsa_stream stream) {
   using namespace hsa;
   Dims s;
-  hsa_rc rc = derive(geom, &s);
+  hsa_rc rc = gather_checks(geom, &s, page_k, page_v, n_pages, HSA_MAX_PAGES, sel_pages, k_cur, v_cur, k_act, v_act);
   if (rc != HSA_OK) return rc;
-  if (!page_k || !page_v || !sel_pages || !k_act || !v_act) return HSA_ERR_NULL_ARG;
-  if (s.split && (!k_cur || !v_cur)) return HSA_ERR_NULL_ARG;
-  if (!s.split && (k_cur || v_cur)) return HSA_ERR_BAD_PARAM;
-  if (n_pages < 1 || n_pages > HSA_MAX_PAGES || s.Kp > n_pages) return HSA_ERR_BAD_PARAM;
   PageTable pk, pv;
   for (int j = 0; j < kMaxPages; ++j) pk.p[j] = pv.p[j] = nullptr;
   for (int j = 0; j < n_pages; ++j) {
@@ -257,14 +288,22 @@ extern "C" hsa_rc hsa_gather_active(const hsa_geom* geom, const void* const* pag
     pk.p[j] = page_k[j];
     pv.p[j] = page_v[j];
   }
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (s.bf16) {
-    if (s.d == 128) launch_gather<bf16_t, 128>(s, pk, pv, n_pages, sel_pages, k_cur, v_cur, k_act, v_act, kblk_mean, st);
-    else launch_gather<bf16_t, 64>(s, pk, pv, n_pages, sel_pages, k_cur, v_cur, k_act, v_act, kblk_mean, st);
-  } else {
-    if (s.d == 128) launch_gather<float, 128>(s, pk, pv, n_pages, sel_pages, k_cur, v_cur, k_act, v_act, kblk_mean, st);
-    else launch_gather<float, 64>(s, pk, pv, n_pages, sel_pages, k_cur, v_cur, k_act, v_act, kblk_mean, st);
-  }
+  gather_any(s, pk, pv, n_pages, sel_pages, k_cur, v_cur, k_act, v_act, kblk_mean,
+             reinterpret_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
+}
+
+extern "C" hsa_rc hsa_gather_active_devtab(const hsa_geom* geom, const void* const* page_k_table,
+                                           const void* const* page_v_table, int32_t n_pages,
+                                           const int32_t* sel_pages, const void* k_cur, const void* v_cur,
+                                           void* k_act, void* v_act, float* kblk_mean, hsa_stream stream) {
+  using namespace hsa;
+  Dims s;
+  hsa_rc rc = gather_checks(geom, &s, page_k_table, page_v_table, n_pages, HSA_MAX_BANK_PAGES, sel_pages, k_cur,
+                            v_cur, k_act, v_act);
+  if (rc != HSA_OK) return rc;
+  gather_any(s, DevPageTable{page_k_table}, DevPageTable{page_v_table}, n_pages, sel_pages, k_cur, v_cur, k_act,
+             v_act, kblk_mean, reinterpret_cast<hipStream_t>(stream));
   return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
 }
 

@@ -54,7 +54,10 @@ hsa_rc derive(const hsa_geom* g, Dims* o) {
 ScorePlan score_plan(const Dims& s, int n_pages, bool few_pages) {
   ScorePlan p;
   const int target = 640;
-  int pc = std::max(1, std::min(cdiv(s.Lp, 16), few_pages ? 64 : cdiv(target, std::max(1, n_pages))));
+  // chunk-restricted scoring reads few pages: each is split into up to 64
+  // chunks, fewer in large banks so the partials stay small
+  const int few = std::max(1, std::min(64, 8192 / std::max(1, n_pages)));
+  int pc = std::max(1, std::min(cdiv(s.Lp, 16), few_pages ? few : cdiv(target, std::max(1, n_pages))));
   p.page_rows = cdiv(s.Lp, pc);
   p.page_chunks = cdiv(s.Lp, p.page_rows);
   int qc = std::max(1, std::min(cdiv(s.Lq, 16), 128));
@@ -149,7 +152,7 @@ size_t hsa_workspace_bytes(const hsa_geom* geom, int32_t n_pages) {
   hsa::Dims s;
   if (hsa::derive(geom, &s) != HSA_OK) return 0;
   if (n_pages < 1) n_pages = 1;
-  if (n_pages > HSA_MAX_PAGES) return 0;
+  if (n_pages > HSA_MAX_BANK_PAGES) return 0;
   return hsa::ws_layout(s, n_pages).total;
 }
 

@@ -51,9 +51,9 @@ __device__ __forceinline__ bool candidate(const ChunkFilter& f, int j) {
   return in;
 }
 
-template <typename T>
+template <typename T, typename Tab>
 __global__ __launch_bounds__(kScoreThreads) void score_partial_kernel(
-    const T* __restrict__ q, PageTable pages, ChunkFilter filt, int n_pages, int Lp, int Lq, int cpr,
+    const T* __restrict__ q, Tab pages, ChunkFilter filt, int n_pages, int Lp, int Lq, int cpr,
     int page_chunks, int page_rows, int q_rows, int mcols, int mpar, float* __restrict__ partial) {
   constexpr int E = Vec<T>::N;
   __shared__ float red[kScoreThreads * E];
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_partial_kernel(
   if (unit < n_pages * page_chunks) {
     const int j = unit / page_chunks, c = unit % page_chunks;
     if (!candidate(filt, j)) return;  // a page outside the chosen chunks is not read
-    base = reinterpret_cast<const T*>(pages.p[j]);
+    base = reinterpret_cast<const T*>(pages.at(j));
     r0 = c * page_rows;
     r1 = min(Lp, r0 + page_rows);
   } else {
@@ -127,8 +127,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_partial_kernel(
 // chunk partials u = s, s+4, ... of its column, and the four sums are added
 // in a fixed order (bitwise reproducible), divided by the token count.
 constexpr int kMeanCols = 64;
+template <typename Tab>
 __global__ __launch_bounds__(kScoreThreads) void score_means_kernel(
-    const float* __restrict__ partial, PageTable pages, ChunkFilter filt, int n_pages, int page_chunks,
+    const float* __restrict__ partial, Tab pages, ChunkFilter filt, int n_pages, int page_chunks,
     int q_chunks, int hd, int Lp, int Lq, float* __restrict__ page_kmean, float* __restrict__ kbar,
     float* __restrict__ qbar) {
   constexpr int kGroups = kScoreThreads / kMeanCols;
@@ -139,9 +140,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_means_kernel(
   const int c = blockIdx.y * kMeanCols + cl;
   const bool is_q = j == n_pages;
   if (!is_q && !candidate(filt, j)) return;  // scored -inf by the ranking kernel
-  const bool resident = is_q || pages.p[j] != nullptr;  // uniform
+  const bool resident = is_q || pages.at(j) != nullptr;  // uniform
   if (!resident) {
-    if (grp == 0 && c < hd) kbar[(size_t)j * hd + c] = page_kmean[(size_t)j * hd + c];
+    // the cached mean; with no cache the page has no mean (NaN: scored -inf)
+    if (grp == 0 && c < hd) kbar[(size_t)j * hd + c] = page_kmean ? page_kmean[(size_t)j * hd + c] : __builtin_nanf("");
     return;
   }
   const int n = is_q ? q_chunks : page_chunks;
@@ -172,24 +174,80 @@ __global__ __launch_bounds__(kScoreThreads) void score_means_kernel(
   }
 }
 
-constexpr int kTopkThreads = 1024;
+constexpr int kRankThreads = 1024;
+constexpr int kMaxBank = HSA_MAX_BANK_PAGES;
+constexpr int kRankPer = kMaxBank / kRankThreads;  // sort positions per thread
+static_assert(kMaxBank % kRankThreads == 0, "whole positions per thread");
+static_assert(kMaxBank <= (1 << 13), "page ids take 13 bits of the sort key");
+static_assert(HSA_MAX_CHUNKS <= (1 << 12), "chunk ids take 12 bits of the sort key");
 
-// Scores and the top-K_p set.  One wave per page computes the dot product in
-// a fixed order; page j is selected iff fewer than K_p pages rank above it
-// (higher score, or equal score and lower id); the selected ids are written
-// in ascending order.
+// Order-preserving code of a score, inverted so that ascending codes are
+// descending scores; -0 counts as +0, so equal scores tie by id.
+__device__ __forceinline__ uint64_t desc_code(float a) {
+  if (a == 0.f) a = 0.f;
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (uint64_t)(~ord);
+}
+
+// Ascending bitonic sort of n2 (a power of two, >= 2) keys in LDS by the
+// whole workgroup: every stage compares disjoint pairs (lo, lo + j).
+__device__ void sort_keys(uint64_t* key, int n2) {
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n2 / 2; i += kRankThreads) {
+        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+        const int hi = lo | j;
+        const bool up = (lo & k) == 0;
+        const uint64_t a = key[lo], b = key[hi];
+        if ((a > b) == up) {
+          key[lo] = b;
+          key[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Exclusive prefix sum over the workgroup's 1024 threads (buf holds 16 ints).
+__device__ int excl_scan_1024(int v, int* buf) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) buf[wave] = x;
+  __syncthreads();
+  int before = 0;
+  for (int k = 0; k < wave; ++k) before += buf[k];
+  __syncthreads();
+  return x - v + before;
+}
+
+// Scores and the top-K_p set of up to HSA_MAX_BANK_PAGES pages.  One wave
+// per page computes the dot product in a fixed order; the pages are then
+// sorted by one 64-bit key (score descending, then id ascending) and the
+// first K_p are chosen; their ids are written in ascending order.
 // With a chunk filter the order has three tiers: the best K_p / k pages of
 // each chosen chunk, the other pages of the chosen chunks, then every other
-// page (score -inf, by id); within a tier, higher score then lower id.
-__global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
+// page (score -inf, by id); within a tier, higher score then lower id.  A
+// first sort by (candidate, chunk, score, id) gives each candidate its rank
+// inside its chunk, hence its tier; a second sort by (tier, score, id)
+// gives the order.
+__global__ __launch_bounds__(kRankThreads) void score_rank_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, ChunkFilter filt, int n_pages, int hd,
     float scale, int kp, float* __restrict__ scores, int32_t* __restrict__ sel) {
-  __shared__ float alpha[kMaxPages];
-  __shared__ int tier[kMaxPages];
-  __shared__ int chunk_of[kMaxPages];
-  __shared__ int chosen[kMaxPages];
+  __shared__ uint64_t key[kMaxBank];
+  __shared__ unsigned char chosen[kMaxBank];
+  __shared__ int buf[kRankThreads / kWave];
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  for (int j = w; j < n_pages; j += kTopkThreads / kWave) {
+  const bool chunked = filt.page_chunk != nullptr;
+  int n2 = 2;
+  while (n2 < n_pages) n2 <<= 1;
+  for (int j = w; j < n_pages; j += kRankThreads / kWave) {
     const bool cand = candidate(filt, j);  // wave-uniform
     float s = 0.f;
     if (cand) {
@@ -203,43 +261,65 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
       for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
     }
     if (lane == 0) {
-      // a NaN score (NaN or Inf in the inputs) ranks as -inf, so the order
-      // stays total and exactly K_p pages are chosen
-      const float a = s * scale;
-      alpha[j] = cand && !__builtin_isnan(a) ? a : -INFINITY;
-      tier[j] = cand ? 1 : 2;
-      chunk_of[j] = filt.page_chunk ? filt.page_chunk[j] : 0;
+      // a NaN score (NaN or Inf in the inputs, or a page with neither keys
+      // nor a cached mean) ranks as -inf, so the order stays total and
+      // exactly K_p pages are chosen
+      const float a0 = s * scale;
+      const float a = cand && !__builtin_isnan(a0) ? a0 : -INFINITY;
+      scores[j] = a;
+      const uint64_t code = desc_code(a) << 13 | (uint64_t)j;
+      // chunk ids are below HSA_MAX_CHUNKS (12 bits); the mask keeps the key well formed
+      key[j] = chunked ? ((uint64_t)(cand ? 0 : 1) << 57 | (uint64_t)(filt.page_chunk[j] & 0xFFF) << 45 | code)
+                       : code;
     }
   }
+  for (int j = n_pages + (int)threadIdx.x; j < n2; j += kRankThreads) key[j] = ~0ull;
   __syncthreads();
-  const int j = threadIdx.x;
-  auto above = [&](int i, int jj) {  // page i ranks above page jj (same tier)
-    return alpha[i] > alpha[jj] || (alpha[i] == alpha[jj] && i < jj);
-  };
-  if (filt.page_chunk != nullptr) {
-    // tier 0: a chosen chunk's best K_p / k pages
+  sort_keys(key, n2);
+  if (chunked) {
     const int share = kp / filt.k;
-    int t = 2;
-    if (j < n_pages && tier[j] == 1) {
-      int r = 0;
-      for (int i = 0; i < n_pages; ++i) r += tier[i] != 2 && chunk_of[i] == chunk_of[j] && above(i, j);
-      t = r < share ? 0 : 1;
+    uint64_t nk[kRankPer];
+#pragma unroll
+    for (int m = 0; m < kRankPer; ++m) {
+      const int i = (int)threadIdx.x + m * kRankThreads;
+      nk[m] = ~0ull;
+      if (i < n_pages) {
+        const uint64_t kk = key[i];
+        const uint64_t grp = kk >> 45;  // (not a candidate, chunk)
+        int lo = 0, hi = i;             // first position of the group
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if ((key[mid] >> 45) < grp) lo = mid + 1;
+          else hi = mid;
+        }
+        const uint64_t tier = (kk >> 57) ? 2 : (i - lo < share ? 0 : 1);
+        nk[m] = tier << 45 | (kk & ((1ull << 45) - 1));
+      }
     }
     __syncthreads();
-    if (j < n_pages) tier[j] = t;
+#pragma unroll
+    for (int m = 0; m < kRankPer; ++m) {
+      const int i = (int)threadIdx.x + m * kRankThreads;
+      if (i < n_pages) key[i] = nk[m];
+    }
     __syncthreads();
+    sort_keys(key, n2);
   }
-  if (j < n_pages) {
-    int rank = 0;
-    for (int i = 0; i < n_pages; ++i) rank += tier[i] < tier[j] || (tier[i] == tier[j] && above(i, j));
-    chosen[j] = rank < kp;
-    scores[j] = alpha[j];
-  }
+  for (int j = threadIdx.x; j < n_pages; j += kRankThreads) chosen[j] = 0;
   __syncthreads();
-  if (j < n_pages && chosen[j]) {
-    int pos = 0;
-    for (int i = 0; i < j; ++i) pos += chosen[i];
-    if (pos < kp) sel[pos] = j;
+  for (int i = threadIdx.x; i < kp; i += kRankThreads) chosen[(int)(key[i] & 0x1FFFull)] = 1;
+  __syncthreads();
+  // the chosen ids in ascending order: thread t owns a contiguous id range
+  const int per = (n_pages + kRankThreads - 1) / kRankThreads;
+  const int j0 = (int)threadIdx.x * per, j1 = min(n_pages, j0 + per);
+  int cnt = 0;
+  for (int j = j0; j < j1; ++j) cnt += chosen[j];
+  int pos = excl_scan_1024(cnt, buf);
+  for (int j = j0; j < j1; ++j) {
+    if (chosen[j]) {
+      if (pos < kp) sel[pos] = j;
+      ++pos;
+    }
   }
 }
 
@@ -300,8 +380,8 @@ __global__ __launch_bounds__(kRetrThreads) void retrieve_chunks_kernel(
   }
 }
 
-template <typename T>
-void launch_score(const Dims& s, const void* q, const PageTable& tab, const ChunkFilter& filt, int n_pages,
+template <typename T, typename Tab>
+void launch_score(const Dims& s, const void* q, const Tab& tab, const ChunkFilter& filt, int n_pages,
                   float* page_kmean, float* scores, int32_t* sel, char* ws, const WsLayout& w, hipStream_t st) {
   const ScorePlan sp = score_plan(s, n_pages, filt.page_chunk != nullptr);
   const int cpr = s.H * s.d * s.esize / 16;
@@ -310,15 +390,15 @@ void launch_score(const Dims& s, const void* q, const PageTable& tab, const Chun
   float* partial = reinterpret_cast<float*>(ws + w.score_partial);
   float* qbar = reinterpret_cast<float*>(ws + w.score_qbar);
   float* kbar = reinterpret_cast<float*>(ws + w.score_kbar);
-  hipLaunchKernelGGL(score_partial_kernel<T>, grid, dim3(kScoreThreads), 0, st,
+  hipLaunchKernelGGL((score_partial_kernel<T, Tab>), grid, dim3(kScoreThreads), 0, st,
                      reinterpret_cast<const T*>(q), tab, filt, n_pages, s.Lp, s.Lq, cpr, sp.page_chunks,
                      sp.page_rows, sp.q_rows, m.cols, m.par, partial);
   const int hd = s.H * s.d;
-  hipLaunchKernelGGL(score_means_kernel, dim3(n_pages + 1, (hd + kMeanCols - 1) / kMeanCols), dim3(kScoreThreads),
+  hipLaunchKernelGGL(score_means_kernel<Tab>, dim3(n_pages + 1, (hd + kMeanCols - 1) / kMeanCols), dim3(kScoreThreads),
                      0, st, partial, tab, filt, n_pages, sp.page_chunks, sp.q_chunks, hd, s.Lp, s.Lq, page_kmean,
                      kbar, qbar);
   const float scale = 1.f / ((float)s.H * sqrtf((float)s.d));
-  hipLaunchKernelGGL(score_topk_kernel, dim3(1), dim3(kTopkThreads), 0, st, qbar, kbar, filt, n_pages, hd,
+  hipLaunchKernelGGL(score_rank_kernel, dim3(1), dim3(kRankThreads), 0, st, qbar, kbar, filt, n_pages, hd,
                      scale, s.Kp, scores, sel);
 }
 
@@ -328,29 +408,51 @@ void launch_score(const Dims& s, const void* q, const PageTable& tab, const Chun
 namespace hsa {
 namespace {
 
-hsa_rc score_entry(const hsa_geom* geom, const void* q, const void* const* page_k, float* page_kmean,
+// Host table (devtab = false): n_pages <= HSA_MAX_PAGES, every entry checked
+// here.  Device table (devtab = true): n_pages <= HSA_MAX_BANK_PAGES, entries
+// read by the kernels.
+hsa_rc score_entry(const hsa_geom* geom, const void* q, const void* const* page_k, bool devtab, float* page_kmean,
                    int32_t n_pages, const ChunkFilter& filt, float* scores, int32_t* sel_pages, void* ws,
                    size_t ws_bytes, hsa_stream stream) {
   Dims s;
   hsa_rc rc = derive(geom, &s);
   if (rc != HSA_OK) return rc;
   if (!q || !page_k || !scores || !sel_pages) return HSA_ERR_NULL_ARG;
-  if (n_pages < 1 || n_pages > HSA_MAX_PAGES || s.Kp > n_pages) return HSA_ERR_BAD_PARAM;
+  if (n_pages < 1 || n_pages > (devtab ? HSA_MAX_BANK_PAGES : HSA_MAX_PAGES) || s.Kp > n_pages)
+    return HSA_ERR_BAD_PARAM;
   PageTable tab;
-  for (int j = 0; j < kMaxPages; ++j) tab.p[j] = nullptr;
-  for (int j = 0; j < n_pages; ++j) {
-    tab.p[j] = page_k[j];
-    if (!page_k[j] && !page_kmean) return HSA_ERR_NULL_ARG;
+  if (!devtab) {
+    for (int j = 0; j < kMaxPages; ++j) tab.p[j] = nullptr;
+    for (int j = 0; j < n_pages; ++j) {
+      tab.p[j] = page_k[j];
+      if (!page_k[j] && !page_kmean) return HSA_ERR_NULL_ARG;
+    }
   }
   const WsLayout w = ws_layout(s, n_pages);
   if (!ws || ws_bytes < w.total) return HSA_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* wsb = static_cast<char*>(ws);
-  if (s.bf16)
-    launch_score<bf16_t>(s, q, tab, filt, n_pages, page_kmean, scores, sel_pages, wsb, w, st);
-  else
-    launch_score<float>(s, q, tab, filt, n_pages, page_kmean, scores, sel_pages, wsb, w, st);
+  const DevPageTable dtab{page_k};
+  if (devtab) {
+    if (s.bf16) launch_score<bf16_t>(s, q, dtab, filt, n_pages, page_kmean, scores, sel_pages, wsb, w, st);
+    else launch_score<float>(s, q, dtab, filt, n_pages, page_kmean, scores, sel_pages, wsb, w, st);
+  } else {
+    if (s.bf16) launch_score<bf16_t>(s, q, tab, filt, n_pages, page_kmean, scores, sel_pages, wsb, w, st);
+    else launch_score<float>(s, q, tab, filt, n_pages, page_kmean, scores, sel_pages, wsb, w, st);
+  }
   return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
+}
+
+hsa_rc chunk_entry(const hsa_geom* geom, const void* q, const void* const* page_k, bool devtab, float* page_kmean,
+                   int32_t n_pages, const int32_t* page_chunk, const int32_t* sel_chunks, int32_t k_chunks,
+                   float* scores, int32_t* sel_pages, void* ws, size_t ws_bytes, hsa_stream stream) {
+  if (!page_chunk || !sel_chunks) return HSA_ERR_NULL_ARG;
+  Dims s;
+  hsa_rc rc = derive(geom, &s);
+  if (rc != HSA_OK) return rc;
+  if (k_chunks < 1 || k_chunks > s.Kp || s.Kp % k_chunks != 0) return HSA_ERR_BAD_PARAM;
+  return score_entry(geom, q, page_k, devtab, page_kmean, n_pages, ChunkFilter{page_chunk, sel_chunks, k_chunks},
+                     scores, sel_pages, ws, ws_bytes, stream);
 }
 
 }  // namespace
@@ -359,22 +461,31 @@ hsa_rc score_entry(const hsa_geom* geom, const void* q, const void* const* page_
 extern "C" hsa_rc hsa_score_pages(const hsa_geom* geom, const void* q, const void* const* page_k,
                                   float* page_kmean, int32_t n_pages, float* scores, int32_t* sel_pages,
                                   void* ws, size_t ws_bytes, hsa_stream stream) {
-  return hsa::score_entry(geom, q, page_k, page_kmean, n_pages, hsa::ChunkFilter{nullptr, nullptr, 1}, scores,
+  return hsa::score_entry(geom, q, page_k, false, page_kmean, n_pages, hsa::ChunkFilter{nullptr, nullptr, 1}, scores,
                           sel_pages, ws, ws_bytes, stream);
+}
+
+extern "C" hsa_rc hsa_score_pages_devtab(const hsa_geom* geom, const void* q, const void* const* page_k_table,
+                                         float* page_kmean, int32_t n_pages, float* scores, int32_t* sel_pages,
+                                         void* ws, size_t ws_bytes, hsa_stream stream) {
+  return hsa::score_entry(geom, q, page_k_table, true, page_kmean, n_pages, hsa::ChunkFilter{nullptr, nullptr, 1},
+                          scores, sel_pages, ws, ws_bytes, stream);
 }
 
 extern "C" hsa_rc hsa_score_chunk_pages(const hsa_geom* geom, const void* q, const void* const* page_k,
                                         float* page_kmean, int32_t n_pages, const int32_t* page_chunk,
                                         const int32_t* sel_chunks, int32_t k_chunks, float* scores,
                                         int32_t* sel_pages, void* ws, size_t ws_bytes, hsa_stream stream) {
-  using namespace hsa;
-  if (!page_chunk || !sel_chunks) return HSA_ERR_NULL_ARG;
-  Dims s;
-  hsa_rc rc = derive(geom, &s);
-  if (rc != HSA_OK) return rc;
-  if (k_chunks < 1 || k_chunks > s.Kp || s.Kp % k_chunks != 0) return HSA_ERR_BAD_PARAM;
-  return score_entry(geom, q, page_k, page_kmean, n_pages, ChunkFilter{page_chunk, sel_chunks, k_chunks}, scores,
-                     sel_pages, ws, ws_bytes, stream);
+  return hsa::chunk_entry(geom, q, page_k, false, page_kmean, n_pages, page_chunk, sel_chunks, k_chunks, scores,
+                          sel_pages, ws, ws_bytes, stream);
+}
+
+extern "C" hsa_rc hsa_score_chunk_pages_devtab(const hsa_geom* geom, const void* q, const void* const* page_k_table,
+                                               float* page_kmean, int32_t n_pages, const int32_t* page_chunk,
+                                               const int32_t* sel_chunks, int32_t k_chunks, float* scores,
+                                               int32_t* sel_pages, void* ws, size_t ws_bytes, hsa_stream stream) {
+  return hsa::chunk_entry(geom, q, page_k_table, true, page_kmean, n_pages, page_chunk, sel_chunks, k_chunks,
+                          scores, sel_pages, ws, ws_bytes, stream);
 }
 
 extern "C" hsa_rc hsa_retrieve_chunks(const float* prompt, const float* chunk_prompts, int32_t n_chunks,

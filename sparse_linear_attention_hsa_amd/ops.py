@@ -80,6 +80,21 @@ def _table(pages: Sequence[Optional[torch.Tensor]]):
     return arr
 
 
+class DeviceTable:
+    """A page pointer table in device memory (the *_devtab calls): entry j is
+    page j's device address, 0 for a page without one.  Holds the pages so
+    their memory stays alive.  Built once per bank (one host-to-device copy),
+    not per step."""
+
+    def __init__(self, pages: Sequence[Optional[torch.Tensor]], device="cuda"):
+        self.pages = list(pages)
+        ptrs = [0 if t is None else t.data_ptr() for t in self.pages]
+        self.ptrs = torch.tensor(ptrs, dtype=torch.int64).to(device)
+
+    def __len__(self) -> int:
+        return len(self.pages)
+
+
 def hsa_workspace_bytes(geom: Geom, n_pages: int) -> int:
     return int(lib().hsa_workspace_bytes(ctypes.byref(geom), n_pages))
 
@@ -93,6 +108,12 @@ def hsa_geom_check(geom: Geom) -> int:
 
 
 def hsa_score_pages(geom, q, pages_k, page_kmean, scores, sel_pages, ws, stream=None):
+    """pages_k: a list of page tensors (host table) or a DeviceTable."""
+    if isinstance(pages_k, DeviceTable):
+        check("hsa_score_pages_devtab", lib().hsa_score_pages_devtab(
+            ctypes.byref(geom), _p(q), _p(pages_k.ptrs), _p(page_kmean), len(pages_k), _p(scores), _p(sel_pages),
+            _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+        return
     check("hsa_score_pages", lib().hsa_score_pages(
         ctypes.byref(geom), _p(q), _table(pages_k), _p(page_kmean), len(pages_k), _p(scores), _p(sel_pages),
         _p(ws), ws.numel() * ws.element_size(), _s(stream)))
@@ -107,6 +128,12 @@ def hsa_retrieve_chunks(prompt, chunk_prompts, k_chunks, sims, sel_chunks, strea
 
 def hsa_score_chunk_pages(geom, q, pages_k, page_kmean, page_chunk, sel_chunks, scores, sel_pages, ws,
                           stream=None):
+    if isinstance(pages_k, DeviceTable):
+        check("hsa_score_chunk_pages_devtab", lib().hsa_score_chunk_pages_devtab(
+            ctypes.byref(geom), _p(q), _p(pages_k.ptrs), _p(page_kmean), len(pages_k), _p(page_chunk),
+            _p(sel_chunks), sel_chunks.numel(), _p(scores), _p(sel_pages), _p(ws), ws.numel() * ws.element_size(),
+            _s(stream)))
+        return
     check("hsa_score_chunk_pages", lib().hsa_score_chunk_pages(
         ctypes.byref(geom), _p(q), _table(pages_k), _p(page_kmean), len(pages_k), _p(page_chunk),
         _p(sel_chunks), sel_chunks.numel(), _p(scores), _p(sel_pages), _p(ws), ws.numel() * ws.element_size(),
@@ -114,6 +141,8 @@ def hsa_score_chunk_pages(geom, q, pages_k, page_kmean, page_chunk, sel_chunks, 
 
 
 def hsa_gather_pages(geom, pages_k, pages_v, sel_pages, k_act, v_act, kblk_mean=None, stream=None):
+    if isinstance(pages_k, DeviceTable):
+        return hsa_gather_active(geom, pages_k, pages_v, sel_pages, None, None, k_act, v_act, kblk_mean, stream)
     check("hsa_gather_pages", lib().hsa_gather_pages(
         ctypes.byref(geom), _table(pages_k), _table(pages_v), len(pages_k), _p(sel_pages), _p(k_act), _p(v_act),
         _p(kblk_mean), _s(stream)))
@@ -122,7 +151,13 @@ def hsa_gather_pages(geom, pages_k, pages_v, sel_pages, k_act, v_act, kblk_mean=
 def hsa_gather_active(geom, pages_k, pages_v, sel_pages, k_cur, v_cur, k_act, v_act, kblk_mean=None,
                       stream=None):
     """k_cur / v_cur: the chunk's own [Lq][H][d] keys and values (None
-    without intra-chunk keys)."""
+    without intra-chunk keys).  pages_k / pages_v: lists (host tables) or
+    DeviceTables."""
+    if isinstance(pages_k, DeviceTable):
+        check("hsa_gather_active_devtab", lib().hsa_gather_active_devtab(
+            ctypes.byref(geom), _p(pages_k.ptrs), _p(pages_v.ptrs), len(pages_k), _p(sel_pages), _p(k_cur),
+            _p(v_cur), _p(k_act), _p(v_act), _p(kblk_mean), _s(stream)))
+        return
     check("hsa_gather_active", lib().hsa_gather_active(
         ctypes.byref(geom), _table(pages_k), _table(pages_v), len(pages_k), _p(sel_pages), _p(k_cur), _p(v_cur),
         _p(k_act), _p(v_act), _p(kblk_mean), _s(stream)))

@@ -24,7 +24,7 @@ from typing import Optional, Sequence
 import torch
 
 from . import ops
-from ._lib import HSA_LIN_REUSE_PROJ
+from ._lib import HSA_LIN_REUSE_PROJ, HSA_MAX_PAGES
 from .ops import Dims, Geom
 
 
@@ -60,13 +60,24 @@ class HsaStep:
         # prompt-level retrieval outputs (sized on first use)
         self.chunk_sims: Optional[torch.Tensor] = None
         self.sel_chunks: Optional[torch.Tensor] = None
+        self._null_table: Optional[ops.DeviceTable] = None
 
     # individual stages --------------------------------------------------
-    def score(self, q, pages_k: Sequence[Optional[torch.Tensor]], stream=None, use_cache: bool = False):
+    def score(self, q, pages_k, stream=None, use_cache: bool = False):
         """use_cache: score every page from the page index (page_kmean,
-        filled by index_pages) instead of reading its keys."""
-        pages = [None] * self.n_pages if use_cache else pages_k
+        filled by index_pages) instead of reading its keys.  pages_k: a list
+        of page tensors, or an ops.DeviceTable (banks beyond HSA_MAX_PAGES)."""
+        pages = self.no_pages() if use_cache else pages_k
         ops.hsa_score_pages(self.geom, q, pages, self.page_kmean, self.scores, self.sel_pages, self.ws, stream)
+
+    def no_pages(self):
+        """A page table of NULL entries (every page scored from the page
+        index): a host list, or a device table for banks beyond HSA_MAX_PAGES."""
+        if self.n_pages <= HSA_MAX_PAGES:
+            return [None] * self.n_pages
+        if self._null_table is None:
+            self._null_table = ops.DeviceTable([None] * self.n_pages, self.k_act.device)
+        return self._null_table
 
     def retrieve(self, q, pages_k, chunks, stream=None):
         """Stage 1 and page scoring inside the retrieved chunks (WorldAttention
@@ -147,7 +158,7 @@ class HsaStep:
         the pages in place, then the fusion."""
         kp, vp, bm = prepared
         main = torch.cuda.current_stream() if stream is None else stream
-        self.score(q, [None] * self.n_pages, main, use_cache=True)
+        self.score(q, None, main, use_cache=True)
         ops.hsa_gather_block_means(self.geom, bm, self.sel_pages, self.kblk_mean, main)
         side = self.side if concurrent else main
         if concurrent:
@@ -179,7 +190,7 @@ class HsaStep:
         intra-chunk keys)."""
         main = torch.cuda.current_stream() if stream is None else stream
         if chunks is not None:
-            self.retrieve(q, [None] * self.n_pages if indexed else pages_k, chunks, main)
+            self.retrieve(q, self.no_pages() if indexed else pages_k, chunks, main)
         else:
             self.score(q, pages_k, main, use_cache=indexed)
         self.gather(pages_k, pages_v, main, k_cur, v_cur)

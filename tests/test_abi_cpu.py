@@ -134,7 +134,7 @@ def test_workspace_sizes(lib):
     a = lib.hsa_workspace_bytes(ctypes.byref(g), 16)
     b = lib.hsa_workspace_bytes(ctypes.byref(g), 120)
     assert 0 < a <= b
-    assert lib.hsa_workspace_bytes(ctypes.byref(g), _lib.HSA_MAX_PAGES + 1) == 0
+    assert lib.hsa_workspace_bytes(ctypes.byref(g), _lib.HSA_MAX_BANK_PAGES + 1) == 0
     # the linear branch's own workspace: smaller than the full one, enough for
     # the linear branch (its check passes with exactly this size, fails below)
     lin = lib.hsa_linear_workspace_bytes(ctypes.byref(g))
@@ -227,3 +227,29 @@ def test_noalloc_select_rejects_before_launching(lib):
     assert lib.hsa_block_select_noalloc(ctypes.byref(c1_geom()), p, None, None, p, p, p, None, None) == 1
     assert lib.hsa_block_select_noalloc(ctypes.byref(c1_geom(dtype=7)), p, p, p, p, p, p, None, None) == 3
     assert _lib.HSA_NOALLOC_SCRATCH_BYTES == 16 << 20
+
+
+def test_bank_limits(lib):
+    """Host page tables stop at HSA_MAX_PAGES, device page tables at
+    HSA_MAX_BANK_PAGES; the workspace is sized up to the latter.  Every
+    rejection happens on the host, before anything is launched."""
+    g = c1_geom()
+    gp = ctypes.byref(g)
+    assert lib.hsa_workspace_bytes(gp, _lib.HSA_MAX_BANK_PAGES) >= lib.hsa_workspace_bytes(gp, 256) >= \
+        lib.hsa_workspace_bytes(gp, 16) > 0
+    assert lib.hsa_workspace_bytes(gp, _lib.HSA_MAX_BANK_PAGES + 1) == 0
+    p = ctypes.c_void_p(256)  # never dereferenced: each call returns before launching
+    ws_big = lib.hsa_workspace_bytes(gp, _lib.HSA_MAX_BANK_PAGES)
+    n_host = _lib.HSA_MAX_PAGES + 1
+    host_tab = (ctypes.c_void_p * n_host)(*([256] * n_host))
+    assert lib.hsa_score_pages(gp, p, host_tab, p, n_host, p, p, p, ws_big, None) == 4
+    assert lib.hsa_gather_active(gp, host_tab, host_tab, n_host, p, None, None, p, p, None, None) == 4
+    for n, rc in ((_lib.HSA_MAX_BANK_PAGES + 1, 4), (0, 4), (3, 4)):  # 3 < K_p = 4
+        assert lib.hsa_score_pages_devtab(gp, p, p, p, n, p, p, p, ws_big, None) == rc, n
+        assert lib.hsa_gather_active_devtab(gp, p, p, n, p, None, None, p, p, None, None) == rc, n
+        assert lib.hsa_score_chunk_pages_devtab(gp, p, p, p, n, p, p, 1, p, p, p, ws_big, None) == rc, n
+    assert lib.hsa_score_pages_devtab(gp, p, None, p, 256, p, p, p, ws_big, None) == 1
+    assert lib.hsa_gather_active_devtab(gp, None, p, 256, p, None, None, p, p, None, None) == 1
+    assert lib.hsa_score_chunk_pages_devtab(gp, p, p, p, 256, None, p, 1, p, p, p, ws_big, None) == 1
+    small = lib.hsa_workspace_bytes(gp, 256) - 1
+    assert lib.hsa_score_pages_devtab(gp, p, p, p, 256, p, p, p, small, None) == 5
