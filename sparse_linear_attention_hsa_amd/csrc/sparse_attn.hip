@@ -153,6 +153,27 @@ __global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
   }
 }
 
+// Partial outputs of split rows: each segment's output normalised by its own
+// softmax sum, so every element is a convex combination of values (|o| <=
+// max |v|).  bf16 workloads keep them in half precision (2^-11 relative,
+// against the 2^-9 of the bf16 operands), halving the bytes the segments
+// write and the merge reads; float32 workloads keep float32.
+template <typename T> struct PartOf { using type = float; };
+template <> struct PartOf<bf16_t> { using type = _Float16; };
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void store4(float* p, const f32x4& v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store4(_Float16* p, const f32x4& v) {
+  *reinterpret_cast<half4_t*>(p) = __builtin_convertvector(v, half4_t);
+}
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4(const _Float16* p) {
+  const half4_t h = *reinterpret_cast<const half4_t*>(p);
+  return make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
+}
+
 // LDS staging of one step (KS keys), written by direct global->LDS loads
 // (each wave instruction writes 1 KB: 64 lanes x 16 bytes, contiguous).
 //  * K: rows of D elements, 16-byte chunks swizzled by kswz (common.h).
@@ -166,7 +187,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
     const T* __restrict__ q, const T* __restrict__ k_act, const T* __restrict__ v_act,
     const int32_t* __restrict__ blk_idx, const int4* __restrict__ items, const int* __restrict__ meta,
     int H, int B, int Bk, int L, int nKB, int nQB, float scale_log2,
-    float* __restrict__ o_sp, float* __restrict__ part_o, float* __restrict__ part_ml, PagedKV<PAGED> pg) {
+    float* __restrict__ o_sp, typename PartOf<T>::type* __restrict__ part_o, float* __restrict__ part_ml,
+    PagedKV<PAGED> pg) {
   constexpr int E = Vec<T>::N;          // elements per 16-byte chunk
   constexpr int KS = Mma<T>::K;         // keys per step
   constexpr int GPS = KS / 16;          // granules per step
@@ -519,10 +541,10 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
           *reinterpret_cast<float4*>(dst + 16 * dt) = make_float4(v[0], v[1], v[2], v[3]);
         }
       } else {
-        float* dst = part_o + ((size_t)slot * B + r) * D + 4 * g;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        auto* dst = part_o + ((size_t)slot * B + r) * D + 4 * g;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<float4*>(dst + 16 * dt) = make_float4(o[t][dt][0], o[t][dt][1], o[t][dt][2], o[t][dt][3]);
+        for (int dt = 0; dt < DT; ++dt) store4(dst + 16 * dt, o[t][dt] * inv);
         if (g == 0) {
           part_ml[((size_t)slot * B + r) * 2 + 0] = m_run[t];
           part_ml[((size_t)slot * B + r) * 2 + 1] = l_tot;
@@ -535,14 +557,15 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
 // Merge the partial outputs of split rows (fixed segment order); rows with
 // no selected block get zeros.  kCombParts workgroups share a row, each with
 // a quarter of its columns (more loads in flight across the chip).  The
-// per-segment weights exp2(m_s - M) / sum go through LDS, then every thread
-// streams its float4 columns once.
+// per-segment weights l_s exp2(m_s - M) / sum_s' l_s' exp2(m_s' - M) (for
+// outputs normalised per segment) go through LDS, then every thread streams
+// its four-column groups once.
 constexpr int kCombThreads = 256;
 constexpr int kCombParts = 4;
 
-template <int D>
+template <int D, typename PartT>
 __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
-    const int2* __restrict__ rowinfo, const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const int2* __restrict__ rowinfo, const PartT* __restrict__ part_o, const float* __restrict__ part_ml,
     int H, int B, int nQB, float* __restrict__ o_sp) {
   // (running max, sum) of every segment row, then (weight, -) in place;
   // max_segs x B entries (dynamic)
@@ -564,9 +587,9 @@ __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
       float den = 0.f;
       for (int sg = 0; sg < nseg; ++sg) {
         const float2 v = ml[sg * B + r];
-        const float wv = exp2f(v.x - M);
+        const float wv = exp2f(v.x - M) * v.y;
         ml[sg * B + r].x = wv;
-        den += wv * v.y;
+        den += wv;
       }
       const float inv = den > 0.f ? 1.f / den : 0.f;
       for (int sg = 0; sg < nseg; ++sg) ml[sg * B + r].x *= inv;
@@ -577,14 +600,14 @@ __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
   // segments of all three in flight together; each column still sums its
   // segments in segment order.
   constexpr int U = 3;
-  constexpr int CW = D / 4 / kCombParts;  // float4 columns of this workgroup per row
+  constexpr int CW = D / 4 / kCombParts;  // four-column groups of this workgroup per row
   const int total = B * CW;
-  const size_t seg_stride = (size_t)B * D / 4;  // float4s between the partials of consecutive segments
-  const float4* base = reinterpret_cast<const float4*>(part_o + (size_t)s0 * B * D) + part * CW;
+  const size_t seg_stride = (size_t)B * D;  // elements between the partials of consecutive segments
+  const PartT* base = part_o + (size_t)s0 * B * D + 4 * part * CW;
   for (int e0 = threadIdx.x; e0 < total; e0 += U * kCombThreads) {
     int rr[U];
     bool ok[U];
-    const float4* src[U];
+    const PartT* src[U];
     float4 acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -592,7 +615,7 @@ __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
       ok[u] = e < total;
       const int ec = ok[u] ? e : 0;  // clamped: a column past the end reads column 0 and is not stored
       rr[u] = ec / CW;
-      src[u] = base + (size_t)rr[u] * (D / 4) + ec % CW;
+      src[u] = base + (size_t)rr[u] * D + 4 * (ec % CW);
       acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     int sg = 0;
@@ -601,7 +624,7 @@ __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[u][k] = src[u][(size_t)(sg + k) * seg_stride];
+        for (int k = 0; k < 4; ++k) v[u][k] = load4(src[u] + (size_t)(sg + k) * seg_stride);
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -614,7 +637,7 @@ __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
     for (; sg < nseg; ++sg) {
       float4 v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = src[u][(size_t)sg * seg_stride];
+      for (int u = 0; u < U; ++u) v[u] = load4(src[u] + (size_t)sg * seg_stride);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const float wv = ml[sg * B + rr[u]].x;
@@ -634,7 +657,8 @@ __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
 template <typename T, int D, int NW, int QPW, bool PAGED>
 void launch_attn(const Dims& s, const SparsePlan& pl, const void* q, const void* k_act, const void* v_act,
                  const int32_t* idx, const int4* items, const int* meta, float* o_sp,
-                 float* po, float* pml, const PagedKV<PAGED>& pg, hipStream_t st) {
+                 void* po, float* pml, const PagedKV<PAGED>& pg, hipStream_t st) {
+  using PartT = typename PartOf<T>::type;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
   // bf16: two query tiles per wave fit 168 registers, three waves per SIMD
   constexpr int WPE = sizeof(T) == 2 ? (QPW <= 2 ? 3 : 2) : 1;
@@ -645,18 +669,18 @@ void launch_attn(const Dims& s, const SparsePlan& pl, const void* q, const void*
     hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE, RING, true, PAGED>), dim3(pl.grid), dim3(NW * kWave),
                        0, st, reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act),
                        reinterpret_cast<const T*>(v_act), idx, items, meta, s.H, s.B, s.Bk, s.L, s.nKB, s.nQB,
-                       scale_log2, o_sp, po, pml, pg);
+                       scale_log2, o_sp, static_cast<PartT*>(po), pml, pg);
   else
   hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE, RING, false, PAGED>), dim3(pl.grid), dim3(NW * kWave),
                      0, st, reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act),
                      reinterpret_cast<const T*>(v_act), idx, items, meta, s.H, s.B, s.Bk, s.L, s.nKB, s.nQB,
-                     scale_log2, o_sp, po, pml, pg);
+                     scale_log2, o_sp, static_cast<PartT*>(po), pml, pg);
 }
 
 template <typename T, int D, bool PAGED>
 void dispatch_attn(const Dims& s, const SparsePlan& pl, const void* q, const void* k_act, const void* v_act,
                    const int32_t* idx, const int4* items, const int* meta, float* o_sp,
-                   float* po, float* pml, const PagedKV<PAGED>& pg, hipStream_t st) {
+                   void* po, float* pml, const PagedKV<PAGED>& pg, hipStream_t st) {
   const int QT = s.B / 16;
   const int nw = (QT + 1) / 2;  // at most two 16-row query tiles per wave
   const int qpw = (QT + nw - 1) / nw;
@@ -678,6 +702,19 @@ void dispatch_attn(const Dims& s, const SparsePlan& pl, const void* q, const voi
 namespace hsa {
 namespace {
 
+template <int D, typename PartT>
+hsa_rc launch_combine(const Dims& s, const int2* rowinfo, const void* po, const float* pml, float* o_sp,
+                      size_t comb_lds, hipStream_t st) {
+  auto comb = sparse_combine_kernel<D, PartT>;
+  if (comb_lds > 65536 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(comb), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)comb_lds) != hipSuccess)
+    return HSA_ERR_HIP;
+  hipLaunchKernelGGL(comb, dim3(s.rows * kCombParts), dim3(kCombThreads), comb_lds, st, rowinfo,
+                     static_cast<const PartT*>(po), pml, s.H, s.B, s.nQB, o_sp);
+  return HSA_OK;
+}
+
 template <bool PAGED>
 hsa_rc sparse_entry(const Dims& s, const void* q, const void* k_act, const void* v_act, const int32_t* blk_count,
                     const int32_t* blk_idx, float* o_sp, void* ws, size_t ws_bytes, hsa_stream stream,
@@ -691,7 +728,7 @@ hsa_rc sparse_entry(const Dims& s, const void* q, const void* k_act, const void*
   int4* items = reinterpret_cast<int4*>(wsb + w.sp_items);
   int2* rowinfo = reinterpret_cast<int2*>(wsb + w.sp_rowinfo);
   int* meta = reinterpret_cast<int*>(wsb + w.sp_meta);
-  float* po = reinterpret_cast<float*>(wsb + w.sp_part_o);
+  void* po = wsb + w.sp_part_o;
   float* pml = reinterpret_cast<float*>(wsb + w.sp_part_ml);
   const int gps = s.bf16 ? 2 : 1;
   hipLaunchKernelGGL(sparse_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, blk_count, s.rows, s.nQB, s.nKB,
@@ -706,13 +743,15 @@ hsa_rc sparse_entry(const Dims& s, const void* q, const void* k_act, const void*
   }
   if (ev_end && hipEventRecord(reinterpret_cast<hipEvent_t>(ev_end), st) != hipSuccess) return HSA_ERR_HIP;
   const size_t comb_lds = (size_t)pl.max_segs * s.B * sizeof(float2);
-  auto comb = s.d == 128 ? sparse_combine_kernel<128> : sparse_combine_kernel<64>;
-  if (comb_lds > 65536 &&
-      hipFuncSetAttribute(reinterpret_cast<const void*>(comb), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)comb_lds) != hipSuccess)
-    return HSA_ERR_HIP;
-  hipLaunchKernelGGL(comb, dim3(s.rows * kCombParts), dim3(kCombThreads), comb_lds, st, rowinfo, po, pml, s.H, s.B,
-                     s.nQB, o_sp);
+  hsa_rc rc;
+  if (s.bf16) {
+    if (s.d == 128) rc = launch_combine<128, _Float16>(s, rowinfo, po, pml, o_sp, comb_lds, st);
+    else rc = launch_combine<64, _Float16>(s, rowinfo, po, pml, o_sp, comb_lds, st);
+  } else {
+    if (s.d == 128) rc = launch_combine<128, float>(s, rowinfo, po, pml, o_sp, comb_lds, st);
+    else rc = launch_combine<64, float>(s, rowinfo, po, pml, o_sp, comb_lds, st);
+  }
+  if (rc != HSA_OK) return rc;
   return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
 }
 
