@@ -107,6 +107,11 @@ typedef struct ihipEvent_t* hsa_event;    /* a hipEvent_t  */
 /* Linear-branch flags. */
 #define HSA_LIN_REUSE_PROJ 1  /* skip the projection: k_proj / v_proj are inputs        */
 #define HSA_LIN_PROJ_ONLY 2   /* only the projection: o_lin (and q) are not touched     */
+#define HSA_LIN_HISTORY_PROJ 4 /* intra_split > 0: only the projection of the history keys
+                                  [0, Lh) into k_proj / v_proj; o_lin (and q) untouched  */
+#define HSA_LIN_CHUNK_PROJ 8   /* intra_split > 0: k_proj / v_proj hold the history's
+                                  projection (in, unchanged); the chunk's keys [Lh, L) are
+                                  projected, added to it, and the attention runs on the sum */
 
 /* ---------------------------------------------------------------------------
  * S1 -- page-level retrieval.  Paper section 3.2, "Stage 2: page-level
@@ -228,6 +233,16 @@ hsa_rc hsa_gather_active(const hsa_geom* geom, const void* const* page_k, const 
                          int32_t n_pages, const int32_t* sel_pages, const void* k_cur, const void* v_cur,
                          void* k_act, void* v_act, float* kblk_mean, hsa_stream stream);
 
+/* The chunk's part of the active buffer alone: writes tokens [Lh, L) of k_act
+ * and v_act and the chunk's key-block means (key blocks nKBh*B/Bk .. nKB-1 of
+ * kblk_mean) from k_cur / v_cur, leaving the history part as it is (section
+ * 3.3: the chunk's own keys change with every denoising step, the retrieved
+ * history does not).  Arguments as hsa_gather_active; requires
+ * intra_split > 0 (HSA_ERR_BAD_PARAM otherwise).
+ * ------------------------------------------------------------------------- */
+hsa_rc hsa_gather_chunk(const hsa_geom* geom, const void* k_cur, const void* v_cur, void* k_act, void* v_act,
+                        float* kblk_mean, hsa_stream stream);
+
 /* ---------------------------------------------------------------------------
  * Page banks larger than HSA_MAX_PAGES: S1 and S2 with the page pointer
  * tables in DEVICE memory.  Paper section 3.2 (the full history stays
@@ -280,8 +295,17 @@ hsa_rc hsa_gather_active_devtab(const hsa_geom* geom, const void* const* page_k_
  *               large and a bf16 copy of Ktil would move the logits by more
  *               than the output tolerance; the bf16 product splits Ktil into
  *               a bf16 high and low part instead.
- *  o_lin        [Lq][H][d] float32 out (untouched with HSA_LIN_PROJ_ONLY).
- *  flags        0, HSA_LIN_REUSE_PROJ or HSA_LIN_PROJ_ONLY.
+ *  o_lin        [Lq][H][d] float32 out (untouched with HSA_LIN_PROJ_ONLY and
+ *               HSA_LIN_HISTORY_PROJ).
+ *  flags        0, HSA_LIN_REUSE_PROJ, HSA_LIN_PROJ_ONLY, HSA_LIN_HISTORY_PROJ or
+ *               HSA_LIN_CHUNK_PROJ (one at a time).  The last two split the
+ *               projection of a geometry with intra-chunk keys (section 3.3,
+ *               "Inter- and intra-chunk sparse granularity") into the history's
+ *               part, reused across denoising steps, and the chunk's part,
+ *               whose keys change every step: Ktil = E_K[:, :Lh] K_hist +
+ *               E_K[:, Lh:] K_chunk (and the same for V).  With
+ *               HSA_LIN_CHUNK_PROJ the sum stays in the workspace.  Both
+ *               return HSA_ERR_BAD_PARAM when intra_split = 0.
  *  With HSA_LIN_REUSE_PROJ, k_act, v_act, e_k and e_v may be NULL.
  *  ws           workspace of ws_bytes >= hsa_workspace_bytes(geom, 1), with
  *               every flag (the projection keeps its per-slice partial sums

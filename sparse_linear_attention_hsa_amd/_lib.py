@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhsa_attn.so")
 
 HSA_F32, HSA_BF16 = 0, 1
-HSA_LIN_REUSE_PROJ, HSA_LIN_PROJ_ONLY = 1, 2
+HSA_LIN_REUSE_PROJ, HSA_LIN_PROJ_ONLY, HSA_LIN_HISTORY_PROJ, HSA_LIN_CHUNK_PROJ = 1, 2, 4, 8
 HSA_MAX_PAGES = 128
 HSA_MAX_BANK_PAGES = 8192
 HSA_MAX_KBLOCKS = 2048
@@ -51,6 +51,7 @@ SIGNATURES = {
     "hsa_gather_pages": (_i32, [_GP, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp, _vp]),
     "hsa_gather_active": (_i32, [_GP, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _vp]),
+    "hsa_gather_chunk": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp]),
     "hsa_linear_branch": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
     "hsa_page_prepare": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp]),
     "hsa_gather_block_means": (_i32, [_GP, ctypes.POINTER(_vp), _i32, _vp, _vp, _vp]),

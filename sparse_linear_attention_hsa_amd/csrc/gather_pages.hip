@@ -27,7 +27,7 @@ constexpr int kBatch = 6;  // passes whose loads are in flight together
 // blocks are B tokens).
 template <typename T, int D, int NSUB, typename Tab>
 __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
-    Tab pk, Tab pv, int n_pages, const int32_t* __restrict__ sel, const T* __restrict__ k_cur,
+    int blk0, Tab pk, Tab pv, int n_pages, const int32_t* __restrict__ sel, const T* __restrict__ k_cur,
     const T* __restrict__ v_cur, int H, int Lp, int Kp, int B, int Bk, int L, int nKB,
     T* __restrict__ k_act, T* __restrict__ v_act, float* __restrict__ kblk_mean) {
   constexpr int E = Vec<T>::N;
@@ -41,11 +41,12 @@ __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
 
   const int bpp = Lp / B;
   const int h = blockIdx.y;
+  const int bx = blockIdx.x + blk0;  // B-token block of the active buffer
   const T* ksrc;
   const T* vsrc;
   size_t tok0, act0;  // first token of the block in its source, and in the active buffer
-  if ((int)blockIdx.x < Kp * bpp) {
-    const int p = blockIdx.x / bpp, blk = blockIdx.x % bpp;
+  if (bx < Kp * bpp) {
+    const int p = bx / bpp, blk = bx % bpp;
     int page = sel ? sel[p] : p;  // no selection: the pages in table order
     page = page < 0 ? 0 : (page >= n_pages ? n_pages - 1 : page);
     ksrc = reinterpret_cast<const T*>(pk.at(page));
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
     tok0 = (size_t)blk * B;
     act0 = (size_t)p * Lp + tok0;
   } else {  // the chunk's own tokens, after the Kp pages
-    const int blk = blockIdx.x - Kp * bpp;
+    const int blk = bx - Kp * bpp;
     ksrc = k_cur;
     vsrc = v_cur;
     tok0 = (size_t)blk * B;
@@ -152,14 +153,17 @@ __global__ __launch_bounds__(kGatherThreads) void gather_block_kernel(
   }
 }
 
+// chunk_only: the chunk's blocks alone (the history part stays as it is)
 template <typename T, int D, typename Tab>
 void launch_gather(const Dims& s, const Tab& pk, const Tab& pv, int n_pages, const int32_t* sel,
                    const void* k_cur, const void* v_cur, void* k_act, void* v_act, float* kblk_mean,
-                   hipStream_t st) {
+                   hipStream_t st, bool chunk_only = false) {
   constexpr int E = Vec<T>::N;
   const int nsub = s.B / s.Bk;
   const size_t smem = (size_t)s.B * (D + E) * sizeof(T) + (size_t)kGatherThreads * E * sizeof(float);
-  dim3 grid(s.Kp * (s.Lp / s.B) + (s.split ? s.Lq / s.B : 0), s.H);
+  const int hist_blocks = s.Kp * (s.Lp / s.B);
+  const int blk0 = chunk_only ? hist_blocks : 0;
+  dim3 grid((chunk_only ? 0 : hist_blocks) + (s.split ? s.Lq / s.B : 0), s.H);
   static_assert(HSA_MAX_INTRA_SPLIT == 4, "one instantiation per key blocks per block");
   auto kern = nsub == 1   ? gather_block_kernel<T, D, 1, Tab>
               : nsub == 2 ? gather_block_kernel<T, D, 2, Tab>
@@ -168,7 +172,7 @@ void launch_gather(const Dims& s, const Tab& pk, const Tab& pv, int n_pages, con
   if (smem > 65536)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)smem);
-  hipLaunchKernelGGL(kern, grid, dim3(kGatherThreads), smem, st, pk, pv, n_pages, sel,
+  hipLaunchKernelGGL(kern, grid, dim3(kGatherThreads), smem, st, blk0, pk, pv, n_pages, sel,
                      reinterpret_cast<const T*>(k_cur), reinterpret_cast<const T*>(v_cur), s.H, s.Lp, s.Kp, s.B,
                      s.Bk, s.L, s.nKB, reinterpret_cast<T*>(k_act), reinterpret_cast<T*>(v_act), kblk_mean);
 }
@@ -313,4 +317,25 @@ extern "C" hsa_rc hsa_gather_pages(const hsa_geom* geom, const void* const* page
   if (geom && geom->intra_split != 0) return HSA_ERR_BAD_PARAM;
   return hsa_gather_active(geom, page_k, page_v, n_pages, sel_pages, nullptr, nullptr, k_act, v_act, kblk_mean,
                            stream);
+}
+
+extern "C" hsa_rc hsa_gather_chunk(const hsa_geom* geom, const void* k_cur, const void* v_cur, void* k_act,
+                                   void* v_act, float* kblk_mean, hsa_stream stream) {
+  using namespace hsa;
+  Dims s;
+  hsa_rc rc = derive(geom, &s);
+  if (rc != HSA_OK) return rc;
+  if (!s.split) return HSA_ERR_BAD_PARAM;
+  if (!k_cur || !v_cur || !k_act || !v_act) return HSA_ERR_NULL_ARG;
+  PageTable none;
+  for (int j = 0; j < kMaxPages; ++j) none.p[j] = nullptr;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (s.bf16) {
+    if (s.d == 128) launch_gather<bf16_t, 128>(s, none, none, 1, nullptr, k_cur, v_cur, k_act, v_act, kblk_mean, st, true);
+    else launch_gather<bf16_t, 64>(s, none, none, 1, nullptr, k_cur, v_cur, k_act, v_act, kblk_mean, st, true);
+  } else {
+    if (s.d == 128) launch_gather<float, 128>(s, none, none, 1, nullptr, k_cur, v_cur, k_act, v_act, kblk_mean, st, true);
+    else launch_gather<float, 64>(s, none, none, 1, nullptr, k_cur, v_cur, k_act, v_act, kblk_mean, st, true);
+  }
+  return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
 }

@@ -67,10 +67,10 @@ ScorePlan score_plan(const Dims& s, int n_pages, bool few_pages) {
   return p;
 }
 
-ProjPlan proj_plan(const Dims& s) {
+ProjPlan proj_plan(const Dims& s, int n_tok) {
   ProjPlan p;
   const int K = s.bf16 ? 32 : 16;
-  p.steps = cdiv(s.L, K);       // stages of one contraction step
+  p.steps = std::max(1, cdiv(n_tok < 0 ? s.L : n_tok, K));  // stages of one contraction step
   // At most one workgroup (8 waves, two heads, 128 KB of LDS) fits on a CU,
   // so the items must not exceed the 256 CUs: one item more would run in a
   // second round and double the kernel's time.
@@ -126,7 +126,10 @@ WsLayout ws_layout(const Dims& s, int n_pages) {
   w.lin_klo = align256(w.lin_khi + kbytes);
   w.lin_vt = align256(w.lin_klo + kbytes);
   w.lin_vlo = align256(w.lin_vt + kbytes);
-  w.lin_end = align256(w.lin_vlo + kbytes);
+  // float32 K~ and V~^T summed from the history and the chunk (HSA_LIN_CHUNK_PROJ)
+  w.lin_ksum = align256(w.lin_vlo + kbytes);
+  w.lin_vsum = align256(w.lin_ksum + (size_t)s.H * s.r * s.d * 4);
+  w.lin_end = align256(w.lin_vsum + (size_t)s.H * s.r * s.d * 4);
   // select
   w.sel_qbar = 0;
   w.sel_kbar = align256((size_t)s.H * s.nQB * s.d * 4);

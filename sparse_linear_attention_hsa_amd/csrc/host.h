@@ -43,7 +43,8 @@ struct ProjPlan {
   int rtiles;        // ceil(r / 16)
   int rpad;          // r padded to the product's contraction step
 };
-ProjPlan proj_plan(const Dims& s);
+// n_tok: tokens the projection contracts (all L by default)
+ProjPlan proj_plan(const Dims& s, int n_tok = -1);
 
 // Linear-branch attention split: units of 32 queries of one head; a
 // workgroup takes a run of units_per_wg of them.
@@ -70,7 +71,7 @@ struct WsLayout {
   // score
   size_t score_partial, score_qbar, score_kbar, score_end;
   // linear
-  size_t lin_partial, lin_khi, lin_klo, lin_vt, lin_vlo, lin_end;
+  size_t lin_partial, lin_khi, lin_klo, lin_vt, lin_vlo, lin_ksum, lin_vsum, lin_end;
   // select
   size_t sel_qbar, sel_kbar, sel_logit, sel_end;
   // sparse

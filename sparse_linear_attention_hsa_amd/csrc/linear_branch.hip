@@ -83,7 +83,8 @@ constexpr int kProjRing = 4;
 template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lin_project_kernel(
     const T* __restrict__ k_act, const T* __restrict__ v_act, const T* __restrict__ e_k,
-    const T* __restrict__ e_v, int H, int L, int r, int splits, float* __restrict__ partial, PagedKV<PAGED> pg) {
+    const T* __restrict__ e_v, int H, int L, int r, int splits, int t_begin, int t_end, float* __restrict__ partial,
+    PagedKV<PAGED> pg) {
   constexpr int E = Vec<T>::N;
   constexpr int KS = Mma<T>::K;                      // tokens per stage (one contraction step)
   constexpr int DT = D / 16;
@@ -122,7 +123,8 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2,
   const int h = hp * 2 + hs;                   // may be == H for an odd head count
   const bool h_ok = h < H;
   const int rtiles = (r + 15) / 16;
-  const int nst = (L + KS - 1) / KS;
+  // the contraction runs over active tokens [t_begin, t_end) (row strides stay L)
+  const int nst = (t_end - t_begin + KS - 1) / KS;
   const int st0 = (int)((long long)nst * split / splits);
   const int st1 = (int)((long long)nst * (split + 1) / splits);
   const T* e = kv ? e_v : e_k;
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2,
 
   // exactly PER loads per wave (tails read the zero page), so the waits can count them
   auto issue = [&](int stg, unsigned char* le, unsigned char* lx) {
-    const int tok0 = stg * KS;
+    const int tok0 = t_begin + stg * KS;
     // paged: the stage's KS tokens lie in at most two pages (16-token
     // granules never straddle one); tokens from bnd on are in the second
     int bnd = 0, first = 0;
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2,
       const int row = (1024 / EROW) * i + lane / (EROW / 16);
       const int chunk = (lane % (EROW / 16)) ^ eswz(row);
       const int tk = tok0 + chunk * E;
-      const void* src = (row < r && tk < L) ? (const void*)(e + (size_t)row * L + tk) : (const void*)(kZeroPage + lane);
+      const void* src = (row < r && tk < t_end) ? (const void*)(e + (size_t)row * L + tk) : (const void*)(kZeroPage + lane);
       __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(le + i * 1024), 16, 0, 0);
     }
 #pragma unroll
@@ -190,12 +192,12 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2,
         if constexpr (PAGED) {
           const bool second = tk >= bnd;
           const int lt = tk - (second ? bnd : first);
-          src = (hh < H && tk < L)
+          src = (hh < H && tk < t_end)
                     ? (const void*)((second ? vpage[1] : vpage[0]) +
                                     (((size_t)hh * (pg.Lp / 16) + lt / 16) * D + rowv) * 16 + part * E)
                     : (const void*)(kZeroPage + lane);
         } else {
-          src = (hh < H && tk < L)
+          src = (hh < H && tk < t_end)
                     ? (const void*)(v_act + (((size_t)hh * (L / 16) + tk / 16) * D + rowv) * 16 + part * E)
                     : (const void*)(kZeroPage + lane);
         }
@@ -206,11 +208,11 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2,
           const int tk = tok0 + tr;
           const bool second = tk >= bnd;
           const int lt = tk - (second ? bnd : first);
-          src = (hh < H && tk < L)
+          src = (hh < H && tk < t_end)
                     ? (const void*)((second ? kpage[1] : kpage[0]) + ((size_t)hh * pg.Lp + lt) * D + chunk * E)
                     : (const void*)(kZeroPage + lane);
         } else {
-          src = (hh < H && tok0 + tr < L) ? (const void*)(k_act + ((size_t)hh * L + tok0 + tr) * D + chunk * E)
+          src = (hh < H && tok0 + tr < t_end) ? (const void*)(k_act + ((size_t)hh * L + tok0 + tr) * D + chunk * E)
                                           : (const void*)(kZeroPage + lane);
         }
       }
@@ -330,10 +332,13 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2,
   }
 }
 
-// Sum the split partials in order; write Ktil [H][r][d] and Vtil^T [H][d][r] (float32).
+// Sum the split partials in order; write Ktil [H][r][d] and Vtil^T [H][d][r]
+// (float32), each added to a given base of the same layout when there is one
+// (the history's projections, to which the chunk's are added).
 // grid = (2H, ceil(r*D/1024)); each thread sums one float4 column group over the splits.
 __global__ __launch_bounds__(256) void lin_reduce_kernel(const float* __restrict__ partial, int H, int D, int r,
-                                                         int splits, float* __restrict__ k_proj,
+                                                         int splits, const float* __restrict__ base_k,
+                                                         const float* __restrict__ base_v, float* __restrict__ k_proj,
                                                          float* __restrict__ v_proj) {
   const int which = blockIdx.x;
   const bool is_v = which >= H;
@@ -358,10 +363,19 @@ __global__ __launch_bounds__(256) void lin_reduce_kernel(const float* __restrict
     s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
   }
   if (is_v) {
-    float* o = v_proj + ((size_t)h * D + col) * r + rr;
+    const size_t o0 = ((size_t)h * D + col) * r + rr;
+    if (base_v) {
+      s.x += base_v[o0]; s.y += base_v[o0 + r]; s.z += base_v[o0 + 2 * r]; s.w += base_v[o0 + 3 * r];
+    }
+    float* o = v_proj + o0;
     o[0] = s.x; o[r] = s.y; o[2 * r] = s.z; o[3 * r] = s.w;
   } else {
-    *reinterpret_cast<float4*>(k_proj + ((size_t)h * r + rr) * D + col) = s;
+    const size_t o0 = ((size_t)h * r + rr) * D + col;
+    if (base_k) {
+      const float4 b = *reinterpret_cast<const float4*>(base_k + o0);
+      s.x += b.x; s.y += b.y; s.z += b.z; s.w += b.w;
+    }
+    *reinterpret_cast<float4*>(k_proj + o0) = s;
   }
 }
 
@@ -585,26 +599,34 @@ template <typename T, int D, bool PAGED>
 void launch_linear(const Dims& s, const void* q, const void* k_act, const void* v_act, const void* e_k,
                    const void* e_v, void* k_proj, void* v_proj, float* o_lin, int flags, char* ws,
                    const WsLayout& w, const PagedKV<PAGED>& pg, hipStream_t st) {
-  const ProjPlan pp = proj_plan(s);
+  // the active tokens the projection contracts: all of them, only the
+  // history's (HSA_LIN_HISTORY_PROJ), or only the chunk's, added to the
+  // history's given projections into the workspace (HSA_LIN_CHUNK_PROJ)
+  const bool chunk = flags & HSA_LIN_CHUNK_PROJ;
+  const int t_begin = chunk ? s.Lh : 0;
+  const int t_end = (flags & HSA_LIN_HISTORY_PROJ) ? s.Lh : s.L;
+  const ProjPlan pp = proj_plan(s, t_end - t_begin);
   float* partial = reinterpret_cast<float*>(ws + w.lin_partial);
+  float* kp = chunk ? reinterpret_cast<float*>(ws + w.lin_ksum) : reinterpret_cast<float*>(k_proj);
+  float* vp = chunk ? reinterpret_cast<float*>(ws + w.lin_vsum) : reinterpret_cast<float*>(v_proj);
   if (!(flags & HSA_LIN_REUSE_PROJ)) {
     const int n_items = pp.splits * 2 * ((s.H + 1) / 2);
     hipLaunchKernelGGL((lin_project_kernel<T, D, PAGED>), dim3((n_items + 7) / 8 * 8), dim3(kProjThreads), 0, st,
                        reinterpret_cast<const T*>(k_act), reinterpret_cast<const T*>(v_act),
                        reinterpret_cast<const T*>(e_k), reinterpret_cast<const T*>(e_v), s.H, s.L, s.r, pp.splits,
-                       partial, pg);
-    hipLaunchKernelGGL(lin_reduce_kernel, dim3(2 * s.H, (s.r * D / 4 + 255) / 256), dim3(256), 0, st, partial, s.H, D, s.r, pp.splits,
-                       reinterpret_cast<float*>(k_proj), reinterpret_cast<float*>(v_proj));
+                       t_begin, t_end, partial, pg);
+    hipLaunchKernelGGL(lin_reduce_kernel, dim3(2 * s.H, (s.r * D / 4 + 255) / 256), dim3(256), 0, st, partial, s.H, D,
+                       s.r, pp.splits, chunk ? reinterpret_cast<const float*>(k_proj) : nullptr,
+                       chunk ? reinterpret_cast<const float*>(v_proj) : nullptr, kp, vp);
   }
-  if (flags & HSA_LIN_PROJ_ONLY) return;
+  if (flags & (HSA_LIN_PROJ_ONLY | HSA_LIN_HISTORY_PROJ)) return;
   // MFMA-ready operands of the attention, then the attention
   T* khi = reinterpret_cast<T*>(ws + w.lin_khi);
   T* klo = reinterpret_cast<T*>(ws + w.lin_klo);
   T* vt = reinterpret_cast<T*>(ws + w.lin_vt);
   T* vlo = reinterpret_cast<T*>(ws + w.lin_vlo);
-  hipLaunchKernelGGL((lin_prep_kernel<T>), dim3((pp.rpad * D + 255) / 256, s.H, 2), dim3(256), 0, st,
-                     reinterpret_cast<const float*>(k_proj), reinterpret_cast<const float*>(v_proj), D, s.r, pp.rpad,
-                     khi, klo, vt, vlo);
+  hipLaunchKernelGGL((lin_prep_kernel<T>), dim3((pp.rpad * D + 255) / 256, s.H, 2), dim3(256), 0, st, kp, vp, D, s.r,
+                     pp.rpad, khi, klo, vt, vlo);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
   const AttendPlan ap = attend_plan(s);
   hipLaunchKernelGGL((lin_attend_kernel<T, D>), dim3(ap.wg_per_head, s.H), dim3(kAttThreads), 0, st,
@@ -622,11 +644,14 @@ template <bool PAGED>
 hsa_rc linear_entry(const Dims& s, const void* q, const void* k_act, const void* v_act, const void* e_k,
                     const void* e_v, void* k_proj, void* v_proj, float* o_lin, int32_t flags, void* ws,
                     size_t ws_bytes, hsa_stream stream, const PagedKV<PAGED>& pg) {
-  if (flags & ~(HSA_LIN_REUSE_PROJ | HSA_LIN_PROJ_ONLY)) return HSA_ERR_BAD_PARAM;
-  if ((flags & HSA_LIN_REUSE_PROJ) && (flags & HSA_LIN_PROJ_ONLY)) return HSA_ERR_BAD_PARAM;
+  constexpr int kModes = HSA_LIN_REUSE_PROJ | HSA_LIN_PROJ_ONLY | HSA_LIN_HISTORY_PROJ | HSA_LIN_CHUNK_PROJ;
+  if (flags & ~kModes) return HSA_ERR_BAD_PARAM;
+  if (__builtin_popcount((unsigned)flags) > 1) return HSA_ERR_BAD_PARAM;  // one mode at a time
+  // the history / chunk split exists only with the chunk's own keys
+  if ((flags & (HSA_LIN_HISTORY_PROJ | HSA_LIN_CHUNK_PROJ)) && (PAGED || !s.split)) return HSA_ERR_BAD_PARAM;
   if (!k_proj || !v_proj) return HSA_ERR_NULL_ARG;
   if (!(flags & HSA_LIN_REUSE_PROJ) && ((!PAGED && (!k_act || !v_act)) || !e_k || !e_v)) return HSA_ERR_NULL_ARG;
-  if (!(flags & HSA_LIN_PROJ_ONLY) && (!q || !o_lin)) return HSA_ERR_NULL_ARG;
+  if (!(flags & (HSA_LIN_PROJ_ONLY | HSA_LIN_HISTORY_PROJ)) && (!q || !o_lin)) return HSA_ERR_NULL_ARG;
   const WsLayout w = ws_layout(s, 1);
   if (!ws || ws_bytes < w.lin_end) return HSA_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

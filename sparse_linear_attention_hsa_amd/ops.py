@@ -163,6 +163,12 @@ def hsa_gather_active(geom, pages_k, pages_v, sel_pages, k_cur, v_cur, k_act, v_
         _p(k_act), _p(v_act), _p(kblk_mean), _s(stream)))
 
 
+def hsa_gather_chunk(geom, k_cur, v_cur, k_act, v_act, kblk_mean=None, stream=None):
+    """Rewrite only the chunk's part of the active K/V and its key-block means."""
+    check("hsa_gather_chunk", lib().hsa_gather_chunk(
+        ctypes.byref(geom), _p(k_cur), _p(v_cur), _p(k_act), _p(v_act), _p(kblk_mean), _s(stream)))
+
+
 def hsa_linear_branch(geom, q, k_act, v_act, e_k, e_v, k_proj, v_proj, o_lin, flags, ws, stream=None):
     check("hsa_linear_branch", lib().hsa_linear_branch(
         ctypes.byref(geom), _p(q), _p(k_act), _p(v_act), _p(e_k), _p(e_v), _p(k_proj), _p(v_proj), _p(o_lin),

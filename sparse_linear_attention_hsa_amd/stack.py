@@ -9,6 +9,14 @@ only on the chunk, so they run once, in the first denoising step, and every
 later step reuses them (HSA_LIN_REUSE_PROJ); the linear attention, block
 selection, sparse branch and fusion run every step, on that step's Q and X.
 
+With intra-chunk keys (section 3.3, "Inter- and intra-chunk sparse
+granularity") the chunk's own keys and values change with every denoising
+step while the retrieved history does not: the first step gathers the
+history and projects it alone (HSA_LIN_HISTORY_PROJ), and every step writes
+its own keys into the chunk's part of the active buffer (hsa_gather_chunk)
+and projects only them, added to the history's projection
+(HSA_LIN_CHUNK_PROJ).
+
 Pages that are not resident in device memory live in pinned host memory.
 Their mean keys were taken while they were resident (the page index), so
 scoring reads the cached mean instead of the page (a NULL page pointer).
@@ -35,7 +43,7 @@ from typing import Callable, Dict, List, Optional, Sequence, Tuple
 import torch
 
 from . import ops
-from ._lib import HSA_LIN_REUSE_PROJ
+from ._lib import HSA_LIN_CHUNK_PROJ, HSA_LIN_HISTORY_PROJ, HSA_LIN_REUSE_PROJ
 from .ops import Dims, Geom
 
 
@@ -53,6 +61,8 @@ class LayerInputs:
     page_kmean: torch.Tensor              # [P][H][d] f32, filled while every page was resident
     q: List[torch.Tensor] = field(default_factory=list)   # per step [Lq][H][d]
     x: List[torch.Tensor] = field(default_factory=list)   # per step [Lq][D]
+    k_cur: List[torch.Tensor] = field(default_factory=list)  # per step [Lq][H][d] (intra-chunk keys)
+    v_cur: List[torch.Tensor] = field(default_factory=list)
 
 
 class _LayerState:
@@ -141,6 +151,7 @@ class HsaStack:
         concurrent=False issues every call on the current stream."""
         g, ws = self.geom, self.ws
         L = self.n_layers
+        intra = bool(g.intra_split)
         stream = torch.cuda.current_stream()
         side = self.side if concurrent else stream
         ws_lin = self.ws_lin if concurrent else ws
@@ -163,11 +174,18 @@ class HsaStack:
                     if copy_done[l] is not None:
                         stream.wait_event(copy_done[l])
                     pk, pv = self._staged_tables(l, inp)
-                    ops.hsa_gather_pages(g, pk, pv, st.sel_pages, st.k_act, st.v_act, st.kblk_mean)
+                    if intra:
+                        ops.hsa_gather_active(g, pk, pv, st.sel_pages, inp.k_cur[0], inp.v_cur[0], st.k_act,
+                                              st.v_act, st.kblk_mean)
+                    else:
+                        ops.hsa_gather_pages(g, pk, pv, st.sel_pages, st.k_act, st.v_act, st.kblk_mean)
                     if inp.host_k:
                         ev = torch.cuda.Event()
                         ev.record(stream)
                         last_reader[l % self.n_slots] = ev
+                elif intra:
+                    # this step's own keys into the chunk's part of the active buffer
+                    ops.hsa_gather_chunk(g, inp.k_cur[step], inp.v_cur[step], st.k_act, st.v_act, st.kblk_mean)
                 if concurrent:
                     # the linear branch needs this layer's gathered K/V (or its
                     # projections) and a free O_lin
@@ -176,7 +194,13 @@ class HsaStack:
                     side.wait_event(ready)
                     if fused is not None:
                         side.wait_event(fused)
-                if step == 0:
+                if intra:
+                    if step == 0:  # the history's projection, kept for every step
+                        ops.hsa_linear_branch(g, None, st.k_act, st.v_act, inp.e_k, inp.e_v, st.k_proj, st.v_proj,
+                                              None, HSA_LIN_HISTORY_PROJ, ws_lin, side)
+                    ops.hsa_linear_branch(g, q, st.k_act, st.v_act, inp.e_k, inp.e_v, st.k_proj, st.v_proj,
+                                          self.o_lin, HSA_LIN_CHUNK_PROJ, ws_lin, side)
+                elif step == 0:
                     ops.hsa_linear_branch(g, q, st.k_act, st.v_act, inp.e_k, inp.e_v, st.k_proj, st.v_proj,
                                           self.o_lin, 0, ws_lin, side)
                 else:
@@ -200,7 +224,8 @@ class HsaStack:
 
 
 def make_layer_inputs(geom: Geom, pages_k: List[torch.Tensor], pages_v: List[torch.Tensor], host_ids: Sequence[int],
-                      e_k, e_v, w_g, tau, qs: List[torch.Tensor], xs: List[torch.Tensor]) -> LayerInputs:
+                      e_k, e_v, w_g, tau, qs: List[torch.Tensor], xs: List[torch.Tensor],
+                      k_cur: Sequence[torch.Tensor] = (), v_cur: Sequence[torch.Tensor] = ()) -> LayerInputs:
     """Set up one layer: index every page (its mean key, through the library's
     scoring call) while all pages are resident, then move the pages in
     host_ids to pinned host memory and drop their device copies."""
@@ -224,4 +249,4 @@ def make_layer_inputs(geom: Geom, pages_k: List[torch.Tensor], pages_v: List[tor
         pk[j] = None
         pv[j] = None
     return LayerInputs(pages_k=pk, pages_v=pv, host_k=host_k, host_v=host_v, e_k=e_k, e_v=e_v, w_g=w_g, tau=tau,
-                       page_kmean=kmean, q=list(qs), x=list(xs))
+                       page_kmean=kmean, q=list(qs), x=list(xs), k_cur=list(k_cur), v_cur=list(v_cur))

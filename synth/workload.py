@@ -268,7 +268,8 @@ class Workload:
 def layer_arrays(cfg: Config, layer: int, n_steps: int, workers: int = 8) -> Dict[str, object]:
     """All inputs of one layer of a stack, as float32 arrays: pages (generated
     on a thread pool), the layer's projections, gate weights and thresholds,
-    and the per-step queries and gate inputs."""
+    the per-step queries and gate inputs, and with intra_split the per-step
+    keys and values of the chunk itself."""
     from concurrent.futures import ThreadPoolExecutor
     w = Workload(cfg, layer)
     with ThreadPoolExecutor(max(1, workers)) as ex:
@@ -276,8 +277,10 @@ def layer_arrays(cfg: Config, layer: int, n_steps: int, workers: int = 8) -> Dic
         pv = list(ex.map(w.page_v, range(cfg.n_pages)))
         qs = list(ex.map(w.q, range(n_steps)))
         xs = list(ex.map(w.x, range(n_steps)))
+        kc = list(ex.map(w.k_cur, range(n_steps))) if cfg.intra_split else []
+        vc = list(ex.map(w.v_cur, range(n_steps))) if cfg.intra_split else []
     return dict(pages_k=pk, pages_v=pv, e_k=w.e_k(), e_v=w.e_v(), w_g=w.w_g(), tau=w.tau(), q=qs, x=xs,
-                target_pages=w.plant.target_pages)
+                k_cur=kc, v_cur=vc, target_pages=w.plant.target_pages)
 
 
 def chunk_prompts(cfg: Config, pages_per_chunk: int, emb_dim: int = 512, noise: float = 0.5, layer: int = 0):

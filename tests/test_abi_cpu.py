@@ -253,3 +253,25 @@ def test_bank_limits(lib):
     assert lib.hsa_score_chunk_pages_devtab(gp, p, p, p, 256, None, p, 1, p, p, p, ws_big, None) == 1
     small = lib.hsa_workspace_bytes(gp, 256) - 1
     assert lib.hsa_score_pages_devtab(gp, p, p, p, 256, p, p, p, small, None) == 5
+
+
+def test_history_and_chunk_modes_need_intra_chunk_keys(lib):
+    """The history/chunk split of the linear branch and the chunk-only gather
+    exist only with intra-chunk keys; one linear mode at a time."""
+    p = ctypes.c_void_p(256)
+    plain, intra = c1_geom(), c1_geom(intra_split=2)
+    ws = lib.hsa_workspace_bytes(ctypes.byref(intra), 16)
+    for flags in (_lib.HSA_LIN_HISTORY_PROJ, _lib.HSA_LIN_CHUNK_PROJ):
+        assert lib.hsa_linear_branch(ctypes.byref(plain), p, p, p, p, p, p, p, p, flags, p, ws, None) == 4
+    for flags in (_lib.HSA_LIN_HISTORY_PROJ | _lib.HSA_LIN_CHUNK_PROJ, _lib.HSA_LIN_REUSE_PROJ | _lib.HSA_LIN_CHUNK_PROJ,
+                  _lib.HSA_LIN_PROJ_ONLY | _lib.HSA_LIN_HISTORY_PROJ, 16):
+        assert lib.hsa_linear_branch(ctypes.byref(intra), p, p, p, p, p, p, p, p, flags, p, ws, None) == 4, flags
+    # the history projection needs no queries or output; the chunk mode needs both
+    assert lib.hsa_linear_branch(ctypes.byref(intra), p, None, p, p, p, p, p, p, _lib.HSA_LIN_HISTORY_PROJ, p, ws,
+                                 None) == 1
+    assert lib.hsa_linear_branch(ctypes.byref(intra), None, p, p, p, p, p, p, p, _lib.HSA_LIN_CHUNK_PROJ, p, ws,
+                                 None) == 1
+    assert lib.hsa_linear_branch(ctypes.byref(intra), p, p, p, p, p, p, p, p, _lib.HSA_LIN_CHUNK_PROJ, p,
+                                 lib.hsa_linear_workspace_bytes(ctypes.byref(intra)) - 1, None) == 5
+    assert lib.hsa_gather_chunk(ctypes.byref(plain), p, p, p, p, None, None) == 4
+    assert lib.hsa_gather_chunk(ctypes.byref(intra), None, p, p, p, None, None) == 1

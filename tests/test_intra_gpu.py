@@ -138,3 +138,55 @@ def test_intra_graph_replays_match_eager():
             assert torch.equal(getattr(st, k), ref[k]), f"replay {rep}: {k}"
         r.run()
         torch.cuda.synchronize()
+
+
+def test_chunk_gather_rewrites_only_the_chunk(ran):
+    """hsa_gather_chunk with another step's keys equals the whole gather with
+    them, bit for bit, and leaves the history part as it was."""
+    from sparse_linear_attention_hsa_amd import ops
+    st, cfg = ran.step, ran.cfg
+    k2 = torch.flip(ran.k_cur, dims=[0]).contiguous()  # other keys and values for the chunk
+    v2 = torch.flip(ran.v_cur, dims=[0]).contiguous()
+    ran.run()
+    hist = st.k_act[:, :cfg.history_tokens].clone()
+    ops.hsa_gather_chunk(st.geom, k2, v2, st.k_act, st.v_act, st.kblk_mean)
+    torch.cuda.synchronize()
+    got = [t.clone() for t in (st.k_act, st.v_act, st.kblk_mean)]
+    assert torch.equal(got[0][:, :cfg.history_tokens], hist)
+    st.gather(ran.pk, ran.pv, k_cur=k2, v_cur=v2)
+    torch.cuda.synchronize()
+    for a, b in zip(got, (st.k_act, st.v_act, st.kblk_mean)):
+        assert torch.equal(a, b)
+
+
+def test_history_and_chunk_projections_add_up(ran):
+    """HSA_LIN_HISTORY_PROJ then HSA_LIN_CHUNK_PROJ gives the linear branch of
+    the whole sequence: the history's projection against the oracle's over
+    the history keys, O_lin against the oracle and against the single call
+    (the sums differ only in order), and the history projection unchanged."""
+    from sparse_linear_attention_hsa_amd import ops
+    from sparse_linear_attention_hsa_amd._lib import HSA_LIN_CHUNK_PROJ, HSA_LIN_HISTORY_PROJ
+    st, cfg = ran.step, ran.cfg
+    ran.run(concurrent=False)
+    full = st.o_lin.clone()
+    kh, vh = torch.empty_like(st.k_proj), torch.empty_like(st.v_proj)
+    ops.hsa_linear_branch(st.geom, None, st.k_act, st.v_act, ran.e_k, ran.e_v, kh, vh, None, HSA_LIN_HISTORY_PROJ,
+                          st.ws)
+    torch.cuda.synchronize()
+    kh0, vh0 = kh.clone(), vh.clone()
+    st.o_lin.zero_()
+    ops.hsa_linear_branch(st.geom, ran.q, st.k_act, st.v_act, ran.e_k, ran.e_v, kh, vh, st.o_lin,
+                          HSA_LIN_CHUNK_PROJ, st.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(kh, kh0) and torch.equal(vh, vh0)
+    sel = st.sel_pages.cpu().numpy()
+    k_hist, v_hist = orc.gather_active(ran.pk_np, sel), orc.gather_active(ran.pv_np, sel)
+    lh = cfg.history_tokens
+    proj_tol = (2e-4, 1e-5)
+    assert_close("history K~", host(kh), orc.project(ran.np["e_k"][:, :lh], k_hist), cfg, proj_tol)
+    assert_close("history V~", host(vh).transpose(0, 2, 1), orc.project(ran.np["e_v"][:, :lh], v_hist), cfg,
+                 proj_tol)
+    ref = ran.oracle(sel_pages=sel)
+    assert_close("o_lin", host(st.o_lin), ref["lin"]["o_lin"], cfg)
+    f32 = cfg.dtype == "f32"
+    assert_close("o_lin vs one call", host(st.o_lin), host(full), cfg, (1e-5, 1e-6) if f32 else (2e-3, 2e-4))

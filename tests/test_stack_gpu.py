@@ -12,6 +12,8 @@ bit for bit.
 """
 from __future__ import annotations
 
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -19,7 +21,7 @@ import torch
 from oracle import hsa_oracle as orc
 from synth import CONFIGS, layer_arrays, stack_host_pages
 
-from gpu_harness import TOL, assert_close, check_block_selection, geom_of
+from gpu_harness import TOL, assert_close, candidates_of, check_block_selection, geom_of
 
 pytestmark = pytest.mark.gpu
 
@@ -41,11 +43,13 @@ def _build(cfg, layers_needed_host=()):
         qs = [up(x) for x in a["q"]]
         xs = [up(x) for x in a["x"]]
         e_k, e_v, w_g = up(a["e_k"]), up(a["e_v"]), up(a["w_g"])
+        kc = [up(x) for x in a["k_cur"]]
+        vc = [up(x) for x in a["v_cur"]]
         tau = torch.from_numpy(a["tau"]).cuda()
-        lay = make_layer_inputs(geom, pk, pv, host_ids[l], e_k, e_v, w_g, tau, qs, xs)
+        lay = make_layer_inputs(geom, pk, pv, host_ids[l], e_k, e_v, w_g, tau, qs, xs, kc, vc)
         streamed.append(lay)
         resident.append(LayerInputs(pages_k=pk, pages_v=pv, host_k={}, host_v={}, e_k=e_k, e_v=e_v, w_g=w_g,
-                                    tau=tau, page_kmean=lay.page_kmean, q=lay.q, x=lay.x))
+                                    tau=tau, page_kmean=lay.page_kmean, q=lay.q, x=lay.x, k_cur=kc, v_cur=vc))
     return geom, host_ids, streamed, resident, keep
 
 
@@ -72,7 +76,8 @@ def _run(cfg, geom, host_ids, inputs, pairs, n_slots=4, concurrent=True):
 
 
 def _check_layer_step(cfg, a, s, gpu_sel, r):
-    """Oracle for one (layer, step) with the first step's pages, over every row."""
+    """Oracle for one (layer, step) with the first step's pages, over every
+    row; with intra-chunk keys the step's own keys follow the pages."""
     B, H = cfg.block, cfg.n_heads
     sc = orc.score_and_select(a["q"][0], a["pages_k"], cfg.n_sel_pages)
     if not np.array_equal(gpu_sel, sc["sel"]):
@@ -80,21 +85,37 @@ def _check_layer_step(cfg, a, s, gpu_sel, r):
     k_act = orc.gather_active(a["pages_k"], gpu_sel)
     v_act = orc.gather_active(a["pages_v"], gpu_sel)
     q, x = a["q"][s], a["x"][s]
-    bs = orc.block_selection(q, k_act, a["tau"], B)
     gl = [[r["idx"][h, i, :r["cnt"][h, i]].astype(np.int64) for i in range(cfg.n_qblocks)] for h in range(H)]
-    check_block_selection(bs, gl, a["tau"])
+    if cfg.intra_split:
+        lh = k_act.shape[1]
+        k_act = np.concatenate([k_act, np.asarray(a["k_cur"][s], np.float64).transpose(1, 0, 2)], axis=1)
+        v_act = np.concatenate([v_act, np.asarray(a["v_cur"][s], np.float64).transpose(1, 0, 2)], axis=1)
+        parts = orc.key_parts(lh, B, cfg.query_tokens, cfg.key_block)
+        bs = orc.block_selection_parts(q, k_act, a["tau"], B, parts)
+        grp, nt = B // cfg.key_block, cfg.n_kblocks
+        cands = [[candidates_of(gl[h][i], nt, grp) for i in range(cfg.n_qblocks)] for h in range(H)]
+        assert all(c is not None for row in cands for c in row), "incomplete history tile"
+        check_block_selection(bs, cands, a["tau"])
+    else:
+        bs = orc.block_selection(q, k_act, a["tau"], B)
+        check_block_selection(bs, gl, a["tau"])
     ktil, vtil = orc.project(a["e_k"], k_act), orc.project(a["e_v"], v_act)
     o_lin_ref = orc.linear_attention(q, ktil, vtil)
-    o_sp_ref = orc.sparse_attention(q, k_act, v_act, gl, B)
+    if cfg.intra_split:
+        o_sp_ref = orc.sparse_attention_parts(q, k_act, v_act, cands, B, parts)
+    else:
+        o_sp_ref = orc.sparse_attention(q, k_act, v_act, gl, B)
     out_ref = orc.fuse(x, a["w_g"], o_lin_ref, o_sp_ref)
     assert_close("o_lin", r["o_lin"], o_lin_ref, cfg)
     assert_close("o_sp", r["o_sp"], o_sp_ref, cfg)
     assert_close("out", r["out"], out_ref, cfg)
 
 
-@pytest.mark.parametrize("n_slots", [2, 4])
-def test_stack_small_every_layer_step(n_slots):
+@pytest.mark.parametrize("n_slots,intra", [(2, 0), (4, 0), (3, 2)], ids=["slots2", "slots4", "intra2"])
+def test_stack_small_every_layer_step(n_slots, intra):
     cfg = CONFIGS["m6_stack"]
+    if intra:  # the chunk's own keys in 48-token blocks, new keys every denoising step
+        cfg = replace(cfg, name="m6_stack_intra2", intra_split=intra)
     print(f"\n[stack] {cfg.name}: {cfg.layers} layers x {cfg.steps} steps, {n_slots} staging slots, host pages "
           f"{[h.tolist() for h in stack_host_pages(cfg)]}", flush=True)
     geom, host_ids, streamed, resident, keep = _build(cfg, layers_needed_host=range(cfg.layers))
