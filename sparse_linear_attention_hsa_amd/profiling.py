@@ -54,6 +54,19 @@ def _one(pattern: str) -> str:
 
 
 def _short(name: str) -> str:
+    if name.startswith("_Z"):  # a name the profiler left mangled: keep the kernel's own identifier
+        i = 2
+        while i < len(name):  # walk the length-prefixed source names
+            m = re.match(r"\d+", name[i:])
+            if not m:
+                i += 1
+                continue
+            n, j = int(m.group(0)), i + len(m.group(0))
+            ident = name[j:j + n]
+            if ident.endswith("_kernel"):
+                return f"hsa::{ident} (mangled)"
+            i = j + n
+        return name
     name = re.sub(r"\(anonymous namespace\)::", "", name)
     name = re.sub(r"\(.*\)$", "", name)  # drop the parameter list
     return name.replace("void ", "", 1)
