@@ -76,7 +76,9 @@ ProjPlan proj_plan(const Dims& s, int n_tok) {
   // second round and double the kernel's time.
   p.splits = std::max(1, std::min(p.steps, 256 / (2 * ((s.H + 1) / 2))));
   p.rtiles = cdiv(s.r, 16);
-  p.rpad = cdiv(s.r, K) * K;
+  // the linear attention streams the rank axis in chunks of K ranks through
+  // a ring of four LDS slots, whole rounds of the ring per pass
+  p.rpad = cdiv(s.r, 4 * K) * 4 * K;
   return p;
 }
 

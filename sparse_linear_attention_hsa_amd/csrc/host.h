@@ -41,7 +41,7 @@ struct ProjPlan {
   int splits;        // S: slices of the sequence axis per (head, K|V)
   int steps;         // contraction steps of the whole sequence
   int rtiles;        // ceil(r / 16)
-  int rpad;          // r padded to the product's contraction step
+  int rpad;          // r padded to four contraction steps (one round of the attention ring)
 };
 // n_tok: tokens the projection contracts (all L by default)
 ProjPlan proj_plan(const Dims& s, int n_tok = -1);

@@ -409,21 +409,25 @@ __global__ __launch_bounds__(256) void lin_prep_kernel(const float* __restrict__
 }
 
 // Attention over the r projected keys.  A workgroup (8 waves) takes a run of
-// 32-query units of one head.  It first stages the head's whole Ktil (and
-// for bf16 its low part) in LDS with direct loads, swizzled by kswz, behind a
-// single barrier; then every wave walks its units independently: S^T =
-// Ktil Q^T chunk by chunk over the rank axis (keys on the rows, one query
-// per accumulator column), an online softmax, and O^T += Vtil^T P^T with the
-// Vtil^T operand (for bf16 its high and low parts) read straight from memory
-// at the start of the chunk (a head's Vtil^T is 64 KB per part and stays in
-// L2).  For bf16 the weights are rounded to bf16 for the product, and the
-// denominator is summed from the same rounded weights (an all-ones tile), so
-// numerator and denominator use identical weights.  Chunk rows past r are
-// masked.
+// 32-query units of one head, eight at a time (one per wave: a pass).  The
+// rank axis is streamed in chunks of KS ranks: each chunk's Ktil rows and
+// Vtil^T columns (for bf16 both high and low parts) are staged in LDS by
+// direct loads, in a ring of four slots three chunks ahead, and all eight
+// waves read them from there, so a chunk crosses the L2 once per pass
+// instead of once per wave.  Per chunk every wave computes S^T = Ktil Q^T
+// (ranks on the rows, one query per accumulator column), an online softmax
+// with lazy rescale, and O^T += Vtil^T P^T.  For bf16 the weights are
+// rounded to bf16 for the product, and the denominator is the product of an
+// all-ones tile with the same packed weights, so numerator and denominator
+// use identical weights.  Chunk rows past r are masked.
 constexpr int kAttWaves = 8;
 constexpr int kAttThreads = kAttWaves * kWave;
-constexpr int kAttMaxRank = 256;
 constexpr int kAttUnit = 32;  // queries per unit: two 16-row tiles share every Ktil operand read
+constexpr int kAttRing = 4;
+
+// V^T chunk rows are 64 bytes (KS ranks): 16-byte slot = chunk ^ vswz(row),
+// so the 16 rows one lane group reads at one chunk index use distinct banks.
+__device__ __forceinline__ int vswz(int row) { return (row >> 2) & 3; }
 
 template <typename T, int D>
 __global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lin_attend_kernel(
@@ -431,165 +435,221 @@ __global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const T* __restrict__ vlo, int H, int Lq, int r, int rpad, int units_per_wg, float scale_log2,
     float* __restrict__ o_lin) {
   constexpr int E = Vec<T>::N;
-  constexpr int KS = Mma<T>::K;        // rank rows per chunk (= one PV contraction step)
+  constexpr int KS = Mma<T>::K;        // ranks per chunk (= one PV contraction step)
   constexpr int GPS = KS / 16;         // 16-row tiles per chunk
   constexpr int CPR = D / E;           // 16-byte chunks per Ktil row
   constexpr int DSTEPS = D / KS;
   constexpr int DT = D / 16;
   constexpr int QT = kAttUnit / 16;
   constexpr bool SPLIT = sizeof(T) == 2;
-  constexpr int ROWB = D * (int)sizeof(T);
-  constexpr int RPI = 1024 / ROWB;     // Ktil rows per direct-load instruction
-  constexpr int PART = kAttMaxRank * ROWB;
-  __shared__ __align__(1024) unsigned char lds_k[SPLIT ? 2 * PART : PART];
+  constexpr int NPART = SPLIT ? 2 : 1;
+  constexpr int KROWB = D * (int)sizeof(T);
+  constexpr int KBYTES = KS * KROWB;   // one part of a chunk's Ktil rows
+  constexpr int VROWB = KS * (int)sizeof(T);
+  constexpr int VBYTES = D * VROWB;    // one part of a chunk's Vtil^T columns
+  constexpr int KRPI = 1024 / KROWB;   // Ktil rows per direct-load instruction
+  constexpr int VRPI = 1024 / VROWB;   // Vtil^T rows per instruction
+  constexpr int VCPR = VROWB / 16;     // 16-byte chunks per Vtil^T row
+  constexpr int NINST = NPART * (KBYTES + VBYTES) / 1024;
+  constexpr int PER = NINST / kAttWaves;  // direct loads per wave per chunk
+  constexpr int STAGE = NPART * (KBYTES + VBYTES);
+  static_assert(VROWB == 64 && VCPR == 4, "V^T chunk rows of 64 bytes");
+  static_assert(NINST % kAttWaves == 0 && PER < 64, "stage tiling");
+  // one LDS object per ring slot, so every operand read names a fixed slot
+  // and the compiler does not make it wait for the loads into the others
+  __shared__ __align__(1024) unsigned char lds0[STAGE], lds1[STAGE], lds2[STAGE], lds3[STAGE];
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g = lane >> 4, c = lane & 15;
   const int h = blockIdx.y;
   const int nchunk = rpad / KS;
-
-  // stage Ktil (high and low parts) of head h
-  const int ninst = rpad / RPI;
-#pragma unroll
-  for (int part = 0; part < (SPLIT ? 2 : 1); ++part) {
-    const T* src = (part ? klo : khi) + (size_t)h * rpad * D;
-    for (int i = w; i < ninst; i += kAttWaves) {
-      const int row = i * RPI + lane / CPR;
-      const int chunk = (lane % CPR) ^ kswz<T>(row, CPR);
-      load_lds16(src + (size_t)row * D + chunk * E, lds_k + part * PART + i * 1024);
-    }
-  }
-  wait_vm();
-  __syncthreads();
-
   const int units = (Lq + kAttUnit - 1) / kAttUnit;
   const int u_begin = blockIdx.x * units_per_wg;
   const int u_end = min(units, u_begin + units_per_wg);
+  if (u_begin >= u_end) return;  // uniform over the workgroup
+  const int passes = (u_end - u_begin + kAttWaves - 1) / kAttWaves;
+  const int nst = passes * nchunk;
+  const T* kh = khi + (size_t)h * rpad * D;
+  const T* kl = klo + (size_t)h * rpad * D;
   const T* vh = vt + (size_t)h * D * rpad;
-  const T* vl = vlo + (size_t)h * D * rpad;  // bf16 only
-  // all-ones A operand (bf16 1.0 pairs): its product with P^T holds in every
-  // row the column sums of the rounded weights, the denominator that matches
-  // the numerator's weights exactly
-  const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
-  for (int u = u_begin + w; u < u_end; u += kAttWaves) {
-    const int qbase = u * kAttUnit;
-    uint4 qreg[QT][DSTEPS];
+  const T* vl = vlo + (size_t)h * D * rpad;
+
+  // chunk (stage % nchunk) into one slot: [Ktil hi][Ktil lo][Vt hi][Vt lo]
+  auto issue = [&](int stage, unsigned char* slot) {
+    const int ch = stage % nchunk;
 #pragma unroll
-    for (int t = 0; t < QT; ++t) {
-      const int qrow = qbase + 16 * t + c;
-#pragma unroll
-      for (int s = 0; s < DSTEPS; ++s)
-        qreg[t][s] = ld16_masked(q + ((size_t)min(qrow, Lq - 1) * H + h) * D + (4 * s + g) * E, qrow < Lq);
-    }
-    f32x4 o[QT][DT];
-    f32x4 lacc[QT];  // bf16: denominators from the ones tile
-    float m_run[QT], l_run[QT];
-#pragma unroll
-    for (int t = 0; t < QT; ++t) {
-      m_run[t] = -INFINITY;
-      l_run[t] = 0.f;
-      lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int ch = 0; ch < nchunk; ++ch) {
-      // this chunk's Vtil^T operands, lane (g, c) holding row 16*dt + c,
-      // ranks ch*KS + g*E ...; their latency hides behind S and the softmax
-      uint4 vop[DT], vop_lo[DT];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const size_t off = (size_t)(16 * dt + c) * rpad + ch * KS + g * E;
-        vop[dt] = ld16(vh + off);
-        if (SPLIT) vop_lo[dt] = ld16(vl + off);
+    for (int ii = 0; ii < PER; ++ii) {
+      const int i = ii * kAttWaves + w;  // instruction index in the stage
+      const void* src;
+      if (i < NPART * KBYTES / 1024) {
+        const int part = i / (KBYTES / 1024), k = i % (KBYTES / 1024);
+        const int row = k * KRPI + lane / CPR;  // row inside the chunk
+        const int chunk = (lane % CPR) ^ kswz<T>(row, CPR);
+        src = (part ? kl : kh) + (size_t)(ch * KS + row) * D + chunk * E;
+      } else {
+        const int iv = i - NPART * KBYTES / 1024;
+        const int part = iv / (VBYTES / 1024), k = iv % (VBYTES / 1024);
+        const int row = k * VRPI + lane / VCPR;  // d row
+        const int chunk = (lane % VCPR) ^ vswz(row);
+        src = (part ? vl : vh) + (size_t)row * rpad + ch * KS + chunk * E;
       }
-      f32x4 sacc[QT][GPS];
+      load_lds16(src, slot + i * 1024);
+    }
+  };
+
+  const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);  // bf16 1.0 pairs
+  uint4 qreg[QT][DSTEPS];
+  f32x4 o[QT][DT];
+  f32x4 lacc[QT];  // bf16: denominators from the ones tile
+  float m_run[QT], l_run[QT];
+
+  // one chunk of ranks against this wave's unit
+  auto compute = [&](int ch, const unsigned char* slot) {
+    const unsigned char* lk = slot;
+    const unsigned char* lv = slot + NPART * KBYTES;
+    f32x4 sacc[QT][GPS];
 #pragma unroll
-      for (int t = 0; t < QT; ++t)
+    for (int t = 0; t < QT; ++t)
 #pragma unroll
-        for (int kt = 0; kt < GPS; ++kt) sacc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kt = 0; kt < GPS; ++kt) sacc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kt = 0; kt < GPS; ++kt) {
-        const int row = ch * KS + perm_row<T>(kt, c);
-        const int sw = kswz<T>(row, CPR);
-        const unsigned char* krow = lds_k + row * ROWB;
+    for (int kt = 0; kt < GPS; ++kt) {
+      const int row = perm_row<T>(kt, c);
+      const int sw = kswz<T>(row, CPR);
+      const unsigned char* krow = lk + row * KROWB;
 #pragma unroll
-        for (int s = 0; s < DSTEPS; ++s) {
-          const int off = ((4 * s + g) ^ sw) * 16;
-          const uint4 ah = *reinterpret_cast<const uint4*>(krow + off);
+      for (int s = 0; s < DSTEPS; ++s) {
+        const int off = ((4 * s + g) ^ sw) * 16;
+        const uint4 ah = *reinterpret_cast<const uint4*>(krow + off);
 #pragma unroll
-          for (int t = 0; t < QT; ++t) Mma<T>::run(sacc[t][kt], ah, qreg[t][s]);
-          if (SPLIT) {
-            const uint4 al = *reinterpret_cast<const uint4*>(krow + PART + off);
+        for (int t = 0; t < QT; ++t) Mma<T>::run(sacc[t][kt], ah, qreg[t][s]);
+        if (SPLIT) {
+          const uint4 al = *reinterpret_cast<const uint4*>(krow + KBYTES + off);
 #pragma unroll
-            for (int t = 0; t < QT; ++t) Mma<T>::run(sacc[t][kt], al, qreg[t][s]);
-          }
+          for (int t = 0; t < QT; ++t) Mma<T>::run(sacc[t][kt], al, qreg[t][s]);
         }
       }
-      const bool ragged = (ch + 1) * KS > r;  // uniform
-      uint4 pk[QT];
-      float alpha[QT];
-      bool need_any = false;
+    }
+    const bool ragged = (ch + 1) * KS > r;  // uniform
+    uint4 pk[QT];
+    float alpha[QT];
+    bool need_any = false;
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < GPS; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (ragged && ch * KS + perm_row<T>(kt, 4 * g + i) >= r) sacc[t][kt][i] = -INFINITY;
+          mx = fmaxf(mx, sacc[t][kt][i]);
+        }
+      mx = max4g(mx) * scale_log2;
+      // lazy rescale: the reference max moves only when the new maximum
+      // exceeds it by more than 2^8 (weights stay <= 256, exact in fp32)
+      const bool need = mx > m_run[t] + 8.f;
+      alpha[t] = need ? fast_exp2(m_run[t] - mx) : 1.f;
+      m_run[t] = need ? mx : m_run[t];
+      need_any = need_any || need;
+      float ls = 0.f;
+      f32x4 p[GPS];
+#pragma unroll
+      for (int kt = 0; kt < GPS; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = fast_exp2(fmaf(sacc[t][kt][i], scale_log2, -m_run[t]));
+          p[kt][i] = e;
+          if (!SPLIT) ls += e;
+        }
+      if (!SPLIT) l_run[t] = l_run[t] * alpha[t] + ls;
+      pk[t] = pack_p<T>(p);
+    }
+    if (__any(need_any)) {
 #pragma unroll
       for (int t = 0; t < QT; ++t) {
-        float mx = -INFINITY;
+        if (SPLIT) lacc[t] *= alpha[t];
 #pragma unroll
-        for (int kt = 0; kt < GPS; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (ragged && ch * KS + perm_row<T>(kt, 4 * g + i) >= r) sacc[t][kt][i] = -INFINITY;
-            mx = fmaxf(mx, sacc[t][kt][i]);
-          }
-        mx = max4g(mx) * scale_log2;
-        // lazy rescale: the reference max moves only when the new maximum
-        // exceeds it by more than 2^8 (weights stay <= 256, exact in fp32)
-        const bool need = mx > m_run[t] + 8.f;
-        alpha[t] = need ? fast_exp2(m_run[t] - mx) : 1.f;
-        m_run[t] = need ? mx : m_run[t];
-        need_any = need_any || need;
-        float ls = 0.f;
-        f32x4 p[GPS];
-#pragma unroll
-        for (int kt = 0; kt < GPS; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float e = fast_exp2(fmaf(sacc[t][kt][i], scale_log2, -m_run[t]));
-            p[kt][i] = e;
-            if (!SPLIT) ls += e;
-          }
-        if (!SPLIT) l_run[t] = l_run[t] * alpha[t] + ls;
-        pk[t] = pack_p<T>(p);
-      }
-      if (__any(need_any)) {
-#pragma unroll
-        for (int t = 0; t < QT; ++t) {
-          if (SPLIT) lacc[t] *= alpha[t];
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha[t];
-        }
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int t = 0; t < QT; ++t) {
-          Mma<T>::run(o[t][dt], vop[dt], pk[t]);
-          if (SPLIT) Mma<T>::run(o[t][dt], vop_lo[dt], pk[t]);
-        }
-      if (SPLIT) {
-#pragma unroll
-        for (int t = 0; t < QT; ++t) Mma<T>::run(lacc[t], ones, pk[t]);
+        for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha[t];
       }
     }
 #pragma unroll
-    for (int t = 0; t < QT; ++t) {
-      const int qrow = qbase + 16 * t + c;
-      if (qrow < Lq) {
-        const float inv = 1.f / (SPLIT ? lacc[t][0] : sum4g(l_run[t]));
-        float* dst = o_lin + ((size_t)qrow * H + h) * D + 4 * g;
+    for (int dt = 0; dt < DT; ++dt) {
+      // lane (g, c) takes V^T row 16*dt + c, ranks g*E .. of the chunk
+      const int vr = 16 * dt + c;
+      const int voff = vr * VROWB + ((g ^ vswz(vr)) * 16);
+      const uint4 a = *reinterpret_cast<const uint4*>(lv + voff);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<float4*>(dst + 16 * dt) =
-              make_float4(o[t][dt][0] * inv, o[t][dt][1] * inv, o[t][dt][2] * inv, o[t][dt][3] * inv);
+      for (int t = 0; t < QT; ++t) Mma<T>::run(o[t][dt], a, pk[t]);
+      if (SPLIT) {
+        const uint4 al = *reinterpret_cast<const uint4*>(lv + VBYTES + voff);
+#pragma unroll
+        for (int t = 0; t < QT; ++t) Mma<T>::run(o[t][dt], al, pk[t]);
+      }
+    }
+    if (SPLIT) {
+#pragma unroll
+      for (int t = 0; t < QT; ++t) Mma<T>::run(lacc[t], ones, pk[t]);
+    }
+  };
+
+  // One ring step: chunk i has landed (later ones may stay in flight) and
+  // every wave is done with chunk i-1, whose slot takes chunk i+3; then
+  // chunk i is used.  Stages run over the passes without a break, so the
+  // next pass's first chunks load during this pass's last ones.
+  bool active = false;
+  auto step = [&](int i, const unsigned char* cur, unsigned char* refill) {
+    const int later = nst - 1 - i;  // stages issued after i: min(later, 2)
+    if (later >= 2) ring_barrier<2 * PER>();
+    else if (later == 1) ring_barrier<PER>();
+    else ring_barrier<0>();
+    if (i + 3 < nst) issue(i + 3, refill);
+    if (active) compute(i % nchunk, cur);
+  };
+  issue(0, lds0);
+  if (nst > 1) issue(1, lds1);
+  if (nst > 2) issue(2, lds2);
+  for (int pass = 0; pass < passes; ++pass) {
+    // this wave's unit of the pass: queries, then fresh softmax state
+    const int u = u_begin + pass * kAttWaves + w;
+    active = u < u_end;  // wave-uniform
+    const int qbase = u * kAttUnit;
+    if (active) {
+#pragma unroll
+      for (int t = 0; t < QT; ++t) {
+        const int qrow = qbase + 16 * t + c;
+        // rows past Lq read row Lq-1 (never stored: each query column is
+        // independent), so the loads need no select right after them
+#pragma unroll
+        for (int s = 0; s < DSTEPS; ++s) qreg[t][s] = ld16(q + ((size_t)min(qrow, Lq - 1) * H + h) * D + (4 * s + g) * E);
+        m_run[t] = -INFINITY;
+        l_run[t] = 0.f;
+        lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    // the ring slot of stage i is i % 4 and a pass has nchunk (a multiple of
+    // 4) stages, so every pass starts at slot 0
+    const int i0 = pass * nchunk;
+    for (int k = 0; k < nchunk; k += kAttRing) {
+      step(i0 + k, lds0, lds3);
+      step(i0 + k + 1, lds1, lds0);
+      step(i0 + k + 2, lds2, lds1);
+      step(i0 + k + 3, lds3, lds2);
+    }
+    if (active) {
+#pragma unroll
+      for (int t = 0; t < QT; ++t) {
+        const int qrow = qbase + 16 * t + c;
+        if (qrow < Lq) {
+          const float inv = 1.f / (SPLIT ? lacc[t][0] : sum4g(l_run[t]));
+          float* dst = o_lin + ((size_t)qrow * H + h) * D + 4 * g;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            *reinterpret_cast<float4*>(dst + 16 * dt) =
+                make_float4(o[t][dt][0] * inv, o[t][dt][1] * inv, o[t][dt][2] * inv, o[t][dt][3] * inv);
+        }
       }
     }
   }
