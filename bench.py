@@ -58,7 +58,9 @@ def stage_model(cfg, n_sel_total: int, indexed: bool = False, scored_pages=None,
     return {
         "score": dict(bound="hbm", bytes=(P * D * 4 if indexed else P * Lp * D * es) + Lq * D * es),
         # paged: the gather stage only moves the selected pages' block means
-        "gather": dict(bound="hbm", bytes=2 * H * (L // Bk) * d * 4 if paged else 2 * (2 * L * D * es)),
+        # (and with intra-chunk keys lays out the chunk's own keys and values)
+        "gather": dict(bound="hbm", bytes=(2 * H * (L // Bk) * d * 4 + (4 * Lq * D * es if cfg.intra_split else 0))
+                       if paged else 2 * (2 * L * D * es)),
         "linear": dict(bound="mfma", flops=2 * 2 * H * r * L * d + 2 * 2 * H * Lq * r * d,
                        bytes=2 * L * D * es + 2 * r * L * es + Lq * D * es + Lq * D * 4),
         "select": dict(bound="hbm", bytes=Lq * D * es + H * (L // Bk) * d * 4,
@@ -424,7 +426,7 @@ def run_single(args, cfg, steps: int, warmup: int, with_cpu: bool, with_peaks: b
         # block selection and the sparse branch, joined before the fusion
         # (on the current stream, which is the capture stream under --graph)
         if paged:
-            st.run_paged(q, prepared, e_k, e_v, w_g, x, tau)
+            st.run_paged(q, prepared, e_k, e_v, w_g, x, tau, k_cur=k_cur, v_cur=v_cur)
         else:
             st.run(q, pk, pv, e_k, e_v, w_g, x, tau, indexed=indexed, chunks=chunks, k_cur=k_cur, v_cur=v_cur)
 
@@ -434,15 +436,19 @@ def run_single(args, cfg, steps: int, warmup: int, with_cpu: bool, with_peaks: b
                  lambda: st.linear(q, e_k, e_v),
                  lambda: st.select(q, tau), lambda: st.sparse(q, kernel_events=kev), lambda: st.fuse(x, w_g))
         if paged:  # the same stages reading the laid-out pages
-            kp_, vp_, bm_ = prepared
-            calls = (score_stage,
-                     lambda: ops.hsa_gather_block_means(geom, bm_, st.sel_pages, st.kblk_mean),
-                     lambda: ops.hsa_linear_branch_paged(geom, q, kp_, vp_, st.sel_pages, e_k, e_v, st.k_proj,
-                                                         st.v_proj, st.o_lin, 0, st.ws),
+            tab = {}
+
+            def paged_gather():  # (with intra-chunk keys the chunk is laid out here)
+                tab["t"] = st.paged_inputs(prepared, k_cur, v_cur)
+                ops.hsa_gather_block_means(geom, tab["t"][2], tab["t"][3], st.kblk_mean)
+
+            calls = (score_stage, paged_gather,
+                     lambda: ops.hsa_linear_branch_paged(geom, q, tab["t"][0], tab["t"][1], tab["t"][3], e_k, e_v,
+                                                         st.k_proj, st.v_proj, st.o_lin, 0, st.ws),
                      lambda: ops.hsa_block_select(geom, q, None, st.kblk_mean, tau, st.blk_count, st.blk_idx,
                                                   st.blk_mass, st.ws),
-                     lambda: ops.hsa_sparse_attn_paged(geom, q, kp_, vp_, st.sel_pages, st.blk_count, st.blk_idx,
-                                                       st.o_sp, st.ws, kev),
+                     lambda: ops.hsa_sparse_attn_paged(geom, q, tab["t"][0], tab["t"][1], tab["t"][3], st.blk_count,
+                                                       st.blk_idx, st.o_sp, st.ws, kev),
                      lambda: st.fuse(x, w_g))
         for i, fn in enumerate(calls):
             ev[i][0].record(stream)
@@ -592,8 +598,8 @@ def main():
     from synth import CONFIGS
 
     cfg = CONFIGS[args.config]
-    if args.paged and (args.intra or args.chunks or args.tiers or cfg.layers > 1 or cfg.steps > 1):
-        print("bench.py: --paged runs the single-step workloads without --intra / --chunks / --tiers",
+    if args.paged and (args.chunks or args.tiers or cfg.layers > 1 or cfg.steps > 1):
+        print("bench.py: --paged runs the single-step workloads without --chunks / --tiers",
               file=sys.stderr)
         sys.exit(2)
     if args.paged:

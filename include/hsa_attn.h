@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define HSA_ATTN_ABI_VERSION 2
+#define HSA_ATTN_ABI_VERSION 3
 #define HSA_MAX_PAGES 128      /* pages per call with HOST page tables (they travel as launch arguments) */
 #define HSA_MAX_BANK_PAGES 8192 /* pages per call with DEVICE page tables (the *_devtab calls) */
 #define HSA_MAX_KBLOCKS 2048   /* nKB limit of the block selection (one sort per row in LDS) */
@@ -431,32 +431,59 @@ hsa_rc hsa_fuse(const hsa_geom* geom, const void* x, const void* w_g, const floa
  * the pages' own profile names as the largest cost of the step.  A page is
  * laid out once, when it is written, in the layouts the kernels read: K as
  * [H][Lp][d] and V as [H][Lp/16][d][16] (the active buffer's layouts over
- * one page), with the mean of every B-token block [H][Lp/B][d] float32.  A
- * step then scores from the page index (hsa_score_pages with NULL page
- * pointers and page_kmean), takes the selected pages' block means
- * (hsa_gather_block_means, for hsa_block_select with k_act = NULL), and runs
- * the linear and sparse branches straight from the laid-out pages: active key
- * t is token t % Lp of page sel_pages[t / Lp], so every result is the one the
- * active-buffer path computes.  Requires intra_split = 0 (HSA_ERR_BAD_PARAM).
+ * one page), with the mean of every key block [H][Lp/Bk][d] float32 (Bk = B,
+ * or B / intra_split).  A step then scores from the page index
+ * (hsa_score_pages with NULL page pointers and page_kmean), takes the
+ * selected pages' block means (hsa_gather_block_means, for hsa_block_select
+ * with k_act = NULL), and runs the linear and sparse branches straight from
+ * the laid-out pages: active key t is token t % Lp of page sel_pages[t / Lp],
+ * so every result is the one the active-buffer path computes.
+ *
+ * Intra-chunk keys (intra_split > 0; paper section 3.3, "Inter- and
+ * intra-chunk sparse granularity"): the chunk's own keys and values are laid
+ * out each step into hsa_chunk_page_count() page-format buffers
+ * (hsa_chunk_prepare), which the caller adds to its page table.  sel_pages
+ * then holds K_p + hsa_chunk_page_count() entries: the K_p selected pages
+ * (as hsa_score_pages writes them) followed by the table indices of the
+ * chunk's buffers in order, so the same rule reaches the chunk's key
+ * t - Lh at token (t - Lh) % Lp of its buffer (t - Lh) / Lp.
  * ------------------------------------------------------------------------- */
 
 /* Lay out one page: k_page, v_page [Lp][H][d] dtype (as the model writes
  * them) -> k_out [H][Lp][d], v_out [H][Lp/16][d][16] dtype, blk_mean
- * [H][Lp/B][d] float32 (or NULL).  The output buffers are the caller's and
+ * [H][Lp/Bk][d] float32 (or NULL).  The output buffers are the caller's and
  * must not overlap the inputs.  Errors: HSA_ERR_NULL_ARG, geometry errors. */
 hsa_rc hsa_page_prepare(const hsa_geom* geom, const void* k_page, const void* v_page, void* k_out, void* v_out,
                         float* blk_mean, hsa_stream stream);
 
-/* kblk_mean [H][nKB][d] float32 out: the block means of the selected pages,
- * from page_blk_mean, a HOST array of n_pages device pointers, each a page's
- * blk_mean from hsa_page_prepare.  sel_pages [K_p] int32 device, as
- * hsa_gather_pages (out-of-range ids are clamped).  Errors: HSA_ERR_NULL_ARG
- * (any entry NULL), HSA_ERR_BAD_PARAM (n_pages). */
+/* Page-format buffers that hold the chunk's own keys with intra-chunk keys:
+ * ceil(Lq / Lp); 0 if the geometry is invalid or has intra_split = 0. */
+int32_t hsa_chunk_page_count(const hsa_geom* geom);
+
+/* Lay out the chunk's own keys and values for the paged calls (intra_split >
+ * 0): k_cur, v_cur [Lq][H][d] dtype -> buffer j = 0 .. n-1 (n =
+ * hsa_chunk_page_count) holds the chunk's tokens j*Lp .. min((j+1)*Lp, Lq)-1
+ * in the page layout (k_out[j] [H][Lp][d], v_out[j] [H][Lp/16][d][16]
+ * dtype, blk_mean[j] [H][Lp/Bk][d] float32); entries past the chunk's last
+ * token are left as they are and never read.  k_out, v_out, blk_mean are HOST
+ * arrays of n device pointers (blk_mean itself may be NULL).  Errors:
+ * HSA_ERR_BAD_PARAM (intra_split = 0), HSA_ERR_NULL_ARG, geometry errors. */
+hsa_rc hsa_chunk_prepare(const hsa_geom* geom, const void* k_cur, const void* v_cur, void* const* k_out,
+                         void* const* v_out, float* const* blk_mean, hsa_stream stream);
+
+/* kblk_mean [H][nKB][d] float32 out: the block means of the selected pages
+ * (and with intra-chunk keys the chunk's), from page_blk_mean, a HOST array
+ * of n_pages device pointers, each a page's blk_mean from hsa_page_prepare
+ * or hsa_chunk_prepare.  sel_pages int32 device: [K_p] as hsa_gather_pages,
+ * or [K_p + hsa_chunk_page_count] with intra-chunk keys (see above);
+ * out-of-range ids are clamped.  Errors: HSA_ERR_NULL_ARG (any entry NULL),
+ * HSA_ERR_BAD_PARAM (n_pages). */
 hsa_rc hsa_gather_block_means(const hsa_geom* geom, const float* const* page_blk_mean, int32_t n_pages,
                               const int32_t* sel_pages, float* kblk_mean, hsa_stream stream);
 
 /* hsa_linear_branch over laid-out pages: page_k, page_v are HOST arrays of
- * n_pages device pointers, each a page's k_out / v_out from hsa_page_prepare;
+ * n_pages device pointers, each a page's k_out / v_out from hsa_page_prepare
+ * (or, with intra-chunk keys, a chunk buffer from hsa_chunk_prepare);
  * sel_pages as above.  Other arguments, flags, workspace and errors as
  * hsa_linear_branch; with HSA_LIN_REUSE_PROJ the pages may be NULL.
  * HSA_ERR_BAD_SHAPE if a page holds fewer than 32 tokens. */

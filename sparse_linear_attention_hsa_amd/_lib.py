@@ -54,6 +54,8 @@ SIGNATURES = {
     "hsa_gather_chunk": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp]),
     "hsa_linear_branch": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
     "hsa_page_prepare": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "hsa_chunk_page_count": (_i32, [_GP]),
+    "hsa_chunk_prepare": (_i32, [_GP, _vp, _vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp]),
     "hsa_gather_block_means": (_i32, [_GP, ctypes.POINTER(_vp), _i32, _vp, _vp, _vp]),
     "hsa_linear_branch_paged": (_i32, [_GP, _vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp,
                                        _vp, _vp, _i32, _vp, _sz, _vp]),

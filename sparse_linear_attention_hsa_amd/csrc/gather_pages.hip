@@ -178,8 +178,10 @@ void launch_gather(const Dims& s, const Tab& pk, const Tab& pv, int n_pages, con
 }
 
 // Key-block means of the selected pages from each page's own block means
-// [H][Lp/B][d] (written when the page was laid out): one thread per element
-// of kblk_mean [H][nKB][d].
+// [H][Lp/Bk][d] (written when the page was laid out): one thread per element
+// of kblk_mean [H][nKB][d]; key block j is block j % bpp of page sel[j / bpp]
+// (with intra-chunk keys the chunk's page-format buffers follow the history
+// in sel).
 __global__ __launch_bounds__(256) void gather_block_means_kernel(PageTable pm, int n_pages,
                                                                 const int32_t* __restrict__ sel, int H, int D,
                                                                 int bpp, int nKB, float* __restrict__ kblk_mean) {
@@ -197,30 +199,74 @@ __global__ __launch_bounds__(256) void gather_block_means_kernel(PageTable pm, i
 }  // namespace
 }  // namespace hsa
 
-extern "C" hsa_rc hsa_page_prepare(const hsa_geom* geom, const void* k_page, const void* v_page, void* k_out,
-                                   void* v_out, float* blk_mean, hsa_stream stream) {
-  using namespace hsa;
-  Dims s;
-  hsa_rc rc = derive(geom, &s);
-  if (rc != HSA_OK) return rc;
-  if (s.split) return HSA_ERR_BAD_PARAM;
-  if (!k_page || !v_page || !k_out || !v_out) return HSA_ERR_NULL_ARG;
-  // the active-buffer gather over one page, in table order
+namespace hsa {
+namespace {
+
+// The active-buffer gather over one page-format buffer: `tokens` tokens of
+// [tokens][H][d] rows at k_src / v_src laid out as K [H][Lp][d], V
+// [H][Lp/16][d][16] and Bk-token block means [H][Lp/Bk][d] (the layouts of
+// the active buffer over one page; a buffer may be filled only in part).
+void prepare_one(const Dims& s, int tokens, const void* k_src, const void* v_src, void* k_out, void* v_out,
+                 float* blk_mean, hipStream_t st) {
   Dims one = s;
+  one.split = 0;          // no chunk blocks of its own
   one.Kp = 1;
-  one.L = one.Lh = s.Lp;
-  one.nKB = one.nKBh = one.nC = s.Lp / s.B;
+  one.Lp = tokens;        // the blocks moved
+  one.L = one.Lh = s.Lp;  // the output strides: one page
+  one.nKB = one.nKBh = one.nC = s.Lp / s.Bk;
   PageTable pk, pv;
   for (int j = 0; j < kMaxPages; ++j) pk.p[j] = pv.p[j] = nullptr;
-  pk.p[0] = k_page;
-  pv.p[0] = v_page;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  pk.p[0] = k_src;
+  pv.p[0] = v_src;
   if (s.bf16) {
     if (s.d == 128) launch_gather<bf16_t, 128>(one, pk, pv, 1, nullptr, nullptr, nullptr, k_out, v_out, blk_mean, st);
     else launch_gather<bf16_t, 64>(one, pk, pv, 1, nullptr, nullptr, nullptr, k_out, v_out, blk_mean, st);
   } else {
     if (s.d == 128) launch_gather<float, 128>(one, pk, pv, 1, nullptr, nullptr, nullptr, k_out, v_out, blk_mean, st);
     else launch_gather<float, 64>(one, pk, pv, 1, nullptr, nullptr, nullptr, k_out, v_out, blk_mean, st);
+  }
+}
+
+}  // namespace
+}  // namespace hsa
+
+extern "C" hsa_rc hsa_page_prepare(const hsa_geom* geom, const void* k_page, const void* v_page, void* k_out,
+                                   void* v_out, float* blk_mean, hsa_stream stream) {
+  using namespace hsa;
+  Dims s;
+  hsa_rc rc = derive(geom, &s);
+  if (rc != HSA_OK) return rc;
+  if (!k_page || !v_page || !k_out || !v_out) return HSA_ERR_NULL_ARG;
+  prepare_one(s, s.Lp, k_page, v_page, k_out, v_out, blk_mean, reinterpret_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
+}
+
+extern "C" int32_t hsa_chunk_page_count(const hsa_geom* geom) {
+  hsa::Dims s;
+  if (hsa::derive(geom, &s) != HSA_OK || !s.split) return 0;
+  return hsa::chunk_pages(s);
+}
+
+extern "C" hsa_rc hsa_chunk_prepare(const hsa_geom* geom, const void* k_cur, const void* v_cur,
+                                    void* const* k_out, void* const* v_out, float* const* blk_mean,
+                                    hsa_stream stream) {
+  using namespace hsa;
+  Dims s;
+  hsa_rc rc = derive(geom, &s);
+  if (rc != HSA_OK) return rc;
+  if (!s.split) return HSA_ERR_BAD_PARAM;
+  if (!k_cur || !v_cur || !k_out || !v_out) return HSA_ERR_NULL_ARG;
+  const int nc = chunk_pages(s);
+  for (int j = 0; j < nc; ++j)
+    if (!k_out[j] || !v_out[j]) return HSA_ERR_NULL_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const size_t row = (size_t)s.H * s.d * s.esize;  // bytes per token of [Lq][H][d]
+  for (int j = 0; j < nc; ++j) {
+    const int t0 = j * s.Lp;
+    const int tokens = s.Lq - t0 < s.Lp ? s.Lq - t0 : s.Lp;
+    prepare_one(s, tokens, static_cast<const char*>(k_cur) + (size_t)t0 * row,
+                static_cast<const char*>(v_cur) + (size_t)t0 * row, k_out[j], v_out[j],
+                blk_mean ? blk_mean[j] : nullptr, st);
   }
   return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
 }
@@ -231,7 +277,6 @@ extern "C" hsa_rc hsa_gather_block_means(const hsa_geom* geom, const float* cons
   Dims s;
   hsa_rc rc = derive(geom, &s);
   if (rc != HSA_OK) return rc;
-  if (s.split) return HSA_ERR_BAD_PARAM;
   if (!page_blk_mean || !sel_pages || !kblk_mean) return HSA_ERR_NULL_ARG;
   if (n_pages < 1 || n_pages > HSA_MAX_PAGES || s.Kp > n_pages) return HSA_ERR_BAD_PARAM;
   PageTable pm;
@@ -243,7 +288,7 @@ extern "C" hsa_rc hsa_gather_block_means(const hsa_geom* geom, const float* cons
   const size_t n = (size_t)s.H * s.nKB * s.d;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(gather_block_means_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, pm, n_pages,
-                     sel_pages, s.H, s.d, s.Lp / s.B, s.nKB, kblk_mean);
+                     sel_pages, s.H, s.d, s.Lp / s.Bk, s.nKB, kblk_mean);
   return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
 }
 

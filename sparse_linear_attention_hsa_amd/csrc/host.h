@@ -24,6 +24,10 @@ struct Dims {
 
 hsa_rc derive(const hsa_geom* g, Dims* out);
 
+// Page-format buffers that hold the chunk's own keys when pages are read in
+// place with intra-chunk keys: ceil(Lq / Lp) (0 without intra-chunk keys).
+inline int chunk_pages(const Dims& s) { return s.split ? (s.Lq + s.Lp - 1) / s.Lp : 0; }
+
 // Page scoring work split: units of `chunk_rows` tokens.
 struct ScorePlan {
   int page_chunks;   // chunks per page

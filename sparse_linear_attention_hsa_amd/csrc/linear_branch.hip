@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2,
     const T* kpage[2] = {nullptr, nullptr};
     const T* vpage[2] = {nullptr, nullptr};
     if constexpr (PAGED) {
-      const int kp = L / pg.Lp;
+      const int kp = (L + pg.Lp - 1) / pg.Lp;  // pages of the active keys (the chunk's last one may be partial)
       const int p0 = tok0 / pg.Lp, p1 = min(p0 + 1, kp - 1);
       first = p0 * pg.Lp;
       bnd = first + pg.Lp;
@@ -708,7 +708,7 @@ hsa_rc linear_entry(const Dims& s, const void* q, const void* k_act, const void*
   if (flags & ~kModes) return HSA_ERR_BAD_PARAM;
   if (__builtin_popcount((unsigned)flags) > 1) return HSA_ERR_BAD_PARAM;  // one mode at a time
   // the history / chunk split exists only with the chunk's own keys
-  if ((flags & (HSA_LIN_HISTORY_PROJ | HSA_LIN_CHUNK_PROJ)) && (PAGED || !s.split)) return HSA_ERR_BAD_PARAM;
+  if ((flags & (HSA_LIN_HISTORY_PROJ | HSA_LIN_CHUNK_PROJ)) && !s.split) return HSA_ERR_BAD_PARAM;
   if (!k_proj || !v_proj) return HSA_ERR_NULL_ARG;
   if (!(flags & HSA_LIN_REUSE_PROJ) && ((!PAGED && (!k_act || !v_act)) || !e_k || !e_v)) return HSA_ERR_NULL_ARG;
   if (!(flags & (HSA_LIN_PROJ_ONLY | HSA_LIN_HISTORY_PROJ)) && (!q || !o_lin)) return HSA_ERR_NULL_ARG;
@@ -749,7 +749,6 @@ extern "C" hsa_rc hsa_linear_branch_paged(const hsa_geom* geom, const void* q, c
   Dims s;
   hsa_rc rc = derive(geom, &s);
   if (rc != HSA_OK) return rc;
-  if (s.split) return HSA_ERR_BAD_PARAM;
   // a contraction step (at most 32 tokens) must span at most two pages
   if (s.Lp < 32) return HSA_ERR_BAD_SHAPE;
   PagedKV<true> pg;

@@ -778,7 +778,6 @@ extern "C" hsa_rc hsa_sparse_attn_paged(const hsa_geom* geom, const void* q, con
   Dims s;
   hsa_rc rc = derive(geom, &s);
   if (rc != HSA_OK) return rc;
-  if (s.split) return HSA_ERR_BAD_PARAM;
   if (!q || !page_k || !page_v || !sel_pages || !blk_count || !blk_idx || !o_sp) return HSA_ERR_NULL_ARG;
   if (n_pages < 1 || n_pages > HSA_MAX_PAGES || s.Kp > n_pages) return HSA_ERR_BAD_PARAM;
   PagedKV<true> pg;

@@ -180,6 +180,16 @@ def hsa_page_prepare(geom, k_page, v_page, k_out, v_out, blk_mean=None, stream=N
         ctypes.byref(geom), _p(k_page), _p(v_page), _p(k_out), _p(v_out), _p(blk_mean), _s(stream)))
 
 
+def hsa_chunk_page_count(geom) -> int:
+    return int(lib().hsa_chunk_page_count(ctypes.byref(geom)))
+
+
+def hsa_chunk_prepare(geom, k_cur, v_cur, k_out, v_out, blk_mean=None, stream=None):
+    check("hsa_chunk_prepare", lib().hsa_chunk_prepare(
+        ctypes.byref(geom), _p(k_cur), _p(v_cur), _table(k_out), _table(v_out),
+        None if blk_mean is None else _table(blk_mean), _s(stream)))
+
+
 def hsa_gather_block_means(geom, page_blk_mean, sel_pages, kblk_mean, stream=None):
     check("hsa_gather_block_means", lib().hsa_gather_block_means(
         ctypes.byref(geom), _table(page_blk_mean), len(page_blk_mean), _p(sel_pages), _p(kblk_mean), _s(stream)))

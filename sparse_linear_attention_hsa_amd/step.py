@@ -37,7 +37,14 @@ class HsaStep:
         f32, i32, dt = torch.float32, torch.int32, s.dtype
         self.page_kmean = torch.empty(n_pages, s.H, s.d, dtype=f32, device=dev)
         self.scores = torch.empty(n_pages, dtype=f32, device=dev)
-        self.sel_pages = torch.empty(s.Kp, dtype=i32, device=dev)
+        # pages read in place with intra-chunk keys: the selected pages, then
+        # the table indices of the chunk's page-format buffers (one array;
+        # sel_pages is its head, which scoring writes)
+        self.n_chunk_pages = ops.hsa_chunk_page_count(geom)
+        self.sel_ext = torch.empty(s.Kp + self.n_chunk_pages, dtype=i32, device=dev)
+        self.sel_pages = self.sel_ext[:s.Kp]
+        self._sel_tail_base: Optional[int] = None
+        self._chunk_bufs = None
         self.k_act = torch.empty(s.H, s.L, s.d, dtype=dt, device=dev)
         self.v_act = torch.empty(s.H, s.L // 16, s.d, 16, dtype=dt, device=dev)
         self.kblk_mean = torch.empty(s.H, s.nKB, s.d, dtype=f32, device=dev)
@@ -138,41 +145,67 @@ class HsaStep:
         """Lay out every page once, as when it is written: K [H][Lp][d], V
         [H][Lp/16][d][16] and the block means [H][Lp/B][d] (the layouts the
         kernels read, over one page).  Returns (k_pages, v_pages, blk_means)."""
-        s, dev = self.s, self.k_act.device
         ks, vs, ms = [], [], []
         for pk, pv in zip(pages_k, pages_v):
-            ko = torch.empty(s.H, s.Lp, s.d, dtype=s.dtype, device=dev)
-            vo = torch.empty(s.H, s.Lp // 16, s.d, 16, dtype=s.dtype, device=dev)
-            mo = torch.empty(s.H, s.Lp // s.B, s.d, dtype=torch.float32, device=dev)
+            ko, vo, mo = self._page_buffers()
             ops.hsa_page_prepare(self.geom, pk, pv, ko, vo, mo, stream)
             ks.append(ko)
             vs.append(vo)
             ms.append(mo)
         return ks, vs, ms
 
+    def _page_buffers(self):
+        s, dev = self.s, self.k_act.device
+        return (torch.empty(s.H, s.Lp, s.d, dtype=s.dtype, device=dev),
+                torch.empty(s.H, s.Lp // 16, s.d, 16, dtype=s.dtype, device=dev),
+                torch.empty(s.H, s.Lp // s.Bk, s.d, dtype=torch.float32, device=dev))
+
+    def paged_inputs(self, prepared, k_cur=None, v_cur=None, stream=None):
+        """Page tables and selection list of a paged step.  With intra-chunk
+        keys the chunk's own keys and values are laid out into page-format
+        buffers (kept from step to step), appended to the tables, and their
+        table indices follow the selected pages in sel_ext.  Returns
+        (k_pages, v_pages, blk_means, sel)."""
+        kp, vp, bm = prepared
+        if not self.n_chunk_pages:
+            return kp, vp, bm, self.sel_ext
+        if k_cur is None or v_cur is None:
+            raise ValueError("this geometry has intra-chunk keys: pass k_cur and v_cur")
+        if self._chunk_bufs is None:
+            self._chunk_bufs = [self._page_buffers() for _ in range(self.n_chunk_pages)]
+        ck, cv, cm = (list(t) for t in zip(*self._chunk_bufs))
+        ops.hsa_chunk_prepare(self.geom, k_cur, v_cur, ck, cv, cm, stream)
+        if self._sel_tail_base != len(kp):  # the chunk buffers' table indices
+            tail = torch.arange(len(kp), len(kp) + self.n_chunk_pages, dtype=torch.int32)
+            self.sel_ext[self.s.Kp:].copy_(tail)
+            self._sel_tail_base = len(kp)
+        return list(kp) + ck, list(vp) + cv, list(bm) + cm, self.sel_ext
+
     def run_paged(self, q, prepared, e_k, e_v, w_g, x, tau, stream=None, concurrent: bool = True,
-                  kernel_events=None):
+                  kernel_events=None, k_cur=None, v_cur=None):
         """The step over laid-out pages, with no active-buffer copy: scoring
         from the page index (index_pages ran before), the selected pages' block
         means, the linear branch (side stream) and the sparse branch reading
-        the pages in place, then the fusion."""
-        kp, vp, bm = prepared
+        the pages in place, then the fusion.  k_cur, v_cur: the chunk's own
+        keys and values (geometries with intra-chunk keys), laid out into
+        page-format buffers first."""
         main = torch.cuda.current_stream() if stream is None else stream
         self.score(q, None, main, use_cache=True)
-        ops.hsa_gather_block_means(self.geom, bm, self.sel_pages, self.kblk_mean, main)
+        kp, vp, bm, sel = self.paged_inputs(prepared, k_cur, v_cur, main)
+        ops.hsa_gather_block_means(self.geom, bm, sel, self.kblk_mean, main)
         side = self.side if concurrent else main
         if concurrent:
             scored = torch.cuda.Event()
             scored.record(main)
             self.side.wait_event(scored)
-        ops.hsa_linear_branch_paged(self.geom, q, kp, vp, self.sel_pages, e_k, e_v, self.k_proj, self.v_proj,
+        ops.hsa_linear_branch_paged(self.geom, q, kp, vp, sel, e_k, e_v, self.k_proj, self.v_proj,
                                     self.o_lin, 0, self.ws_lin if concurrent else self.ws, side)
         if concurrent:
             linear_done = torch.cuda.Event()
             linear_done.record(side)
         ops.hsa_block_select(self.geom, q, None, self.kblk_mean, tau, self.blk_count, self.blk_idx, self.blk_mass,
                              self.ws, main)
-        ops.hsa_sparse_attn_paged(self.geom, q, kp, vp, self.sel_pages, self.blk_count, self.blk_idx, self.o_sp,
+        ops.hsa_sparse_attn_paged(self.geom, q, kp, vp, sel, self.blk_count, self.blk_idx, self.o_sp,
                                   self.ws, kernel_events, main)
         if concurrent:
             main.wait_event(linear_done)

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(_lib.SIGNATURES), names
     for n in names:
         assert hasattr(lib, n)
-    assert lib.hsa_abi_version() == 2
+    assert lib.hsa_abi_version() == 3
 
 
 def test_geometry_validation(lib):
@@ -101,17 +101,29 @@ def test_paged_entry_points_reject_bad_arguments(lib):
     pages = (ctypes.c_void_p * 16)(*([0x1000] * 16))
     null_pages = (ctypes.c_void_p * 16)()
     big = 1 << 40
-    # page layout: NULL buffers; no intra-chunk keys
+    # page layout: NULL buffers
     assert lib.hsa_page_prepare(ctypes.byref(g), None, fake, fake, fake, None, None) == 1
     assert lib.hsa_page_prepare(ctypes.byref(g), fake, fake, fake, None, None, None) == 1
-    assert lib.hsa_page_prepare(ctypes.byref(intra), fake, fake, fake, fake, None, None) == 4
+    assert lib.hsa_page_prepare(ctypes.byref(intra), None, fake, fake, fake, None, None) == 1
+    # the chunk's page-format buffers: only with intra-chunk keys, ceil(Lq / Lp) of them
+    assert lib.hsa_chunk_page_count(ctypes.byref(g)) == 0
+    assert lib.hsa_chunk_page_count(ctypes.byref(intra)) == 1  # Lq = Lp / 2
+    assert lib.hsa_chunk_page_count(ctypes.byref(c1_geom(intra_split=2, frames_per_page=4, query_frames=12))) == 3
+    assert lib.hsa_chunk_page_count(None) == 0
+    outs = (ctypes.c_void_p * 1)(0x1000)
+    null_outs = (ctypes.c_void_p * 1)()
+    cp = lib.hsa_chunk_prepare
+    assert cp(ctypes.byref(g), fake, fake, outs, outs, None, None) == 4
+    assert cp(ctypes.byref(intra), None, fake, outs, outs, None, None) == 1
+    assert cp(ctypes.byref(intra), fake, fake, null_outs, outs, None, None) == 1
+    assert cp(ctypes.byref(intra), fake, fake, outs, None, None, None) == 1
     # block means of the selected pages: NULL entries, page counts
     gm = lib.hsa_gather_block_means
     assert gm(ctypes.byref(g), null_pages, 16, fake, fake, None) == 1
     assert gm(ctypes.byref(g), pages, 16, None, fake, None) == 1
     assert gm(ctypes.byref(g), pages, 3, fake, fake, None) == 4
     assert gm(ctypes.byref(g), pages, 200, fake, fake, None) == 4
-    assert gm(ctypes.byref(intra), pages, 16, fake, fake, None) == 4
+    assert gm(ctypes.byref(intra), null_pages, 16, fake, fake, None) == 1
     # linear branch over pages: NULL pages (unless the projection is reused), counts, flags, workspace
     lp = lib.hsa_linear_branch_paged
     assert lp(ctypes.byref(g), fake, null_pages, pages, 16, fake, fake, fake, fake, fake, fake, 0, fake, big, None) == 1
@@ -119,14 +131,18 @@ def test_paged_entry_points_reject_bad_arguments(lib):
     assert lp(ctypes.byref(g), fake, pages, pages, 3, fake, fake, fake, fake, fake, fake, 0, fake, big, None) == 4
     assert lp(ctypes.byref(g), fake, pages, pages, 16, fake, fake, fake, fake, fake, fake, 3, fake, big, None) == 4
     assert lp(ctypes.byref(g), fake, pages, pages, 16, fake, fake, fake, fake, fake, fake, 0, fake, 16, None) == 5
-    assert lp(ctypes.byref(intra), fake, pages, pages, 16, fake, fake, fake, fake, fake, fake, 0, fake, big, None) == 4
+    # with intra-chunk keys the paged calls get as far as the workspace check;
+    # the history / chunk projection modes need them
+    assert lp(ctypes.byref(intra), fake, pages, pages, 16, fake, fake, fake, fake, fake, fake, 0, fake, 16, None) == 5
+    assert lp(ctypes.byref(g), fake, pages, pages, 16, fake, fake, fake, fake, fake, fake,
+              _lib.HSA_LIN_HISTORY_PROJ, fake, big, None) == 4
     # sparse branch over pages
     sp = lib.hsa_sparse_attn_paged
     assert sp(ctypes.byref(g), fake, pages, null_pages, 16, fake, fake, fake, fake, fake, big, None, None, None) == 1
     assert sp(ctypes.byref(g), fake, pages, pages, 16, None, fake, fake, fake, fake, big, None, None, None) == 1
     assert sp(ctypes.byref(g), fake, pages, pages, 2, fake, fake, fake, fake, fake, big, None, None, None) == 4
     assert sp(ctypes.byref(g), fake, pages, pages, 16, fake, fake, fake, fake, fake, 16, None, None, None) == 5
-    assert sp(ctypes.byref(intra), fake, pages, pages, 16, fake, fake, fake, fake, fake, big, None, None, None) == 4
+    assert sp(ctypes.byref(intra), fake, pages, pages, 16, fake, fake, fake, fake, fake, 16, None, None, None) == 5
 
 
 def test_workspace_sizes(lib):

@@ -5,6 +5,8 @@ straight from the pages.  Active key t is token t % Lp of page sel[t / Lp], so
 every result must equal the active-buffer path's bit for bit; the laid-out
 pages are checked against the oracle's index relation and block means, and the
 outputs against the oracle."""
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -85,3 +87,86 @@ def test_paged_graph_replays_match_eager():
             assert torch.equal(getattr(st, k), want[k]), f"replay {rep}: {k}"
         st.run_paged(r.q, prepared, r.e_k, r.e_v, r.w_g, r.x, r.tau)  # eager work between replays
         torch.cuda.synchronize()
+
+
+# Intra-chunk keys over pages read in place (paper section 3.3, "Inter- and
+# intra-chunk sparse granularity"): the chunk's own keys and values are laid
+# out into ceil(Lq / Lp) page-format buffers each step and follow the
+# selected pages in the selection list, so the paged step must again equal
+# the gathered step (with the chunk in the active buffer) bit for bit.
+INTRA = [replace(M1, name="m1_intra2", intra_split=2),
+         replace(M2, name="m2_intra3_ragged", intra_split=3),      # Lp = 144: a 32-token step spans page and chunk
+         replace(M3, name="m3_intra2_long_rows", intra_split=2),
+         replace(M4, name="m4_intra3_f32", intra_split=3),
+         replace(M5, name="m5_intra2_lq_eq_lp", intra_split=2),    # the chunk fills its one buffer
+         replace(M1, name="m1_intra2_two_chunk_pages", intra_split=2, frames_per_page=2, query_frames=4)]
+
+
+def _both_intra(cfg, concurrent=True):
+    r = Run(cfg)
+    st = r.step
+    st.index_pages(r.q, r.pk)
+    prepared = st.prepare_pages(r.pk, r.pv)
+    r.run()
+    want = {k: getattr(st, k).clone() for k in NAMES}
+    st.run_paged(r.q, prepared, r.e_k, r.e_v, r.w_g, r.x, r.tau, concurrent=concurrent, k_cur=r.k_cur,
+                 v_cur=r.v_cur)
+    torch.cuda.synchronize()
+    return r, st, prepared, want
+
+
+@pytest.mark.parametrize("cfg", INTRA, ids=lambda c: c.name)
+def test_paged_intra_step_equals_gathered_intra_step(cfg):
+    nc = -(-cfg.query_tokens // cfg.page_tokens)
+    print(f"\n[paged intra] config={cfg.name} Lp={cfg.page_tokens} Lq={cfg.query_tokens} chunk buffers={nc}",
+          flush=True)
+    r, st, (kp, vp, bm), want = _both_intra(cfg)
+    assert st.n_chunk_pages == nc
+    for k in NAMES:
+        assert torch.equal(getattr(st, k), want[k]), k
+    # the selection list: the selected pages, then the chunk buffers' table indices
+    assert st.sel_ext[cfg.n_sel_pages:].tolist() == list(range(cfg.n_pages, cfg.n_pages + nc))
+    # the chunk's buffers: the index relation, bit-exact, and the key-block means
+    kc = r.np["k_cur"].transpose(1, 0, 2)
+    vc = r.np["v_cur"].transpose(1, 0, 2)
+    Lp, Bk = cfg.page_tokens, cfg.key_block
+    for j, (ck, cv, cm) in enumerate(st._chunk_bufs):
+        n = min(Lp, cfg.query_tokens - j * Lp)
+        part_k, part_v = kc[:, j * Lp:j * Lp + n], vc[:, j * Lp:j * Lp + n]
+        assert np.array_equal(host(ck)[:, :n], part_k), f"chunk k buffer {j}"
+        assert np.array_equal(untile_v(host(cv))[:, :n], part_v), f"chunk v buffer {j}"
+        np.testing.assert_allclose(host(cm)[:, :n // Bk], orc.block_means(part_k, Bk), rtol=0, atol=2e-5)
+    # a laid-out page keeps its key-block means at the chunk's block size
+    np.testing.assert_allclose(host(bm[0]), orc.block_means(r.pk_np[0].transpose(1, 0, 2), Bk), rtol=0, atol=2e-5)
+    ref = r.oracle(sel_pages=st.sel_pages.cpu().numpy())
+    if not ref["blocks"]["flags"].any():
+        assert_close("out", host(st.out), ref["out"], cfg)
+
+
+def test_paged_intra_in_order_and_repeated():
+    """In order on one stream, then a second concurrent paged step reusing the
+    chunk's buffers: the same bits."""
+    r, st, prepared, want = _both_intra(INTRA[1], concurrent=False)
+    for k in NAMES:
+        assert torch.equal(getattr(st, k), want[k]), k
+    st.run_paged(r.q, prepared, r.e_k, r.e_v, r.w_g, r.x, r.tau, k_cur=r.k_cur, v_cur=r.v_cur)
+    torch.cuda.synchronize()
+    for k in NAMES:
+        assert torch.equal(getattr(st, k), want[k]), k
+
+
+def test_paged_intra_needs_the_chunk():
+    r = Run(INTRA[0])
+    prepared = r.step.prepare_pages(r.pk, r.pv)
+    with pytest.raises(ValueError):
+        r.step.run_paged(r.q, prepared, r.e_k, r.e_v, r.w_g, r.x, r.tau)
+
+
+def test_paged_intra_full_size_equals_gathered():
+    cfg = replace(CONFIGS["c1_full"], name="c1_intra2", intra_split=2)
+    print(f"\n[paged intra full size] {cfg.name}", flush=True)
+    r, st, prepared, want = _both_intra(cfg)
+    for k in NAMES:
+        assert torch.equal(getattr(st, k), want[k]), k
+    del r, st, prepared
+    torch.cuda.empty_cache()
