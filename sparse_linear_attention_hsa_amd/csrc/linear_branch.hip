@@ -29,9 +29,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // N transposing 64-bit LDS reads (ds_read_b64_tr_b16) issued back to back,
 // with the wait for all of them inside the same asm statement, so the outputs
-// are complete when the statement ends.  (The compiler's own form of this
-// read carries no alias information, so it would wait for every
-// direct-to-LDS load in flight before it.)
+// are complete when the statement ends.  (The addresses here are 32-bit LDS
+// offsets built by integer arithmetic; the compiler's own form of this read,
+// given such an address, cannot tell it from the direct-to-LDS loads in
+// flight and waits for all of them first.)
 template <int N> __device__ __forceinline__ void tr_read_b16(const uint32_t* addr, uint2* out);
 template <> __device__ __forceinline__ void tr_read_b16<16>(const uint32_t* a, uint2* o) {
   asm volatile(
