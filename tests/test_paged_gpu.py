@@ -170,3 +170,33 @@ def test_paged_intra_full_size_equals_gathered():
         assert torch.equal(getattr(st, k), want[k]), k
     del r, st, prepared
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg", [INTRA[0], INTRA[1], INTRA[5]], ids=lambda c: c.name)
+def test_paged_intra_history_and_chunk_projections(cfg):
+    """The projection split into the history's part (kept across denoising
+    steps) and the chunk's part, over pages read in place, equals the same
+    split over the active buffer bit for bit."""
+    from sparse_linear_attention_hsa_amd import ops
+    from sparse_linear_attention_hsa_amd._lib import HSA_LIN_CHUNK_PROJ, HSA_LIN_HISTORY_PROJ
+    print(f"\n[paged intra split projection] config={cfg.name}", flush=True)
+    r, st, prepared, _ = _both_intra(cfg)  # st.k_act / v_act hold the gathered active buffer
+    kp, vp, _, sel = st.paged_inputs(prepared, r.k_cur, r.v_cur)
+
+    def gathered(flags, kh, vh, o):
+        ops.hsa_linear_branch(st.geom, None if o is None else r.q, st.k_act, st.v_act, r.e_k, r.e_v, kh, vh, o,
+                              flags, st.ws)
+
+    def paged(flags, kh, vh, o):
+        ops.hsa_linear_branch_paged(st.geom, None if o is None else r.q, kp, vp, sel, r.e_k, r.e_v, kh, vh, o,
+                                    flags, st.ws)
+
+    got = {}
+    for name, call in (("gathered", gathered), ("paged", paged)):
+        kh, vh, o = torch.empty_like(st.k_proj), torch.empty_like(st.v_proj), torch.empty_like(st.o_lin)
+        call(HSA_LIN_HISTORY_PROJ, kh, vh, None)
+        call(HSA_LIN_CHUNK_PROJ, kh, vh, o)
+        torch.cuda.synchronize()
+        got[name] = (kh, vh, o)
+    for what, a, b in zip(("history K~", "history V~", "O_lin"), got["gathered"], got["paged"]):
+        assert torch.equal(a, b), what
