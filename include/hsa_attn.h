@@ -501,6 +501,24 @@ hsa_rc hsa_sparse_attn_paged(const hsa_geom* geom, const void* q, const void* co
                              const int32_t* blk_count, const int32_t* blk_idx, float* o_sp, void* ws,
                              size_t ws_bytes, hsa_stream stream, hsa_event ev_begin, hsa_event ev_end);
 
+/* The three paged calls above with their page tables in DEVICE memory, for
+ * banks beyond HSA_MAX_PAGES: page_k_table, page_v_table (and
+ * page_blk_mean_table) are device arrays of n_pages (<= HSA_MAX_BANK_PAGES)
+ * device pointers, read by the kernels; a NULL entry is a page without a
+ * laid-out buffer, which reads as zeros (as the gather of such a page writes
+ * zeros into the active buffer).  Other arguments, results and errors as the
+ * host-table calls, except that no entry is checked on the host. */
+hsa_rc hsa_gather_block_means_devtab(const hsa_geom* geom, const float* const* page_blk_mean_table, int32_t n_pages,
+                                     const int32_t* sel_pages, float* kblk_mean, hsa_stream stream);
+hsa_rc hsa_linear_branch_paged_devtab(const hsa_geom* geom, const void* q, const void* const* page_k_table,
+                                      const void* const* page_v_table, int32_t n_pages, const int32_t* sel_pages,
+                                      const void* e_k, const void* e_v, void* k_proj, void* v_proj, float* o_lin,
+                                      int32_t flags, void* ws, size_t ws_bytes, hsa_stream stream);
+hsa_rc hsa_sparse_attn_paged_devtab(const hsa_geom* geom, const void* q, const void* const* page_k_table,
+                                    const void* const* page_v_table, int32_t n_pages, const int32_t* sel_pages,
+                                    const int32_t* blk_count, const int32_t* blk_idx, float* o_sp, void* ws,
+                                    size_t ws_bytes, hsa_stream stream, hsa_event ev_begin, hsa_event ev_end);
+
 /* Bytes of workspace every call above needs for this geometry and a bank of
  * n_pages pages (0 if the geometry is invalid or n_pages exceeds
  * HSA_MAX_BANK_PAGES).  One workspace serves all calls on one stream. */

@@ -61,6 +61,10 @@ SIGNATURES = {
                                        _vp, _vp, _i32, _vp, _sz, _vp]),
     "hsa_sparse_attn_paged": (_i32, [_GP, _vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp,
                                      _vp, _sz, _vp, _vp, _vp]),
+    "hsa_gather_block_means_devtab": (_i32, [_GP, _vp, _i32, _vp, _vp, _vp]),
+    "hsa_linear_branch_paged_devtab": (_i32, [_GP, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz,
+                                              _vp]),
+    "hsa_sparse_attn_paged_devtab": (_i32, [_GP, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),
     "hsa_block_select": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "hsa_block_select_noalloc": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "hsa_sparse_attn": (_i32, [_GP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),

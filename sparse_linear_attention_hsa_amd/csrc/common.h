@@ -35,14 +35,21 @@ struct DevPageTable {
 // Keys and values read in place from laid-out pages (PAGED kernels): page j
 // holds K as [H][Lp][d] and V as [H][Lp/16][d][16] (the active buffer's
 // layouts over one page), and active key t is token t % Lp of page
-// sel[t / Lp].  The unpaged form carries nothing.
+// sel[t / Lp].  The page pointers come from a table passed by value (pk, pv)
+// or, for banks larger than one launch argument holds, from tables in device
+// memory (dk, dv, used when non-NULL); a NULL page there reads as zeros.  The
+// unpaged form carries nothing.
 template <bool PAGED> struct PagedKV {
   static constexpr int Lp = 0;
 };
 template <> struct PagedKV<true> {
   PageTable pk, pv;
+  const void* const* dk = nullptr;
+  const void* const* dv = nullptr;
   const int32_t* sel;
   int n_pages, Lp;
+  __device__ __forceinline__ const void* kpage(int j) const { return dk ? dk[j] : pk.p[j]; }
+  __device__ __forceinline__ const void* vpage(int j) const { return dv ? dv[j] : pv.p[j]; }
 };
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t v) {

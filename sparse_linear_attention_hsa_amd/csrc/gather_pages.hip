@@ -181,10 +181,11 @@ void launch_gather(const Dims& s, const Tab& pk, const Tab& pv, int n_pages, con
 // [H][Lp/Bk][d] (written when the page was laid out): one thread per element
 // of kblk_mean [H][nKB][d]; key block j is block j % bpp of page sel[j / bpp]
 // (with intra-chunk keys the chunk's page-format buffers follow the history
-// in sel).
-__global__ __launch_bounds__(256) void gather_block_means_kernel(PageTable pm, int n_pages,
-                                                                const int32_t* __restrict__ sel, int H, int D,
-                                                                int bpp, int nKB, float* __restrict__ kblk_mean) {
+// in sel).  A page a device table holds no means for reads as zeros.
+template <typename Tab>
+__global__ __launch_bounds__(256) void gather_block_means_kernel(Tab pm, int n_pages, const int32_t* __restrict__ sel,
+                                                                int H, int D, int bpp, int nKB,
+                                                                float* __restrict__ kblk_mean) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (size_t)H * nKB * D) return;
   const int e = (int)(i % D);
@@ -193,7 +194,8 @@ __global__ __launch_bounds__(256) void gather_block_means_kernel(PageTable pm, i
   const int p = j / bpp, lb = j % bpp;
   int page = sel[p];
   page = page < 0 ? 0 : (page >= n_pages ? n_pages - 1 : page);
-  kblk_mean[i] = reinterpret_cast<const float*>(pm.at(page))[((size_t)h * bpp + lb) * D + e];
+  const float* src = reinterpret_cast<const float*>(pm.at(page));
+  kblk_mean[i] = src ? src[((size_t)h * bpp + lb) * D + e] : 0.f;
 }
 
 }  // namespace
@@ -271,6 +273,22 @@ extern "C" hsa_rc hsa_chunk_prepare(const hsa_geom* geom, const void* k_cur, con
   return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
 }
 
+namespace hsa {
+namespace {
+
+template <typename Tab>
+hsa_rc block_means_entry(const Dims& s, const Tab& pm, int32_t n_pages, const int32_t* sel_pages, float* kblk_mean,
+                         hsa_stream stream) {
+  const size_t n = (size_t)s.H * s.nKB * s.d;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(gather_block_means_kernel<Tab>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, pm, n_pages,
+                     sel_pages, s.H, s.d, s.Lp / s.Bk, s.nKB, kblk_mean);
+  return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace hsa
+
 extern "C" hsa_rc hsa_gather_block_means(const hsa_geom* geom, const float* const* page_blk_mean, int32_t n_pages,
                                          const int32_t* sel_pages, float* kblk_mean, hsa_stream stream) {
   using namespace hsa;
@@ -285,11 +303,20 @@ extern "C" hsa_rc hsa_gather_block_means(const hsa_geom* geom, const float* cons
     if (!page_blk_mean[j]) return HSA_ERR_NULL_ARG;
     pm.p[j] = page_blk_mean[j];
   }
-  const size_t n = (size_t)s.H * s.nKB * s.d;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(gather_block_means_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, pm, n_pages,
-                     sel_pages, s.H, s.d, s.Lp / s.Bk, s.nKB, kblk_mean);
-  return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
+  return block_means_entry(s, pm, n_pages, sel_pages, kblk_mean, stream);
+}
+
+extern "C" hsa_rc hsa_gather_block_means_devtab(const hsa_geom* geom, const float* const* page_blk_mean_table,
+                                                int32_t n_pages, const int32_t* sel_pages, float* kblk_mean,
+                                                hsa_stream stream) {
+  using namespace hsa;
+  Dims s;
+  hsa_rc rc = derive(geom, &s);
+  if (rc != HSA_OK) return rc;
+  if (!page_blk_mean_table || !sel_pages || !kblk_mean) return HSA_ERR_NULL_ARG;
+  if (n_pages < 1 || n_pages > HSA_MAX_BANK_PAGES || s.Kp > n_pages) return HSA_ERR_BAD_PARAM;
+  return block_means_entry(s, DevPageTable{reinterpret_cast<const void* const*>(page_blk_mean_table)}, n_pages,
+                           sel_pages, kblk_mean, stream);
 }
 
 namespace hsa {

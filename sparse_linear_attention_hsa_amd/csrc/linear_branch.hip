@@ -163,10 +163,10 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2,
       int pa = pg.sel[p0], pb = pg.sel[p1];
       pa = pa < 0 ? 0 : (pa >= pg.n_pages ? pg.n_pages - 1 : pa);
       pb = pb < 0 ? 0 : (pb >= pg.n_pages ? pg.n_pages - 1 : pb);
-      kpage[0] = reinterpret_cast<const T*>(pg.pk.p[pa]);
-      kpage[1] = reinterpret_cast<const T*>(pg.pk.p[pb]);
-      vpage[0] = reinterpret_cast<const T*>(pg.pv.p[pa]);
-      vpage[1] = reinterpret_cast<const T*>(pg.pv.p[pb]);
+      kpage[0] = reinterpret_cast<const T*>(pg.kpage(pa));
+      kpage[1] = reinterpret_cast<const T*>(pg.kpage(pb));
+      vpage[0] = reinterpret_cast<const T*>(pg.vpage(pa));
+      vpage[1] = reinterpret_cast<const T*>(pg.vpage(pb));
     }
 #pragma unroll
     for (int ii = 0; ii < EINST / NW; ++ii) {
@@ -193,9 +193,9 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2,
         if constexpr (PAGED) {
           const bool second = tk >= bnd;
           const int lt = tk - (second ? bnd : first);
-          src = (hh < H && tk < t_end)
-                    ? (const void*)((second ? vpage[1] : vpage[0]) +
-                                    (((size_t)hh * (pg.Lp / 16) + lt / 16) * D + rowv) * 16 + part * E)
+          const T* vp = second ? vpage[1] : vpage[0];  // (NULL: a page of a device table without one)
+          src = (hh < H && tk < t_end && vp != nullptr)
+                    ? (const void*)(vp + (((size_t)hh * (pg.Lp / 16) + lt / 16) * D + rowv) * 16 + part * E)
                     : (const void*)(kZeroPage + lane);
         } else {
           src = (hh < H && tk < t_end)
@@ -209,8 +209,9 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2,
           const int tk = tok0 + tr;
           const bool second = tk >= bnd;
           const int lt = tk - (second ? bnd : first);
-          src = (hh < H && tk < t_end)
-                    ? (const void*)((second ? kpage[1] : kpage[0]) + ((size_t)hh * pg.Lp + lt) * D + chunk * E)
+          const T* kp = second ? kpage[1] : kpage[0];
+          src = (hh < H && tk < t_end && kp != nullptr)
+                    ? (const void*)(kp + ((size_t)hh * pg.Lp + lt) * D + chunk * E)
                     : (const void*)(kZeroPage + lane);
         } else {
           src = (hh < H && tok0 + tr < t_end) ? (const void*)(k_act + ((size_t)hh * L + tok0 + tr) * D + chunk * E)
@@ -762,6 +763,31 @@ extern "C" hsa_rc hsa_linear_branch_paged(const hsa_geom* geom, const void* q, c
       pg.pk.p[j] = page_k[j];
       pg.pv.p[j] = page_v[j];
     }
+  }
+  pg.sel = sel_pages;
+  pg.n_pages = n_pages;
+  pg.Lp = s.Lp;
+  return linear_entry<true>(s, q, nullptr, nullptr, e_k, e_v, k_proj, v_proj, o_lin, flags, ws, ws_bytes, stream,
+                            pg);
+}
+
+extern "C" hsa_rc hsa_linear_branch_paged_devtab(const hsa_geom* geom, const void* q, const void* const* page_k_table,
+                                                 const void* const* page_v_table, int32_t n_pages,
+                                                 const int32_t* sel_pages, const void* e_k, const void* e_v,
+                                                 void* k_proj, void* v_proj, float* o_lin, int32_t flags, void* ws,
+                                                 size_t ws_bytes, hsa_stream stream) {
+  using namespace hsa;
+  Dims s;
+  hsa_rc rc = derive(geom, &s);
+  if (rc != HSA_OK) return rc;
+  if (s.Lp < 32) return HSA_ERR_BAD_SHAPE;
+  PagedKV<true> pg;
+  for (int j = 0; j < kMaxPages; ++j) pg.pk.p[j] = pg.pv.p[j] = nullptr;
+  if (!(flags & HSA_LIN_REUSE_PROJ)) {
+    if (!page_k_table || !page_v_table || !sel_pages) return HSA_ERR_NULL_ARG;
+    if (n_pages < 1 || n_pages > HSA_MAX_BANK_PAGES || s.Kp > n_pages) return HSA_ERR_BAD_PARAM;
+    pg.dk = page_k_table;
+    pg.dv = page_v_table;
   }
   pg.sel = sel_pages;
   pg.n_pages = n_pages;

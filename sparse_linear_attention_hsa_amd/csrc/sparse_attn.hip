@@ -241,8 +241,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
     lblk_lane = valid ? blk_lane - ps * bpp : -1;
     int page = pg.sel[ps];
     page = page < 0 ? 0 : (page >= pg.n_pages ? pg.n_pages - 1 : page);
-    const uint64_t kp = reinterpret_cast<uint64_t>(pg.pk.p[page]);
-    const uint64_t vp = reinterpret_cast<uint64_t>(pg.pv.p[page]);
+    const uint64_t kp = reinterpret_cast<uint64_t>(pg.kpage(page));
+    const uint64_t vp = reinterpret_cast<uint64_t>(pg.vpage(page));
     kp_lo = (uint32_t)kp;
     kp_hi = (uint32_t)(kp >> 32);
     vp_lo = (uint32_t)vp;
@@ -365,7 +365,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
       if constexpr (PAGED) {
         const uint32_t lo = __builtin_amdgcn_readfirstlane(kb_lo[kgran[ii]]);
         const uint32_t hi = __builtin_amdgcn_readfirstlane(kb_hi[kgran[ii]]);
-        buffer_load_lds16(ptr_of(lo, hi) + page_head_elems, page_head_bytes, lk + i * 1024,
+        // a page a device table holds no buffer for: an empty range, so the loads return zeros
+        buffer_load_lds16(ptr_of(lo, hi) + page_head_elems, (lo | hi) ? page_head_bytes : 0, lk + i * 1024,
                           koff[ii] * (int)sizeof(T), kg * D * (int)sizeof(T));
       } else {
         buffer_load_lds16(kh, head_bytes, lk + i * 1024, koff[ii] * (int)sizeof(T), kg * D * (int)sizeof(T));
@@ -379,7 +380,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
       if constexpr (PAGED) {
         const uint32_t lo = __builtin_amdgcn_readfirstlane(vb_lo[vgran[ii]]);
         const uint32_t hi = __builtin_amdgcn_readfirstlane(vb_hi[vgran[ii]]);
-        buffer_load_lds16(ptr_of(lo, hi) + page_head_elems, page_head_bytes, lv + i * 1024,
+        buffer_load_lds16(ptr_of(lo, hi) + page_head_elems, (lo | hi) ? page_head_bytes : 0, lv + i * 1024,
                           voff[ii] * (int)sizeof(T), kg * D * (int)sizeof(T));
       } else {
         buffer_load_lds16(vh, head_bytes, lv + i * 1024, voff[ii] * (int)sizeof(T), kg * D * (int)sizeof(T));
@@ -787,6 +788,28 @@ extern "C" hsa_rc hsa_sparse_attn_paged(const hsa_geom* geom, const void* q, con
     pg.pk.p[j] = page_k[j];
     pg.pv.p[j] = page_v[j];
   }
+  pg.sel = sel_pages;
+  pg.n_pages = n_pages;
+  pg.Lp = s.Lp;
+  return sparse_entry<true>(s, q, nullptr, nullptr, blk_count, blk_idx, o_sp, ws, ws_bytes, stream, ev_begin, ev_end,
+                            pg);
+}
+
+extern "C" hsa_rc hsa_sparse_attn_paged_devtab(const hsa_geom* geom, const void* q, const void* const* page_k_table,
+                                               const void* const* page_v_table, int32_t n_pages,
+                                               const int32_t* sel_pages, const int32_t* blk_count,
+                                               const int32_t* blk_idx, float* o_sp, void* ws, size_t ws_bytes,
+                                               hsa_stream stream, hsa_event ev_begin, hsa_event ev_end) {
+  using namespace hsa;
+  Dims s;
+  hsa_rc rc = derive(geom, &s);
+  if (rc != HSA_OK) return rc;
+  if (!q || !page_k_table || !page_v_table || !sel_pages || !blk_count || !blk_idx || !o_sp) return HSA_ERR_NULL_ARG;
+  if (n_pages < 1 || n_pages > HSA_MAX_BANK_PAGES || s.Kp > n_pages) return HSA_ERR_BAD_PARAM;
+  PagedKV<true> pg;
+  for (int k = 0; k < kMaxPages; ++k) pg.pk.p[k] = pg.pv.p[k] = nullptr;
+  pg.dk = page_k_table;
+  pg.dv = page_v_table;
   pg.sel = sel_pages;
   pg.n_pages = n_pages;
   pg.Lp = s.Lp;

@@ -191,12 +191,24 @@ def hsa_chunk_prepare(geom, k_cur, v_cur, k_out, v_out, blk_mean=None, stream=No
 
 
 def hsa_gather_block_means(geom, page_blk_mean, sel_pages, kblk_mean, stream=None):
+    """page_blk_mean: a list of per-page block-mean tensors (host table) or a DeviceTable."""
+    if isinstance(page_blk_mean, DeviceTable):
+        check("hsa_gather_block_means_devtab", lib().hsa_gather_block_means_devtab(
+            ctypes.byref(geom), _p(page_blk_mean.ptrs), len(page_blk_mean), _p(sel_pages), _p(kblk_mean), _s(stream)))
+        return
     check("hsa_gather_block_means", lib().hsa_gather_block_means(
         ctypes.byref(geom), _table(page_blk_mean), len(page_blk_mean), _p(sel_pages), _p(kblk_mean), _s(stream)))
 
 
 def hsa_linear_branch_paged(geom, q, pages_k, pages_v, sel_pages, e_k, e_v, k_proj, v_proj, o_lin, flags, ws,
                             stream=None):
+    """pages_k, pages_v: lists of laid-out page tensors (host tables) or DeviceTables."""
+    if isinstance(pages_k, DeviceTable):
+        check("hsa_linear_branch_paged_devtab", lib().hsa_linear_branch_paged_devtab(
+            ctypes.byref(geom), _p(q), _p(pages_k.ptrs), _p(pages_v.ptrs), len(pages_k), _p(sel_pages), _p(e_k),
+            _p(e_v), _p(k_proj), _p(v_proj), _p(o_lin), flags, _p(ws),
+            0 if ws is None else ws.numel() * ws.element_size(), _s(stream)))
+        return
     check("hsa_linear_branch_paged", lib().hsa_linear_branch_paged(
         ctypes.byref(geom), _p(q), _table(pages_k), _table(pages_v), len(pages_k), _p(sel_pages), _p(e_k), _p(e_v),
         _p(k_proj), _p(v_proj), _p(o_lin), flags, _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
@@ -208,6 +220,12 @@ def hsa_sparse_attn_paged(geom, q, pages_k, pages_v, sel_pages, blk_count, blk_i
     """events: optional (begin, end) torch.cuda.Event pair (enable_timing=True)
     recorded around the attention kernel alone."""
     handles = _event_handles(events, stream) if events is not None else (None, None)
+    if isinstance(pages_k, DeviceTable):
+        check("hsa_sparse_attn_paged_devtab", lib().hsa_sparse_attn_paged_devtab(
+            ctypes.byref(geom), _p(q), _p(pages_k.ptrs), _p(pages_v.ptrs), len(pages_k), _p(sel_pages),
+            _p(blk_count), _p(blk_idx), _p(o_sp), _p(ws), ws.numel() * ws.element_size(), _s(stream), handles[0],
+            handles[1]))
+        return
     check("hsa_sparse_attn_paged", lib().hsa_sparse_attn_paged(
         ctypes.byref(geom), _p(q), _table(pages_k), _table(pages_v), len(pages_k), _p(sel_pages), _p(blk_count),
         _p(blk_idx), _p(o_sp), _p(ws), ws.numel() * ws.element_size(), _s(stream), handles[0], handles[1]))

@@ -45,6 +45,7 @@ class HsaStep:
         self.sel_pages = self.sel_ext[:s.Kp]
         self._sel_tail_base: Optional[int] = None
         self._chunk_bufs = None
+        self._devtabs = None  # (key, device tables) of the last paged bank
         self.k_act = torch.empty(s.H, s.L, s.d, dtype=dt, device=dev)
         self.v_act = torch.empty(s.H, s.L // 16, s.d, 16, dtype=dt, device=dev)
         self.kblk_mean = torch.empty(s.H, s.nKB, s.d, dtype=f32, device=dev)
@@ -160,12 +161,26 @@ class HsaStep:
                 torch.empty(s.H, s.Lp // 16, s.d, 16, dtype=s.dtype, device=dev),
                 torch.empty(s.H, s.Lp // s.Bk, s.d, dtype=torch.float32, device=dev))
 
-    def paged_inputs(self, prepared, k_cur=None, v_cur=None, stream=None):
+    def paged_inputs(self, prepared, k_cur=None, v_cur=None, stream=None, device_tables: Optional[bool] = None):
         """Page tables and selection list of a paged step.  With intra-chunk
         keys the chunk's own keys and values are laid out into page-format
         buffers (kept from step to step), appended to the tables, and their
-        table indices follow the selected pages in sel_ext.  Returns
+        table indices follow the selected pages in sel_ext.  device_tables:
+        the tables in device memory (built once per bank and kept), which
+        banks beyond HSA_MAX_PAGES need; by default only for those.  Returns
         (k_pages, v_pages, blk_means, sel)."""
+        kp, vp, bm, sel = self._paged_lists(prepared, k_cur, v_cur, stream)
+        if device_tables is None:
+            device_tables = len(kp) > HSA_MAX_PAGES
+        if not device_tables:
+            return kp, vp, bm, sel
+        key = (id(prepared[0]), len(kp))
+        if self._devtabs is None or self._devtabs[0] != key:
+            self._devtabs = (key, (ops.DeviceTable(kp), ops.DeviceTable(vp), ops.DeviceTable(bm)))
+        dk, dv, dm = self._devtabs[1]
+        return dk, dv, dm, sel
+
+    def _paged_lists(self, prepared, k_cur, v_cur, stream):
         kp, vp, bm = prepared
         if not self.n_chunk_pages:
             return kp, vp, bm, self.sel_ext
@@ -182,16 +197,16 @@ class HsaStep:
         return list(kp) + ck, list(vp) + cv, list(bm) + cm, self.sel_ext
 
     def run_paged(self, q, prepared, e_k, e_v, w_g, x, tau, stream=None, concurrent: bool = True,
-                  kernel_events=None, k_cur=None, v_cur=None):
+                  kernel_events=None, k_cur=None, v_cur=None, device_tables: Optional[bool] = None):
         """The step over laid-out pages, with no active-buffer copy: scoring
         from the page index (index_pages ran before), the selected pages' block
         means, the linear branch (side stream) and the sparse branch reading
         the pages in place, then the fusion.  k_cur, v_cur: the chunk's own
         keys and values (geometries with intra-chunk keys), laid out into
-        page-format buffers first."""
+        page-format buffers first.  device_tables: see paged_inputs."""
         main = torch.cuda.current_stream() if stream is None else stream
         self.score(q, None, main, use_cache=True)
-        kp, vp, bm, sel = self.paged_inputs(prepared, k_cur, v_cur, main)
+        kp, vp, bm, sel = self.paged_inputs(prepared, k_cur, v_cur, main, device_tables)
         ops.hsa_gather_block_means(self.geom, bm, sel, self.kblk_mean, main)
         side = self.side if concurrent else main
         if concurrent:

@@ -124,6 +124,21 @@ def test_paged_entry_points_reject_bad_arguments(lib):
     assert gm(ctypes.byref(g), pages, 3, fake, fake, None) == 4
     assert gm(ctypes.byref(g), pages, 200, fake, fake, None) == 4
     assert gm(ctypes.byref(intra), null_pages, 16, fake, fake, None) == 1
+    # the same three over device tables: NULL tables, bank limits
+    big_bank = _lib.HSA_MAX_BANK_PAGES
+    assert lib.hsa_gather_block_means_devtab(ctypes.byref(g), None, 16, fake, fake, None) == 1
+    assert lib.hsa_gather_block_means_devtab(ctypes.byref(g), fake, big_bank + 1, fake, fake, None) == 4
+    assert lib.hsa_gather_block_means_devtab(ctypes.byref(g), fake, 3, fake, fake, None) == 4
+    lpd = lib.hsa_linear_branch_paged_devtab
+    assert lpd(ctypes.byref(g), fake, None, fake, 16, fake, fake, fake, fake, fake, fake, 0, fake, big, None) == 1
+    assert lpd(ctypes.byref(g), fake, fake, fake, big_bank + 1, fake, fake, fake, fake, fake, fake, 0, fake, big,
+               None) == 4
+    assert lpd(ctypes.byref(g), fake, fake, fake, 300, fake, fake, fake, fake, fake, fake, 0, fake, 16, None) == 5
+    spd = lib.hsa_sparse_attn_paged_devtab
+    assert spd(ctypes.byref(g), fake, fake, None, 16, fake, fake, fake, fake, fake, big, None, None, None) == 1
+    assert spd(ctypes.byref(g), fake, fake, fake, big_bank + 1, fake, fake, fake, fake, fake, big, None, None,
+               None) == 4
+    assert spd(ctypes.byref(g), fake, fake, fake, 300, fake, fake, fake, fake, fake, 16, None, None, None) == 5
     # linear branch over pages: NULL pages (unless the projection is reused), counts, flags, workspace
     lp = lib.hsa_linear_branch_paged
     assert lp(ctypes.byref(g), fake, null_pages, pages, 16, fake, fake, fake, fake, fake, fake, 0, fake, big, None) == 1

@@ -200,3 +200,66 @@ def test_paged_intra_history_and_chunk_projections(cfg):
         got[name] = (kh, vh, o)
     for what, a, b in zip(("history K~", "history V~", "O_lin"), got["gathered"], got["paged"]):
         assert torch.equal(a, b), what
+
+
+# Page tables in device memory (the *_devtab calls), which banks beyond
+# HSA_MAX_PAGES need: the same bits as host tables; a 300-page bank read in
+# place equals the gathered step over the same bank; a selected page with no
+# laid-out buffer reads as zeros, as the gather of a missing page writes.
+@pytest.mark.parametrize("cfg", [C0, M1, INTRA[1]], ids=lambda c: c.name)
+def test_paged_device_tables_equal_host_tables(cfg):
+    print(f"\n[paged devtab] config={cfg.name}", flush=True)
+    r = Run(cfg)
+    st = r.step
+    st.index_pages(r.q, r.pk)
+    prepared = st.prepare_pages(r.pk, r.pv)
+    st.run_paged(r.q, prepared, r.e_k, r.e_v, r.w_g, r.x, r.tau, k_cur=r.k_cur, v_cur=r.v_cur, device_tables=False)
+    torch.cuda.synchronize()
+    want = {k: getattr(st, k).clone() for k in NAMES}
+    st.run_paged(r.q, prepared, r.e_k, r.e_v, r.w_g, r.x, r.tau, k_cur=r.k_cur, v_cur=r.v_cur, device_tables=True)
+    torch.cuda.synchronize()
+    for k in NAMES:
+        assert torch.equal(getattr(st, k), want[k]), k
+
+
+def test_paged_bank_of_300_pages():
+    from sparse_linear_attention_hsa_amd.ops import DeviceTable
+    from synth import with_
+    cfg = with_(M1, name="m1_bank300", n_pages=300, seed=2301)
+    print(f"\n[paged devtab] {cfg.name}: {cfg.n_pages} pages read in place", flush=True)
+    r = Run(cfg)
+    st = r.step
+    kt, vt = DeviceTable(r.pk), DeviceTable(r.pv)
+    st.index_pages(r.q, kt)
+    st.run(r.q, kt, vt, r.e_k, r.e_v, r.w_g, r.x, r.tau, indexed=True)
+    torch.cuda.synchronize()
+    want = {k: getattr(st, k).clone() for k in NAMES}
+    prepared = st.prepare_pages(r.pk, r.pv)
+    st.run_paged(r.q, prepared, r.e_k, r.e_v, r.w_g, r.x, r.tau)  # device tables by default beyond 128 pages
+    torch.cuda.synchronize()
+    assert st._devtabs is not None and len(st._devtabs[1][0]) == cfg.n_pages
+    for k in NAMES:
+        assert torch.equal(getattr(st, k), want[k]), k
+
+
+def test_paged_missing_page_reads_as_zeros():
+    from sparse_linear_attention_hsa_amd.ops import DeviceTable
+    cfg = M1
+    r = Run(cfg)
+    st = r.step
+    st.index_pages(r.q, r.pk)  # the index still scores the page, so it is selected
+    r.run(indexed=True)
+    j = int(st.sel_pages[0])
+    print(f"\n[paged devtab] {cfg.name}: selected page {j} without a buffer", flush=True)
+    pk = [None if i == j else t for i, t in enumerate(r.pk)]
+    pv = [None if i == j else t for i, t in enumerate(r.pv)]
+    st.run(r.q, DeviceTable(pk), DeviceTable(pv), r.e_k, r.e_v, r.w_g, r.x, r.tau, indexed=True)
+    torch.cuda.synchronize()
+    assert int(st.sel_pages[0]) == j and not torch.any(st.k_act[:, :cfg.page_tokens].float() != 0)
+    want = {k: getattr(st, k).clone() for k in NAMES}
+    kp, vp, bm = st.prepare_pages(r.pk, r.pv)
+    kp[j] = vp[j] = bm[j] = None
+    st.run_paged(r.q, (kp, vp, bm), r.e_k, r.e_v, r.w_g, r.x, r.tau, device_tables=True)
+    torch.cuda.synchronize()
+    for k in NAMES:
+        assert torch.equal(getattr(st, k), want[k]), k
