@@ -75,3 +75,37 @@ def test_caller_block_lists(cfg):
         h, i = divmod(row, nqb)
         assert np.all(got[i * B:(i + 1) * B, h] == 0.0), f"row {row} has no valid block: zeros"
     assert_close("o_sp", got, want, cfg)
+
+
+@pytest.mark.parametrize("cfg", [M1, M3], ids=lambda c: c.name)
+def test_caller_page_selection_is_clamped(cfg):
+    """A page selection a caller writes, with ids below 0 and past the bank:
+    the gather (host and device page tables) and, over laid-out pages, the
+    block-means gather clamp them to the first and last page, as documented."""
+    from sparse_linear_attention_hsa_amd.ops import DeviceTable
+    r = Run(cfg)
+    st = r.step
+    n, kp = cfg.n_pages, cfg.n_sel_pages
+    raw = [-7, n + 3] + list(range(1, kp - 1))
+    clamped = np.clip(np.array(raw[:kp]), 0, n - 1)
+    sel = torch.tensor(raw[:kp], dtype=torch.int32, device="cuda")
+    print(f"\n[page selection] {cfg.name}: {raw[:kp]} -> pages {clamped.tolist()}", flush=True)
+    want_k = orc.gather_active(r.pk_np, clamped)
+    want_v = orc.gather_active(r.pv_np, clamped)
+    for tables in ((r.pk, r.pv), (DeviceTable(r.pk), DeviceTable(r.pv))):
+        st.k_act.zero_()
+        st.v_act.zero_()
+        if isinstance(tables[0], DeviceTable):
+            ops.hsa_gather_active(st.geom, tables[0], tables[1], sel, None, None, st.k_act, st.v_act, st.kblk_mean)
+        else:
+            ops.hsa_gather_pages(st.geom, tables[0], tables[1], sel, st.k_act, st.v_act, st.kblk_mean)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(st.k_act), want_k)
+        assert np.array_equal(untile_v(host(st.v_act)), want_v)
+    # over laid-out pages: the block means of the same (clamped) pages
+    kblk_gathered = st.kblk_mean.clone()
+    prepared = st.prepare_pages(r.pk, r.pv)
+    st.kblk_mean.zero_()
+    ops.hsa_gather_block_means(st.geom, prepared[2], sel, st.kblk_mean)
+    torch.cuda.synchronize()
+    assert torch.equal(st.kblk_mean, kblk_gathered)
