@@ -66,6 +66,7 @@ struct SparsePlan {
   int max_segs;            // per row
   int max_items;           // rows * max_segs
   int grid;                // launch size (multiple of 8)
+  int bucket_shift;        // items are ordered by (head, middle key block >> bucket_shift)
 };
 SparsePlan sparse_plan(const Dims& s);
 
