@@ -108,9 +108,9 @@ SparsePlan sparse_plan(const Dims& s) {
   p.max_segs = cdiv(s.nKB * p.granules_per_block, sg);
   p.max_items = s.rows * p.max_segs;
   p.grid = cdiv(p.max_items, 8) * 8;
-  // key ranges of 8 blocks or more, and at most 2048 (head, range) buckets
+  // key ranges of 8 blocks or more, and at most kPlanMaxBuckets (head, range) buckets
   p.bucket_shift = 3;
-  while (s.H * cdiv(s.nKB, 1 << p.bucket_shift) > 2048) ++p.bucket_shift;
+  while (s.H * cdiv(s.nKB, 1 << p.bucket_shift) > kPlanMaxBuckets) ++p.bucket_shift;
   return p;
 }
 

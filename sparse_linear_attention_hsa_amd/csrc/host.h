@@ -60,6 +60,10 @@ struct AttendPlan {
 AttendPlan attend_plan(const Dims& s);
 
 // Sparse-branch segmentation of the selected-block rows.
+// (head, key range) buckets the sparse plan kernel orders its work items by
+// (counters in LDS)
+constexpr int kPlanMaxBuckets = 2048;
+
 struct SparsePlan {
   int granules_per_block;  // Bk / 16
   int seg_granules;        // target granules per work item

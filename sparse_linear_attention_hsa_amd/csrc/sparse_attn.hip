@@ -65,7 +65,8 @@ __device__ int scan_incl_1024(int v, int* buf) {
 // rowinfo[row] = {segments, first slot}; meta = {items, slots}.
 constexpr int kMaxPlanRows = HSA_MAX_ROWS;
 constexpr int kMaxPlanSegs = 64;
-constexpr int kMaxPlanKeys = 2048;  // (head, key bucket) pairs
+constexpr int kMaxPlanKeys = kPlanMaxBuckets;  // (head, key bucket) pairs
+static_assert(kMaxPlanKeys <= 2 * kPlanThreads, "the bucket scan takes two entries per thread");
 constexpr int kPlanBatch = 4;       // items per thread whose block-id loads are in flight together
 
 __global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
