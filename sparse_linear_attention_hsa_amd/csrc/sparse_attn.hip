@@ -600,7 +600,10 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
 
 // Merge the partial outputs of split rows (fixed segment order); rows with
 // no selected block get zeros.  kCombParts workgroups share a row, each with
-// a quarter of its columns (more loads in flight across the chip).  The
+// a quarter of its query rows and all their columns, so a wave reads whole
+// 128-byte lines of the half-precision partials.  (Split by columns instead,
+// each workgroup read half of every line, and the four workgroups of a row
+// run on different XCDs, so each line came from memory twice.)  The
 // per-segment weights l_s exp2(m_s - M) / sum_s' l_s' exp2(m_s' - M) (for
 // outputs normalised per segment) go through LDS, then every thread streams
 // its four-column groups once.
@@ -644,10 +647,11 @@ __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
   // segments of all three in flight together; each column still sums its
   // segments in segment order.
   constexpr int U = 3;
-  constexpr int CW = D / 4 / kCombParts;  // four-column groups of this workgroup per row
-  const int total = B * CW;
+  constexpr int CW = D / 4;  // four-column groups per query row
+  const int prow = B / kCombParts;  // query rows of this workgroup
+  const int total = prow * CW;
   const size_t seg_stride = (size_t)B * D;  // elements between the partials of consecutive segments
-  const PartT* base = part_o + (size_t)s0 * B * D + 4 * part * CW;
+  const PartT* base = part_o + (size_t)s0 * B * D + (size_t)part * prow * D;
   for (int e0 = threadIdx.x; e0 < total; e0 += U * kCombThreads) {
     int rr[U];
     bool ok[U];
@@ -658,8 +662,8 @@ __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
       const int e = e0 + u * kCombThreads;
       ok[u] = e < total;
       const int ec = ok[u] ? e : 0;  // clamped: a column past the end reads column 0 and is not stored
-      rr[u] = ec / CW;
-      src[u] = base + (size_t)rr[u] * D + 4 * (ec % CW);
+      rr[u] = part * prow + ec / CW;
+      src[u] = base + (size_t)(ec / CW) * D + 4 * (ec % CW);
       acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     int sg = 0;
@@ -692,7 +696,7 @@ __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
     for (int u = 0; u < U; ++u) {
       if (ok[u]) {
         const int e = e0 + u * kCombThreads;
-        reinterpret_cast<float4*>(o_sp + (((size_t)qb * B + rr[u]) * H + h) * D)[part * CW + e % CW] = acc[u];
+        reinterpret_cast<float4*>(o_sp + (((size_t)qb * B + rr[u]) * H + h) * D)[e % CW] = acc[u];
       }
     }
   }
