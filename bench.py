@@ -27,7 +27,6 @@ Variants (each reports its own line; the default is the headline workload):
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -101,14 +100,12 @@ def measured_peaks():
     return {"mfma_bf16_tflops": round(mfma_tf, 1), "hbm_copy_gbs": round(2 * n / (best * 1e-3) / 1e9, 1)}
 
 
-ATTN_SOURCE = os.path.join(ROOT, "sparse_linear_attention_hsa_amd", "csrc", "sparse_attn.hip")
-
-
 def measured_traffic(workload: str):
     """HBM bytes per launch of the attention kernel from the committed counter
     summary (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by the copy-kernel
     calibration), or None when there is none for this workload or the kernel
-    source has changed since the counters were taken."""
+    source (or the host code that cuts its work items) has changed since the counters
+    were taken."""
     path = os.path.join(ROOT, "profiles", f"sparse_attn_kernel_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -117,9 +114,8 @@ def measured_traffic(workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    with open(ATTN_SOURCE, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
-    if kv.get("source_sha256") != digest:
+    from sparse_linear_attention_hsa_amd.profiling import source_digest
+    if kv.get("source_sha256") != source_digest():
         return None
     try:
         return int(float(kv["traffic_bytes_per_launch"]))

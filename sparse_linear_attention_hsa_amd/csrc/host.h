@@ -63,6 +63,9 @@ AttendPlan attend_plan(const Dims& s);
 // (head, key range) buckets the sparse plan kernel orders its work items by
 // (counters in LDS)
 constexpr int kPlanMaxBuckets = 2048;
+// Segments per row the sparse plan handles (its per-row tables and the merge's
+// LDS are sized for this many).
+constexpr int kPlanMaxSegs = 64;
 
 struct SparsePlan {
   int granules_per_block;  // Bk / 16

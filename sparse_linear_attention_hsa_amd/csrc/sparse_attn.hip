@@ -64,7 +64,7 @@ __device__ int scan_incl_1024(int v, int* buf) {
 // items[k] = {row, first granule, granules, partial slot or -1};
 // rowinfo[row] = {segments, first slot}; meta = {items, slots}.
 constexpr int kMaxPlanRows = HSA_MAX_ROWS;
-constexpr int kMaxPlanSegs = 64;
+constexpr int kMaxPlanSegs = kPlanMaxSegs;
 constexpr int kMaxPlanKeys = kPlanMaxBuckets;  // (head, key bucket) pairs
 static_assert(kMaxPlanKeys <= 2 * kPlanThreads, "the bucket scan takes two entries per thread");
 constexpr int kPlanBatch = 4;       // items per thread whose block-id loads are in flight together

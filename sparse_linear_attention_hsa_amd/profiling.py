@@ -44,6 +44,9 @@ from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ATTN_SOURCE = os.path.join(PKG, "csrc", "sparse_attn.hip")
+# the attention kernel's traffic depends on its source and on the host code
+# that cuts rows into segments (the segment length sets the item order's L2 reuse)
+TRAFFIC_SOURCES = (ATTN_SOURCE, os.path.join(PKG, "csrc", "host.cpp"))
 
 
 def _one(pattern: str) -> str:
@@ -97,8 +100,12 @@ def counter_per_dispatch(pmc_dir: str, counter: str, kernel_regex: str) -> float
 
 
 def source_digest() -> str:
-    with open(ATTN_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 over the sources that fix the attention kernel's traffic, in order."""
+    h = hashlib.sha256()
+    for path in TRAFFIC_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def trace_durations(stats_dir: str, kernel_regex: str):
