@@ -111,7 +111,16 @@ SparsePlan sparse_plan(const Dims& s) {
   p.seg_granules = sg;
   p.max_segs = cdiv(s.nKB * p.granules_per_block, sg);
   p.max_items = s.rows * p.max_segs;
-  p.grid = cdiv(p.max_items, 8) * 8;
+  // Phases of heads: all XCDs run the items of heads_per_phase heads, each
+  // XCD one contiguous range of them, before any starts on the next heads, so
+  // the K/V that the misses of the XCDs' L2s fetch at one time (those heads'
+  // active keys and values) stays within about 128 MB of the 256 MB
+  // last-level cache.
+  const double head_kv_bytes = 2.0 * s.L * s.d * s.esize;
+  p.heads_per_phase = std::max(1, std::min(s.H, (int)(128.0 * (1 << 20) / head_kv_bytes)));
+  const int phases = cdiv(s.H, p.heads_per_phase);
+  // every phase rounds its items up to whole multiples of 8 (one per XCD)
+  p.grid = (cdiv(p.max_items, 8) + phases) * 8;
   // key ranges of 8 blocks or more, and at most kPlanMaxBuckets (head, range) buckets
   p.bucket_shift = 3;
   while (s.H * cdiv(s.nKB, 1 << p.bucket_shift) > kPlanMaxBuckets) ++p.bucket_shift;
@@ -149,7 +158,7 @@ WsLayout ws_layout(const Dims& s, int n_pages) {
   w.sp_items = 0;
   w.sp_rowinfo = align256((size_t)qp.max_items * 16);
   w.sp_meta = align256(w.sp_rowinfo + (size_t)s.rows * 8);
-  w.sp_part_o = align256(w.sp_meta + 64);
+  w.sp_part_o = align256(w.sp_meta + (size_t)kPlanMetaInts * 4);
   w.sp_part_ml = align256(w.sp_part_o + (size_t)qp.max_items * s.B * s.d * 4);
   w.sp_end = align256(w.sp_part_ml + (size_t)qp.max_items * s.B * 2 * 4);
   w.total = std::max(std::max(w.score_end, w.lin_end), std::max(w.sel_end, w.sp_end));

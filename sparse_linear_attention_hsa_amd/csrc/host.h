@@ -74,7 +74,11 @@ struct SparsePlan {
   int max_items;           // rows * max_segs
   int grid;                // launch size (multiple of 8)
   int bucket_shift;        // items are ordered by (head, middle key block >> bucket_shift)
+  int heads_per_phase;     // heads whose items all XCDs run before moving on to the next ones
 };
+// The sparse plan's metadata: {items, partial slots, first item of each head
+// (H + 1 entries, the last = items)}.
+constexpr int kPlanMetaInts = 2 + 32 + 1;
 SparsePlan sparse_plan(const Dims& s);
 
 // Byte offsets inside the caller's workspace; each call uses the regions it

@@ -21,10 +21,12 @@
 //    one query column), an online softmax per query, and O^T += V^T P^T.
 //    Keeping queries on the lane-column axis puts the softmax state and the
 //    output column of a query in the same lane: no cross-lane rescaling.
-//  * XCD-aware item order: items are laid out (head, segment, query block) and
-//    each XCD runs one contiguous range of them, so the workgroups running
-//    together on an XCD read the same head's key/value blocks in the same
-//    order and share them through that XCD's L2.
+//  * XCD-aware item order: items are laid out head by head and, inside a
+//    head, by the key range they cover; each XCD runs one contiguous range of
+//    them, so the workgroups running together on an XCD read the same key and
+//    value blocks and share them through that XCD's L2.  Heads run in phases
+//    (all XCDs on a few heads at a time), so that what the L2 misses fetch
+//    stays within the last-level cache.
 #include "common.h"
 #include "host.h"
 
@@ -181,6 +183,9 @@ __global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
     if (2 * t + 1 < nkeys) off_s[2 * t + 1] = incl - a1;
   }
   __syncthreads();
+  // the first item of every head (and the item count after the last head)
+  const int nheads = rows / nQB;
+  if (t <= nheads) meta[2 + t] = t < nheads ? off_s[t * nb] : n_items;
   // 4) every item to the next place of its bucket
   for (int k0 = t; k0 < n_items; k0 += kPlanBatch * kPlanThreads) {
     int key[kPlanBatch], row[kPlanBatch], sg[kPlanBatch];
@@ -217,6 +222,26 @@ __device__ __forceinline__ float4 load4(const _Float16* p) {
   return make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
 }
 
+// Work item of workgroup bid.  Heads run in phases of heads_per_phase: the
+// XCDs (which receive consecutive workgroup ids round-robin) all take items
+// of one phase, each XCD one contiguous range of them, before the next
+// phase's items.  meta[2 + h] is the first item of head h (meta[2 + H] the
+// item count); -1 for a surplus workgroup.
+__device__ __forceinline__ int phased_remap(int bid, const int* meta, int H, int heads_per_phase) {
+  const int x = bid & 7, k = bid >> 3;
+  int k0 = 0;  // first per-XCD index of the phase
+  for (int h0 = 0; h0 < H; h0 += heads_per_phase) {
+    const int a = meta[2 + h0], b = meta[2 + min(h0 + heads_per_phase, H)];
+    const int per = ceil_div(b - a, 8);
+    if (k < k0 + per) {
+      const int item = a + x * per + (k - k0);
+      return item < b ? item : -1;
+    }
+    k0 += per;
+  }
+  return -1;
+}
+
 // LDS staging of one step (KS keys), written by direct global->LDS loads
 // (each wave instruction writes 1 KB: 64 lanes x 16 bytes, contiguous).
 //  * K: rows of D elements, 16-byte chunks swizzled by kswz (common.h).
@@ -229,7 +254,7 @@ template <typename T, int D, int NW, int QPW, int WPE, int RING, bool FULL, bool
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void sparse_attn_kernel(
     const T* __restrict__ q, const T* __restrict__ k_act, const T* __restrict__ v_act,
     const int32_t* __restrict__ blk_idx, const int4* __restrict__ items, const int* __restrict__ meta,
-    int H, int B, int Bk, int L, int nKB, int nQB, float scale_log2,
+    int H, int B, int Bk, int L, int nKB, int nQB, int heads_per_phase, float scale_log2,
     float* __restrict__ o_sp, typename PartOf<T>::type* __restrict__ part_o, float* __restrict__ part_ml,
     PagedKV<PAGED> pg) {
   constexpr int E = Vec<T>::N;          // elements per 16-byte chunk
@@ -253,7 +278,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE,
   __shared__ __align__(1024) unsigned char lds_k0[KBYTES], lds_k1[KBYTES], lds_k2[RING == 3 ? KBYTES : 16];
   __shared__ __align__(1024) unsigned char lds_v0[VBYTES], lds_v1[VBYTES], lds_v2[RING == 3 ? VBYTES : 16];
 
-  const int item = xcd_remap(blockIdx.x, meta[0]);
+  const int item = phased_remap(blockIdx.x, meta, H, heads_per_phase);
   if (item < 0) return;
   const int4 it = items[item];
   const int row = it.x, g0 = it.y, gcount = it.z, slot = it.w;
@@ -716,12 +741,12 @@ void launch_attn(const Dims& s, const SparsePlan& pl, const void* q, const void*
   if (s.B == 16 * NW * QPW)
     hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE, RING, true, PAGED>), dim3(pl.grid), dim3(NW * kWave),
                        0, st, reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act),
-                       reinterpret_cast<const T*>(v_act), idx, items, meta, s.H, s.B, s.Bk, s.L, s.nKB, s.nQB,
+                       reinterpret_cast<const T*>(v_act), idx, items, meta, s.H, s.B, s.Bk, s.L, s.nKB, s.nQB, pl.heads_per_phase,
                        scale_log2, o_sp, static_cast<PartT*>(po), pml, pg);
   else
   hipLaunchKernelGGL((sparse_attn_kernel<T, D, NW, QPW, WPE, RING, false, PAGED>), dim3(pl.grid), dim3(NW * kWave),
                      0, st, reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k_act),
-                     reinterpret_cast<const T*>(v_act), idx, items, meta, s.H, s.B, s.Bk, s.L, s.nKB, s.nQB,
+                     reinterpret_cast<const T*>(v_act), idx, items, meta, s.H, s.B, s.Bk, s.L, s.nKB, s.nQB, pl.heads_per_phase,
                      scale_log2, o_sp, static_cast<PartT*>(po), pml, pg);
 }
 
