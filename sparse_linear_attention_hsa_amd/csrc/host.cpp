@@ -72,9 +72,12 @@ ProjPlan proj_plan(const Dims& s, int n_tok) {
   const int K = s.bf16 ? 32 : 16;
   p.steps = std::max(1, cdiv(n_tok < 0 ? s.L : n_tok, K));  // stages of one contraction step
   // At most one workgroup (8 waves, two heads, 128 KB of LDS) fits on a CU,
-  // so the items must not exceed the 256 CUs: one item more would run in a
-  // second round and double the kernel's time.
-  p.splits = std::max(1, std::min(p.steps, 256 / (2 * ((s.H + 1) / 2))));
+  // so the items must not exceed the CUs: one item more would run in a
+  // second round and double the kernel's time.  They take at most 224 of the
+  // 256 CUs: the projection runs beside block selection and the start of
+  // the sparse branch, which need CUs of their own (with all 256 the step
+  // was 2-3% slower on the long-row workloads, and no faster otherwise).
+  p.splits = std::max(1, std::min(p.steps, 224 / (2 * ((s.H + 1) / 2))));
   p.rtiles = cdiv(s.r, 16);
   // the linear attention streams the rank axis in chunks of K ranks through
   // a ring of four LDS slots, whole rounds of the ring per pass

@@ -189,4 +189,11 @@ def test_history_and_chunk_projections_add_up(ran):
     ref = ran.oracle(sel_pages=sel)
     assert_close("o_lin", host(st.o_lin), ref["lin"]["o_lin"], cfg)
     f32 = cfg.dtype == "f32"
-    assert_close("o_lin vs one call", host(st.o_lin), host(full), cfg, (1e-5, 1e-6) if f32 else (2e-3, 2e-4))
+    # The two call patterns sum the projection's fp32 slice partials in
+    # different groupings.  For bf16, K~ reaches the products as a bf16 high
+    # part plus the bf16 rounding of the rest (about 16 significant bits), so
+    # a regrouped sum can move K~ by one unit of the low part (2^-17
+    # relative).  With the peaked heads of the imbalance workload that moves a
+    # logit by about 1e-3 and an output element by up to about 6e-3; the
+    # relative-L2 bound stays tight.
+    assert_close("o_lin vs one call", host(st.o_lin), host(full), cfg, (1e-5, 1e-6) if f32 else (1e-2, 2e-4))
