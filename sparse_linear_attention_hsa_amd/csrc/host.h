@@ -77,8 +77,9 @@ struct SparsePlan {
   int heads_per_phase;     // heads whose items all XCDs run before moving on to the next ones
 };
 // The sparse plan's metadata: {items, partial slots, first item of each head
-// (H + 1 entries, the last = items)}.
-constexpr int kPlanMetaInts = 2 + 32 + 1;
+// (H + 1 entries, the last = items), ..., per-XCD item indices in use (the
+// last entry)}.
+constexpr int kPlanMetaInts = 2 + 32 + 1 + 1;
 SparsePlan sparse_plan(const Dims& s);
 
 // Byte offsets inside the caller's workspace; each call uses the regions it

@@ -73,8 +73,8 @@ constexpr int kPlanBatch = 4;       // items per thread whose block-id loads are
 
 __global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
     const int32_t* __restrict__ blk_count, const int32_t* __restrict__ blk_idx, int rows, int nQB, int nKB, int gpb,
-    int gps, int seg_granules, int bucket_shift, int4* __restrict__ items, int2* __restrict__ rowinfo,
-    int* __restrict__ meta) {
+    int gps, int seg_granules, int bucket_shift, int heads_per_phase, int4* __restrict__ items,
+    int2* __restrict__ rowinfo, int* __restrict__ meta) {
   __shared__ short nseg_s[kMaxPlanRows];
   __shared__ int per_s[kMaxPlanRows];
   __shared__ int gran_s[kMaxPlanRows];   // granules of every row
@@ -183,9 +183,20 @@ __global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
     if (2 * t + 1 < nkeys) off_s[2 * t + 1] = incl - a1;
   }
   __syncthreads();
-  // the first item of every head (and the item count after the last head)
+  // the first item of every head (and the item count after the last head),
+  // and how many per-XCD indices the phases use (a workgroup past them has
+  // no item, whatever its phase)
   const int nheads = rows / nQB;
   if (t <= nheads) meta[2 + t] = t < nheads ? off_s[t * nb] : n_items;
+  if (t == 0) {
+    int k_used = 0;
+    for (int h0 = 0; h0 < nheads; h0 += heads_per_phase) {
+      const int hb = min(h0 + heads_per_phase, nheads);
+      k_used += ceil_div((hb < nheads ? off_s[hb * nb] : n_items) - off_s[h0 * nb], 8);
+    }
+    meta[kPlanMetaInts - 1] = k_used;
+  }
+  __syncthreads();  // the head starts are read before step 4 advances off_s
   // 4) every item to the next place of its bucket
   for (int k0 = t; k0 < n_items; k0 += kPlanBatch * kPlanThreads) {
     int key[kPlanBatch], row[kPlanBatch], sg[kPlanBatch];
@@ -229,6 +240,7 @@ __device__ __forceinline__ float4 load4(const _Float16* p) {
 // item count); -1 for a surplus workgroup.
 __device__ __forceinline__ int phased_remap(int bid, const int* meta, int H, int heads_per_phase) {
   const int x = bid & 7, k = bid >> 3;
+  if (k >= meta[kPlanMetaInts - 1]) return -1;  // past every phase: one load, no walk
   int k0 = 0;  // first per-XCD index of the phase
   for (int h0 = 0; h0 < H; h0 += heads_per_phase) {
     const int a = meta[2 + h0], b = meta[2 + min(h0 + heads_per_phase, H)];
@@ -805,7 +817,8 @@ hsa_rc sparse_entry(const Dims& s, const void* q, const void* k_act, const void*
   float* pml = reinterpret_cast<float*>(wsb + w.sp_part_ml);
   const int gps = s.bf16 ? 2 : 1;
   hipLaunchKernelGGL(sparse_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, blk_count, blk_idx, s.rows, s.nQB,
-                     s.nKB, pl.granules_per_block, gps, pl.seg_granules, pl.bucket_shift, items, rowinfo, meta);
+                     s.nKB, pl.granules_per_block, gps, pl.seg_granules, pl.bucket_shift, pl.heads_per_phase, items,
+                     rowinfo, meta);
   if (ev_begin && hipEventRecord(reinterpret_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return HSA_ERR_HIP;
   if (s.bf16) {
     if (s.d == 128) dispatch_attn<bf16_t, 128, PAGED>(s, pl, q, k_act, v_act, blk_idx, items, meta, o_sp, po, pml, pg, st);
